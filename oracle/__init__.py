@@ -1,0 +1,185 @@
+"""Oracle for the tiled dense GEMM (+ReLU): plain fp64 CPU reference.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this package.  It shares no code with the GPU
+library (``dense_tiled_gemm_tile_amd``) and neither imports the other; the
+product path never falls back to it.
+
+The arithmetic lives in ``ref_gemm.c`` (plain C, built with gcc -O2, no
+fast-math): for every requested (m, n) it forms the fp64 sum over k < K of the
+decoded a[m,k] * b[k,n] in ascending k, then alpha times that sum, clamped at
+zero when ReLU is on (Tylo.jl manual, "Walk through GEMM", opening paragraph and
+section 5; cuTile.jl tutorial "Matrix Multiplication", Step 3).  Alongside it
+returns mag[m,n] = sum over k of |alpha * a[m,k] * b[k,n]|, the magnitude that the
+fp32 acceptance bound is stated in.
+
+Storage follows the Tylo manual, section 2: A is (M,K) stored K-contiguous with
+leading stride lda (element m*lda + k), B is (K,N) stored K-contiguous with
+leading stride ldb (element k + n*ldb).  Arrays passed here are the raw storage:
+``uint16`` bit patterns for bf16/fp16, ``float32`` for fp32.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
+forms, exact integer and rational arithmetic, and library decoders.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+BF16, F16, F32 = 1, 2, 3
+_DTYPES = {"bf16": BF16, "f16": F16, "f32": F32}
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "ref_gemm.c"
+_LIB = _HERE / "_build" / "libgemm_oracle.so"
+_lib = None
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def compile_source(src: Path, out: Path) -> Path:
+    """Compile an oracle C source file into a shared library with gcc -O2."""
+    out.parent.mkdir(parents=True, exist_ok=True)
+    tmp = out.with_name(out.name + ".tmp")
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-Wall", "-Wextra", "-o", str(tmp), str(src), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> Path:
+    """Compile the C oracle (always recompiles)."""
+    return compile_source(_SRC, _LIB)
+
+
+def bind(path) -> ctypes.CDLL:
+    """Load a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(str(path))
+    lib.oracle_gemm.argtypes = [_i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                _ptr, _i64, _ptr, _i64, ctypes.c_int,
+                                _i64, _i64, _ptr, _ptr, _i64, ctypes.c_int]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_entries.argtypes = [_i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                        _ptr, _i64, _ptr, _i64, ctypes.c_int,
+                                        _i64, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [_ptr, ctypes.c_int, _i64, _ptr]
+    lib.oracle_decode.restype = ctypes.c_int
+    for name in ("oracle_decode_bf16", "oracle_decode_f16"):
+        getattr(lib, name).argtypes = [ctypes.c_uint16]
+        getattr(lib, name).restype = ctypes.c_double
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+            build()
+        _lib = bind(_LIB)
+    return _lib
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: the process's CPU share, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _code(dtype) -> int:
+    return _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _storage(arr: np.ndarray, dtype: int) -> np.ndarray:
+    want = np.float32 if dtype == F32 else np.uint16
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype != want:
+        raise TypeError(f"storage for dtype {dtype} must be {np.dtype(want)}, got {arr.dtype}")
+    return arr
+
+
+def decode(bits: np.ndarray, dtype, lib=None) -> np.ndarray:
+    """Decode raw storage (uint16 for bf16/fp16, float32 for fp32) to fp64."""
+    dt = _code(dtype)
+    src = _storage(np.asarray(bits), dt)
+    out = np.empty(src.shape, dtype=np.float64)
+    rc = (lib or _load()).oracle_decode(src.ctypes.data, dt, src.size, out.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def gemm(M, N, K, alpha, relu, A, lda, B, ldb, dtype, n0=0, n1=None, threads=None, lib=None):
+    """Columns n0..n1-1 of the oracle result.
+
+    A is the raw storage of A (at least (M-1)*lda + K elements, row-major
+    (M, lda) is the usual shape), B likewise for B ((N, ldb)).  Returns
+    ``(ref, mag)``, both float64 arrays of shape (n1 - n0, M): row j holds
+    output column n0 + j, i.e. the M-contiguous storage of the result.
+    """
+    dt = _code(dtype)
+    n1 = N if n1 is None else n1
+    a = _storage(np.asarray(A), dt)
+    b = _storage(np.asarray(B), dt)
+    cols = max(0, n1 - n0)
+    ref = np.zeros((cols, M), dtype=np.float64)
+    mag = np.zeros((cols, M), dtype=np.float64)
+    rc = (lib or _load()).oracle_gemm(M, N, K, float(alpha), int(bool(relu)),
+                             a.ctypes.data if a.size else None, lda,
+                             b.ctypes.data if b.size else None, ldb, dt,
+                             n0, n1, ref.ctypes.data, mag.ctypes.data, max(M, 1),
+                             threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm failed ({rc})")
+    return ref, mag
+
+
+def gemm_entries(M, N, K, alpha, relu, A, lda, B, ldb, dtype, ms, ns, threads=None, lib=None):
+    """Oracle result at the sampled coordinates (ms[i], ns[i]); returns (ref, mag)."""
+    dt = _code(dtype)
+    a = _storage(np.asarray(A), dt)
+    b = _storage(np.asarray(B), dt)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    if ms.shape != ns.shape:
+        raise ValueError("ms and ns must have the same shape")
+    ref = np.zeros(ms.shape, dtype=np.float64)
+    mag = np.zeros(ms.shape, dtype=np.float64)
+    rc = (lib or _load()).oracle_gemm_entries(M, N, K, float(alpha), int(bool(relu)),
+                                     a.ctypes.data if a.size else None, lda,
+                                     b.ctypes.data if b.size else None, ldb, dt,
+                                     ms.size, ms.ctypes.data, ns.ctypes.data,
+                                     ref.ctypes.data, mag.ctypes.data,
+                                     threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm_entries failed ({rc})")
+    return ref, mag
+
+
+def tolerance(K: int, mag: np.ndarray) -> np.ndarray:
+    """Acceptance bound for an fp32-accumulated result: 4*K*2^-24*mag + 1e-6.
+
+    A K-term fp32 sum carries at most about K unit roundoffs (2^-24) of the
+    summed magnitudes; the factor 4 is slack for the summation tree and the
+    alpha scaling, and 1e-6 is an absolute floor for results near zero.
+    """
+    return 4.0 * K * 2.0 ** -24 * np.asarray(mag, dtype=np.float64) + 1e-6
+
+
+def check(d: np.ndarray, ref: np.ndarray, mag: np.ndarray, K: int):
+    """Return (ok, worst_ratio): |d - ref| <= tolerance elementwise, and max |d-ref|/tol."""
+    d = np.asarray(d, dtype=np.float64)
+    err = np.abs(d - ref)
+    tol = tolerance(K, mag)
+    ratio = float(np.max(err / tol)) if err.size else 0.0
+    ok = bool(np.all(err <= tol)) and not bool(np.any(np.isnan(d)))
+    return ok, ratio

@@ -1,0 +1,233 @@
+/*
+ * Oracle for the tiled dense GEMM D = alpha * A * B with optional ReLU.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load or call this code.  It shares no
+ * code, header, table or helper with the GPU library and must never be used
+ * as a fallback for it.
+ *
+ * What it computes (Tylo.jl manual, "Walk through GEMM", opening paragraph
+ * and section 5 "Apply the epilogue and store by ownership"; cuTile.jl
+ * tutorial "Matrix Multiplication", Step 3 "Looping over K"):
+ *
+ *   S[m,n]   = sum over k < K of a[m,k] * b[k,n]      (fp64, k ascending)
+ *   ref[m,n] = relu ? max(alpha * S[m,n], 0) : alpha * S[m,n]
+ *   mag[m,n] = sum over k < K of |alpha * a[m,k] * b[k,n]|
+ *
+ * The scalar epilogue applies alpha first and then clamps at zero (Tylo
+ * manual section 5).  K = 0 gives the empty sum, so ref = 0 (the pages are
+ * silent on this; the plain reading of an empty sum is taken).
+ *
+ * Storage (Tylo manual section 2 "Bind runtime global arrays"; coordinates
+ * are zero-based): a[m,k] lives at element m*lda + k of A (K-contiguous),
+ * b[k,n] at element k + n*ldb of B (K-contiguous).  The result is written to
+ * ref[(n - n0)*ldr + m], i.e. M-contiguous like the product's own output.
+ *
+ * Element decoding is written here from the format definitions:
+ *   bf16: the 16 stored bits are the upper half of an IEEE binary32;
+ *   fp16: IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 fraction
+ *         bits), subnormals decoded exactly as fraction * 2^-24;
+ *   fp32: IEEE binary32 as stored.
+ * Every decoded value is exactly representable in fp64.
+ *
+ * Built with plain -O2 (no fast-math), so the k order of each sum is kept.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_F32 = 3 };
+
+double oracle_decode_bf16(uint16_t bits) {
+    uint32_t word = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &word, sizeof f);
+    return (double)f;
+}
+
+double oracle_decode_f16(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 10) & 31;
+    int frac = bits & 1023;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);            /* zero and subnormals */
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25); /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+double oracle_decode_f32(uint32_t bits) {
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int elem_size(int dtype) {
+    return dtype == ORACLE_F32 ? 4 : (dtype == ORACLE_BF16 || dtype == ORACLE_F16) ? 2 : 0;
+}
+
+static double decode_at(const void* base, int dtype, int64_t idx) {
+    if (dtype == ORACLE_BF16) return oracle_decode_bf16(((const uint16_t*)base)[idx]);
+    if (dtype == ORACLE_F16) return oracle_decode_f16(((const uint16_t*)base)[idx]);
+    return oracle_decode_f32(((const uint32_t*)base)[idx]);
+}
+
+/* Decode `count` stored elements into fp64 (used by tests of the decoders). */
+int oracle_decode(const void* src, int dtype, int64_t count, double* dst) {
+    if (!elem_size(dtype)) return -5;
+    for (int64_t i = 0; i < count; ++i) dst[i] = decode_at(src, dtype, i);
+    return 0;
+}
+
+/* One output element, straight from the definition. */
+static void one_entry(int64_t m, int64_t n, int64_t K, double alpha, int relu,
+                      const double* arow, const double* bcol, double* out, double* mag) {
+    double s = 0.0, t = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = arow[k] * bcol[k];
+        s += p;
+        t += fabs(p);
+    }
+    (void)m; (void)n;
+    double r = alpha * s;
+    if (relu && r < 0.0) r = 0.0;
+    *out = r;
+    *mag = fabs(alpha) * t;
+}
+
+typedef struct {
+    int64_t M, N, K, lda, ldb, n0, n1, ldr;
+    double alpha;
+    int relu, dtype, nthreads, tid;
+    const double* a;   /* decoded A, row m at a + m*K (NULL when M*K == 0) */
+    const void* B;
+    double* ref;
+    double* mag;
+    /* sampled-entry mode */
+    int64_t count;
+    const int64_t* ms;
+    const int64_t* ns;
+    const void* A;
+} job_t;
+
+static void* full_worker(void* arg) {
+    job_t* j = (job_t*)arg;
+    double* bcol = (double*)malloc(sizeof(double) * (size_t)(j->K > 0 ? j->K : 1));
+    if (!bcol) return (void*)1;
+    /* columns n0 + tid, n0 + tid + nthreads, ...: loop order n -> m -> k */
+    for (int64_t n = j->n0 + j->tid; n < j->n1; n += j->nthreads) {
+        for (int64_t k = 0; k < j->K; ++k) bcol[k] = decode_at(j->B, j->dtype, k + n * j->ldb);
+        for (int64_t m = 0; m < j->M; ++m) {
+            int64_t o = (n - j->n0) * j->ldr + m;
+            one_entry(m, n, j->K, j->alpha, j->relu, j->a + m * j->K, bcol, &j->ref[o], &j->mag[o]);
+        }
+    }
+    free(bcol);
+    return NULL;
+}
+
+static void* entry_worker(void* arg) {
+    job_t* j = (job_t*)arg;
+    size_t kk = (size_t)(j->K > 0 ? j->K : 1);
+    double* arow = (double*)malloc(sizeof(double) * kk);
+    double* bcol = (double*)malloc(sizeof(double) * kk);
+    if (!arow || !bcol) { free(arow); free(bcol); return (void*)1; }
+    for (int64_t i = j->tid; i < j->count; i += j->nthreads) {
+        int64_t m = j->ms[i], n = j->ns[i];
+        for (int64_t k = 0; k < j->K; ++k) {
+            arow[k] = decode_at(j->A, j->dtype, m * j->lda + k);
+            bcol[k] = decode_at(j->B, j->dtype, k + n * j->ldb);
+        }
+        one_entry(m, n, j->K, j->alpha, j->relu, arow, bcol, &j->ref[i], &j->mag[i]);
+    }
+    free(arow);
+    free(bcol);
+    return NULL;
+}
+
+static int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, int dtype) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1)) return -2;
+    if (!elem_size(dtype)) return -5;
+    if (K > 0 && ((M > 0 && !A) || (N > 0 && !B))) return -3;
+    return 0;
+}
+
+static int run_threads(job_t* proto, int nthreads, void* (*fn)(void*)) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    job_t jobs[256];
+    pthread_t th[256];
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].nthreads = nthreads;
+        jobs[t].tid = t;
+    }
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, fn, &jobs[t]) != 0) { rc = -9; break; }
+        ++started;
+    }
+    for (int t = 0; t < started; ++t) {
+        void* ret = NULL;
+        pthread_join(th[t], &ret);
+        if (ret) rc = -9;
+    }
+    return rc;
+}
+
+/*
+ * Full columns n in [n0, n1) of the result, every m < M.
+ * ref and mag are (n1 - n0) columns of ldr >= M doubles each.
+ * Returns 0, or a negative code for bad arguments / allocation failure.
+ */
+int oracle_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                int64_t n0, int64_t n1, double* ref, double* mag, int64_t ldr, int nthreads) {
+    int rc = check_args(M, N, K, A, lda, B, ldb, dtype);
+    if (rc) return rc;
+    if (n0 < 0 || n1 > N || n0 > n1 || ldr < M) return -2;
+    if (M == 0 || n1 == n0) return 0;
+    double* a = NULL;
+    if (K > 0) {
+        a = (double*)malloc(sizeof(double) * (size_t)M * (size_t)K);
+        if (!a) return -9;
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t k = 0; k < K; ++k) a[m * K + k] = decode_at(A, dtype, m * lda + k);
+    }
+    job_t p;
+    memset(&p, 0, sizeof p);
+    p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.n0 = n0; p.n1 = n1; p.ldr = ldr;
+    p.alpha = (double)alpha; p.relu = relu; p.dtype = dtype;
+    p.a = a; p.B = B; p.ref = ref; p.mag = mag;
+    int64_t cols = n1 - n0;
+    rc = run_threads(&p, nthreads > cols ? (int)cols : nthreads, full_worker);
+    free(a);
+    return rc;
+}
+
+/* Sampled entries (ms[i], ns[i]), i < count, into ref[i] and mag[i]. */
+int oracle_gemm_entries(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                        int64_t count, const int64_t* ms, const int64_t* ns,
+                        double* ref, double* mag, int nthreads) {
+    int rc = check_args(M, N, K, A, lda, B, ldb, dtype);
+    if (rc) return rc;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+    if (count == 0) return 0;
+    job_t p;
+    memset(&p, 0, sizeof p);
+    p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb;
+    p.alpha = (double)alpha; p.relu = relu; p.dtype = dtype;
+    p.A = A; p.B = B; p.ref = ref; p.mag = mag;
+    p.count = count; p.ms = ms; p.ns = ns;
+    return run_threads(&p, nthreads > count ? (int)count : nthreads, entry_worker);
+}

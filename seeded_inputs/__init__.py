@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the tiled dense GEMM, shared by the tests, the
+smoke check and the benchmark.
+
+This module only draws numbers and lays them out in storage; it holds none of
+the product's arithmetic, so both the GPU path and the oracle can consume its
+output without sharing any computation.
+
+Storage conventions (Tylo.jl manual, "Walk through GEMM", section 2): A is
+logically (M,K) and stored K-contiguous, so its storage is a row-major
+(M, lda) array whose first K columns hold A; B is logically (K,N) and stored
+K-contiguous, so its storage is a row-major (N, ldb) array whose first K
+columns hold B transposed; D is logically (M,N) stored M-contiguous, i.e. a
+row-major (N, ldd) array whose first M columns hold D transposed.  Padding
+columns of A and B are filled with NaN by default so that any read of them
+shows up in the result.
+
+Distributions are drawn in fp32 with a seeded torch CPU generator and then
+rounded to the operand type (round-to-nearest-even, torch's cast); the rounded
+values are the ground truth.  "normal(0, 1/sqrt(K))" is read as standard
+deviation 1/sqrt(K).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+D_SENTINEL = -7777.0  # value planted in D storage that the product must never write
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One GEMM workload: shapes, strides, operand type, distribution, epilogue."""
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str            # operand type of A and B: "bf16", "f16" or "f32"
+    dist: str             # "uniform_pm1", "uniform_01" or "normal_invsqrtk"
+    alpha: float
+    relu: bool
+    lda: int
+    ldb: int
+    ldd: int
+    seed_a: int
+    seed_b: int
+    notes: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def _w(name, M, N, K, dtype, dist, alpha, relu, seed_base, pad_ab=0, pad_d=0, notes=""):
+    return Workload(name, M, N, K, dtype, dist, alpha, relu,
+                    lda=K + pad_ab, ldb=K + pad_ab, ldd=M + pad_d,
+                    seed_a=seed_base + 1, seed_b=seed_base + 2, notes=notes)
+
+
+# The five measured/parity workloads, in order; the large square comes in both
+# 16-bit operand types.
+WORKLOADS = {
+    "tiny_bounded_65x97x73_bf16": _w("tiny_bounded_65x97x73_bf16", 65, 97, 73, "bf16",
+                                     "uniform_pm1", 1.5, True, 1000,
+                                     notes="bounded tile: every edge ragged, K tail of 9"),
+    "full_tile_1024_bf16": _w("full_tile_1024_bf16", 1024, 1024, 1024, "bf16",
+                              "uniform_pm1", 1.0, False, 2000),
+    "fp32_2048": _w("fp32_2048", 2048, 2048, 2048, "f32", "uniform_01", 1.0, False, 3000),
+    "square_8192_bf16_relu": _w("square_8192_bf16_relu", 8192, 8192, 8192, "bf16",
+                                "normal_invsqrtk", 0.5, True, 4000),
+    "square_8192_f16_relu": _w("square_8192_f16_relu", 8192, 8192, 8192, "f16",
+                               "normal_invsqrtk", 0.5, True, 4010),
+    "ragged_strided_12289x5003x4099_bf16": _w("ragged_strided_12289x5003x4099_bf16",
+                                              12289, 5003, 4099, "bf16", "uniform_pm1",
+                                              2.0, True, 5000, pad_ab=8, pad_d=16,
+                                              notes="lda=ldb=K+8, ldd=M+16"),
+}
+
+
+def _draw(rows: int, cols: int, dist: str, K: int, gen: torch.Generator) -> torch.Tensor:
+    if dist == "uniform_pm1":
+        return torch.rand(rows, cols, generator=gen, dtype=torch.float32) * 2.0 - 1.0
+    if dist == "uniform_01":
+        return torch.rand(rows, cols, generator=gen, dtype=torch.float32)
+    if dist == "normal_invsqrtk":
+        return torch.randn(rows, cols, generator=gen, dtype=torch.float32) * (1.0 / math.sqrt(max(K, 1)))
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def _stored(rows: int, K: int, ld: int, values: torch.Tensor, dtype: str, pad: float) -> torch.Tensor:
+    st = torch.full((rows, ld), pad, dtype=torch.float32).to(TORCH_DTYPES[dtype])
+    if rows and K:
+        st[:, :K] = values.to(TORCH_DTYPES[dtype])
+    return st
+
+
+def operands(M, N, K, dtype, dist, seed_a, seed_b, lda=None, ldb=None, pad=float("nan")):
+    """Seeded storage for A ((M, lda) row-major) and B ((N, ldb) row-major), torch CPU."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ga = torch.Generator().manual_seed(int(seed_a))
+    gb = torch.Generator().manual_seed(int(seed_b))
+    a = _draw(M, K, dist, K, ga)
+    b = _draw(N, K, dist, K, gb)
+    return _stored(M, K, lda, a, dtype, pad), _stored(N, K, ldb, b, dtype, pad)
+
+
+def workload_operands(w: Workload, pad=float("nan")):
+    return operands(w.M, w.N, w.K, w.dtype, w.dist, w.seed_a, w.seed_b, w.lda, w.ldb, pad)
+
+
+def int_operands(M, N, K, dtype, seed, lda=None, ldb=None, lo=-3, hi=3, pad=float("nan")):
+    """Seeded integer-valued storage (values in [lo, hi]) for A and B, torch CPU."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    g = torch.Generator().manual_seed(int(seed))
+    a = torch.randint(lo, hi + 1, (M, K), generator=g).to(torch.float32)
+    b = torch.randint(lo, hi + 1, (N, K), generator=g).to(torch.float32)
+    return _stored(M, K, lda, a, dtype, pad), _stored(N, K, ldb, b, dtype, pad)
+
+
+def out_storage(M, N, ldd=None, sentinel=D_SENTINEL) -> torch.Tensor:
+    """D storage: row-major (N, ldd) fp32 pre-filled with a sentinel."""
+    ldd = M if ldd is None else ldd
+    return torch.full((N, ldd), sentinel, dtype=torch.float32)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage of a CPU tensor as numpy: uint16 for bf16/fp16, float32 for fp32."""
+    t = t.contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+def sample_coords(M, N, count, seed, include_edges=True):
+    """Seeded sample of output coordinates; optionally every entry of the last
+    row band and column band plus the four corners, so ragged edges are
+    always covered."""
+    g = np.random.default_rng(int(seed))
+    ms = g.integers(0, M, size=count, dtype=np.int64)
+    ns = g.integers(0, N, size=count, dtype=np.int64)
+    if include_edges and M and N:
+        em = np.concatenate([np.full(N, M - 1), np.arange(M), [0, 0, M - 1, M - 1]]).astype(np.int64)
+        en = np.concatenate([np.arange(N), np.full(M, N - 1), [0, N - 1, 0, N - 1]]).astype(np.int64)
+        ms = np.concatenate([ms, em])
+        ns = np.concatenate([ns, en])
+    return ms, ns

@@ -1,0 +1,301 @@
+"""Pins for the oracle: what the pages and the mathematics fix, independent of
+the oracle's own formula.
+
+Each pin is a function ``pin_*(lib) -> None`` that raises AssertionError when
+the oracle library ``lib`` is wrong, so the same pins run against the real
+oracle (must pass) and against copies of its source with planted mistakes
+(each must be caught by at least one pin; see ``test_planted_mistakes``).
+
+Pins used:
+  * decoders against the IEEE/bfloat16 format definitions (golden table) and
+    against numpy's float16 and torch's bfloat16 conversions for every bit
+    pattern;
+  * identity and permutation B: the product reduces to a scaled column copy
+    of A (closed form);
+  * rank-1 operands: a[m,k] = u_m w_k, b[k,n] = w_k v_n gives
+    alpha u_m v_n sum_k w_k^2 (closed form);
+  * small-integer operands: exact against numpy's int64 matmul;
+  * tiny shapes: within fp64 rounding of the exact rational result
+    (Python fractions), and against numpy's float64 matmul;
+  * invariants: zero-padding K does not change the result (cuTile.jl
+    tutorial, "Sizes that are not a multiple of the tile shape"), NaN in
+    the stride padding never reaches the result, the alpha-then-clamp order of
+    the scalar epilogue (Tylo.jl manual, "Walk through GEMM", section 5),
+    sampled entries equal the full result, K = 0 gives zeros.
+"""
+from __future__ import annotations
+
+import itertools
+import re
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+
+GOLDEN = Path(__file__).resolve().parent / "golden" / "decode_table.txt"
+
+
+def _bits(t):
+    return si.bits(t)
+
+
+def _full(lib, M, N, K, alpha, relu, A, lda, B, ldb, dt, threads=4):
+    return oracle.gemm(M, N, K, alpha, relu, A, lda, B, ldb, dt, threads=threads, lib=lib)
+
+
+def _exact_values(t: torch.Tensor) -> np.ndarray:
+    """Decoded values through torch's own conversion (independent of the oracle)."""
+    return t.to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------- pins
+
+def pin_decode_golden(lib):
+    for line in GOLDEN.read_text().splitlines():
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        dt, hexbits, num, den = line.split()
+        want = Fraction(int(num), int(den))
+        got = oracle.decode(np.array([int(hexbits, 16)], dtype=np.uint16), dt, lib=lib)[0]
+        assert Fraction(got) == want, (dt, hexbits, got, float(want))
+        if int(hexbits, 16) == 0x8000:
+            assert np.signbit(got)
+
+
+def pin_decode_all_patterns(lib):
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = oracle.decode(pats, "f16", lib=lib)
+    want16 = pats.view(np.float16).astype(np.float64)
+    nan = np.isnan(want16)
+    assert np.array_equal(np.isnan(f16), nan)
+    assert np.array_equal(f16[~nan], want16[~nan])
+    bf = oracle.decode(pats, "bf16", lib=lib)
+    wantbf = torch.from_numpy(pats.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nanb = np.isnan(wantbf)
+    assert np.array_equal(np.isnan(bf), nanb)
+    assert np.array_equal(bf[~nanb], wantbf[~nanb])
+    f32 = np.array([0.0, -1.5, 3.0e-39, 1.0e30, 1.0 / 3.0], dtype=np.float32)
+    assert np.array_equal(oracle.decode(f32, "f32", lib=lib), f32.astype(np.float64))
+
+
+def pin_permutation(lib):
+    """B[k, n] = [k == pi(n)] makes D[:, n] = relu(alpha * A[:, pi(n)]) exactly."""
+    g = torch.Generator().manual_seed(11)
+    for dt, (M, N, K), alpha, relu in [("bf16", (37, 29, 41), 1.5, True),
+                                       ("f16", (20, 33, 33), -2.0, True),
+                                       ("f32", (31, 17, 23), 0.5, False),
+                                       ("bf16", (16, 40, 40), 1.0, False)]:
+        pi = torch.randint(0, K, (N,), generator=g) if N > K else torch.randperm(K, generator=g)[:N]
+        A, _ = si.operands(M, 1, K, dt, "uniform_pm1", 5, 6, lda=K + 3)
+        Bst = torch.zeros(N, K, dtype=si.TORCH_DTYPES[dt])
+        Bst[torch.arange(N), pi] = 1
+        ref, mag = _full(lib, M, N, K, alpha, relu, _bits(A), K + 3, _bits(Bst), K, dt)
+        a = _exact_values(A[:, :K])
+        want = np.float64(np.float32(alpha)) * a[:, pi.numpy()].T  # (N, M)
+        if relu:
+            want = np.maximum(want, 0.0)
+        assert np.array_equal(ref, want), dt
+        assert np.array_equal(mag, np.abs(np.float64(np.float32(alpha)) * a[:, pi.numpy()].T))
+
+
+def pin_identity(lib):
+    M = K = N = 48
+    A, _ = si.operands(M, 1, K, "bf16", "uniform_pm1", 7, 8)
+    eye = torch.eye(K, dtype=torch.bfloat16)
+    ref, _ = _full(lib, M, N, K, 1.0, False, _bits(A), K, _bits(eye), K, "bf16")
+    assert np.array_equal(ref, _exact_values(A).T)
+
+
+def pin_rank1(lib):
+    """a[m,k] = u_m w_k, b[k,n] = w_k v_n: D = relu(alpha u_m v_n sum w_k^2)."""
+    g = torch.Generator().manual_seed(12)
+    for dt, (M, N, K), alpha, relu in [("bf16", (13, 19, 57), 0.5, True),
+                                       ("f16", (24, 9, 31), -1.5, True),
+                                       ("f32", (7, 30, 64), 2.0, False)]:
+        u = torch.randint(-2, 3, (M,), generator=g).double()
+        v = torch.randint(-2, 3, (N,), generator=g).double()
+        w = torch.randint(-3, 4, (K,), generator=g).double()
+        A = (u[:, None] * w[None, :]).to(si.TORCH_DTYPES[dt])
+        Bst = (v[:, None] * w[None, :]).to(si.TORCH_DTYPES[dt])
+        ref, mag = _full(lib, M, N, K, alpha, relu, _bits(A), K, _bits(Bst), K, dt)
+        al = float(np.float32(alpha))
+        want = al * np.outer(v.numpy(), u.numpy()) * float((w * w).sum())
+        if relu:
+            want = np.maximum(want, 0.0)
+        assert np.array_equal(ref, want), dt
+        assert np.array_equal(mag, abs(al) * np.abs(np.outer(v.numpy(), u.numpy())) * float((w * w).sum()))
+
+
+def pin_small_integers(lib):
+    """Integer operands: exact against numpy's int64 matmul, with padded strides."""
+    for dt, (M, N, K), (pa, pb) in [("bf16", (65, 97, 73), (0, 0)), ("f16", (40, 31, 130), (5, 2)),
+                                    ("f32", (33, 50, 77), (3, 9)), ("bf16", (1, 1, 1), (0, 0))]:
+        A, B = si.int_operands(M, N, K, dt, seed=M * N + K, lda=K + pa, ldb=K + pb)
+        ai = A[:, :K].to(torch.float64).numpy().astype(np.int64)
+        bi = B[:, :K].to(torch.float64).numpy().astype(np.int64)
+        for alpha, relu in [(1.0, False), (2.0, True), (-0.5, True)]:
+            ref, mag = _full(lib, M, N, K, alpha, relu, _bits(A), K + pa, _bits(B), K + pb, dt)
+            s = (bi @ ai.T).astype(np.float64)           # (N, M): S[m, n] at [n, m]
+            want = alpha * s
+            if relu:
+                want = np.maximum(want, 0.0)
+            assert np.array_equal(ref, want), (dt, M, N, K, alpha)
+            assert np.array_equal(mag, abs(alpha) * (np.abs(bi) @ np.abs(ai).T).astype(np.float64))
+
+
+def pin_tiny_rational(lib):
+    """Every (M, N, K) in [1..4]^3: within fp64 rounding of the exact rational result."""
+    for dt in ("bf16", "f16", "f32"):
+        for M, N, K in itertools.product(range(1, 5), repeat=3):
+            A, B = si.operands(M, N, K, dt, "uniform_pm1", 100 + M, 200 + N * 7 + K)
+            alpha = 1.25
+            ref, mag = _full(lib, M, N, K, alpha, True, _bits(A), K, _bits(B), K, dt, threads=1)
+            av = _exact_values(A)
+            bv = _exact_values(B)
+            for m in range(M):
+                for n in range(N):
+                    s = sum(Fraction(av[m, k]) * Fraction(bv[n, k]) for k in range(K))
+                    t = sum(abs(Fraction(av[m, k]) * Fraction(bv[n, k])) for k in range(K))
+                    exact = max(Fraction(alpha) * s, Fraction(0))
+                    bound = (K + 1) * Fraction(1, 2 ** 52) * abs(Fraction(alpha)) * t
+                    assert abs(Fraction(ref[n, m]) - exact) <= bound, (dt, M, N, K, m, n)
+                    assert abs(Fraction(mag[n, m]) - abs(Fraction(alpha)) * t) <= bound
+    # and a library matmul in fp64 on a bigger random case
+    M, N, K = 23, 17, 301
+    A, B = si.operands(M, N, K, "f16", "normal_invsqrtk", 1, 2)
+    ref, mag = _full(lib, M, N, K, 1.0, False, _bits(A), K, _bits(B), K, "f16")
+    want = (_exact_values(A) @ _exact_values(B).T).T
+    assert np.all(np.abs(ref - want) <= 1e-13 * (mag + 1e-300))
+
+
+def pin_zero_padded_k(lib):
+    """Appending zero columns along K (and zero padding) leaves the result unchanged."""
+    M, N, K, extra = 30, 21, 45, 19
+    A, B = si.operands(M, N, K, "bf16", "uniform_pm1", 31, 32, lda=K + extra, ldb=K + extra, pad=0.0)
+    ref_a, _ = _full(lib, M, N, K, 1.5, True, _bits(A), K + extra, _bits(B), K + extra, "bf16")
+    ref_b, _ = _full(lib, M, N, K + extra, 1.5, True, _bits(A), K + extra, _bits(B), K + extra, "bf16")
+    assert np.array_equal(ref_a, ref_b)
+
+
+def pin_nan_padding_unread(lib):
+    M, N, K = 19, 26, 37
+    A, B = si.operands(M, N, K, "f16", "uniform_pm1", 41, 42, lda=K + 8, ldb=K + 5)
+    assert torch.isnan(A[:, K:].float()).all() and torch.isnan(B[:, K:].float()).all()
+    ref, mag = _full(lib, M, N, K, 1.0, False, _bits(A), K + 8, _bits(B), K + 5, "f16")
+    Ac, Bc = A[:, :K].contiguous(), B[:, :K].contiguous()
+    ref_c, mag_c = _full(lib, M, N, K, 1.0, False, _bits(Ac), K, _bits(Bc), K, "f16")
+    assert np.isfinite(ref).all()
+    assert np.array_equal(ref, ref_c) and np.array_equal(mag, mag_c)
+
+
+def pin_alpha_then_relu(lib):
+    """relu(alpha * S): a negative alpha flips which entries survive."""
+    A = torch.tensor([[1.0, 2.0], [-3.0, 0.5]], dtype=torch.bfloat16)   # a[m, k]
+    B = torch.tensor([[1.0, 1.0], [2.0, -1.0]], dtype=torch.bfloat16)   # b[k, n] at [n, k]
+    # S[m,n]: S[0,0]=3, S[0,1]=0, S[1,0]=-2.5, S[1,1]=-6.5
+    ref, _ = _full(lib, 2, 2, 2, -2.0, True, _bits(A), 2, _bits(B), 2, "bf16")
+    assert np.array_equal(ref, np.array([[0.0, 5.0], [0.0, 13.0]]))
+    ref, _ = _full(lib, 2, 2, 2, 2.0, True, _bits(A), 2, _bits(B), 2, "bf16")
+    assert np.array_equal(ref, np.array([[6.0, 0.0], [0.0, 0.0]]))
+    ref, _ = _full(lib, 2, 2, 2, -2.0, False, _bits(A), 2, _bits(B), 2, "bf16")
+    assert np.array_equal(ref, np.array([[-6.0, 5.0], [0.0, 13.0]]))
+
+
+def pin_entries_and_column_ranges(lib):
+    M, N, K = 70, 45, 66
+    A, B = si.operands(M, N, K, "bf16", "uniform_pm1", 51, 52, lda=K + 2, ldb=K + 6)
+    ref, mag = _full(lib, M, N, K, 0.75, True, _bits(A), K + 2, _bits(B), K + 6, "bf16")
+    ms, ns = si.sample_coords(M, N, 300, seed=3)
+    er, em = oracle.gemm_entries(M, N, K, 0.75, True, _bits(A), K + 2, _bits(B), K + 6, "bf16",
+                                 ms, ns, threads=3, lib=lib)
+    assert np.array_equal(er, ref[ns, ms]) and np.array_equal(em, mag[ns, ms])
+    part, _ = oracle.gemm(M, N, K, 0.75, True, _bits(A), K + 2, _bits(B), K + 6, "bf16",
+                          n0=10, n1=23, threads=2, lib=lib)
+    assert np.array_equal(part, ref[10:23])
+
+
+def pin_degenerate(lib):
+    A = np.zeros((5, 1), dtype=np.uint16)
+    B = np.zeros((4, 1), dtype=np.uint16)
+    ref, mag = _full(lib, 5, 4, 0, 3.0, False, A, 1, B, 1, "bf16")
+    assert ref.shape == (4, 5) and not ref.any() and not mag.any()
+    ref, _ = _full(lib, 0, 4, 3, 1.0, False, np.zeros(0, np.uint16), 3, np.zeros(12, np.uint16), 3, "bf16")
+    assert ref.shape == (4, 0)
+    with pytest.raises(ValueError):
+        _full(lib, 2, 2, 3, 1.0, False, np.zeros(6, np.uint16), 2, np.zeros(6, np.uint16), 3, "bf16")
+
+
+PINS = [pin_decode_golden, pin_decode_all_patterns, pin_permutation, pin_identity, pin_rank1,
+        pin_small_integers, pin_tiny_rational, pin_zero_padded_k, pin_nan_padding_unread,
+        pin_alpha_then_relu, pin_entries_and_column_ranges, pin_degenerate]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle._load())
+
+
+# ------------------------------------------------------------- planted mistakes
+
+# Each mutation plants a plausible mistake in a copy of the oracle's C source;
+# at least one pin must catch every one of them.
+MUTATIONS = {
+    "drop_last_k": ("for (int64_t k = 0; k < K; ++k) {\n        double p", "for (int64_t k = 0; k + 1 < K; ++k) {\n        double p"),
+    "relu_before_alpha": ("double r = alpha * s;\n    if (relu && r < 0.0) r = 0.0;", "double r = s;\n    if (relu && r < 0.0) r = 0.0;\n    r *= alpha;"),
+    "b_transposed": ("decode_at(j->B, j->dtype, k + n * j->ldb)", "decode_at(j->B, j->dtype, n + k * j->ldb)"),
+    "a_stride_is_k": ("decode_at(A, dtype, m * lda + k)", "decode_at(A, dtype, m * K + k)"),
+    "f16_subnormal_flush": ("v = ldexp((double)frac, -24);", "v = 0.0;"),
+    "f16_bias_off_by_one": ("expo - 25", "expo - 24"),
+    "bf16_wrong_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    "mag_signed": ("t += fabs(p);", "t += p;"),
+    "sign_flip": ("s += p;", "s -= p;"),
+    "relu_inverted": ("if (relu && r < 0.0) r = 0.0;", "if (relu && r > 0.0) r = 0.0;"),
+}
+
+
+def _mutant(tmp_path: Path, name: str):
+    src = (Path(oracle.__file__).parent / "ref_gemm.c").read_text()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, f"mutation {name} no longer matches the oracle source"
+    path = tmp_path / f"mutant_{name}.c"
+    path.write_text(src.replace(old, new))
+    return oracle.bind(oracle.compile_source(path, tmp_path / f"libmutant_{name}.so"))
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes(tmp_path, name):
+    lib = _mutant(tmp_path, name)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name!r}"
+
+
+def test_tolerance_bound_holds_for_fp32_accumulation():
+    """The acceptance bound admits a genuine fp32 accumulation of the same products
+    (sequential fp32 sum in numpy) and rejects a result missing one K-stage."""
+    M, N, K = 16, 16, 2048
+    A, B = si.operands(M, N, K, "bf16", "normal_invsqrtk", 61, 62)
+    ref, mag = oracle.gemm(M, N, K, 0.5, False, _bits(A), K, _bits(B), K, "bf16")
+    a32 = A.float().numpy()
+    b32 = B.float().numpy()
+    acc = np.zeros((N, M), dtype=np.float32)
+    for k in range(K):
+        acc += np.outer(b32[:, k], a32[:, k]).astype(np.float32)
+    d = np.float32(0.5) * acc
+    ok, ratio = oracle.check(d, ref, mag, K)
+    assert ok and ratio < 0.25, ratio
+    # all ones: dropping one 64-wide K stage changes every entry by 64
+    ones = np.full((M, K), 0x3F80, dtype=np.uint16)
+    ref1, mag1 = oracle.gemm(M, N, K, 1.0, False, ones, K, ones[:N], K, "bf16")
+    ok, _ = oracle.check(ref1 - 64.0, ref1, mag1, K)
+    assert not ok
