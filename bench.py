@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled GEMM+ReLU on one MI355X, through the tile_gemm C ABI.
+
+One step = one tile_gemm call on the measured workload (default: M=N=K=8192,
+bf16 operands drawn from normal(0, 1/sqrt(K)), alpha=0.5, ReLU on, fp32 D),
+inputs already resident in HBM.  Prints one JSON line with the throughput in
+TFLOP/s (2MNK/t), the roofline position of the GEMM kernel, a parity check of
+the output against the oracle on the CPU-baseline sample, and the oracle's own
+throughput on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kernel-id ID]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "TFLOP/s (2MNK/t) bf16 GEMM+ReLU at 8192³; % of dense MFMA peak"
+# MI355X dense peaks (no sparsity): 256 CUs at 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+SOURCES = ["dense_tiled_gemm_tile_amd/csrc/gemm_kernels.hip", "dense_tiled_gemm_tile_amd/csrc/tile_math.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, kernel_id: int):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    data = json.loads(TRAFFIC_FILE.read_text())
+    entry = data.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash() or entry.get("kernel_id") != kernel_id:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device copy of known size, run under the counter profiler to scale
+    FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="square_8192_bf16_relu")
+    ap.add_argument("--kernel-id", type=int, default=-1)
+    ap.add_argument("--cpu-cols", type=int, default=256,
+                    help="output columns the CPU-baseline oracle computes (all rows, full K)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM shards into independent column panels, one per GPU, with no exchange)",
+              file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    import torch
+
+    import dense_tiled_gemm_tile_amd as tg
+    import seeded_inputs as si
+
+    w = si.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A_st, B_st = si.workload_operands(w)
+    A, B = A_st.to(dev), B_st.to(dev)
+    D = si.out_storage(w.M, w.N, w.ldd).to(dev)
+    Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
+    plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        tg.gemm(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        tg.gemm(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
+                   "ldd": w.ldd, "alpha": w.alpha, "relu": w.relu, "dist": w.dist,
+                   "kernel_id": plan.kernel_id,
+                   "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic_for(w.name, plan.kernel_id),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+
+        cols = min(args.cpu_cols, w.N)
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        ref, mag = oracle.gemm(w.M, w.N, w.K, w.alpha, w.relu, si.bits(A_st), w.lda, si.bits(B_st), w.ldb,
+                               w.dtype, n0=0, n1=cols, threads=threads)
+        cpu_s = time.perf_counter() - t0
+        cpu_flops = 2.0 * w.M * cols * w.K
+        result["cpu_baseline"] = {
+            "value": round(cpu_flops / cpu_s / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"output columns n < {cols} of the {w.M}x{w.N}x{w.K} workload (all m, full K), "
+                      f"fp64; {cpu_s:.2f} s wall",
+        }
+        d = D[:cols, :w.M].double().cpu().numpy()
+        ok, ratio = oracle.check(d, ref, mag, w.K)
+        result["parity"] = {"entries": int(d.size), "ok": bool(ok and not np.isnan(d).any()),
+                            "worst_err_over_tol": round(ratio, 5)}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+"""Python binding of the tile_gemm C ABI (``include/tile_gemm.h``).
+
+Argument marshalling only: every step of the GEMM runs in the HIP library
+``_lib/libtile_gemm.so``; PyTorch supplies device memory and the stream.  If
+the library is missing this module raises instead of computing anything on
+another path.
+
+Storage conventions (Tylo.jl manual, "Walk through GEMM", section 2): A is
+logically (M,K) stored K-contiguous, B is logically (K,N) stored
+K-contiguous, D is logically (M,N) fp32 stored M-contiguous.  ``gemm`` takes
+torch views with exactly those logical shapes and unit strides along K (A, B)
+and along M (D), e.g. ``A = A_st[:, :K]``, ``B = B_st[:, :K].t()``,
+``D = D_st[:, :M].t()`` for row-major storages A_st (M, lda), B_st (N, ldb),
+D_st (N, ldd).
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "_lib" / "libtile_gemm.so"
+HEADER_PATH = _PKG.parent / "include" / "tile_gemm.h"
+
+BF16, F16, F32 = 1, 2, 3
+DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32}
+
+TG_OK = 0
+STATUS = {0: "TG_OK", -1: "TG_ERR_DIMS", -2: "TG_ERR_LD", -3: "TG_ERR_NULL", -4: "TG_ERR_ALIGN",
+          -5: "TG_ERR_DTYPE", -6: "TG_ERR_ALIAS", -7: "TG_ERR_LAUNCH", -8: "TG_ERR_DEVICE",
+          -9: "TG_ERR_PLAN"}
+
+
+class TileGemmError(RuntimeError):
+    """A tile_gemm entry point returned a nonzero status."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``tile_gemm_plan_info``."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "kernel_id", "dtype", "block_m", "block_n", "block_k", "waves_m", "waves_n",
+        "wave_tile_m", "wave_tile_n", "threads", "stages", "lds_bytes", "acc_per_lane",
+        "load_class", "group_m", "reserved")] + [
+        ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_i64, _ptr, _int, _f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_SIGNATURES = {
+    "tile_gemm": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr]),
+    "tile_gemm_ex": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _int]),
+    "tile_gemm_query_plan": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int,
+                                    ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_kernel_count": (_int, []),
+    "tile_gemm_kernel_info": (_int, [_int, ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_strerror": (ctypes.c_char_p, [_int]),
+    "tile_gemm_abi_version": (_int, []),
+}
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m dense_tiled_gemm_tile_amd.build`")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/tile_gemm.h."""
+    text = re.sub(r"/\*.*?\*/", "", HEADER_PATH.read_text(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tile_gemm\w*)\s*\(", text, flags=re.M)
+
+
+def strerror(code: int) -> str:
+    return load_library().tile_gemm_strerror(code).decode()
+
+
+def _check(code: int) -> int:
+    if code != TG_OK:
+        raise TileGemmError(code, strerror(code))
+    return code
+
+
+# ---------------------------------------------------------------- raw entry points
+
+def tile_gemm(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, stream=None) -> int:
+    """Raw C call; pointers and the stream are integers (device addresses / hipStream_t)."""
+    return load_library().tile_gemm(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd,
+                                     dtype, stream)
+
+
+def tile_gemm_ex(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, stream=None, kernel_id=-1) -> int:
+    return load_library().tile_gemm_ex(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd,
+                                       dtype, stream, kernel_id)
+
+
+def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1) -> PlanInfo:
+    """Host-only plan query; raises TileGemmError on invalid arguments."""
+    info = PlanInfo()
+    _check(load_library().tile_gemm_query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id,
+                                               ctypes.byref(info)))
+    return info
+
+
+def kernel_count() -> int:
+    return load_library().tile_gemm_kernel_count()
+
+
+def kernel_info(kernel_id: int) -> PlanInfo:
+    info = PlanInfo()
+    _check(load_library().tile_gemm_kernel_info(kernel_id, ctypes.byref(info)))
+    return info
+
+
+def abi_version() -> int:
+    return load_library().tile_gemm_abi_version()
+
+
+# ---------------------------------------------------------------- torch views
+
+def _operand_args(A, B, D):
+    import torch
+
+    codes = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
+    if A.dim() != 2 or B.dim() != 2 or D.dim() != 2:
+        raise ValueError("A, B and D must be 2-D views")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(D.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
+    if A.dtype != B.dtype or A.dtype not in codes:
+        raise TypeError(f"A and B must share a dtype in {list(codes)}; got {A.dtype}, {B.dtype}")
+    if D.dtype != torch.float32:
+        raise TypeError("D must be float32")
+    if not (A.is_cuda and B.is_cuda and D.is_cuda):
+        raise ValueError("A, B and D must be device tensors")
+    if (K > 1 and A.stride(1) != 1) or (K > 1 and B.stride(0) != 1) or (M > 1 and D.stride(0) != 1):
+        raise ValueError("A must be K-contiguous, B K-contiguous and D M-contiguous")
+    lda = A.stride(0) if (M > 1 and K > 0) else max(K, 1)
+    ldb = B.stride(1) if (N > 1 and K > 0) else max(K, 1)
+    ldd = D.stride(1) if N > 1 else max(M, 1)
+    return M, N, K, lda, ldb, ldd, codes[A.dtype]
+
+
+def gemm(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, kernel_id: int = -1):
+    """D = alpha*A@B (+ReLU) on the GPU through the C ABI; returns D.
+
+    A: (M,K) view with stride (lda, 1); B: (K,N) view with stride (1, ldb);
+    D: (M,N) float32 view with stride (1, ldd).  The kernel is enqueued on
+    `stream` (a torch.cuda.Stream, default: the current stream of D's device).
+    """
+    import torch
+
+    M, N, K, lda, ldb, ldd, dt = _operand_args(A, B, D)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.device(D.device):
+        _check(tile_gemm_ex(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb,
+                            D.data_ptr(), ldd, dt, stream.cuda_stream, kernel_id))
+    return D
+
+
+def plan_for(A, B, D, kernel_id: int = -1) -> PlanInfo:
+    """The plan ``gemm`` would launch for these views."""
+    M, N, K, lda, ldb, ldd, dt = _operand_args(A, B, D)
+    return query_plan(M, N, K, dt, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd, kernel_id)

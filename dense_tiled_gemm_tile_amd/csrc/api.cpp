@@ -1,0 +1,238 @@
+// C ABI of the tiled GEMM library: argument validation, the host plan chooser
+// and the launch.
+//
+// The plan is chosen on the host from the problem and the operands' alignment
+// (Tylo.jl manual, "Walk through GEMM", section 1: the configuration runs on
+// the host and picks a compiled kernel, while problem sizes and leading
+// strides stay runtime kernel arguments).  The 16-byte vector staging needs
+// every operand row start to be at least 4-byte aligned; the caller's pointers
+// and strides decide the class, and 2-byte aligned rows take the shifting
+// loader (section 3: the caller establishes pointer alignment; the plan must
+// respect it).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kernel_table.h"
+#include "tile_gemm.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxGrid = int64_t(1) << 24;
+constexpr int kCusPerGpu = 256;
+
+int elem_size(int dtype) {
+    switch (dtype) {
+        case TG_BF16:
+        case TG_F16: return 2;
+        case TG_F32: return 4;
+        default: return 0;
+    }
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, const float* D, int64_t ldd, int dtype) {
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TG_ERR_DIMS;
+    const int es = elem_size(dtype);
+    if (!es) return TG_ERR_DTYPE;
+    const int64_t kmin = K > 1 ? K : 1;
+    if (lda < kmin || ldb < kmin || ldd < (M > 1 ? M : 1)) return TG_ERR_LD;
+    if (M == 0 || N == 0) return TG_OK;
+    const bool reads = K > 0;
+    if (!D || (reads && (!A || !B))) return TG_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(D) & 3u) ||
+        (reads && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & uintptr_t(es - 1))))
+        return TG_ERR_ALIGN;
+    if (reads) {
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
+        const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * 4u;
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(A);
+        const uintptr_t a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(B);
+        const uintptr_t b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
+        if (overlaps(d0, d1, a0, a1) || overlaps(d0, d1, b0, b1)) return TG_ERR_ALIAS;
+    }
+    return TG_OK;
+}
+
+// Byte alignment class shared by every operand row start: 16, 4 or 2.
+int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, int64_t ldb, int es) {
+    uintptr_t bits = reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B);
+    if (M > 1) bits |= uintptr_t(lda * es);
+    if (N > 1) bits |= uintptr_t(ldb * es);
+    if ((bits & 15u) == 0) return 16;
+    if ((bits & 3u) == 0) return 4;
+    return 2;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Relative cost of a plan: each CU works through ceil(tiles / CUs) tiles one
+// after another (co-resident workgroups share the CU's MFMA pipes), each tile
+// costing its area divided by the instance's expected MFMA efficiency.
+double plan_cost(const TgKernelDesc& k, int64_t M, int64_t N) {
+    const int64_t tiles = cdiv(M, k.block_m) * cdiv(N, k.block_n);
+    const double eff = (k.block_m * k.block_n >= 256 * 256) ? 1.0 : 0.55;
+    return double(cdiv(tiles, kCusPerGpu)) * double(k.block_m) * double(k.block_n) / eff;
+}
+
+bool usable(const TgKernelDesc& k, int dtype, int cls) { return k.dtype == dtype && cls >= k.load_class; }
+
+int choose(int64_t M, int64_t N, int dtype, int cls) {
+    int best = -1;
+    double best_cost = 0;
+    for (int i = 0; i < tg_kernel_table_size; ++i) {
+        const TgKernelDesc& k = tg_kernel_table[i];
+        if (!usable(k, dtype, cls)) continue;
+        // among instances of one tile shape prefer the widest loader that fits
+        const double c = plan_cost(k, M, N) * (k.load_class >= 4 ? 1.0 : 1.001);
+        if (best < 0 || c < best_cost) { best = i; best_cost = c; }
+    }
+    return best;
+}
+
+void describe(const TgKernelDesc& k, int64_t M, int64_t N, tile_gemm_plan_info* out) {
+    memset(out, 0, sizeof *out);
+    out->kernel_id = k.id;
+    out->dtype = k.dtype;
+    out->block_m = k.block_m;
+    out->block_n = k.block_n;
+    out->block_k = k.block_k;
+    out->waves_m = k.waves_m;
+    out->waves_n = k.waves_n;
+    out->wave_tile_m = k.wave_tile_m;
+    out->wave_tile_n = k.wave_tile_n;
+    out->threads = k.threads;
+    out->stages = k.stages;
+    out->lds_bytes = k.lds_bytes;
+    out->acc_per_lane = k.acc_per_lane;
+    out->load_class = k.load_class;
+    out->group_m = k.group_m;
+    if (M > 0 && N > 0) {
+        out->tiles_m = cdiv(M, k.block_m);
+        out->tiles_n = cdiv(N, k.block_n);
+        out->grid = out->tiles_m * out->tiles_n;
+    }
+}
+
+int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+         int64_t ldb, const float* D, int64_t ldd, int kernel_id, tile_gemm_plan_info* out) {
+    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype);
+    if (rc) return rc;
+    const int es = elem_size(dtype);
+    const int cls = row_class(M, N, A, lda, B, ldb, es);
+    int id = kernel_id;
+    if (id < 0) {
+        id = choose(M, N, dtype, cls);
+        if (id < 0) return TG_ERR_PLAN;
+    } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls)) {
+        return TG_ERR_PLAN;
+    }
+    describe(tg_kernel_table[id], M, N, out);
+    out->load_class = cls;
+    if (out->grid > kMaxGrid) return TG_ERR_DIMS;
+    return TG_OK;
+}
+
+// gfx950 check, cached per device (0 unknown, 1 yes, 2 no).
+std::atomic<int> g_arch_ok[64];
+
+int device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return TG_ERR_DEVICE;
+    }
+    if (dev < 64) {
+        int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (v == 1) return TG_OK;
+        if (v == 2) return TG_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return TG_ERR_DEVICE;
+    }
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? TG_OK : TG_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, const float* D, int64_t ldd, int kernel_id,
+                         tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id, out);
+}
+
+int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
+                 int64_t lda, const void* B, int64_t ldb, float* D, int64_t ldd, int dtype,
+                 void* stream, int kernel_id) {
+    tile_gemm_plan_info pl;
+    int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id, &pl);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return TG_OK;
+    rc = device_ok();
+    if (rc) return rc;
+    const int es = elem_size(dtype);
+    GemmArgs a;
+    a.A = static_cast<const char*>(A);
+    a.B = static_cast<const char*>(B);
+    a.D = D;
+    a.lda_b = lda * es;
+    a.ldb_b = ldb * es;
+    a.ldd = ldd;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.alpha = alpha;
+    a.relu = relu ? 1 : 0;
+    a.tiles_m = static_cast<int>(pl.tiles_m);
+    a.tiles_n = static_cast<int>(pl.tiles_n);
+    a.group_m = pl.group_m;
+    const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+int tile_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+              const void* B, int64_t ldb, float* D, int64_t ldd, int dtype, void* stream) {
+    return tile_gemm_ex(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, stream, -1);
+}
+
+int tile_gemm_kernel_count(void) { return tg_kernel_table_size; }
+
+int tile_gemm_kernel_info(int kernel_id, tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    if (kernel_id < 0 || kernel_id >= tg_kernel_table_size) return TG_ERR_PLAN;
+    describe(tg_kernel_table[kernel_id], 0, 0, out);
+    return TG_OK;
+}
+
+const char* tile_gemm_strerror(int code) {
+    switch (code) {
+        case TG_OK: return "success";
+        case TG_ERR_DIMS: return "invalid dimensions (negative, above 2^30, or grid too large)";
+        case TG_ERR_LD: return "leading stride too small (lda,ldb >= max(1,K); ldd >= max(1,M))";
+        case TG_ERR_NULL: return "null pointer for an operand that is read or written";
+        case TG_ERR_ALIGN: return "pointer not aligned to its element size";
+        case TG_ERR_DTYPE: return "unknown operand dtype";
+        case TG_ERR_ALIAS: return "output overlaps an input operand";
+        case TG_ERR_LAUNCH: return "HIP kernel launch failed";
+        case TG_ERR_DEVICE: return "no current gfx950 HIP device";
+        case TG_ERR_PLAN: return "kernel instance unknown or not valid for these operands";
+        default: return "unknown status";
+    }
+}
+
+int tile_gemm_abi_version(void) { return TILE_GEMM_ABI_VERSION; }
+
+}  // extern "C"

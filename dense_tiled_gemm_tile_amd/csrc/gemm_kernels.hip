@@ -1,0 +1,329 @@
+// Tiled dense GEMM with fused alpha/ReLU epilogue for gfx950 (CDNA4).
+//
+// One workgroup owns one BM x BN output tile (cuTile.jl tutorial "Matrix
+// Multiplication", Step 2: each output tile depends on no other, so each gets
+// its own block) and walks K in stages of 128 bytes per operand row
+// (Step 3: the K loop carries an fp32 accumulator).  Each stage is staged
+// global -> registers -> LDS with 16-byte vectors along logical K for both
+// operands (Tylo.jl manual, "Walk through GEMM", section 3 "Copy one K stage"),
+// double-buffered, and consumed by MFMA instructions reading 16-byte fragments
+// from LDS (section 4).  The epilogue scales by alpha, clamps at zero when
+// ReLU is on, and stores every accumulator at the output coordinate its
+// lane/register ownership gives (section 5).
+//
+// Memory roles (all operands K-contiguous, D M-contiguous):
+//   A storage: BM rows of the tile are A rows m (stride lda bytes lda_b)
+//   B storage: BN rows of the tile are B columns n (stride ldb bytes ldb_b)
+//   MFMA "A" operand <- B rows (n), MFMA "B" operand <- A rows (m), so the
+//   32 lanes of an MFMA output column group walk consecutive m: stores of one
+//   accumulator register write 2 x 128 contiguous bytes of D.
+//
+// LDS layout of one stage: [A: BM rows x 128 B][B: BN rows x 128 B].  Row r
+// keeps its eight 16-byte chunks in swizzled slots, chunk c at slot
+// c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  Any 8 consecutive rows at one
+// logical chunk then hit 8 distinct 16-byte slots modulo 128 bytes, and any 16
+// consecutive rows hit 16 distinct slots modulo 256 bytes, for both the
+// fragment reads (ds_read_b128) and the stage writes (ds_write_b128).
+//
+// Edges: rows beyond M (or N) are clamped to the last valid row; they only feed
+// accumulators that are never stored.  Elements with k >= K are never read and
+// are replaced by exact zeros (the final, partial K stage).  Stores are masked
+// to m < M, n < N.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernel_table.h"
+#include "tile_math.h"
+
+namespace tg {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte vector that only promises 4-byte alignment: still one dwordx4 access.
+typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int kThreads = 256;  // 4 waves
+
+// ---------------------------------------------------------------- loaders
+
+// One 16-byte chunk whose elements all lie below K.
+template <int LOADCLASS>
+__device__ __forceinline__ u32x4 load_chunk(const char* p) {
+    if constexpr (LOADCLASS >= 4) {
+        return *reinterpret_cast<const u32x4_a4*>(p);
+    } else {
+        // 2-byte aligned rows: load the dword-aligned 16 bytes at or below p
+        // plus, when p sits mid-dword, the next dword, then shift by 2 bytes.
+        const uintptr_t sub = reinterpret_cast<uintptr_t>(p) & 2u;
+        const unsigned* q = reinterpret_cast<const unsigned*>(p - sub);
+        u32x4 lo = *reinterpret_cast<const u32x4_a4*>(q);
+        unsigned hi = 0;
+        if (sub) hi = q[4];
+        const unsigned sh = static_cast<unsigned>(sub);
+        u32x4 v;
+        v.x = __builtin_amdgcn_alignbyte(lo.y, lo.x, sh);
+        v.y = __builtin_amdgcn_alignbyte(lo.z, lo.y, sh);
+        v.z = __builtin_amdgcn_alignbyte(lo.w, lo.z, sh);
+        v.w = __builtin_amdgcn_alignbyte(hi, lo.w, sh);
+        return v;
+    }
+}
+
+// A chunk that starts at element k0 of a row and may run past K: each element
+// with k >= K becomes an exact zero and is not read.
+template <int ES>
+__device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int K) {
+    unsigned w[4];
+    if constexpr (ES == 2) {
+        const unsigned short* r = reinterpret_cast<const unsigned short*>(row);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int k = k0 + 2 * d;
+            const unsigned lo = (k < K) ? r[k] : 0u;
+            const unsigned hi = (k + 1 < K) ? r[k + 1] : 0u;
+            w[d] = lo | (hi << 16);
+        }
+    } else {
+        const unsigned* r = reinterpret_cast<const unsigned*>(row);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int k = k0 + d;
+            w[d] = (k < K) ? r[k] : 0u;
+        }
+    }
+    u32x4 v;
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+    return v;
+}
+
+// ---------------------------------------------------------------- MFMA step
+
+// One 128-byte K slab of the (n-block i, m-block j) accumulator: the lane's
+// 16-byte fragments of two consecutive chunks (lanes 0-31 chunk 2q, lanes
+// 32-63 chunk 2q+1) feed the MFMA.  A and B use the same K order, so the sum is
+// the same set of products.
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_slab(u32x4 nfrag, u32x4 mfrag, f32x16 acc) {
+    if constexpr (DT == TG_BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, nfrag), __builtin_bit_cast(bf16x8, mfrag), acc, 0, 0, 0);
+    } else if constexpr (DT == TG_F16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8, nfrag), __builtin_bit_cast(f16x8, mfrag), acc, 0, 0, 0);
+    } else {
+        // fp32: four K=2 MFMAs, element e of each lane's 4-float fragment.
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.x),
+                                                   __builtin_bit_cast(float, mfrag.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.y),
+                                                   __builtin_bit_cast(float, mfrag.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.z),
+                                                   __builtin_bit_cast(float, mfrag.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.w),
+                                                   __builtin_bit_cast(float, mfrag.w), acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// ---------------------------------------------------------------- kernel
+
+template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES>
+__global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
+    constexpr int ES = (DT == TG_F32) ? 4 : 2;  // element bytes
+    constexpr int EPC = 16 / ES;                    // elements per 16-byte chunk
+    constexpr int BKE = kRowBytes / ES;             // K elements per stage
+    constexpr int WTM = BM / 2, WTN = BN / 2;       // 2 x 2 waves
+    constexpr int FM = WTM / 32, FN = WTN / 32;     // 32 x 32 MFMA blocks per wave
+    constexpr int RA = BM / 32, RB = BN / 32;       // staged rows per thread
+    constexpr int STAGE = (BM + BN) * kRowBytes;
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_m = wave & 1, wave_n = wave >> 1;
+
+    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+    const int m0 = tile.tm * BM, n0 = tile.tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    // ---- staging assignment: thread covers chunk column c of rows srow + 32*i
+    const int c = stage_chunk(tid);
+    const int srow = stage_row(tid, 0);
+    // rows srow + 32*i share srow's swizzle, so one offset serves every i
+    const int wslot = lds_chunk_offset(srow, c);
+    const char* arow[RA];
+    const char* brow[RB];
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+        arow[i] = p.A + static_cast<int64_t>(min(m0 + srow + 32 * i, M - 1)) * p.lda_b;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+        brow[i] = p.B + static_cast<int64_t>(min(n0 + srow + 32 * i, N - 1)) * p.ldb_b;
+
+    // ---- fragment read offsets (bytes within a stage)
+    // (wave tile origins and block steps are multiples of 32 rows, which
+    // leave the swizzle unchanged)
+    int mread[4], nread[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        mread[q] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+        nread[q] = (BM + wave_n * WTN) * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+    }
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Full stages 0 .. nfull-1, then (when K is not a multiple of BKE) one
+    // ragged stage whose elements past K load as exact zeros.
+    const int nfull = K / BKE;
+    const int nk = nfull + ((K % BKE) != 0 ? 1 : 0);
+
+    u32x4 sa[RA], sb[RB];
+    auto load_full = [&](int s) {
+        const int kb = s * kRowBytes + c * 16;
+#pragma unroll
+        for (int i = 0; i < RA; ++i) sa[i] = load_chunk<LOADCLASS>(arow[i] + kb);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) sb[i] = load_chunk<LOADCLASS>(brow[i] + kb);
+    };
+    auto load_ragged = [&](int s) {
+        const int k0 = s * BKE + c * EPC;
+#pragma unroll
+        for (int i = 0; i < RA; ++i) sa[i] = load_chunk_bounded<ES>(arow[i], k0, K);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) sb[i] = load_chunk_bounded<ES>(brow[i], k0, K);
+    };
+    auto store_stage = [&](int buf) {
+        char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < RA; ++i)
+            *reinterpret_cast<u32x4*>(base + 32 * i * kRowBytes + wslot) = sa[i];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            *reinterpret_cast<u32x4*>(base + (BM + 32 * i) * kRowBytes + wslot) = sb[i];
+    };
+    // Fragments of slab q come from LDS while the MFMAs of slab q-1 run.
+    auto read_frags = [&](const char* base, int q, u32x4* mf, u32x4* nf) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            mf[j] = *reinterpret_cast<const u32x4*>(base + mread[q] + j * 32 * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            nf[i] = *reinterpret_cast<const u32x4*>(base + nread[q] + i * 32 * kRowBytes);
+    };
+    auto compute = [&](int buf) {
+        const char* base = smem + buf * STAGE;
+        u32x4 mf[2][FM], nf[2][FN];
+        read_frags(base, 0, mf[0], nf[0]);
+        // The scheduling barriers pin the order "reads of slab q+1, then MFMAs
+        // of slab q"; left alone, the scheduler sinks the reads next to their
+        // first use and the MFMA pipe waits on LDS latency.
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q < 3) read_frags(base, q + 1, mf[(q + 1) & 1], nf[(q + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(nf[q & 1][i], mf[q & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Double-buffered pipeline with one barrier per stage: while stage s is
+    // consumed from LDS buffer s&1, stage s+1 travels global -> registers; it
+    // is written to the other buffer only after this wave's MFMAs of stage s
+    // were issued, and the barrier publishes it (and frees buffer s&1).
+    int s = 0;
+    if (nk > 0) {
+        if (nfull > 0) load_full(0); else load_ragged(0);
+        store_stage(0);
+        __syncthreads();
+        for (; s + 1 < nfull; ++s) {
+            load_full(s + 1);
+            __builtin_amdgcn_sched_barrier(0);  // keep the global loads ahead of the MFMAs
+            compute(s & 1);
+            store_stage((s + 1) & 1);
+            __syncthreads();
+        }
+        if (s + 1 < nk) {  // the ragged stage is still to come
+            load_ragged(s + 1);
+            compute(s & 1);
+            store_stage((s + 1) & 1);
+            __syncthreads();
+            ++s;
+        }
+        compute(s & 1);
+    }
+
+    // ---- epilogue: alpha, optional ReLU, store by ownership.
+    // Accumulator register r of lane l in block (i, j) holds
+    //   m = m0 + wave_m*WTM + 32*j + (l & 31)
+    //   n = n0 + wave_n*WTN + 32*i + 8*(r/4) + 4*(l/32) + (r%4).
+    const float alpha = p.alpha;
+    const bool relu = p.relu != 0;
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+            const int nb = n0 + wave_n * WTN + 32 * i;
+            float* col = p.D + m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = nb + acc_row(lane, r);
+                float v = acc[i][j][r] * alpha;
+                if (relu) v = fmaxf(v, 0.0f);
+                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- table
+
+template <int DT, int BM, int BN, int LC, int MW>
+static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, LC, MW>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace tg
+
+// Kernel instances: (id, dtype, BM, BN, minimum row alignment class, minimum
+// waves per SIMD, tile-rows per group).
+#define TG_KERNEL_LIST(X)                   \
+    X(0, TG_BF16, 256, 256, 4, 1, 4)        \
+    X(1, TG_BF16, 256, 256, 2, 1, 4)        \
+    X(2, TG_F16, 256, 256, 4, 1, 4)         \
+    X(3, TG_F16, 256, 256, 2, 1, 4)         \
+    X(4, TG_BF16, 128, 128, 4, 2, 4)        \
+    X(5, TG_BF16, 128, 128, 2, 2, 4)        \
+    X(6, TG_F16, 128, 128, 4, 2, 4)         \
+    X(7, TG_F16, 128, 128, 2, 2, 4)         \
+    X(8, TG_F32, 128, 128, 4, 2, 4)
+
+// Explicit instantiation, seen by both the device and the host pass.
+#define TG_INSTANTIATE(id, DT, BM, BN, LC, MW, GM) \
+    template __global__ void tg::gemm_kernel<DT, BM, BN, LC, MW>(GemmArgs);
+TG_KERNEL_LIST(TG_INSTANTIATE)
+
+// The table holds host launch functions, so it exists only in the host pass.
+#ifndef __HIP_DEVICE_COMPILE__
+#define TG_ENTRY(id, DT, BM, BN, LC, MW, GM)                                                    \
+    { id, DT, BM, BN, (128 / ((DT) == TG_F32 ? 4 : 2)), 2, 2, (BM) / 2, (BN) / 2, 256, 2,       \
+      2 * ((BM) + (BN)) * 128, ((BM) / 2) * ((BN) / 2) / 64, LC, GM, &tg::launch<DT, BM, BN, LC, MW> },
+
+extern "C" const TgKernelDesc tg_kernel_table[] = {TG_KERNEL_LIST(TG_ENTRY)};
+extern "C" const int tg_kernel_table_size = sizeof(tg_kernel_table) / sizeof(tg_kernel_table[0]);
+#endif  // __HIP_DEVICE_COMPILE__

@@ -1,0 +1,42 @@
+// Internal interface between the host plan/ABI layer and the kernel
+// instances: the argument block every GEMM kernel takes and the static table
+// describing each compiled instance.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tile_gemm.h"
+
+struct GemmArgs {
+    const char* A;   // a[m,k] at A + m*lda_b + k*s
+    const char* B;   // b[k,n] at B + n*ldb_b + k*s
+    float* D;        // d[m,n] at D[m + n*ldd]
+    int64_t lda_b;   // A leading stride in bytes
+    int64_t ldb_b;   // B leading stride in bytes
+    int64_t ldd;     // D leading stride in elements
+    int M, N, K;
+    float alpha;
+    int relu;
+    int tiles_m, tiles_n, group_m;
+};
+
+typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, hipStream_t stream);
+
+struct TgKernelDesc {
+    int id;
+    int dtype;         // tile_gemm_dtype
+    int block_m, block_n, block_k;
+    int waves_m, waves_n;
+    int wave_tile_m, wave_tile_n;
+    int threads;
+    int stages;
+    int lds_bytes;
+    int acc_per_lane;
+    int load_class;    // minimum byte alignment of operand row starts (4 or 2)
+    int group_m;
+    TgLaunchFn launch;
+};
+
+extern "C" const TgKernelDesc tg_kernel_table[];
+extern "C" const int tg_kernel_table_size;

@@ -1,0 +1,147 @@
+/*
+ * tile_gemm — tiled dense GEMM with fused alpha/ReLU epilogue for AMD MI355X
+ * (gfx950, CDNA4), C ABI.
+ *
+ * Operation (Tylo.jl manual, "Walk through GEMM": opening paragraph, section 2
+ * "Bind runtime global arrays" and section 5 "Apply the epilogue and store by
+ * ownership"):
+ *
+ *     D = alpha * A * B,  optionally followed by D = max(D, 0)  (ReLU)
+ *
+ * with FP32 accumulation.  All coordinates are zero-based; s is the operand
+ * element size (2 for bf16/fp16, 4 for fp32):
+ *
+ *   A is logically (M,K), stored K-contiguous:  a[m,k] at byte A + (m*lda + k)*s
+ *   B is logically (K,N), stored K-contiguous:  b[k,n] at byte B + (k + n*ldb)*s
+ *   D is logically (M,N), fp32, M-contiguous:   d[m,n] at byte D + (m + n*ldd)*4
+ *
+ * For 0 <= m < M and 0 <= n < N the call writes
+ *
+ *     d[m,n] = relu ? max(alpha * S, 0) : alpha * S,   S = sum_{k<K} a[m,k]*b[k,n]
+ *
+ * (alpha is applied to the fp32 accumulator, then the clamp).  No other byte
+ * of D is written: the padding rows m >= M of each D column are left alone.
+ * There is no beta; prior contents of D are irrelevant.  K = 0 writes zeros;
+ * M = 0 or N = 0 is a no-op.  Ragged edges are handled inside the kernel:
+ * operand elements with k >= K are never read and contribute exactly zero
+ * (cuTile.jl tutorial "Matrix Multiplication", section "Sizes that are not a
+ * multiple of the tile shape").
+ *
+ * Ownership: A, B and D are device pointers owned by the caller and only
+ * borrowed for the duration of the enqueued kernel.  The library allocates no
+ * device memory, keeps no pointer after the call returns and does not
+ * synchronise: the kernel is enqueued on `stream` (a hipStream_t; NULL means
+ * the default stream) and the call returns after the enqueue.  D must not
+ * overlap A or B.  Calls are thread-safe.
+ *
+ * Alignment: pointers must be aligned to their element size.  Nothing
+ * stronger is required: rows whose byte offsets are not 16-byte aligned (odd
+ * lda/ldb) take a narrower load path automatically.
+ *
+ * Errors: every entry point returns 0 on success or one of the negative
+ * tile_gemm_status codes below; no exception or abort crosses the ABI.
+ * Argument validation happens before any HIP call, so invalid arguments are
+ * reported even on a machine without a GPU.
+ */
+#ifndef TILE_GEMM_H
+#define TILE_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Operand element type of A and B.  D is always fp32. */
+enum tile_gemm_dtype {
+    TG_BF16 = 1, /* bfloat16 operands, bf16 MFMA */
+    TG_F16 = 2,  /* IEEE binary16 operands, fp16 MFMA */
+    TG_F32 = 3   /* IEEE binary32 operands, fp32 MFMA (full fp32 products) */
+};
+
+enum tile_gemm_status {
+    TG_OK = 0,
+    TG_ERR_DIMS = -1,   /* M, N or K negative or above 2^30, or more than 2^24 tiles */
+    TG_ERR_LD = -2,     /* lda < max(1,K), ldb < max(1,K) or ldd < max(1,M) */
+    TG_ERR_NULL = -3,   /* NULL pointer for an operand that is read or written */
+    TG_ERR_ALIGN = -4,  /* pointer not aligned to its element size */
+    TG_ERR_DTYPE = -5,  /* dtype not one of tile_gemm_dtype */
+    TG_ERR_ALIAS = -6,  /* D's byte range overlaps A's or B's */
+    TG_ERR_LAUNCH = -7, /* the HIP launch failed (hipGetLastError) */
+    TG_ERR_DEVICE = -8, /* no current HIP device, or it is not gfx950 */
+    TG_ERR_PLAN = -9    /* requested kernel id unknown or not valid for the call */
+};
+
+/* The host plan for one call (what the kernel will be launched with). */
+typedef struct tile_gemm_plan_info {
+    int32_t kernel_id;     /* index of the compiled kernel instance */
+    int32_t dtype;         /* tile_gemm_dtype */
+    int32_t block_m;       /* macro-tile extent along m (A rows) */
+    int32_t block_n;       /* macro-tile extent along n (B columns) */
+    int32_t block_k;       /* K elements staged per pipeline stage */
+    int32_t waves_m;       /* wave grid of one workgroup */
+    int32_t waves_n;
+    int32_t wave_tile_m;   /* output extent owned by one wave */
+    int32_t wave_tile_n;
+    int32_t threads;       /* threads per workgroup (64 per wave) */
+    int32_t stages;        /* LDS buffering stages */
+    int32_t lds_bytes;     /* static LDS per workgroup */
+    int32_t acc_per_lane;  /* fp32 accumulators held by each lane */
+    int32_t load_class;    /* 16, 4 or 2: byte alignment of every operand row start */
+    int32_t group_m;       /* tile-rows per group in the grouped tile order */
+    int32_t reserved;
+    int64_t tiles_m;       /* ceil(M / block_m) */
+    int64_t tiles_n;       /* ceil(N / block_n) */
+    int64_t grid;          /* workgroups launched = tiles_m * tiles_n */
+} tile_gemm_plan_info;
+
+/*
+ * D = alpha*A*B (+ReLU if relu != 0), fp32 accumulation, enqueued on `stream`.
+ * M, N, K: problem sizes (>= 0).  lda, ldb: operand leading strides in
+ * elements (>= max(1,K)); ldd: output leading stride in elements (>= max(1,M)).
+ * dtype: tile_gemm_dtype of A and B.  Returns TG_OK or a tile_gemm_status.
+ */
+int tile_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+              const void* A, int64_t lda, const void* B, int64_t ldb,
+              float* D, int64_t ldd, int dtype, void* stream);
+
+/*
+ * As tile_gemm, but with an explicit kernel instance (kernel_id from
+ * tile_gemm_query_plan or tile_gemm_kernel_count; -1 = the automatic
+ * choice).  For tests and tuning: every instance computes the same result.
+ * Returns TG_ERR_PLAN if the instance does not exist, has another dtype, or
+ * needs a stronger row alignment than the operands have.
+ */
+int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                 const void* A, int64_t lda, const void* B, int64_t ldb,
+                 float* D, int64_t ldd, int dtype, void* stream, int kernel_id);
+
+/*
+ * Host-only: validate the arguments exactly as tile_gemm does and describe the
+ * plan it would launch (no HIP call is made; pointers are only inspected for
+ * alignment and overlap).  kernel_id -1 = automatic choice.
+ */
+int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype,
+                         const void* A, int64_t lda, const void* B, int64_t ldb,
+                         const float* D, int64_t ldd, int kernel_id,
+                         tile_gemm_plan_info* out);
+
+/* Number of compiled kernel instances (valid kernel ids are 0 .. count-1). */
+int tile_gemm_kernel_count(void);
+
+/* Static description of kernel instance `kernel_id` (grid fields are 0). */
+int tile_gemm_kernel_info(int kernel_id, tile_gemm_plan_info* out);
+
+/* Static string for a status code ("unknown status" for codes not listed). */
+const char* tile_gemm_strerror(int code);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int tile_gemm_abi_version(void);
+
+#define TILE_GEMM_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILE_GEMM_H */

@@ -1,0 +1,127 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/tile_gemm.h declares, validates arguments with the documented
+status codes before touching HIP, and plans every benchmark workload the way
+the kernels require."""
+import ctypes
+import json
+from pathlib import Path
+
+import pytest
+
+import dense_tiled_gemm_tile_amd as tg
+import seeded_inputs as si
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def test_library_exports_every_declared_function():
+    lib = tg.load_library()
+    declared = tg.header_functions()
+    assert {"tile_gemm", "tile_gemm_query_plan", "tile_gemm_strerror"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert tg.abi_version() == 1
+
+
+def test_strerror_covers_every_status():
+    for code, name in tg.STATUS.items():
+        msg = tg.strerror(code)
+        assert msg and msg != "unknown status", name
+    assert tg.strerror(-1234) == "unknown status"
+
+
+# fake but well-aligned device addresses: validation only inspects them
+A, B, D = 0x7F0000000000, 0x7F0010000000, 0x7F0020000000
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(M=-1), -1), (dict(N=-5), -1), (dict(K=-1), -1), (dict(M=(1 << 30) + 1), -1),
+    (dict(lda=63), -2), (dict(ldb=10), -2), (dict(ldd=63), -2),
+    (dict(A=0), -3), (dict(B=0), -3), (dict(D=0), -3),
+    (dict(A=A + 1), -4), (dict(D=D + 2), -4), (dict(dtype=3, B=B + 2), -4),
+    (dict(dtype=0), -5), (dict(dtype=7), -5),
+    (dict(D=A + 64), -6), (dict(D=B - 16), -6),
+])
+def test_validation_codes(args, code):
+    p = dict(M=64, N=48, K=64, alpha=1.0, relu=0, A=A, lda=64, B=B, ldb=64, D=D, ldd=64, dtype=1)
+    p.update(args)
+    rc = tg.tile_gemm(p["M"], p["N"], p["K"], p["alpha"], p["relu"], p["A"], p["lda"], p["B"],
+                      p["ldb"], p["D"], p["ldd"], p["dtype"], None)
+    assert rc == code, tg.STATUS.get(rc, rc)
+    info = tg.PlanInfo()
+    rc2 = tg.load_library().tile_gemm_query_plan(p["M"], p["N"], p["K"], p["dtype"], p["A"], p["lda"],
+                                                 p["B"], p["ldb"], p["D"], p["ldd"], -1, ctypes.byref(info))
+    assert rc2 == code
+
+
+def test_degenerate_shapes_need_no_operands():
+    # M = 0 or N = 0: no-op, nothing is read or written, no device needed
+    assert tg.tile_gemm(0, 5, 7, 1.0, 0, 0, 7, 0, 7, 0, 1, 1, None) == 0
+    assert tg.tile_gemm(5, 0, 7, 1.0, 0, 0, 7, 0, 7, 0, 5, 1, None) == 0
+    # K = 0: A and B are not read, so they may be NULL; D still required
+    assert tg.query_plan(5, 4, 0, 1, 0, 1, 0, 1, D, 5).grid == 1
+    with pytest.raises(tg.TileGemmError):
+        tg.query_plan(5, 4, 0, 1, 0, 1, 0, 1, 0, 5)
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert tg.tile_gemm(64, 48, 64, 1.0, 0, A, 64, B, 64, D, 64, 1, None) == -8
+
+
+def _plan(w: si.Workload, a=A, b=B, d=D, kernel_id=-1):
+    return tg.query_plan(w.M, w.N, w.K, tg.DTYPE_CODES[w.dtype], a, w.lda, b, w.ldb, d, w.ldd, kernel_id)
+
+
+def test_plans_for_the_workloads():
+    W = si.WORKLOADS
+    big = _plan(W["square_8192_bf16_relu"])
+    assert (big.block_m, big.block_n, big.load_class, big.grid) == (256, 256, 16, 1024)
+    assert big.acc_per_lane == 256 and big.lds_bytes == 131072
+    assert _plan(W["square_8192_f16_relu"]).dtype == tg.F16
+    ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
+    assert ragged.load_class == 2 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
+    tiny = _plan(W["tiny_bounded_65x97x73_bf16"])
+    assert tiny.load_class == 2 and tiny.grid == 1
+    mid = _plan(W["full_tile_1024_bf16"])
+    assert (mid.block_m, mid.block_n, mid.grid) == (128, 128, 64)
+    f32 = _plan(W["fp32_2048"])
+    assert f32.dtype == tg.F32 and f32.grid == 256 and f32.block_k == 32
+
+
+def test_plan_alignment_classes_and_forced_instances():
+    W = si.WORKLOADS["square_8192_bf16_relu"]
+    assert _plan(W, a=A + 4).load_class == 4
+    assert _plan(W, b=B + 2).load_class == 2
+    # a 2-byte aligned operand cannot run an instance that needs 4-byte rows
+    narrow = [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 4
+              and tg.kernel_info(k).dtype == tg.BF16]
+    with pytest.raises(tg.TileGemmError) as e:
+        _plan(W, b=B + 2, kernel_id=narrow[0])
+    assert e.value.code == -9
+    with pytest.raises(tg.TileGemmError):
+        _plan(W, kernel_id=tg.kernel_count())
+
+
+def test_every_instance_has_consistent_ownership_arithmetic():
+    """acc/lane * threads == tile size, as in the worked plan of the Tylo manual
+    (golden/tylo_plan_example.json): 32 accumulators x 128 threads own 64x64."""
+    ex = json.loads((GOLDEN / "tylo_plan_example.json").read_text())
+    tm, tn, _ = ex["tile_mnk"]
+    assert ex["acc_per_thread"] * ex["threads"] == tm * tn
+    assert ex["threads"] == 32 * ex["warps"][0] * ex["warps"][1]
+    atom_m, atom_n, _ = ex["atom_mnk"]
+    assert ex["warps"][0] * ex["reps"][0] * atom_m == tm and ex["warps"][1] * ex["reps"][1] * atom_n == tn
+    for k in range(tg.kernel_count()):
+        info = tg.kernel_info(k)
+        assert info.kernel_id == k
+        assert info.acc_per_lane * info.threads == info.block_m * info.block_n
+        assert info.threads == 64 * info.waves_m * info.waves_n
+        assert info.wave_tile_m * info.waves_m == info.block_m
+        assert info.wave_tile_n * info.waves_n == info.block_n
+        es = 4 if info.dtype == tg.F32 else 2
+        assert info.block_k * es == 128
+        assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * 128
+        assert info.lds_bytes <= 160 * 1024
