@@ -68,7 +68,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square_8192_bf16_relu")
     ap.add_argument("--kernel-id", type=int, default=-1)
-    ap.add_argument("--cpu-cols", type=int, default=256,
+    ap.add_argument("--cpu-cols", type=int, default=512,
                     help="output columns the CPU-baseline oracle computes (all rows, full K)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

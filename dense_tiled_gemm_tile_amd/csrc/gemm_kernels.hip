@@ -38,6 +38,7 @@
 namespace tg {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -114,14 +115,14 @@ __device__ __forceinline__ f32x16 mfma_slab(u32x4 nfrag, u32x4 mfrag, f32x16 acc
             __builtin_bit_cast(f16x8, nfrag), __builtin_bit_cast(f16x8, mfrag), acc, 0, 0, 0);
     } else {
         // fp32: four K=2 MFMAs, element e of each lane's 4-float fragment.
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.x),
-                                                   __builtin_bit_cast(float, mfrag.x), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.y),
-                                                   __builtin_bit_cast(float, mfrag.y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.z),
-                                                   __builtin_bit_cast(float, mfrag.z), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, nfrag.w),
-                                                   __builtin_bit_cast(float, mfrag.w), acc, 0, 0, 0);
+        // (Cast the whole vector: a bit-cast of a single vector element
+        // lvalue reads element 0 with this compiler.)
+        const f32x4 nv = __builtin_bit_cast(f32x4, nfrag);
+        const f32x4 mv = __builtin_bit_cast(f32x4, mfrag);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(nv.x, mv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(nv.y, mv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(nv.z, mv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(nv.w, mv.w, acc, 0, 0, 0);
         return acc;
     }
 }

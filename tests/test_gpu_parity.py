@@ -125,9 +125,14 @@ def test_every_kernel_instance(kid):
     M, N = 2 * info.block_m + 37, 2 * info.block_n + 11
     K = 3 * info.block_k + 9
     es = 4 if dt == "f32" else 2
-    # lda*es = 4 mod 16 (class 4) or odd element stride (class 2)
-    pad = 1 if info.load_class == 2 else (2 if es == 2 else 1)
-    lda, ldb = K + pad, K + pad + (4 if es == 2 else 0)
+    # narrowest accepted row alignment: odd element strides for class 2,
+    # strides with lda*es = 4 (mod 16) for class 4
+    if info.load_class == 2:
+        lda, ldb = K + 2, K + 4  # K is odd here
+    else:
+        lda = K + (2 - K) % 8 if es == 2 else K + (1 - K) % 4
+        ldb = lda + 8 if es == 2 else lda + 4
+    assert (lda * es) % 16 in ((4, 12) if info.load_class == 4 else (2, 6, 10, 14))
     _log(f"[instance {kid}] {dt} {info.block_m}x{info.block_n} class {info.load_class}: {M}x{N}x{K} lda={lda} ldb={ldb}")
     A_st, B_st = si.int_operands(M, N, K, dt, seed=kid, lda=lda, ldb=ldb)
     D_st = run(A_st, B_st, M, N, K, -1.5, True, M + 3, kernel_id=kid)
@@ -223,7 +228,8 @@ def test_degenerate_shapes():
     assert bool((D[:, :37] == 0).all()) and bool((D[:, 37:] == si.D_SENTINEL).all())
     # M = 0 / N = 0: nothing written
     D = si.out_storage(8, 8).to(dev)
-    A, B = torch.ones(8, 8, dtype=torch.float16, device=dev), torch.ones(8, 8, dtype=torch.float16, device=dev)
+    A = torch.ones(8, 8, dtype=torch.float16, device=dev)
+    B = torch.ones(8, 8, dtype=torch.float16, device=dev).t()  # (K, N), K-contiguous
     tg.gemm(A[:0], B, D[:, :0].t(), 1.0, False)
     tg.gemm(A, B[:, :0], D[:0, :].t(), 1.0, False)
     torch.cuda.synchronize()
