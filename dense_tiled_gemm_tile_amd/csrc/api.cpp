@@ -77,8 +77,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // costing its area divided by the instance's expected MFMA efficiency.
 double plan_cost(const TgKernelDesc& k, int64_t M, int64_t N) {
     const int64_t tiles = cdiv(M, k.block_m) * cdiv(N, k.block_n);
-    const double eff = (k.block_m * k.block_n >= 256 * 256) ? 1.0 : 0.55;
-    return double(cdiv(tiles, kCusPerGpu)) * double(k.block_m) * double(k.block_n) / eff;
+    return double(cdiv(tiles, kCusPerGpu)) * double(k.block_m) * double(k.block_n) / (0.01 * k.eff_pct);
 }
 
 bool usable(const TgKernelDesc& k, int dtype, int cls) { return k.dtype == dtype && cls >= k.load_class; }
@@ -89,8 +88,8 @@ int choose(int64_t M, int64_t N, int dtype, int cls) {
     for (int i = 0; i < tg_kernel_table_size; ++i) {
         const TgKernelDesc& k = tg_kernel_table[i];
         if (!usable(k, dtype, cls)) continue;
-        // among instances of one tile shape prefer the widest loader that fits
-        const double c = plan_cost(k, M, N) * (k.load_class >= 4 ? 1.0 : 1.001);
+        // among equal costs prefer the instance that needs the strongest alignment
+        const double c = plan_cost(k, M, N) * (1.0 + 0.001 / k.load_class);
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
     }
     return best;

@@ -290,6 +290,242 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------- streaming kernel
+//
+// For operands whose rows are 16-byte aligned: stages of 64 bytes of K per row
+// go global -> LDS directly (gfx950 LDS-DMA, one 16-byte vector per lane per
+// instruction, no register staging), S stages deep, so each copy is issued
+// about S-2 stages before its data is consumed.  Per stage, each wave runs two
+// slabs of MFMAs; the LDS reads of the next slab and the copies of a future
+// stage are issued one per MFMA so that the MFMA pipe never waits for them.
+// One barrier per stage, between the two slabs, both publishes stage s+1
+// (every wave waited for its own copies first) and frees the buffer of stage
+// s-1 for the copies issued right after it.
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 64 lanes x 16 bytes from per-lane global addresses to LDS bytes
+// [lds, lds + 1024), lane t at lds + 16*t.  Inline assembly keeps the
+// compiler's wait-count pass from serialising every later LDS read behind the
+// copy; completion is tracked with wait_vm below.
+__device__ __forceinline__ void dma16(const void* g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Workgroup barrier without the LDS fence of __syncthreads(): the streaming
+// pipeline orders its LDS traffic explicitly (copies by wait_vm, fragment reads
+// by the waits in front of the MFMAs that consume them), so waiting for every
+// in-flight fragment read here would only stall the MFMA pipe.  The memory
+// clobber keeps the compiler from moving LDS reads across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+// The MFMAs of one slab in (n-block, m-block) order; after MFMA m the side
+// operations k in [ceil(m*T/MF), ceil((m+1)*T/MF)) are issued, and a
+// scheduling barrier keeps the compiler from regrouping them.
+template <int DT, int FM, int FN, int T, typename Side>
+__device__ __forceinline__ void slab_with_side(f32x16 (&acc)[FN][FM], const u32x4 (&fa)[FM],
+                                               const u32x4 (&fb)[FN], Side&& side) {
+    constexpr int MF = FM * FN;
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+        const int i = m / FM, j = m % FM;
+        acc[i][j] = mfma_slab<DT>(fb[i], fa[j], acc[i][j]);
+#pragma unroll
+        for (int k = (m * T + MF - 1) / MF; k < ((m + 1) * T + MF - 1) / MF; ++k) side(k);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int DT, int BM, int BN, int S>
+__global__ __launch_bounds__(kThreads, 1) void gemm_stream_kernel(GemmArgs p) {
+    constexpr int ES = (DT == TG_F32) ? 4 : 2;
+    constexpr int EPC = 16 / ES;
+    constexpr int BKE = kRow64Bytes / ES;       // K elements per stage
+    constexpr int WTM = BM / 2, WTN = BN / 2;   // 2 x 2 waves
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NA = BM / 64, NB = BN / 64;   // 1 KiB copies per wave per stage
+    constexpr int PER = NA + NB;
+    constexpr int NR = FM + FN;                 // fragment reads per slab
+    constexpr int STAGE = (BM + BN) * kRow64Bytes;
+    static_assert(FM == FN, "square wave tiles");
+    static_assert(S >= 3, "at least one stage in flight beyond the next");
+
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wave_m = wave & 1, wave_n = wave >> 1;
+
+    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+    const int m0 = tile.tm * BM, n0 = tile.tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const unsigned lds_base = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char*)(smem))));
+
+    // ---- copy sources (rows past M or N clamp to the last row: their
+    // products only reach accumulators that are never stored)
+    const char* asrc[NA];
+    const char* bsrc[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int j = wave * NA + i;
+        asrc[i] = p.A + static_cast<int64_t>(min(m0 + dma_row(j, lane), M - 1)) * p.lda_b +
+                  dma_chunk(j, lane) * kChunkBytes;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int j = wave * NB + i;
+        bsrc[i] = p.B + static_cast<int64_t>(min(n0 + dma_row(j, lane), N - 1)) * p.ldb_b +
+                  dma_chunk(j, lane) * kChunkBytes;
+    }
+    // copy d of stage t into buffer b
+    auto copy = [&](int d, int t, int b) {
+        const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + b * STAGE);
+        if (d < NA)
+            dma16(asrc[d] + t * kRow64Bytes, dst + (wave * NA + d) * 1024);
+        else
+            dma16(bsrc[d - NA] + t * kRow64Bytes, dst + BM * kRow64Bytes + (wave * NB + d - NA) * 1024);
+    };
+
+    // ---- fragment read offsets within a stage; block steps are 32 rows
+    int mread[2], nread[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        mread[q] = wave_m * WTM * kRow64Bytes + lds64_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+        nread[q] = (BM + wave_n * WTN) * kRow64Bytes + lds64_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+    }
+    // read r of slab q from buffer b: m-side and n-side fragments alternate so
+    // the first MFMAs of the slab get their operands first
+    auto read = [&](int r, int q, int b, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
+        const char* base = smem + b * STAGE;
+        const int blk = r >> 1;
+        if ((r & 1) == 0)
+            fa[blk] = *reinterpret_cast<const u32x4*>(base + mread[q] + blk * 32 * kRow64Bytes);
+        else
+            fb[blk] = *reinterpret_cast<const u32x4*>(base + nread[q] + blk * 32 * kRow64Bytes);
+    };
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nfull = K / BKE;
+    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+    if (nfull > 0) {
+        // prologue: stages 0 .. S-2 (indices past the last full stage reload
+        // it, so every iteration sees the same number of copies in flight)
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t)
+#pragma unroll
+            for (int d = 0; d < PER; ++d) copy(d, min(t, nfull - 1), t);
+        wait_vm<(S - 2) * PER>();
+        barrier();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read(r, 0, 0, fa0, fb0);
+
+        int buf = 0;           // buffer of stage s
+        int fill = S - 1;      // buffer that receives stage s + S - 1
+        for (int s = 0; s < nfull; ++s) {
+            // slab 0 of stage s; meanwhile read slab 1 of stage s
+            slab_with_side<DT, FM, FN, NR>(acc, fa0, fb0, [&](int k) { read(k, 1, buf, fa1, fb1); });
+            wait_vm<(S - 3) * PER>();  // this wave's copies of stage s+1 have landed
+            barrier();                 // ... and everyone's; stage s-1's buffer is free
+            const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
+            const int tload = min(s + S - 1, nfull - 1);
+            // slab 1 of stage s; meanwhile read slab 0 of stage s+1 (on the last
+            // stage this reads a buffer whose values go unused), then copy stage s+S-1
+            slab_with_side<DT, FM, FN, NR + PER>(acc, fa1, fb1, [&](int k) {
+                if (k < NR)
+                    read(k, 0, nbuf, fa0, fb0);
+                else
+                    copy(k - NR, tload, fill);
+            });
+            buf = nbuf;
+            fill = (fill + 1 == S) ? 0 : fill + 1;
+        }
+        wait_vm<0>();  // no copy outlives the loop
+    }
+
+    if (K % BKE != 0) {
+        // ragged last stage: loaded through registers, elements with k >= K
+        // become exact zeros; buffer 0 is free once every wave is past the loop
+        __syncthreads();
+        const int c = tid & 3;
+        const int k0 = nfull * BKE + c * EPC;
+        char* base = smem;
+#pragma unroll
+        for (int i = 0; i < BM / 64; ++i) {
+            const int r = (tid >> 2) + 64 * i;
+            const char* row = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+            *reinterpret_cast<u32x4*>(base + lds64_chunk_offset(r, c)) = load_chunk_bounded<ES>(row, k0, K);
+        }
+#pragma unroll
+        for (int i = 0; i < BN / 64; ++i) {
+            const int r = (tid >> 2) + 64 * i;
+            const char* row = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+            *reinterpret_cast<u32x4*>(base + BM * kRow64Bytes + lds64_chunk_offset(r, c)) =
+                load_chunk_bounded<ES>(row, k0, K);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, q, 0, fa0, fb0);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+        }
+    }
+
+    // ---- epilogue: alpha, optional ReLU, store by ownership (as above)
+    const float alpha = p.alpha;
+    const bool relu = p.relu != 0;
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+            const int nb = n0 + wave_n * WTN + 32 * i;
+            float* col = p.D + m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = nb + acc_row(lane, r);
+                float v = acc[i][j][r] * alpha;
+                if (relu) v = fmaxf(v, 0.0f);
+                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+            }
+        }
+    }
+}
+
+template <int DT, int BM, int BN, int S>
+static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, S>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- table
 
 template <int DT, int BM, int BN, int LC, int MW>
@@ -301,30 +537,53 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 
 }  // namespace tg
 
-// Kernel instances: (id, dtype, BM, BN, minimum row alignment class, minimum
-// waves per SIMD, tile-rows per group).
-#define TG_KERNEL_LIST(X)                   \
-    X(0, TG_BF16, 256, 256, 4, 1, 4)        \
-    X(1, TG_BF16, 256, 256, 2, 1, 4)        \
-    X(2, TG_F16, 256, 256, 4, 1, 4)         \
-    X(3, TG_F16, 256, 256, 2, 1, 4)         \
-    X(4, TG_BF16, 128, 128, 4, 2, 4)        \
-    X(5, TG_BF16, 128, 128, 2, 2, 4)        \
-    X(6, TG_F16, 128, 128, 4, 2, 4)         \
-    X(7, TG_F16, 128, 128, 2, 2, 4)         \
-    X(8, TG_F32, 128, 128, 4, 2, 4)
+// Kernel instances.
+//   register-staged: (id, dtype, BM, BN, min row alignment class, min waves per SIMD, group_m, eff%)
+//   streaming:       (id, dtype, BM, BN, LDS stages, group_m, eff%)
+// eff% is the expected MFMA efficiency the host plan chooser weighs tiles by.
+#define TG_RS_LIST(X)                           \
+    X(2, TG_BF16, 256, 256, 4, 1, 4, 70)        \
+    X(3, TG_BF16, 256, 256, 2, 1, 4, 70)        \
+    X(4, TG_F16, 256, 256, 4, 1, 4, 70)         \
+    X(5, TG_F16, 256, 256, 2, 1, 4, 70)         \
+    X(6, TG_BF16, 128, 128, 4, 2, 4, 45)        \
+    X(7, TG_BF16, 128, 128, 2, 2, 4, 45)        \
+    X(8, TG_F16, 128, 128, 4, 2, 4, 45)         \
+    X(9, TG_F16, 128, 128, 2, 2, 4, 45)         \
+    X(10, TG_F32, 128, 128, 4, 2, 4, 45)
+#define TG_STREAM_LIST(X)                       \
+    X(0, TG_BF16, 256, 256, 4, 4, 100)          \
+    X(1, TG_F16, 256, 256, 4, 4, 100)
 
 // Explicit instantiation, seen by both the device and the host pass.
-#define TG_INSTANTIATE(id, DT, BM, BN, LC, MW, GM) \
+#define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
     template __global__ void tg::gemm_kernel<DT, BM, BN, LC, MW>(GemmArgs);
-TG_KERNEL_LIST(TG_INSTANTIATE)
+#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, S, GM, EFF) \
+    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, S>(GemmArgs);
+TG_RS_LIST(TG_INSTANTIATE_RS)
+TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 
 // The table holds host launch functions, so it exists only in the host pass.
 #ifndef __HIP_DEVICE_COMPILE__
-#define TG_ENTRY(id, DT, BM, BN, LC, MW, GM)                                                    \
-    { id, DT, BM, BN, (128 / ((DT) == TG_F32 ? 4 : 2)), 2, 2, (BM) / 2, (BN) / 2, 256, 2,       \
-      2 * ((BM) + (BN)) * 128, ((BM) / 2) * ((BN) / 2) / 64, LC, GM, &tg::launch<DT, BM, BN, LC, MW> },
+#define TG_ES(DT) ((DT) == TG_F32 ? 4 : 2)
+#define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, EFF)                                                \
+    {id, DT, BM, BN, 128 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,    \
+     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW>},
+#define TG_ENTRY_STREAM(id, DT, BM, BN, S, GM, EFF)                                                 \
+    {id, DT, BM, BN, 64 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, S, (S) * ((BM) + (BN)) * 64,    \
+     ((BM) / 2) * ((BN) / 2) / 64, 16, GM, EFF, &tg::launch_stream<DT, BM, BN, S>},
 
-extern "C" const TgKernelDesc tg_kernel_table[] = {TG_KERNEL_LIST(TG_ENTRY)};
-extern "C" const int tg_kernel_table_size = sizeof(tg_kernel_table) / sizeof(tg_kernel_table[0]);
+static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)};
+constexpr int kCount = sizeof(kUnsorted) / sizeof(kUnsorted[0]);
+
+// The table is indexed by kernel id.
+struct TgTable {
+    TgKernelDesc k[kCount];
+    TgTable() {
+        for (int i = 0; i < kCount; ++i) k[kUnsorted[i].id] = kUnsorted[i];
+    }
+};
+static const TgTable kTable;
+extern "C" const TgKernelDesc* const tg_kernel_table = kTable.k;
+extern "C" const int tg_kernel_table_size = kCount;
 #endif  // __HIP_DEVICE_COMPILE__

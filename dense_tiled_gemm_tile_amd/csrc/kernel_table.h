@@ -33,10 +33,12 @@ struct TgKernelDesc {
     int stages;
     int lds_bytes;
     int acc_per_lane;
-    int load_class;    // minimum byte alignment of operand row starts (4 or 2)
+    int load_class;    // minimum byte alignment of operand row starts (16, 4 or 2)
     int group_m;
+    int eff_pct;       // expected MFMA efficiency, weighs tiles in the plan chooser
     TgLaunchFn launch;
 };
 
-extern "C" const TgKernelDesc tg_kernel_table[];
+// Indexed by kernel id.
+extern "C" const TgKernelDesc* const tg_kernel_table;
 extern "C" const int tg_kernel_table_size;

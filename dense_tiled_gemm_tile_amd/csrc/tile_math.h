@@ -63,6 +63,27 @@ TG_HD int lds_chunk_offset(int row, int chunk) {
 TG_HD int stage_chunk(int t) { return t & 7; }
 TG_HD int stage_row(int t, int i) { return (t >> 3) + 32 * i; }
 
+// ---------------------------------------------------------------- 64-byte rows
+//
+// The streaming (LDS-DMA) kernels stage 64 bytes of K per row per stage.  Two
+// rows share a 128-byte line, so the swizzle must separate rows of equal
+// parity within 8 consecutive rows and rows of equal residue mod 4 within 16:
+// chunk c of row r sits in slot c ^ lds64_swizzle(r).
+constexpr int kRow64Bytes = 64;
+constexpr int kChunksPerRow64 = kRow64Bytes / kChunkBytes;
+
+TG_HD int lds64_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+TG_HD int lds64_chunk_offset(int row, int chunk) {
+    return row * kRow64Bytes + ((chunk ^ lds64_swizzle(row)) * kChunkBytes);
+}
+
+// One LDS-DMA instruction moves 64 lanes x 16 bytes into 1 KiB of LDS: lane t
+// lands at byte 16*t of block j, i.e. row 16*j + t/4, physical slot t%4.  The
+// lane therefore fetches the logical chunk that the swizzle puts in that slot.
+TG_HD int dma_row(int j, int lane) { return 16 * j + (lane >> 2); }
+TG_HD int dma_chunk(int j, int lane) { return (lane & 3) ^ lds64_swizzle(dma_row(j, lane)); }
+
 // ---------------------------------------------------------------- MFMA maps
 //
 // 32x32 MFMA block, operand side: lane l supplies row frag_row(l) of the

@@ -129,10 +129,14 @@ def test_every_kernel_instance(kid):
     # strides with lda*es = 4 (mod 16) for class 4
     if info.load_class == 2:
         lda, ldb = K + 2, K + 4  # K is odd here
-    else:
+    elif info.load_class == 4:
         lda = K + (2 - K) % 8 if es == 2 else K + (1 - K) % 4
         ldb = lda + 8 if es == 2 else lda + 4
-    assert (lda * es) % 16 in ((4, 12) if info.load_class == 4 else (2, 6, 10, 14))
+    else:
+        lda = K + (-K) % (16 // es)
+        ldb = lda + 16 // es
+    want = {2: (2, 6, 10, 14), 4: (4, 12), 16: (0,)}[info.load_class]
+    assert (lda * es) % 16 in want
     _log(f"[instance {kid}] {dt} {info.block_m}x{info.block_n} class {info.load_class}: {M}x{N}x{K} lda={lda} ldb={ldb}")
     A_st, B_st = si.int_operands(M, N, K, dt, seed=kid, lda=lda, ldb=ldb)
     D_st = run(A_st, B_st, M, N, K, -1.5, True, M + 3, kernel_id=kid)
@@ -143,6 +147,28 @@ def test_every_kernel_instance(kid):
 
 
 EDGE_DIMS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _stream_instances():
+    return [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 16]
+
+
+@pytest.mark.parametrize("kid", _stream_instances())
+def test_stream_instance_k_sweep(kid):
+    """The streaming instances across K: fewer full stages than pipeline
+    depth, exact multiples of the stage, and ragged tails."""
+    info = tg.kernel_info(kid)
+    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
+    bk = info.block_k
+    M, N = info.block_m + 45, 2 * info.block_n - 3
+    Ks = sorted({1, bk // 2, bk - 1, bk, bk + 1, 2 * bk, 2 * bk + 7, 3 * bk, 3 * bk + 1,
+                 4 * bk, 5 * bk - 1, 9 * bk, 9 * bk + 3})
+    _log(f"[stream K sweep] instance {kid}: K in {Ks}")
+    for K in Ks:
+        lda = K + (-K) % 8
+        A_st, B_st = si.int_operands(M, N, K, dt, seed=K, lda=lda, ldb=lda)
+        D_st = run(A_st, B_st, M, N, K, 1.0, False, M + 5, kernel_id=kid)
+        check_full(D_st, A_st, B_st, M, N, K, 1.0, False, dt, exact=True)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])

@@ -161,8 +161,35 @@ static void check_ownership(int BM, int BN) {
     CHECK(acc_per_lane * 256 == BM * BN, "acc/lane %d * 256 != %d*%d", acc_per_lane, BM, BN);
 }
 
+// 64-byte-row layout of the streaming kernels: every DMA lane lands exactly
+// where the swizzled layout puts its logical chunk, each (row, chunk) of a
+// stage is written once, and fragment reads of both slabs are conflict-free.
+static void check_dma_layout(int rows) {
+    const int blocks = rows * kRow64Bytes / 1024;
+    std::vector<int> count(rows * kChunksPerRow64, 0);
+    for (int j = 0; j < blocks; ++j)
+        for (int t = 0; t < 64; ++t) {
+            const int r = dma_row(j, t), c = dma_chunk(j, t);
+            CHECK(r < rows && c >= 0 && c < kChunksPerRow64, "dma out of range");
+            CHECK(lds64_chunk_offset(r, c) == j * 1024 + 16 * t, "dma lane %d of block %d lands elsewhere", t, j);
+            count[r * kChunksPerRow64 + c]++;
+        }
+    bool once = true;
+    for (int v : count) once = once && v == 1;
+    CHECK(once, "dma does not cover %d rows x 4 chunks exactly once", rows);
+    for (int q = 0; q < 2; ++q)
+        for (int blk = 0; blk < rows / 32; ++blk) {
+            std::vector<int> off;
+            for (int l = 0; l < 64; ++l) off.push_back(lds64_chunk_offset(32 * blk + frag_row(l), frag_chunk(l, q)));
+            CHECK(conflict_free(off, 8, 128) && conflict_free(off, 16, 256),
+                  "64-byte-row fragment reads conflict (slab %d block %d)", q, blk);
+        }
+}
+
 int main() {
     check_tile_order();
+    check_dma_layout(256);
+    check_dma_layout(128);
     check_staging(128);
     check_staging(256);
     check_fragments();
