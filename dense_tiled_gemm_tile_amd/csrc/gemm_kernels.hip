@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernel_table.h"
 #include "tile_math.h"
 
@@ -347,18 +349,21 @@ __device__ __forceinline__ void slab_with_side(f32x16 (&acc)[FN][FM], const u32x
     }
 }
 
-template <int DT, int BM, int BN, int S>
-__global__ __launch_bounds__(kThreads, 1) void gemm_stream_kernel(GemmArgs p) {
+template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
+__global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kernel(GemmArgs p) {
+    constexpr int NW = WM * WN;                 // waves per workgroup
+    constexpr int NT = 64 * NW;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
     constexpr int EPC = 16 / ES;
     constexpr int BKE = kRow64Bytes / ES;       // K elements per stage
-    constexpr int WTM = BM / 2, WTN = BN / 2;   // 2 x 2 waves
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int NA = BM / 64, NB = BN / 64;   // 1 KiB copies per wave per stage
+    constexpr int WTM = BM / WM, WTN = BN / WN; // output owned by one wave
+    constexpr int FM = WTM / 32, FN = WTN / 32; // 32 x 32 MFMA blocks per wave
+    constexpr int NA = BM / (16 * NW);          // 1 KiB copies of A per wave per stage
+    constexpr int NB = BN / (16 * NW);
     constexpr int PER = NA + NB;
     constexpr int NR = FM + FN;                 // fragment reads per slab
     constexpr int STAGE = (BM + BN) * kRow64Bytes;
-    static_assert(FM == FN, "square wave tiles");
+    static_assert(NA * 16 * NW == BM && NB * 16 * NW == BN, "copies must tile the stage");
     static_assert(S >= 3, "at least one stage in flight beyond the next");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
@@ -366,9 +371,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_stream_kernel(GemmArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    const int wave_m = wave & 1, wave_n = wave >> 1;
+    const int wave_m = wave % WM, wave_n = wave / WM;
 
-    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 
@@ -408,12 +413,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_stream_kernel(GemmArgs p) {
         mread[q] = wave_m * WTM * kRow64Bytes + lds64_chunk_offset(frag_row(lane), frag_chunk(lane, q));
         nread[q] = (BM + wave_n * WTN) * kRow64Bytes + lds64_chunk_offset(frag_row(lane), frag_chunk(lane, q));
     }
-    // read r of slab q from buffer b: m-side and n-side fragments alternate so
-    // the first MFMAs of the slab get their operands first
+    // read r of slab q from buffer b: m-side and n-side fragments alternate
+    // while both last, so the first MFMAs of the slab get their operands first
     auto read = [&](int r, int q, int b, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
+        constexpr int P = FM < FN ? FM : FN;
         const char* base = smem + b * STAGE;
-        const int blk = r >> 1;
-        if ((r & 1) == 0)
+        bool is_m;
+        int blk;
+        if (r < 2 * P) {
+            is_m = (r & 1) == 0;
+            blk = r >> 1;
+        } else {
+            is_m = FM > FN;
+            blk = r - P;
+        }
+        if (is_m)
             fa[blk] = *reinterpret_cast<const u32x4*>(base + mread[q] + blk * 32 * kRow64Bytes);
         else
             fb[blk] = *reinterpret_cast<const u32x4*>(base + nread[q] + blk * 32 * kRow64Bytes);
@@ -473,14 +487,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_stream_kernel(GemmArgs p) {
         const int k0 = nfull * BKE + c * EPC;
         char* base = smem;
 #pragma unroll
-        for (int i = 0; i < BM / 64; ++i) {
-            const int r = (tid >> 2) + 64 * i;
+        for (int i = 0; i < BM * 4 / NT; ++i) {
+            const int r = (tid >> 2) + (NT / 4) * i;
             const char* row = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
             *reinterpret_cast<u32x4*>(base + lds64_chunk_offset(r, c)) = load_chunk_bounded<ES>(row, k0, K);
         }
 #pragma unroll
-        for (int i = 0; i < BN / 64; ++i) {
-            const int r = (tid >> 2) + 64 * i;
+        for (int i = 0; i < BN * 4 / NT; ++i) {
+            const int r = (tid >> 2) + (NT / 4) * i;
             const char* row = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
             *reinterpret_cast<u32x4*>(base + BM * kRow64Bytes + lds64_chunk_offset(r, c)) =
                 load_chunk_bounded<ES>(row, k0, K);
@@ -519,10 +533,245 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_stream_kernel(GemmArgs p) {
     }
 }
 
-template <int DT, int BM, int BN, int S>
+template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
 static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, S>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- hybrid kernel
+//
+// On gfx950 an LDS read issued on a SIMD more often than about once per 128
+// MFMA cycles slows that SIMD's MFMA pipe (twice that rate halves it), whatever
+// wave it comes from, while vector-memory loads and LDS-DMA copies issue almost
+// for free.  A 128 x 128 wave tile with both operands in LDS needs twice that
+// read rate, so here only the A side (the m rows) goes through LDS, staged by
+// LDS-DMA S stages deep; the B side (the n rows) is loaded by each wave
+// straight from global memory (L2/L1) into registers in MFMA operand layout,
+// P stages ahead, through a ring of P+1 stages of fragments.  16x16x32 MFMAs
+// are used so that each direct load reads 16 rows x 64 contiguous bytes (one
+// fully used 64-byte sector per row) instead of 32 rows x 32 bytes.  One
+// barrier per stage publishes the next A stage and frees the oldest.
+
+// The MFMA is written as inline assembly with the accumulator tied in place
+// ("+a"): with the builtin, the register allocator does not keep the result
+// in the accumulator's registers for this many 16x16 accumulators and adds
+// chains of AGPR moves that serialise on MFMA completion.  In this kernel the
+// operands come only from loads (waited by vmcnt/lgkmcnt), each accumulator
+// is touched once per stage, and mfma16_drain() pads before any other read of
+// the accumulators, which covers the MFMA hazards the compiler cannot see.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(u32x4 afrag, u32x4 bfrag, f32x4 acc) {
+    if constexpr (DT == TG_BF16)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(afrag), "v"(bfrag));
+    else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(afrag), "v"(bfrag));
+    return acc;
+}
+
+// Wait states after the last MFMA before its results are read by other
+// instructions (more than the 16x16x32 pass count requires).
+__device__ __forceinline__ void mfma16_drain() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+template <int DT, int S, int P>
+__global__ __launch_bounds__(256, 1) void gemm_hybrid_kernel(GemmArgs p) {
+    static_assert(DT == TG_BF16 || DT == TG_F16, "16-bit operands");
+    constexpr int BM = 256, BN = 256;
+    constexpr int EPC = 8;                   // elements per 16-byte chunk
+    constexpr int BKE = kRow64Bytes / 2;     // K elements per stage
+    constexpr int WTM = 128, WTN = 128;      // 2 x 2 waves
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int NA = BM / 64;              // 1 KiB A copies per wave per stage
+    constexpr int ASTAGE = BM * kRow64Bytes;
+    constexpr int G = P + 1;                 // B fragment ring, in stages
+    constexpr int OPS = FN + NA;             // vector-memory operations per stage
+    static_assert(P >= S - 3, "the steady-state copy wait assumes P >= S - 3");
+    static_assert(S >= 3, "at least one stage in flight beyond the next");
+    // copies of stage t are the last vector-memory operations of stage t-S+1;
+    // waiting for stage s+1 at the start of stage s leaves the operations of
+    // stages s-S+3 .. s-1 in flight
+    constexpr int WAIT_FIRST = (S - 2) * NA + P * FN;
+    constexpr int WAIT_STEADY = (S - 3) * OPS;
+    static_assert(WAIT_FIRST < 64 && WAIT_STEADY < 64, "vmcnt is 6 bits");
+    constexpr int LDS = (S * ASTAGE > (BM + BN) * kRow64Bytes) ? S * ASTAGE : (BM + BN) * kRow64Bytes;
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave & 1, wave_n = wave >> 1;
+
+    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+    const int m0 = tile.tm * BM, n0 = tile.tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const unsigned lds_base = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char*)(smem))));
+
+    // ---- A copies (rows past M clamp to the last row)
+    const char* asrc[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int j = wave * NA + i;
+        asrc[i] = p.A + static_cast<int64_t>(min(m0 + dma_row(j, lane), M - 1)) * p.lda_b +
+                  dma_chunk(j, lane) * kChunkBytes;
+    }
+    auto copy = [&](int d, int t, int b) {
+        const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + b * ASTAGE);
+        dma16(asrc[d] + t * kRow64Bytes, dst + (wave * NA + d) * 1024);
+    };
+    // ---- A fragment reads: block j covers rows wave_m*WTM + 16j .. +15
+    const int aread = wave_m * WTM * kRow64Bytes + lds64_chunk_offset(frag16_row(lane), frag16_chunk(lane));
+    auto read_a = [&](int j, int b, u32x4 (&fa)[FM]) {
+        fa[j] = *reinterpret_cast<const u32x4*>(smem + b * ASTAGE + aread + j * 16 * kRow64Bytes);
+    };
+    // ---- B fragments straight from global memory: stage t of row block i is
+    // the 16 bytes at k = 32t + 8*(lane/16) of row n0 + wave_n*WTN + 16i + lane%16
+    // (the same k order as the A fragments read from LDS)
+    const char* bsrc[FN];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+        bsrc[i] = p.B + static_cast<int64_t>(min(n0 + wave_n * WTN + 16 * i + frag16_row(lane), N - 1)) * p.ldb_b +
+                  frag16_chunk(lane) * kChunkBytes;
+    u32x4 fb[G][FN];
+    auto load_b = [&](int i, int t, int slot) {
+        fb[slot][i] = *reinterpret_cast<const u32x4*>(bsrc[i] + t * kRow64Bytes);
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nfull = K / BKE;
+    u32x4 fa[FM];  // A fragments of the current stage, refilled in place
+
+    if (nfull > 0) {
+        // prologue: A stages 0 .. S-2, then B stages 0 .. P-1 (indices past the
+        // end repeat the last one, keeping the number of operations in flight
+        // the same every stage)
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t)
+#pragma unroll
+            for (int d = 0; d < NA; ++d) copy(d, min(t, nfull - 1), t);
+#pragma unroll
+        for (int t = 0; t < P; ++t)
+#pragma unroll
+            for (int i = 0; i < FN; ++i) load_b(i, min(t, nfull - 1), t);
+        wait_vm<WAIT_FIRST>();
+        barrier();
+#pragma unroll
+        for (int j = 0; j < FM; ++j) read_a(j, 0, fa);
+
+        int nbuf = 1;      // A buffer of stage s+1
+        int fill = S - 1;  // A buffer that receives stage s + S - 1
+        // Stage s; u = s mod G picks the B ring slot.  MFMAs run m-block by
+        // m-block: once the eight MFMAs of A fragment j are issued, fragment j
+        // of stage s+1 is read into the same registers.  Between MFMAs go one
+        // B load (stage s+P) per m-block and the NA copies (stage s+S-1), so
+        // every group of eight MFMAs carries at most one LDS read, one load
+        // and one copy.  A of stage s was read during stage s-1, so at the
+        // barrier that opens stage s every wave is done with stage s-1's buffer.
+        auto stage = [&](int s, int u) {
+            const int cur = u % G, pf = (u + P) % G;
+            const int tb = min(s + P, nfull - 1);
+            const int tload = min(s + S - 1, nfull - 1);
+            wait_vm<WAIT_STEADY>();  // this wave's copies of stage s+1 have landed
+            barrier();               // ... and everyone's
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    acc[i][j] = mfma16<DT>(fb[cur][i], fa[j], acc[i][j]);
+                    if (i == 2) load_b(j, tb, pf);
+                    if (i == 5 && j < NA) copy(j, tload, fill);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // on the last stage this reads a buffer whose values go unused
+                read_a(j, nbuf, fa);
+            }
+            nbuf = (nbuf + 1 == S) ? 0 : nbuf + 1;
+            fill = (fill + 1 == S) ? 0 : fill + 1;
+        };
+        // whole ring turns without guards, then the last nfull mod G stages
+        int s0 = 0;
+        for (; s0 + G <= nfull; s0 += G) {
+#pragma unroll
+            for (int u = 0; u < G; ++u) stage(s0 + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u < G - 1; ++u)
+            if (s0 + u < nfull) stage(s0 + u, u);
+        wait_vm<0>();  // no copy outlives the loop
+    }
+
+    if (K % BKE != 0) {
+        // ragged last stage, both operands through LDS with exact zeros past K
+        __syncthreads();
+        const int c = tid & 3;
+        const int k0 = nfull * BKE + c * EPC;
+#pragma unroll
+        for (int i = 0; i < BM / 64; ++i) {
+            const int r = (tid >> 2) + 64 * i;
+            const char* row = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+            *reinterpret_cast<u32x4*>(smem + lds64_chunk_offset(r, c)) = load_chunk_bounded<2>(row, k0, K);
+        }
+#pragma unroll
+        for (int i = 0; i < BN / 64; ++i) {
+            const int r = (tid >> 2) + 64 * i;
+            const char* row = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+            *reinterpret_cast<u32x4*>(smem + BM * kRow64Bytes + lds64_chunk_offset(r, c)) =
+                load_chunk_bounded<2>(row, k0, K);
+        }
+        __syncthreads();
+        u32x4 fbt[FN];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) read_a(j, 0, fa);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            fbt[i] = *reinterpret_cast<const u32x4*>(
+                smem + (BM + wave_n * WTN + 16 * i) * kRow64Bytes +
+                lds64_chunk_offset(frag16_row(lane), frag16_chunk(lane)));
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = mfma16<DT>(fbt[i], fa[j], acc[i][j]);
+    }
+
+    mfma16_drain();
+
+    // ---- epilogue: alpha, optional ReLU, store by ownership
+    const float alpha = p.alpha;
+    const bool relu = p.relu != 0;
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wave_m * WTM + 16 * j + acc16_col(lane);
+            const int nb = n0 + wave_n * WTN + 16 * i;
+            float* col = p.D + m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = nb + acc16_row(lane, r);
+                float v = acc[i][j][r] * alpha;
+                if (relu) v = fmaxf(v, 0.0f);
+                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+            }
+        }
+    }
+}
+
+template <int DT, int S, int P>
+static hipError_t launch_hybrid(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_hybrid_kernel<DT, S, P>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -539,7 +788,8 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 
 // Kernel instances.
 //   register-staged: (id, dtype, BM, BN, min row alignment class, min waves per SIMD, group_m, eff%)
-//   streaming:       (id, dtype, BM, BN, LDS stages, group_m, eff%)
+//   streaming:       (id, dtype, BM, BN, waves along m, waves along n, LDS stages, group_m, eff%)
+//   hybrid:          (id, dtype, A stages in LDS, B prefetch stages, group_m, eff%), 256 x 256
 // eff% is the expected MFMA efficiency the host plan chooser weighs tiles by.
 #define TG_RS_LIST(X)                           \
     X(2, TG_BF16, 256, 256, 4, 1, 4, 70)        \
@@ -552,16 +802,25 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     X(9, TG_F16, 128, 128, 2, 2, 4, 45)         \
     X(10, TG_F32, 128, 128, 4, 2, 4, 45)
 #define TG_STREAM_LIST(X)                       \
-    X(0, TG_BF16, 256, 256, 4, 4, 100)          \
-    X(1, TG_F16, 256, 256, 4, 4, 100)
+    X(0, TG_BF16, 256, 256, 2, 4, 4, 4, 100)    \
+    X(1, TG_F16, 256, 256, 2, 4, 4, 4, 100)     \
+    X(11, TG_BF16, 256, 256, 2, 2, 4, 4, 90)    \
+    X(12, TG_F16, 256, 256, 2, 2, 4, 4, 90)
+
+#define TG_HYBRID_LIST(X)                       \
+    X(13, TG_BF16, 5, 2, 4, 75)                 \
+    X(14, TG_F16, 5, 2, 4, 75)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
     template __global__ void tg::gemm_kernel<DT, BM, BN, LC, MW>(GemmArgs);
-#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, S, GM, EFF) \
-    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, S>(GemmArgs);
+#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF) \
+    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>(GemmArgs);
+#define TG_INSTANTIATE_HYBRID(id, DT, S, P, GM, EFF) \
+    template __global__ void tg::gemm_hybrid_kernel<DT, S, P>(GemmArgs);
 TG_RS_LIST(TG_INSTANTIATE_RS)
 TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
+TG_HYBRID_LIST(TG_INSTANTIATE_HYBRID)
 
 // The table holds host launch functions, so it exists only in the host pass.
 #ifndef __HIP_DEVICE_COMPILE__
@@ -569,11 +828,18 @@ TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 #define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, EFF)                                                \
     {id, DT, BM, BN, 128 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,    \
      ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW>},
-#define TG_ENTRY_STREAM(id, DT, BM, BN, S, GM, EFF)                                                 \
-    {id, DT, BM, BN, 64 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, S, (S) * ((BM) + (BN)) * 64,    \
-     ((BM) / 2) * ((BN) / 2) / 64, 16, GM, EFF, &tg::launch_stream<DT, BM, BN, S>},
+#define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF)                                         \
+    {id, DT, BM, BN, 64 / TG_ES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,           \
+     (S) * ((BM) + (BN)) * 64, ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                    \
+     &tg::launch_stream<DT, BM, BN, WM, WN, S, GM>},
 
-static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)};
+#define TG_ENTRY_HYBRID(id, DT, S, P, GM, EFF)                                                      \
+    {id, DT, 256, 256, 64 / TG_ES(DT), 2, 2, 128, 128, 256, S,                                      \
+     ((S) * 256 * 64 > 512 * 64 ? (S) * 256 * 64 : 512 * 64), 256, 16, GM, EFF,                     \
+     &tg::launch_hybrid<DT, S, P>},
+
+static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
+                                             TG_HYBRID_LIST(TG_ENTRY_HYBRID)};
 constexpr int kCount = sizeof(kUnsorted) / sizeof(kUnsorted[0]);
 
 // The table is indexed by kernel id.

@@ -65,14 +65,16 @@ TG_HD int stage_row(int t, int i) { return (t >> 3) + 32 * i; }
 
 // ---------------------------------------------------------------- 64-byte rows
 //
-// The streaming (LDS-DMA) kernels stage 64 bytes of K per row per stage.  Two
-// rows share a 128-byte line, so the swizzle must separate rows of equal
-// parity within 8 consecutive rows and rows of equal residue mod 4 within 16:
-// chunk c of row r sits in slot c ^ lds64_swizzle(r).
+// The streaming (LDS-DMA) kernels stage 64 bytes of K per row per stage;
+// chunk c of row r sits in slot c ^ lds64_swizzle(r).  The swizzle was chosen
+// by measurement on gfx950 (the SQ_LDS_BANK_CONFLICT counter over the exact
+// fragment-read pattern of these kernels): (r >> 2) & 3 reads conflict-free,
+// while for example ((r >> 1) ^ (r >> 3)) & 3, which a plain 64-bank model
+// predicts conflict-free, costs a 2-way conflict.
 constexpr int kRow64Bytes = 64;
 constexpr int kChunksPerRow64 = kRow64Bytes / kChunkBytes;
 
-TG_HD int lds64_swizzle(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+TG_HD int lds64_swizzle(int row) { return (row >> 2) & 3; }
 
 TG_HD int lds64_chunk_offset(int row, int chunk) {
     return row * kRow64Bytes + ((chunk ^ lds64_swizzle(row)) * kChunkBytes);
@@ -92,6 +94,15 @@ TG_HD int dma_chunk(int j, int lane) { return (lane & 3) ^ lds64_swizzle(dma_row
 // equal k.
 TG_HD int frag_row(int lane) { return lane & 31; }
 TG_HD int frag_chunk(int lane, int q) { return 2 * q + (lane >> 5); }
+
+// 16x16x32 MFMA blocks (used where one operand is loaded straight into
+// registers): lane l supplies row frag16_row(l) and the 16-byte chunk
+// frag16_chunk(l) of the stage's 64-byte K slice; register r of lane l holds
+// output element (acc16_row(l, r), acc16_col(l)) of the 16x16 block.
+TG_HD int frag16_row(int lane) { return lane & 15; }
+TG_HD int frag16_chunk(int lane) { return lane >> 4; }
+TG_HD int acc16_row(int lane, int r) { return 4 * (lane >> 4) + r; }
+TG_HD int acc16_col(int lane) { return lane & 15; }
 
 // Output side: accumulator register r (0..15) of lane l holds element
 // (row acc_row(l, r), column acc_col(l)) of the 32x32 block.  Rows of the MFMA

