@@ -540,6 +540,209 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t str
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- wide-row streaming kernel
+//
+// 256 x 256 tile, 4 waves of 128 x 128, stages of 128 bytes of K per operand
+// row copied global -> LDS by LDS-DMA.  Each group of 8 lanes of a copy reads
+// one whole 128-byte row segment (a full cache line), which halves the number
+// of memory requests per byte against 64-byte rows; the L2 -> LDS request rate
+// is what bounds the copy path of these kernels.  Per stage each wave runs four
+// slabs of 16 MFMAs (32 bytes of K each).
+//
+// LDS holds NS slots of 32 KiB; a slot holds one operand's half of a stage
+// (256 rows x 128 bytes).  Half-stage h (stage h/2, A if h is even, B if odd)
+// lives in slot h % NS.  NS = 4 is plain double buffering; NS = 5 fills the
+// 160 KiB of a CU and keeps one and a half stages of copies in flight.
+//
+// Schedule of stage s (barrier B_s sits between slabs 2 and 3):
+//   slab 0: read slab 1 fragments; copy half-stage 2s + NS - 1
+//   slab 1: read slab 2 fragments
+//   slab 2: read slab 3 fragments
+//   wait for this wave's reads and for its copies of stage s+1; B_s
+//   (stage s+1 is published, and every wave is done reading stage s)
+//   slab 3: read slab 0 of stage s+1; copy half-stage 2s + NS into the slot
+//   stage s's A half just left
+// A slot is refilled only after the barrier that ends the reads of the
+// half-stage NS places earlier, which the two copy points respect.
+template <int DT, int GM, int NS, int RS>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
+    constexpr int BM = 256, BN = 256, WM = 2;
+    constexpr int ES = (DT == TG_F32) ? 4 : 2;
+    constexpr int EPC = 16 / ES;
+    constexpr int BKE = kRowBytes / ES;          // K elements per stage
+    constexpr int WTM = 128, WTN = 128;          // output owned by one wave
+    constexpr int FM = WTM / 32, FN = WTN / 32;  // 32 x 32 MFMA blocks per wave
+    constexpr int NC = BM / (8 * 4);             // 1 KiB copies per wave per half-stage
+    constexpr int NR = FM + FN;                  // fragment reads per slab
+    constexpr int MF = FM * FN;                  // MFMAs per slab
+    constexpr int SLOT = BM * kRowBytes;         // 32 KiB
+    static_assert(BM == BN && NC == 8 && MF == 16, "schedule assumes 8 copies per half-stage, 16 MFMAs a slab");
+    static_assert(NS == 4 || NS == 5, "4 or 5 half-stage slots");
+    static_assert(RS >= 1 && RS <= MF, "reads spread over at most one slab");
+
+    __shared__ __attribute__((aligned(1024))) char smem[NS * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave % WM, wave_n = wave / WM;
+
+    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
+    const int m0 = tile.tm * BM, n0 = tile.tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const unsigned lds_base = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
+
+    // copy sources (rows past M or N clamp to the last row)
+    const char* src[2][NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int j = wave * NC + i;
+        src[0][i] = p.A + static_cast<int64_t>(min(m0 + dma128_row(j, lane), M - 1)) * p.lda_b +
+                    dma128_chunk(j, lane) * kChunkBytes;
+        src[1][i] = p.B + static_cast<int64_t>(min(n0 + dma128_row(j, lane), N - 1)) * p.ldb_b +
+                    dma128_chunk(j, lane) * kChunkBytes;
+    }
+    // copy i of operand o (0: A, 1: B) of stage t into slot `slot`
+    auto copy = [&](int o, int i, int t, int slot) {
+        dma16(src[o][i] + static_cast<int64_t>(t) * kRowBytes,
+              __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + i) * 1024));
+    };
+    auto wrap = [](int x) { return x >= NS ? x - NS : x; };
+
+    // fragment read offsets within a slot (block steps are 32 rows, which
+    // keep the swizzle)
+    int mread[4], nread[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        mread[q] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+        nread[q] = wave_n * WTN * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+    }
+    // read r of slab q from slots (sa, sb); m-side and n-side fragments alternate
+    auto read = [&](int r, int q, int sa, int sb, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
+        const int blk = r >> 1;
+        if ((r & 1) == 0)
+            fa[blk] = *reinterpret_cast<const u32x4*>(smem + sa * SLOT + mread[q] + blk * 32 * kRowBytes);
+        else
+            fb[blk] = *reinterpret_cast<const u32x4*>(smem + sb * SLOT + nread[q] + blk * 32 * kRowBytes);
+    };
+    // the NR fragment reads of a slab go out after the first RS of its MFMAs
+    auto reads_at = [&](int m, auto&& f) {
+        if (m < RS) {
+#pragma unroll
+            for (int k = (m * NR + RS - 1) / RS; k < ((m + 1) * NR + RS - 1) / RS; ++k) f(k);
+        }
+    };
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nfull = K / BKE;
+    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+    if (nfull > 0) {
+        // prologue: half-stages 0 .. NS-2 (a stage index past the last full
+        // stage reloads that stage, so the copy counts stay uniform)
+#pragma unroll
+        for (int h = 0; h < NS - 1; ++h)
+#pragma unroll
+            for (int i = 0; i < NC; ++i) copy(h & 1, i, min(h >> 1, nfull - 1), h);
+        wait_vm<(NS - 3) * NC>();
+        barrier();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
+
+        constexpr int H0 = NS - 1;                 // half-stage copied in slab 0, minus 2s
+        int slot0 = 0;                             // slot of stage s's A half, (2s) % NS
+        for (int s = 0; s < nfull; ++s) {
+            const int sa = slot0, sb = wrap(slot0 + 1);
+            const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
+            const int t0 = min(s + (H0 >> 1), nfull - 1);       // stage of half-stage 2s + H0
+            const int t3 = min(s + ((H0 + 1) >> 1), nfull - 1); // stage of half-stage 2s + H0 + 1
+            const int slot_h0 = wrap(slot0 + NS - 1);
+            slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
+                if (m & 1) copy(H0 & 1, m >> 1, t0, slot_h0);
+            });
+            slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); });
+            });
+            slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); });
+            });
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+            wait_vm<(NS - 4) * NC>();
+            barrier();
+            // on the last stage the reads below fetch values that go unused
+            slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
+                if (m & 1) copy((H0 + 1) & 1, m >> 1, t3, sa);
+            });
+            slot0 = na;
+        }
+        wait_vm<0>();  // no copy outlives the loop
+    }
+
+    if (K % BKE != 0) {
+        // ragged last stage through registers into slots 0 (A) and 1 (B);
+        // k >= K become exact zeros
+        __syncthreads();
+        const int c = stage_chunk(tid);
+        const int k0 = nfull * BKE + c * EPC;
+#pragma unroll
+        for (int i = 0; i < BM / 32; ++i) {
+            const int r = stage_row(tid, i);
+            const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+            const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+            *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+            *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+        }
+    }
+
+    // epilogue: alpha, optional ReLU, masked store by ownership
+    const float alpha = p.alpha;
+    const bool relu = p.relu != 0;
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+            const int nbase = n0 + wave_n * WTN + 32 * i;
+            float* col = p.D + m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = nbase + acc_row(lane, r);
+                float v = acc[i][j][r] * alpha;
+                if (relu) v = fmaxf(v, 0.0f);
+                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+            }
+        }
+    }
+}
+
+template <int DT, int GM, int NS, int RS>
+static hipError_t launch_wide(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- hybrid kernel
 //
 // On gfx950 an LDS read issued on a SIMD more often than about once per 128
@@ -811,6 +1014,13 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     X(13, TG_BF16, 5, 2, 4, 75)                 \
     X(14, TG_F16, 5, 2, 4, 75)
 
+#define TG_WIDE_LIST(X)                         \
+    X(15, TG_BF16, 4, 5, 16, 105)               \
+    X(16, TG_F16, 4, 5, 16, 105)                \
+    X(17, TG_F32, 4, 5, 16, 40)                 \
+    X(18, TG_BF16, 4, 4, 16, 10)                \
+    X(19, TG_BF16, 4, 5, 8, 10)
+
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
     template __global__ void tg::gemm_kernel<DT, BM, BN, LC, MW>(GemmArgs);
@@ -821,6 +1031,9 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 TG_RS_LIST(TG_INSTANTIATE_RS)
 TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 TG_HYBRID_LIST(TG_INSTANTIATE_HYBRID)
+#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, EFF) \
+    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS>(GemmArgs);
+TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 // The table holds host launch functions, so it exists only in the host pass.
 #ifndef __HIP_DEVICE_COMPILE__
@@ -838,8 +1051,12 @@ TG_HYBRID_LIST(TG_INSTANTIATE_HYBRID)
      ((S) * 256 * 64 > 512 * 64 ? (S) * 256 * 64 : 512 * 64), 256, 16, GM, EFF,                     \
      &tg::launch_hybrid<DT, S, P>},
 
+#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, EFF)                                                      \
+    {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
+     &tg::launch_wide<DT, GM, NS, RS>},
+
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
-                                             TG_HYBRID_LIST(TG_ENTRY_HYBRID)};
+                                             TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};
 constexpr int kCount = sizeof(kUnsorted) / sizeof(kUnsorted[0]);
 
 // The table is indexed by kernel id.

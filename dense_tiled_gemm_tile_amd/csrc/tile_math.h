@@ -63,6 +63,13 @@ TG_HD int lds_chunk_offset(int row, int chunk) {
 TG_HD int stage_chunk(int t) { return t & 7; }
 TG_HD int stage_row(int t, int i) { return (t >> 3) + 32 * i; }
 
+// LDS-DMA into 128-byte rows: one instruction moves 64 lanes x 16 bytes into
+// 1 KiB of LDS, lane t at byte 16*t of block j, i.e. row 8*j + t/8, physical
+// slot t%8.  The lane fetches the logical chunk the swizzle puts in that slot,
+// so each group of 8 lanes reads one whole 128-byte row segment.
+TG_HD int dma128_row(int j, int lane) { return 8 * j + (lane >> 3); }
+TG_HD int dma128_chunk(int j, int lane) { return (lane & 7) ^ lds_swizzle(dma128_row(j, lane)); }
+
 // ---------------------------------------------------------------- 64-byte rows
 //
 // The streaming (LDS-DMA) kernels stage 64 bytes of K per row per stage;

@@ -188,7 +188,36 @@ static void check_dma_layout(int rows) {
     }
 }
 
+// 128-byte-row DMA layout of the wide streaming kernel: lane t of block j lands
+// where the swizzled layout puts its logical chunk, every (row, chunk) of a
+// stage is written once, and each group of 8 lanes reads one whole row segment.
+static void check_dma128_layout(int rows) {
+    const int blocks = rows * kRowBytes / 1024;
+    std::vector<int> count(rows * kChunksPerRow, 0);
+    for (int j = 0; j < blocks; ++j)
+        for (int t = 0; t < 64; ++t) {
+            const int r = dma128_row(j, t), c = dma128_chunk(j, t);
+            CHECK(r < rows && c >= 0 && c < kChunksPerRow, "dma128 out of range");
+            CHECK(lds_chunk_offset(r, c) == j * 1024 + 16 * t, "dma128 lane %d of block %d lands elsewhere", t, j);
+            count[r * kChunksPerRow + c]++;
+        }
+    bool once = true;
+    for (int v : count) once = once && v == 1;
+    CHECK(once, "dma128 does not cover %d rows x 8 chunks exactly once", rows);
+    for (int j = 0; j < blocks; ++j)
+        for (int g = 0; g < 8; ++g) {
+            std::set<int> chunks;
+            for (int t = 8 * g; t < 8 * g + 8; ++t) {
+                CHECK(dma128_row(j, t) == dma128_row(j, 8 * g), "dma128 lane group %d spans rows", g);
+                chunks.insert(dma128_chunk(j, t));
+            }
+            CHECK(chunks.size() == 8, "dma128 lane group %d of block %d misses part of its row", g, j);
+        }
+}
+
 int main() {
+    check_dma128_layout(256);
+    check_dma128_layout(128);
     check_tile_order();
     check_dma_layout(256);
     check_dma_layout(128);
