@@ -68,7 +68,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square_8192_bf16_relu")
     ap.add_argument("--kernel-id", type=int, default=-1)
-    ap.add_argument("--cpu-cols", type=int, default=512,
+    ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns the CPU-baseline oracle computes (all rows, full K)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -102,16 +102,20 @@ def main() -> int:
     for _ in range(args.warmup):
         tg.gemm(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # one event before every launch and one after the last, all on the stream
+    # the kernel runs on: the whole-region average is the launch duration used
+    # for the throughput and the roofline, the per-launch median is reported too
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i].record(stream)
         tg.gemm(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
-    end.record(stream)
+    ev[args.steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
+    ms = ev[0].elapsed_time(ev[args.steps]) / args.steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    median_ms = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
@@ -134,6 +138,7 @@ def main() -> int:
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "median_ms_per_launch": round(median_ms, 4),
         "wall_s_timed_region": round(wall, 4),
         "roofline": {
             "bound": "mfma",

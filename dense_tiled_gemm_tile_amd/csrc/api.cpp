@@ -80,14 +80,16 @@ double plan_cost(const TgKernelDesc& k, int64_t M, int64_t N) {
     return double(cdiv(tiles, kCusPerGpu)) * double(k.block_m) * double(k.block_n) / (0.01 * k.eff_pct);
 }
 
-bool usable(const TgKernelDesc& k, int dtype, int cls) { return k.dtype == dtype && cls >= k.load_class; }
+bool usable(const TgKernelDesc& k, int dtype, int cls, int64_t row_stride) {
+    return k.dtype == dtype && cls >= k.load_class && (k.max_row_stride == 0 || row_stride <= k.max_row_stride);
+}
 
-int choose(int64_t M, int64_t N, int dtype, int cls) {
+int choose(int64_t M, int64_t N, int dtype, int cls, int64_t row_stride) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tg_kernel_table_size; ++i) {
         const TgKernelDesc& k = tg_kernel_table[i];
-        if (!usable(k, dtype, cls)) continue;
+        if (!usable(k, dtype, cls, row_stride)) continue;
         // among equal costs prefer the instance that needs the strongest alignment
         const double c = plan_cost(k, M, N) * (1.0 + 0.001 / k.load_class);
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
@@ -125,11 +127,12 @@ int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
     if (rc) return rc;
     const int es = elem_size(dtype);
     const int cls = row_class(M, N, A, lda, B, ldb, es);
+    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
     int id = kernel_id;
     if (id < 0) {
-        id = choose(M, N, dtype, cls);
+        id = choose(M, N, dtype, cls, row_stride);
         if (id < 0) return TG_ERR_PLAN;
-    } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls)) {
+    } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls, row_stride)) {
         return TG_ERR_PLAN;
     }
     describe(tg_kernel_table[id], M, N, out);

@@ -316,7 +316,30 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds) {
                  : "v"(g), "s"(lds)
                  : "memory", "m0");
 }
+// The same copy through a buffer resource: base and byte range in SGPRs
+// (`rsrc`), a 32-bit per-lane offset `voff` and a wave-uniform offset `soff`.
+// Lanes whose offset falls outside the range write zeros instead of reading.
+// Half the per-lane address data of dma16, and no per-copy vector arithmetic.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, unsigned voff, unsigned soff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(lds), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Raw buffer resource over [base, base + bytes) (gfx9 layout: 48-bit base,
+// stride 0, byte count, 32-bit data format word); every field wave-uniform.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, unsigned bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    r.w = 0x00020000;
+    return r;
+}
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
@@ -564,7 +587,7 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t str
 //   stage s's A half just left
 // A slot is refilled only after the barrier that ends the reads of the
 // half-stage NS places earlier, which the two copy points respect.
-template <int DT, int GM, int NS, int RS>
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256, WM = 2;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
@@ -578,6 +601,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     constexpr int SLOT = BM * kRowBytes;         // 32 KiB
     static_assert(BM == BN && NC == 8 && MF == 16, "schedule assumes 8 copies per half-stage, 16 MFMAs a slab");
     static_assert(NS == 4 || NS == 5, "4 or 5 half-stage slots");
+    static_assert(SCHED == 0 || NS == 5, "the spread copy schedule needs 5 slots");
     static_assert(RS >= 1 && RS <= MF, "reads spread over at most one slab");
 
     __shared__ __attribute__((aligned(1024))) char smem[NS * SLOT];
@@ -594,20 +618,42 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     const unsigned lds_base = __builtin_amdgcn_readfirstlane(
         static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
 
-    // copy sources (rows past M or N clamp to the last row)
+    // copy sources.  ADDR 0: 64-bit addresses, rows past M or N clamp to
+    // the last row.  ADDR 1: buffer resources over the tile's valid rows, 32-bit
+    // row offsets (the plan keeps 256 * stride below 2^31); rows past M or N
+    // fall outside the range and load zeros.  Either way those rows only feed
+    // accumulators that are never stored.
     const char* src[2][NC];
+    unsigned voff[2][NC];
+    i32x4 rsrc[2];
+    if constexpr (ADDR == 0) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int j = wave * NC + i;
-        src[0][i] = p.A + static_cast<int64_t>(min(m0 + dma128_row(j, lane), M - 1)) * p.lda_b +
-                    dma128_chunk(j, lane) * kChunkBytes;
-        src[1][i] = p.B + static_cast<int64_t>(min(n0 + dma128_row(j, lane), N - 1)) * p.ldb_b +
-                    dma128_chunk(j, lane) * kChunkBytes;
+        for (int i = 0; i < NC; ++i) {
+            const int j = wave * NC + i;
+            src[0][i] = p.A + static_cast<int64_t>(min(m0 + dma128_row(j, lane), M - 1)) * p.lda_b +
+                        dma128_chunk(j, lane) * kChunkBytes;
+            src[1][i] = p.B + static_cast<int64_t>(min(n0 + dma128_row(j, lane), N - 1)) * p.ldb_b +
+                        dma128_chunk(j, lane) * kChunkBytes;
+        }
+    } else {
+        rsrc[0] = buffer_rsrc(p.A + static_cast<int64_t>(m0) * p.lda_b,
+                              static_cast<unsigned>(min(BM, M - m0) * p.lda_b));
+        rsrc[1] = buffer_rsrc(p.B + static_cast<int64_t>(n0) * p.ldb_b,
+                              static_cast<unsigned>(min(BN, N - n0) * p.ldb_b));
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int j = wave * NC + i;
+            voff[0][i] = static_cast<unsigned>(dma128_row(j, lane) * p.lda_b) + dma128_chunk(j, lane) * kChunkBytes;
+            voff[1][i] = static_cast<unsigned>(dma128_row(j, lane) * p.ldb_b) + dma128_chunk(j, lane) * kChunkBytes;
+        }
     }
     // copy i of operand o (0: A, 1: B) of stage t into slot `slot`
     auto copy = [&](int o, int i, int t, int slot) {
-        dma16(src[o][i] + static_cast<int64_t>(t) * kRowBytes,
-              __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + i) * 1024));
+        const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + i) * 1024);
+        if constexpr (ADDR == 0)
+            dma16(src[o][i] + static_cast<int64_t>(t) * kRowBytes, dst);
+        else
+            dma16_buf(rsrc[o], voff[o][i], __builtin_amdgcn_readfirstlane(t * kRowBytes), dst);
     };
     auto wrap = [](int x) { return x >= NS ? x - NS : x; };
 
@@ -649,11 +695,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     if (nfull > 0) {
         // prologue: half-stages 0 .. NS-2 (a stage index past the last full
         // stage reloads that stage, so the copy counts stay uniform)
+        constexpr int PRO = (SCHED == 0) ? (NS - 1) * NC : 3 * NC + NC / 2;  // prologue copies
 #pragma unroll
-        for (int h = 0; h < NS - 1; ++h)
-#pragma unroll
-            for (int i = 0; i < NC; ++i) copy(h & 1, i, min(h >> 1, nfull - 1), h);
-        wait_vm<(NS - 3) * NC>();
+        for (int c = 0; c < PRO; ++c) {
+            const int h = c / NC;
+            copy(h & 1, c % NC, min(h >> 1, nfull - 1), h);
+        }
+        wait_vm<PRO - 2 * NC>();
         barrier();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
@@ -666,15 +714,29 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             const int t0 = min(s + (H0 >> 1), nfull - 1);       // stage of half-stage 2s + H0
             const int t3 = min(s + ((H0 + 1) >> 1), nfull - 1); // stage of half-stage 2s + H0 + 1
             const int slot_h0 = wrap(slot0 + NS - 1);
+            // SCHED 1 (5 slots): one copy every 4 MFMAs through the whole stage --
+            // the second half of B(s+1) in slab 0, A(s+2) in slabs 1-2 and the
+            // first half of B(s+2) in slab 3 -- instead of bursts in slabs 0 and 3
+            const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
             slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
                 reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
-                if (m & 1) copy(H0 & 1, m >> 1, t0, slot_h0);
+                if constexpr (SCHED == 0) {
+                    if (m & 1) copy(H0 & 1, m >> 1, t0, slot_h0);
+                } else {
+                    if ((m & 3) == 1) copy(1, NC / 2 + (m >> 2), t1, nb);
+                }
             });
             slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
                 reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); });
+                if constexpr (SCHED == 1) {
+                    if ((m & 3) == 1) copy(0, m >> 2, t2, slot_h0);
+                }
             });
             slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
                 reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); });
+                if constexpr (SCHED == 1) {
+                    if ((m & 3) == 1) copy(0, NC / 2 + (m >> 2), t2, slot_h0);
+                }
             });
             asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
             wait_vm<(NS - 4) * NC>();
@@ -682,7 +744,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             // on the last stage the reads below fetch values that go unused
             slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
                 reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
-                if (m & 1) copy((H0 + 1) & 1, m >> 1, t3, sa);
+                if constexpr (SCHED == 0) {
+                    if (m & 1) copy((H0 + 1) & 1, m >> 1, t3, sa);
+                } else {
+                    if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
+                }
             });
             slot0 = na;
         }
@@ -737,9 +803,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     }
 }
 
-template <int DT, int GM, int NS, int RS>
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED>
 static hipError_t launch_wide(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1015,11 +1081,17 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     X(14, TG_F16, 5, 2, 4, 75)
 
 #define TG_WIDE_LIST(X)                         \
-    X(15, TG_BF16, 4, 5, 16, 105)               \
-    X(16, TG_F16, 4, 5, 16, 105)                \
-    X(17, TG_F32, 4, 5, 16, 40)                 \
-    X(18, TG_BF16, 4, 4, 16, 10)                \
-    X(19, TG_BF16, 4, 5, 8, 10)
+    X(15, TG_BF16, 4, 5, 16, 0, 0, 105)         \
+    X(16, TG_F16, 4, 5, 16, 0, 0, 105)          \
+    X(17, TG_F32, 4, 5, 16, 0, 0, 40)           \
+    X(18, TG_BF16, 4, 4, 16, 0, 0, 10)          \
+    X(19, TG_BF16, 4, 5, 8, 0, 0, 10)           \
+    X(20, TG_BF16, 4, 5, 8, 1, 0, 10)           \
+    X(21, TG_BF16, 4, 5, 16, 1, 0, 10)          \
+    X(22, TG_BF16, 4, 5, 16, 1, 1, 107)         \
+    X(23, TG_BF16, 4, 5, 8, 1, 1, 10)           \
+    X(24, TG_F16, 4, 5, 16, 1, 1, 107)          \
+    X(25, TG_F32, 4, 5, 16, 1, 1, 41)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
@@ -1031,8 +1103,8 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 TG_RS_LIST(TG_INSTANTIATE_RS)
 TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 TG_HYBRID_LIST(TG_INSTANTIATE_HYBRID)
-#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, EFF) \
-    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS>(GemmArgs);
+#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EFF) \
+    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED>(GemmArgs);
 TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 // The table holds host launch functions, so it exists only in the host pass.
@@ -1051,9 +1123,9 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
      ((S) * 256 * 64 > 512 * 64 ? (S) * 256 * 64 : 512 * 64), 256, 16, GM, EFF,                     \
      &tg::launch_hybrid<DT, S, P>},
 
-#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, EFF)                                                      \
+#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EFF)                                         \
     {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
-     &tg::launch_wide<DT, GM, NS, RS>},
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED>, (ADDR) ? (int64_t(1) << 23) : 0},
 
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
                                              TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};

@@ -37,6 +37,7 @@ struct TgKernelDesc {
     int group_m;
     int eff_pct;       // expected MFMA efficiency, weighs tiles in the plan chooser
     TgLaunchFn launch;
+    int64_t max_row_stride;  // largest lda/ldb in bytes the instance can address (0: any)
 };
 
 // Indexed by kernel id.

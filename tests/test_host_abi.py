@@ -127,3 +127,26 @@ def test_every_instance_has_consistent_ownership_arithmetic():
         assert row_bytes in (64, 128)
         # every instance keeps at least its A stages in LDS, within the 160 KiB of a CU
         assert info.stages * info.block_m * row_bytes <= info.lds_bytes <= 160 * 1024
+
+
+def test_row_stride_limited_instances_are_refused_for_huge_strides():
+    """Instances that address a tile through 32-bit byte offsets (256 rows x
+    stride < 2^31) refuse larger strides; the planner then takes another."""
+    W = si.WORKLOADS["square_8192_bf16_relu"]
+    huge = (1 << 22) + 64  # elements: 8 MiB + 128 bytes per bf16 row
+    a, b, d = 0x100000000000, 0x200000000000, 0x300000000000  # far apart: no overlap
+    small_plan = _plan(W)
+    refused = []
+    for k in range(tg.kernel_count()):
+        info = tg.kernel_info(k)
+        if info.dtype != tg.BF16:
+            continue
+        try:
+            tg.query_plan(512, 512, W.K, tg.BF16, a, huge, b, huge, d, 512, k)
+        except tg.TileGemmError as e:
+            assert e.code == -9
+            refused.append(k)
+    assert refused, "no stride-limited instance"
+    assert small_plan.kernel_id in refused  # the default for ordinary strides is one of them
+    p = tg.query_plan(512, 512, W.K, tg.BF16, a, huge, b, huge, d, 512, -1)
+    assert p.kernel_id not in refused and p.load_class == 16
