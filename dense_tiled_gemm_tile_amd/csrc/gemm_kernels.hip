@@ -587,7 +587,16 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t str
 //   stage s's A half just left
 // A slot is refilled only after the barrier that ends the reads of the
 // half-stage NS places earlier, which the two copy points respect.
-template <int DT, int GM, int NS, int RS, int ADDR, int SCHED>
+//
+// Knobs: GM tile-order group; RS = the MFMAs of a slab over which its 8
+// fragment reads are spread; ADDR 0 = 64-bit per-lane addresses, 1 = buffer
+// resources with 32-bit offsets; SCHED 0 = copies in bursts in slabs 0 and 3,
+// 1 = one copy every 4 MFMAs over the whole stage (5 slots); EPI bit 0 =
+// nontemporal D stores (D lines then do not displace operand panels in L2,
+// measured ~2 % faster main loop), bit 1 = transpose through LDS so each store
+// writes a whole 1 KiB row run (measured no faster: the D write burst at the
+// end of a tile is bound by memory bandwidth either way).
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256, WM = 2;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
@@ -781,31 +790,85 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         }
     }
 
-    // epilogue: alpha, optional ReLU, masked store by ownership
+    // epilogue: alpha, then ReLU, in registers
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
-    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
-            const int nbase = n0 + wave_n * WTN + 32 * i;
-            float* col = p.D + m;
+        for (int j = 0; j < FM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int n = nbase + acc_row(lane, r);
                 float v = acc[i][j][r] * alpha;
-                if (relu) v = fmaxf(v, 0.0f);
-                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+                acc[i][j][r] = relu ? fmaxf(v, 0.0f) : v;
             }
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    auto put = [&](float* dst, float v) {
+        if constexpr (EPI & 1)
+            __builtin_nontemporal_store(v, dst);
+        else
+            *dst = v;
+    };
+    const bool rows16 = (reinterpret_cast<uintptr_t>(p.D) & 15) == 0 && (p.ldd & 3) == 0;
+    if (EPI < 2 || !interior || !rows16) {
+        // store by ownership: each instruction writes 2 x 128 contiguous bytes
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+                const int nbase = n0 + wave_n * WTN + 32 * i;
+                float* col = p.D + m;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = nbase + acc_row(lane, r);
+                    if (interior || (m < M && n < N)) put(col + static_cast<int64_t>(n) * p.ldd, acc[i][j][r]);
+                }
+            }
+        }
+    } else {
+        // interior tile with 16-byte aligned D rows: transpose through LDS so
+        // that each store instruction writes one whole 1 KiB row run of the
+        // tile (256 consecutive m), which the memory system drains faster
+        // than scattered 128-byte pieces.  Two passes of 128 rows (n); the
+        // row pitch of 1056 bytes keeps the two half-waves of each LDS write
+        // on disjoint banks.
+        constexpr int PITCH = 1056;
+        static_assert(EPI < 2 || 128 * PITCH <= NS * SLOT, "transpose buffer fits the ring");
+        __syncthreads();  // every wave is done with the ring
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if (wave_n == pass) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int nl = 32 * i + acc_row(lane, r);
+                            const int ml = wave_m * WTM + 32 * j + acc_col(lane);
+                            *reinterpret_cast<float*>(smem + nl * PITCH + ml * 4) = acc[i][j][r];
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                const int nl = 32 * wave + q;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(smem + nl * PITCH + lane * 16);
+                f32x4* dst = reinterpret_cast<f32x4*>(p.D + static_cast<int64_t>(n0 + 128 * pass + nl) * p.ldd + m0) + lane;
+                if constexpr (EPI & 1)
+                    __builtin_nontemporal_store(v, dst);
+                else
+                    *dst = v;
+            }
+            __syncthreads();
         }
     }
 }
 
-template <int DT, int GM, int NS, int RS, int ADDR, int SCHED>
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 static hipError_t launch_wide(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1081,17 +1144,20 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     X(14, TG_F16, 5, 2, 4, 75)
 
 #define TG_WIDE_LIST(X)                         \
-    X(15, TG_BF16, 4, 5, 16, 0, 0, 105)         \
-    X(16, TG_F16, 4, 5, 16, 0, 0, 105)          \
-    X(17, TG_F32, 4, 5, 16, 0, 0, 40)           \
-    X(18, TG_BF16, 4, 4, 16, 0, 0, 10)          \
-    X(19, TG_BF16, 4, 5, 8, 0, 0, 10)           \
-    X(20, TG_BF16, 4, 5, 8, 1, 0, 10)           \
-    X(21, TG_BF16, 4, 5, 16, 1, 0, 10)          \
-    X(22, TG_BF16, 4, 5, 16, 1, 1, 107)         \
-    X(23, TG_BF16, 4, 5, 8, 1, 1, 10)           \
-    X(24, TG_F16, 4, 5, 16, 1, 1, 107)          \
-    X(25, TG_F32, 4, 5, 16, 1, 1, 41)
+    X(15, TG_BF16, 4, 5, 16, 0, 0, 0, 105)      \
+    X(16, TG_F16, 4, 5, 16, 0, 0, 0, 105)       \
+    X(17, TG_F32, 4, 5, 16, 0, 0, 0, 40)        \
+    X(18, TG_BF16, 4, 4, 16, 0, 0, 0, 10)       \
+    X(19, TG_BF16, 4, 5, 8, 0, 0, 0, 10)        \
+    X(20, TG_BF16, 4, 5, 8, 1, 0, 0, 10)        \
+    X(21, TG_BF16, 4, 5, 16, 1, 0, 0, 10)       \
+    X(22, TG_BF16, 4, 5, 16, 1, 1, 1, 107)      \
+    X(23, TG_BF16, 4, 5, 8, 1, 1, 1, 10)        \
+    X(24, TG_F16, 4, 5, 16, 1, 1, 1, 107)       \
+    X(25, TG_F32, 4, 5, 16, 1, 1, 1, 41)        \
+    X(26, TG_BF16, 4, 5, 16, 1, 1, 0, 10)       \
+    X(27, TG_BF16, 4, 5, 16, 1, 1, 2, 10)       \
+    X(28, TG_BF16, 4, 5, 16, 1, 1, 3, 10)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
@@ -1103,8 +1169,8 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 TG_RS_LIST(TG_INSTANTIATE_RS)
 TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 TG_HYBRID_LIST(TG_INSTANTIATE_HYBRID)
-#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EFF) \
-    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED>(GemmArgs);
+#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF) \
+    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>(GemmArgs);
 TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 // The table holds host launch functions, so it exists only in the host pass.
@@ -1123,9 +1189,9 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
      ((S) * 256 * 64 > 512 * 64 ? (S) * 256 * 64 : 512 * 64), 256, 16, GM, EFF,                     \
      &tg::launch_hybrid<DT, S, P>},
 
-#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EFF)                                         \
+#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                    \
     {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
-     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED>, (ADDR) ? (int64_t(1) << 23) : 0},
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0},
 
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
                                              TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};
