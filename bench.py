@@ -68,6 +68,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square_8192_bf16_relu")
     ap.add_argument("--kernel-id", type=int, default=-1)
+    ap.add_argument("--out-dtype", choices=["f32", "bf16", "f16"], default="f32",
+                    help="element type of D (bf16/f16: fp32 epilogue rounded on the way out)")
     ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns the CPU-baseline oracle computes (all rows, full K)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,7 +96,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     A_st, B_st = si.workload_operands(w)
     A, B = A_st.to(dev), B_st.to(dev)
-    D = si.out_storage(w.M, w.N, w.ldd).to(dev)
+    out_torch = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.out_dtype]
+    D = si.out_storage(w.M, w.N, w.ldd).to(out_torch).to(dev)
     Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
     plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
     stream = torch.cuda.current_stream(dev)
@@ -134,6 +137,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                    "ldd": w.ldd, "alpha": w.alpha, "relu": w.relu, "dist": w.dist,
+                   "out_dtype": args.out_dtype,
                    "kernel_id": plan.kernel_id,
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},
@@ -146,7 +150,8 @@ def main() -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": traffic_for(w.name, plan.kernel_id),
+            "traffic": traffic_for(w.name if args.out_dtype == "f32" else f"{w.name}:out_{args.out_dtype}",
+                                   plan.kernel_id),
         },
     }
 
@@ -170,8 +175,13 @@ def main() -> int:
             "sample": f"output columns n < {cols} of the {w.M}x{w.N}x{w.K} workload (all m, full K), "
                       f"fp64; {cpu_s:.2f} s wall",
         }
-        d = D[:cols, :w.M].double().cpu().numpy()
-        ok, ratio = oracle.check(d, ref, mag, w.K)
+        if args.out_dtype == "f32":
+            d = D[:cols, :w.M].double().cpu().numpy()
+            ok, ratio = oracle.check(d, ref, mag, w.K)
+        else:
+            raw = D[:cols, :w.M].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            d = oracle.decode(raw, args.out_dtype)
+            ok, ratio = oracle.check_out(d, ref, mag, w.K, args.out_dtype)
         result["parity"] = {"entries": int(d.size), "ok": bool(ok and not np.isnan(d).any()),
                             "worst_err_over_tol": round(ratio, 5)}
     print(json.dumps(result), flush=True)

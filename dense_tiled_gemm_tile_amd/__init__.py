@@ -7,7 +7,8 @@ another path.
 
 Storage conventions (Tylo.jl manual, "Walk through GEMM", section 2): A is
 logically (M,K) stored K-contiguous, B is logically (K,N) stored
-K-contiguous, D is logically (M,N) fp32 stored M-contiguous.  ``gemm`` takes
+K-contiguous, D is logically (M,N) stored M-contiguous, fp32 (or bf16/fp16
+through ``tile_gemm_out``).  ``gemm`` takes
 torch views with exactly those logical shapes and unit strides along K (A, B)
 and along M (D), e.g. ``A = A_st[:, :K]``, ``B = B_st[:, :K].t()``,
 ``D = D_st[:, :M].t()`` for row-major storages A_st (M, lda), B_st (N, ldb),
@@ -56,8 +57,12 @@ _i64, _ptr, _int, _f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c
 _SIGNATURES = {
     "tile_gemm": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr]),
     "tile_gemm_ex": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _int]),
+    "tile_gemm_out": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                             _ptr, _int]),
     "tile_gemm_query_plan": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int,
                                     ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                                        ctypes.POINTER(PlanInfo)]),
     "tile_gemm_kernel_count": (_int, []),
     "tile_gemm_kernel_info": (_int, [_int, ctypes.POINTER(PlanInfo)]),
     "tile_gemm_strerror": (ctypes.c_char_p, [_int]),
@@ -111,11 +116,22 @@ def tile_gemm_ex(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, stream=Non
                                        dtype, stream, kernel_id)
 
 
-def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1) -> PlanInfo:
+def tile_gemm_out(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream=None,
+                  kernel_id=-1) -> int:
+    return load_library().tile_gemm_out(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd,
+                                        dtype, out_dtype, stream, kernel_id)
+
+
+def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1, out_dtype=F32) -> PlanInfo:
     """Host-only plan query; raises TileGemmError on invalid arguments."""
     info = PlanInfo()
-    _check(load_library().tile_gemm_query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id,
-                                               ctypes.byref(info)))
+    if out_dtype == F32:
+        rc = load_library().tile_gemm_query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id,
+                                                 ctypes.byref(info))
+    else:
+        rc = load_library().tile_gemm_query_plan_out(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype,
+                                                     kernel_id, ctypes.byref(info))
+    _check(rc)
     return info
 
 
@@ -147,8 +163,8 @@ def _operand_args(A, B, D):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
     if A.dtype != B.dtype or A.dtype not in codes:
         raise TypeError(f"A and B must share a dtype in {list(codes)}; got {A.dtype}, {B.dtype}")
-    if D.dtype != torch.float32:
-        raise TypeError("D must be float32")
+    if D.dtype not in codes:
+        raise TypeError(f"D must have a dtype in {list(codes)}; got {D.dtype}")
     if not (A.is_cuda and B.is_cuda and D.is_cuda):
         raise ValueError("A, B and D must be device tensors")
     if (K > 1 and A.stride(1) != 1) or (K > 1 and B.stride(0) != 1) or (M > 1 and D.stride(0) != 1):
@@ -156,28 +172,36 @@ def _operand_args(A, B, D):
     lda = A.stride(0) if (M > 1 and K > 0) else max(K, 1)
     ldb = B.stride(1) if (N > 1 and K > 0) else max(K, 1)
     ldd = D.stride(1) if N > 1 else max(M, 1)
-    return M, N, K, lda, ldb, ldd, codes[A.dtype]
+    return M, N, K, lda, ldb, ldd, codes[A.dtype], codes[D.dtype]
 
 
 def gemm(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, kernel_id: int = -1):
     """D = alpha*A@B (+ReLU) on the GPU through the C ABI; returns D.
 
     A: (M,K) view with stride (lda, 1); B: (K,N) view with stride (1, ldb);
-    D: (M,N) float32 view with stride (1, ldd).  The kernel is enqueued on
-    `stream` (a torch.cuda.Stream, default: the current stream of D's device).
+    D: (M,N) view with stride (1, ldd), float32 (tile_gemm_ex) or
+    bfloat16/float16 (tile_gemm_out: fp32 epilogue rounded on the way out).
+    The kernel is enqueued on `stream` (a torch.cuda.Stream, default: the
+    current stream of D's device).
     """
     import torch
 
-    M, N, K, lda, ldb, ldd, dt = _operand_args(A, B, D)
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
     if stream is None:
         stream = torch.cuda.current_stream(D.device)
     with torch.cuda.device(D.device):
-        _check(tile_gemm_ex(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb,
-                            D.data_ptr(), ldd, dt, stream.cuda_stream, kernel_id))
+        if ot == F32:
+            rc = tile_gemm_ex(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb,
+                              D.data_ptr(), ldd, dt, stream.cuda_stream, kernel_id)
+        else:
+            rc = tile_gemm_out(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb,
+                               D.data_ptr(), ldd, dt, ot, stream.cuda_stream, kernel_id)
+        _check(rc)
     return D
 
 
 def plan_for(A, B, D, kernel_id: int = -1) -> PlanInfo:
-    """The plan ``gemm`` would launch for these views."""
-    M, N, K, lda, ldb, ldd, dt = _operand_args(A, B, D)
-    return query_plan(M, N, K, dt, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd, kernel_id)
+    """The plan ``gemm`` would launch for these views (the plan does not depend
+    on the output type)."""
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
+    return query_plan(M, N, K, dt, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd, kernel_id, ot)

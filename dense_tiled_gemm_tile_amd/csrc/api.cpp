@@ -36,21 +36,22 @@ int elem_size(int dtype) {
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
 int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-             int64_t ldb, const float* D, int64_t ldd, int dtype) {
+             int64_t ldb, const void* D, int64_t ldd, int dtype, int out_dtype) {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TG_ERR_DIMS;
     const int es = elem_size(dtype);
-    if (!es) return TG_ERR_DTYPE;
+    const int os = elem_size(out_dtype);
+    if (!es || !os) return TG_ERR_DTYPE;
     const int64_t kmin = K > 1 ? K : 1;
     if (lda < kmin || ldb < kmin || ldd < (M > 1 ? M : 1)) return TG_ERR_LD;
     if (M == 0 || N == 0) return TG_OK;
     const bool reads = K > 0;
     if (!D || (reads && (!A || !B))) return TG_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(D) & 3u) ||
+    if ((reinterpret_cast<uintptr_t>(D) & uintptr_t(os - 1)) ||
         (reads && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & uintptr_t(es - 1))))
         return TG_ERR_ALIGN;
     if (reads) {
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
-        const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * 4u;
+        const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
         const uintptr_t a0 = reinterpret_cast<uintptr_t>(A);
         const uintptr_t a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(B);
@@ -122,8 +123,8 @@ void describe(const TgKernelDesc& k, int64_t M, int64_t N, tile_gemm_plan_info* 
 }
 
 int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
-         int64_t ldb, const float* D, int64_t ldd, int kernel_id, tile_gemm_plan_info* out) {
-    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype);
+         int64_t ldb, const void* D, int64_t ldd, int out_dtype, int kernel_id, tile_gemm_plan_info* out) {
+    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype);
     if (rc) return rc;
     const int es = elem_size(dtype);
     const int cls = row_class(M, N, A, lda, B, ldb, es);
@@ -173,14 +174,21 @@ int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype, const void*
                          const void* B, int64_t ldb, const float* D, int64_t ldd, int kernel_id,
                          tile_gemm_plan_info* out) {
     if (!out) return TG_ERR_NULL;
-    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id, out);
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, TG_F32, kernel_id, out);
 }
 
-int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
-                 int64_t lda, const void* B, int64_t ldb, float* D, int64_t ldd, int dtype,
-                 void* stream, int kernel_id) {
+int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, const void* D, int64_t ldd, int out_dtype,
+                             int kernel_id, tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out);
+}
+
+int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
+                  int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int dtype,
+                  int out_dtype, void* stream, int kernel_id) {
     tile_gemm_plan_info pl;
-    int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id, &pl);
+    int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, &pl);
     if (rc) return rc;
     if (M == 0 || N == 0) return TG_OK;
     rc = device_ok();
@@ -201,13 +209,20 @@ int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const v
     a.tiles_m = static_cast<int>(pl.tiles_m);
     a.tiles_n = static_cast<int>(pl.tiles_n);
     a.group_m = pl.group_m;
+    a.out_dtype = out_dtype;
     const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
+int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
+                 int64_t lda, const void* B, int64_t ldb, float* D, int64_t ldd, int dtype,
+                 void* stream, int kernel_id) {
+    return tile_gemm_out(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, TG_F32, stream, kernel_id);
+}
+
 int tile_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
               const void* B, int64_t ldb, float* D, int64_t ldd, int dtype, void* stream) {
-    return tile_gemm_ex(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, stream, -1);
+    return tile_gemm_out(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, TG_F32, stream, -1);
 }
 
 int tile_gemm_kernel_count(void) { return tg_kernel_table_size; }
@@ -226,7 +241,7 @@ const char* tile_gemm_strerror(int code) {
         case TG_ERR_LD: return "leading stride too small (lda,ldb >= max(1,K); ldd >= max(1,M))";
         case TG_ERR_NULL: return "null pointer for an operand that is read or written";
         case TG_ERR_ALIGN: return "pointer not aligned to its element size";
-        case TG_ERR_DTYPE: return "unknown operand dtype";
+        case TG_ERR_DTYPE: return "unknown operand or output dtype";
         case TG_ERR_ALIAS: return "output overlaps an input operand";
         case TG_ERR_LAUNCH: return "HIP kernel launch failed";
         case TG_ERR_DEVICE: return "no current gfx950 HIP device";

@@ -129,6 +129,49 @@ __device__ __forceinline__ f32x16 mfma_slab(u32x4 nfrag, u32x4 mfrag, f32x16 acc
     }
 }
 
+// ---------------------------------------------------------------- output
+
+// fp32 -> bfloat16, round to nearest even (the upper 16 bits of the binary32
+// after adding half an ulp of the target, plus one when the kept part is odd);
+// NaN stays a quiet NaN.
+__device__ __forceinline__ unsigned short bf16_rne(float f) {
+    const unsigned u = __builtin_bit_cast(unsigned, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<unsigned short>((u >> 16) | 0x40u);
+    return static_cast<unsigned short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Store epilogue value v to element idx of D in output type OUT (cuTile.jl
+// tutorial "Matrix Multiplication", Step 4: keep the fp32 accumulator and
+// convert on the way out).  fp16 uses the hardware conversion (round to
+// nearest even, overflow to infinity, subnormals kept).
+template <int OUT, bool NT = false>
+__device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
+    if constexpr (OUT == TG_F32) {
+        float* d = static_cast<float*>(D) + idx;
+        if constexpr (NT) __builtin_nontemporal_store(v, d); else *d = v;
+    } else if constexpr (OUT == TG_BF16) {
+        unsigned short* d = static_cast<unsigned short*>(D) + idx;
+        const unsigned short b = bf16_rne(v);
+        if constexpr (NT) __builtin_nontemporal_store(b, d); else *d = b;
+    } else {
+        _Float16* d = static_cast<_Float16*>(D) + idx;
+        const _Float16 h = static_cast<_Float16>(v);
+        if constexpr (NT) __builtin_nontemporal_store(h, d); else *d = h;
+    }
+}
+
+// Run f with the output type as a compile-time constant (one uniform branch
+// per kernel, outside the unrolled store loops).
+template <typename F>
+__device__ __forceinline__ void with_out_type(int out, F&& f) {
+    if (out == TG_BF16)
+        f(std::integral_constant<int, TG_BF16>{});
+    else if (out == TG_F16)
+        f(std::integral_constant<int, TG_F16>{});
+    else
+        f(std::integral_constant<int, TG_F32>{});
+}
+
 // ---------------------------------------------------------------- kernel
 
 template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES>
@@ -274,22 +317,24 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    with_out_type(p.out_dtype, [&](auto out) {
+        constexpr int OUT = decltype(out)::value;
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+        for (int i = 0; i < FN; ++i) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
-            const int nb = n0 + wave_n * WTN + 32 * i;
-            float* col = p.D + m;
+            for (int j = 0; j < FM; ++j) {
+                const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+                const int nb = n0 + wave_n * WTN + 32 * i;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = nb + acc_row(lane, r);
-                float v = acc[i][j][r] * alpha;
-                if (relu) v = fmaxf(v, 0.0f);
-                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+                for (int r = 0; r < 16; ++r) {
+                    const int n = nb + acc_row(lane, r);
+                    float v = acc[i][j][r] * alpha;
+                    if (relu) v = fmaxf(v, 0.0f);
+                    if (interior || (m < M && n < N)) store_out<OUT>(p.D, static_cast<int64_t>(n) * p.ldd + m, v);
+                }
             }
         }
-    }
+    });
 }
 
 // ---------------------------------------------------------------- streaming kernel
@@ -538,22 +583,24 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    with_out_type(p.out_dtype, [&](auto out) {
+        constexpr int OUT = decltype(out)::value;
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+        for (int i = 0; i < FN; ++i) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
-            const int nb = n0 + wave_n * WTN + 32 * i;
-            float* col = p.D + m;
+            for (int j = 0; j < FM; ++j) {
+                const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+                const int nb = n0 + wave_n * WTN + 32 * i;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = nb + acc_row(lane, r);
-                float v = acc[i][j][r] * alpha;
-                if (relu) v = fmaxf(v, 0.0f);
-                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+                for (int r = 0; r < 16; ++r) {
+                    const int n = nb + acc_row(lane, r);
+                    float v = acc[i][j][r] * alpha;
+                    if (relu) v = fmaxf(v, 0.0f);
+                    if (interior || (m < M && n < N)) store_out<OUT>(p.D, static_cast<int64_t>(n) * p.ldd + m, v);
+                }
             }
         }
-    }
+    });
 }
 
 template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
@@ -593,9 +640,11 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t str
 // resources with 32-bit offsets; SCHED 0 = copies in bursts in slabs 0 and 3,
 // 1 = one copy every 4 MFMAs over the whole stage (5 slots); EPI bit 0 =
 // nontemporal D stores (D lines then do not displace operand panels in L2,
-// measured ~2 % faster main loop), bit 1 = transpose through LDS so each store
-// writes a whole 1 KiB row run (measured no faster: the D write burst at the
-// end of a tile is bound by memory bandwidth either way).
+// measured ~2 % faster main loop), bit 1 = fp32 D through an LDS transpose so
+// each store writes a whole 1 KiB row run (measured no faster: the D write
+// burst at the end of a tile is bound by memory bandwidth either way), bit 2 =
+// the same for bf16/fp16 D, whose direct stores would write 64-byte halves of
+// lines.
 template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256, WM = 2;
@@ -803,29 +852,70 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 acc[i][j][r] = relu ? fmaxf(v, 0.0f) : v;
             }
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
-    auto put = [&](float* dst, float v) {
-        if constexpr (EPI & 1)
-            __builtin_nontemporal_store(v, dst);
-        else
-            *dst = v;
-    };
-    const bool rows16 = (reinterpret_cast<uintptr_t>(p.D) & 15) == 0 && (p.ldd & 3) == 0;
-    if (EPI < 2 || !interior || !rows16) {
-        // store by ownership: each instruction writes 2 x 128 contiguous bytes
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
+    const bool trans32 = (EPI & 2) && p.out_dtype == TG_F32 && interior && aligned16 && (p.ldd & 3) == 0;
+    const bool trans16 = (EPI & 4) && p.out_dtype != TG_F32 && interior && aligned16 && (p.ldd & 7) == 0;
+    if (!trans32 && !trans16) {
+        // store by ownership: each instruction writes 2 x 32 consecutive m
+        with_out_type(p.out_dtype, [&](auto out) {
+            constexpr int OUT = decltype(out)::value;
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
+            for (int i = 0; i < FN; ++i) {
 #pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
-                const int nbase = n0 + wave_n * WTN + 32 * i;
-                float* col = p.D + m;
+                for (int j = 0; j < FM; ++j) {
+                    const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+                    const int nbase = n0 + wave_n * WTN + 32 * i;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int n = nbase + acc_row(lane, r);
-                    if (interior || (m < M && n < N)) put(col + static_cast<int64_t>(n) * p.ldd, acc[i][j][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        const int n = nbase + acc_row(lane, r);
+                        if (interior || (m < M && n < N))
+                            store_out<OUT, (EPI & 1) != 0>(p.D, static_cast<int64_t>(n) * p.ldd + m, acc[i][j][r]);
+                    }
                 }
             }
-        }
+        });
+    } else if (trans16) {
+        // 16-bit D, interior tile, 16-byte aligned rows: the whole rounded
+        // tile (256 x 256 x 2 bytes) goes through LDS in one pass and each
+        // store instruction writes two whole 512-byte row runs, instead of
+        // 64-byte pieces of lines that other instructions complete later.
+        constexpr int PITCH16 = 528;
+        static_assert((EPI & 4) == 0 || 256 * PITCH16 <= NS * SLOT, "16-bit tile fits the ring");
+        __syncthreads();  // every wave is done with the ring
+        with_out_type(p.out_dtype, [&](auto out) {
+            constexpr int OUT = decltype(out)::value;
+            if constexpr (OUT != TG_F32) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int nl = wave_n * WTN + 32 * i + acc_row(lane, r);
+                            const int ml = wave_m * WTM + 32 * j + acc_col(lane);
+                            const float v = acc[i][j][r];
+                            unsigned short h;
+                            if constexpr (OUT == TG_BF16)
+                                h = bf16_rne(v);
+                            else
+                                h = __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+                            *reinterpret_cast<unsigned short*>(smem + nl * PITCH16 + ml * 2) = h;
+                        }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 32; ++q) {
+                    const int nl = 64 * wave + 2 * q + (lane >> 5);
+                    const int c = lane & 31;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + nl * PITCH16 + c * 16);
+                    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<unsigned short*>(p.D) +
+                                                          static_cast<int64_t>(n0 + nl) * p.ldd + m0) + c;
+                    if constexpr (EPI & 1)
+                        __builtin_nontemporal_store(v, dst);
+                    else
+                        *dst = v;
+                }
+            }
+        });
     } else {
         // interior tile with 16-byte aligned D rows: transpose through LDS so
         // that each store instruction writes one whole 1 KiB row run of the
@@ -855,7 +945,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             for (int q = 0; q < 32; ++q) {
                 const int nl = 32 * wave + q;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(smem + nl * PITCH + lane * 16);
-                f32x4* dst = reinterpret_cast<f32x4*>(p.D + static_cast<int64_t>(n0 + 128 * pass + nl) * p.ldd + m0) + lane;
+                f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.D) +
+                                                      static_cast<int64_t>(n0 + 128 * pass + nl) * p.ldd + m0) + lane;
                 if constexpr (EPI & 1)
                     __builtin_nontemporal_store(v, dst);
                 else
@@ -1082,22 +1173,24 @@ __global__ __launch_bounds__(256, 1) void gemm_hybrid_kernel(GemmArgs p) {
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    with_out_type(p.out_dtype, [&](auto out) {
+        constexpr int OUT = decltype(out)::value;
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+        for (int i = 0; i < FN; ++i) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = m0 + wave_m * WTM + 16 * j + acc16_col(lane);
-            const int nb = n0 + wave_n * WTN + 16 * i;
-            float* col = p.D + m;
+            for (int j = 0; j < FM; ++j) {
+                const int m = m0 + wave_m * WTM + 16 * j + acc16_col(lane);
+                const int nb = n0 + wave_n * WTN + 16 * i;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = nb + acc16_row(lane, r);
-                float v = acc[i][j][r] * alpha;
-                if (relu) v = fmaxf(v, 0.0f);
-                if (interior || (m < M && n < N)) col[static_cast<int64_t>(n) * p.ldd] = v;
+                for (int r = 0; r < 4; ++r) {
+                    const int n = nb + acc16_row(lane, r);
+                    float v = acc[i][j][r] * alpha;
+                    if (relu) v = fmaxf(v, 0.0f);
+                    if (interior || (m < M && n < N)) store_out<OUT>(p.D, static_cast<int64_t>(n) * p.ldd + m, v);
+                }
             }
         }
-    }
+    });
 }
 
 template <int DT, int S, int P>
@@ -1151,13 +1244,14 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     X(19, TG_BF16, 4, 5, 8, 0, 0, 0, 10)        \
     X(20, TG_BF16, 4, 5, 8, 1, 0, 0, 10)        \
     X(21, TG_BF16, 4, 5, 16, 1, 0, 0, 10)       \
-    X(22, TG_BF16, 4, 5, 16, 1, 1, 1, 107)      \
-    X(23, TG_BF16, 4, 5, 8, 1, 1, 1, 10)        \
-    X(24, TG_F16, 4, 5, 16, 1, 1, 1, 107)       \
-    X(25, TG_F32, 4, 5, 16, 1, 1, 1, 41)        \
+    X(22, TG_BF16, 4, 5, 16, 1, 1, 5, 107)      \
+    X(23, TG_BF16, 4, 5, 8, 1, 1, 5, 10)        \
+    X(24, TG_F16, 4, 5, 16, 1, 1, 5, 107)       \
+    X(25, TG_F32, 4, 5, 16, 1, 1, 5, 41)        \
     X(26, TG_BF16, 4, 5, 16, 1, 1, 0, 10)       \
     X(27, TG_BF16, 4, 5, 16, 1, 1, 2, 10)       \
-    X(28, TG_BF16, 4, 5, 16, 1, 1, 3, 10)
+    X(28, TG_BF16, 4, 5, 16, 1, 1, 3, 10)       \
+    X(29, TG_BF16, 4, 5, 16, 1, 1, 1, 10)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \

@@ -11,7 +11,7 @@
 struct GemmArgs {
     const char* A;   // a[m,k] at A + m*lda_b + k*s
     const char* B;   // b[k,n] at B + n*ldb_b + k*s
-    float* D;        // d[m,n] at D[m + n*ldd]
+    void* D;         // d[m,n] at element m + n*ldd of D, in type out_dtype
     int64_t lda_b;   // A leading stride in bytes
     int64_t ldb_b;   // B leading stride in bytes
     int64_t ldd;     // D leading stride in elements
@@ -19,6 +19,7 @@ struct GemmArgs {
     float alpha;
     int relu;
     int tiles_m, tiles_n, group_m;
+    int out_dtype;   // element type of D: TG_F32, TG_BF16 or TG_F16
 };
 
 typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, hipStream_t stream);

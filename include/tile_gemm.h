@@ -52,7 +52,8 @@
 extern "C" {
 #endif
 
-/* Operand element type of A and B.  D is always fp32. */
+/* Element type of A and B (both the same), and of D for tile_gemm_out.
+ * tile_gemm and tile_gemm_ex always write fp32 D. */
 enum tile_gemm_dtype {
     TG_BF16 = 1, /* bfloat16 operands, bf16 MFMA */
     TG_F16 = 2,  /* IEEE binary16 operands, fp16 MFMA */
@@ -65,7 +66,7 @@ enum tile_gemm_status {
     TG_ERR_LD = -2,     /* lda < max(1,K), ldb < max(1,K) or ldd < max(1,M) */
     TG_ERR_NULL = -3,   /* NULL pointer for an operand that is read or written */
     TG_ERR_ALIGN = -4,  /* pointer not aligned to its element size */
-    TG_ERR_DTYPE = -5,  /* dtype not one of tile_gemm_dtype */
+    TG_ERR_DTYPE = -5,  /* dtype or out_dtype not one of tile_gemm_dtype */
     TG_ERR_ALIAS = -6,  /* D's byte range overlaps A's or B's */
     TG_ERR_LAUNCH = -7, /* the HIP launch failed (hipGetLastError) */
     TG_ERR_DEVICE = -8, /* no current HIP device, or it is not gfx950 */
@@ -117,6 +118,21 @@ int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                  float* D, int64_t ldd, int dtype, void* stream, int kernel_id);
 
 /*
+ * As tile_gemm_ex, with D of element type out_dtype (TG_F32, TG_BF16 or
+ * TG_F16): d[m,n] at byte D + (m + n*ldd)*out_size, out_size 4 or 2.  The
+ * accumulation and the epilogue stay fp32 (alpha, then the clamp); the
+ * epilogue value is then rounded to nearest-even in out_dtype (fp16: values
+ * beyond its range become +-inf, subnormals are kept) on the way out (cuTile.jl
+ * tutorial "Matrix Multiplication", Step 4: keep the Float32 accumulator and
+ * convert on the way out).  D must be aligned to out_size; everything else is
+ * as for tile_gemm, and out_dtype TG_F32 is exactly tile_gemm_ex.
+ */
+int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  void* D, int64_t ldd, int dtype, int out_dtype,
+                  void* stream, int kernel_id);
+
+/*
  * Host-only: validate the arguments exactly as tile_gemm does and describe the
  * plan it would launch (no HIP call is made; pointers are only inspected for
  * alignment and overlap).  kernel_id -1 = automatic choice.
@@ -125,6 +141,13 @@ int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype,
                          const void* A, int64_t lda, const void* B, int64_t ldb,
                          const float* D, int64_t ldd, int kernel_id,
                          tile_gemm_plan_info* out);
+
+/* Host-only: as tile_gemm_query_plan, for a tile_gemm_out call with D of
+ * element type out_dtype (the plan itself does not depend on out_dtype). */
+int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype,
+                             const void* A, int64_t lda, const void* B, int64_t ldb,
+                             const void* D, int64_t ldd, int out_dtype, int kernel_id,
+                             tile_gemm_plan_info* out);
 
 /* Number of compiled kernel instances (valid kernel ids are 0 .. count-1). */
 int tile_gemm_kernel_count(void);
@@ -138,7 +161,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 1
+#define TILE_GEMM_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

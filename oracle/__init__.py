@@ -71,6 +71,8 @@ def bind(path) -> ctypes.CDLL:
     lib.oracle_gemm_entries.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_ptr, ctypes.c_int, _i64, _ptr]
     lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_encode.argtypes = [_ptr, ctypes.c_int, _i64, _ptr]
+    lib.oracle_encode.restype = ctypes.c_int
     for name in ("oracle_decode_bf16", "oracle_decode_f16"):
         getattr(lib, name).argtypes = [ctypes.c_uint16]
         getattr(lib, name).restype = ctypes.c_double
@@ -115,6 +117,17 @@ def decode(bits: np.ndarray, dtype, lib=None) -> np.ndarray:
     rc = (lib or _load()).oracle_decode(src.ctypes.data, dt, src.size, out.ctypes.data)
     if rc:
         raise ValueError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def encode(values: np.ndarray, dtype, lib=None) -> np.ndarray:
+    """Round fp64 values to bf16 or fp16 (nearest, ties to even); uint16 bits."""
+    dt = _code(dtype)
+    src = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(src.shape, dtype=np.uint16)
+    rc = (lib or _load()).oracle_encode(src.ctypes.data, dt, src.size, out.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_encode failed ({rc})")
     return out
 
 
@@ -173,6 +186,33 @@ def tolerance(K: int, mag: np.ndarray) -> np.ndarray:
     alpha scaling, and 1e-6 is an absolute floor for results near zero.
     """
     return 4.0 * K * 2.0 ** -24 * np.asarray(mag, dtype=np.float64) + 1e-6
+
+
+# significant bits and smallest normal exponent of the 16-bit output formats
+_FORMAT = {BF16: (8, -126), F16: (11, -14)}
+
+
+def out_tolerance(K: int, mag: np.ndarray, ref: np.ndarray, out_dtype) -> np.ndarray:
+    """Bound for a result rounded to a 16-bit output format: the fp32 bound plus
+    half a unit in the last place of the output format at |ref| + that bound
+    (the stored value is the nearest format value to an fp32 result within the
+    fp32 bound of ref)."""
+    p, emin = _FORMAT[_code(out_dtype)]
+    tol = tolerance(K, mag)
+    x = np.abs(np.asarray(ref, dtype=np.float64)) + tol
+    _, e = np.frexp(x)
+    E = np.maximum(e - 1, emin)
+    return tol + 0.5 * np.ldexp(1.0, E - (p - 1))
+
+
+def check_out(d: np.ndarray, ref: np.ndarray, mag: np.ndarray, K: int, out_dtype):
+    """check() for a bf16/fp16 output (d decoded to fp64)."""
+    d = np.asarray(d, dtype=np.float64)
+    err = np.abs(d - ref)
+    tol = out_tolerance(K, mag, ref, out_dtype)
+    ratio = float(np.max(err / tol)) if err.size else 0.0
+    ok = bool(np.all(err <= tol)) and not bool(np.any(np.isnan(d)))
+    return ok, ratio
 
 
 def check(d: np.ndarray, ref: np.ndarray, mag: np.ndarray, K: int):

@@ -84,6 +84,53 @@ int oracle_decode(const void* src, int dtype, int64_t count, double* dst) {
     return 0;
 }
 
+/*
+ * Round x to the nearest value of the 16-bit format `dtype` (ties to the even
+ * significand) and return its bits; used to predict low-precision outputs
+ * (cuTile.jl tutorial "Matrix Multiplication", Step 4: the fp32 accumulator is
+ * converted on the way out).  Formats, from their definitions:
+ *   bf16: 8 significant bits, normal exponents -126..127 (bias 127),
+ *         subnormal spacing 2^-133;
+ *   fp16: 11 significant bits, normal exponents -14..15 (bias 15),
+ *         subnormal spacing 2^-24, largest finite 65504.
+ * A rounded magnitude above the largest finite value becomes infinity; NaN
+ * becomes the quiet NaN with the input's sign.  The rounding works on the
+ * exact fp64 value (scaling by powers of two is exact), so there is no double
+ * rounding.
+ */
+static uint16_t encode16(double x, int p, int emin, int emax, int mant_bits) {
+    const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    const uint16_t exp_all = (uint16_t)(((1u << (15 - mant_bits)) - 1u) << mant_bits);
+    if (isnan(x)) return (uint16_t)(sign | exp_all | (1u << (mant_bits - 1)));
+    const double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | exp_all);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                      /* a = f * 2^e, f in [0.5, 1) */
+    int E = e - 1;                     /* floor(log2 a) */
+    if (E < emin) E = emin;            /* subnormal range: fixed spacing */
+    const double ulp = ldexp(1.0, E - (p - 1));
+    const double v = nearbyint(a / ulp) * ulp;  /* default mode: ties to even */
+    const double maxf = ldexp(2.0 - ldexp(1.0, -(p - 1)), emax);
+    if (v > maxf) return (uint16_t)(sign | exp_all);
+    int ev;
+    frexp(v, &ev);
+    const int Ev = ev - 1;
+    if (v == 0.0 || Ev < emin)         /* subnormal (or rounded to zero) */
+        return (uint16_t)(sign | (uint16_t)(v / ldexp(1.0, emin - (p - 1))));
+    const int bias = emax;
+    const uint16_t frac = (uint16_t)((v / ldexp(1.0, Ev) - 1.0) * (double)(1u << mant_bits));
+    return (uint16_t)(sign | (uint16_t)((Ev + bias) << mant_bits) | frac);
+}
+
+/* Encode `count` fp64 values to bf16 or fp16 bits (round to nearest even). */
+int oracle_encode(const double* src, int dtype, int64_t count, uint16_t* dst) {
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return -5;
+    for (int64_t i = 0; i < count; ++i)
+        dst[i] = dtype == ORACLE_BF16 ? encode16(src[i], 8, -126, 127, 7) : encode16(src[i], 11, -14, 15, 10);
+    return 0;
+}
+
 /* One output element, straight from the definition. */
 static void one_entry(int64_t m, int64_t n, int64_t K, double alpha, int relu,
                       const double* arow, const double* bcol, double* out, double* mag) {

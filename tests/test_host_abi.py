@@ -17,10 +17,10 @@ GOLDEN = Path(__file__).resolve().parent / "golden"
 def test_library_exports_every_declared_function():
     lib = tg.load_library()
     declared = tg.header_functions()
-    assert {"tile_gemm", "tile_gemm_query_plan", "tile_gemm_strerror"} <= set(declared)
+    assert {"tile_gemm", "tile_gemm_out", "tile_gemm_query_plan", "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 1
+    assert tg.abi_version() == 2
 
 
 def test_strerror_covers_every_status():
@@ -52,6 +52,34 @@ def test_validation_codes(args, code):
     rc2 = tg.load_library().tile_gemm_query_plan(p["M"], p["N"], p["K"], p["dtype"], p["A"], p["lda"],
                                                  p["B"], p["ldb"], p["D"], p["ldd"], -1, ctypes.byref(info))
     assert rc2 == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(out=0), -5), (dict(out=9), -5),
+    (dict(out=1, D=D + 1), -4), (dict(out=2, D=D + 3), -4), (dict(out=3, D=D + 2), -4),
+    (dict(out=1, D=D + 2), None), (dict(out=2, D=D + 6), None),
+    # the output range scales with the output element size
+    (dict(out=3, D=A - 64 * 48 * 4 + 8), -6), (dict(out=1, D=A - 64 * 48 * 4 + 8), None),
+])
+def test_low_precision_output_validation(args, code):
+    """tile_gemm_out validates the output type, D's alignment to it and the
+    overlap of D's byte range, before any HIP call (no GPU here: a valid call
+    reports the missing device)."""
+    import torch
+
+    p = dict(M=64, N=48, K=64, A=A, B=B, D=D, out=1)
+    p.update(args)
+    rc = tg.tile_gemm_out(p["M"], p["N"], p["K"], 1.0, 0, p["A"], 64, p["B"], 64, p["D"], 64, 1, p["out"],
+                          None, -1)
+    info = tg.PlanInfo()
+    rq = tg.load_library().tile_gemm_query_plan_out(p["M"], p["N"], p["K"], 1, p["A"], 64, p["B"], 64,
+                                                    p["D"], 64, p["out"], -1, ctypes.byref(info))
+    assert rq == (0 if code is None else code)
+    if code is None:
+        code = 0 if torch.cuda.is_available() else -8
+        if code == 0:
+            pytest.skip("fake pointers cannot be launched on a GPU")
+    assert rc == code, tg.STATUS.get(rc, rc)
 
 
 def test_degenerate_shapes_need_no_operands():

@@ -21,7 +21,12 @@ Pins used:
     tutorial, "Sizes that are not a multiple of the tile shape"), NaN in
     the stride padding never reaches the result, the alpha-then-clamp order of
     the scalar epilogue (Tylo.jl manual, "Walk through GEMM", section 5),
-    sampled entries equal the full result, K = 0 gives zeros.
+    sampled entries equal the full result, K = 0 gives zeros;
+  * the 16-bit output encoder (round to nearest, ties to even): every finite
+    bf16/fp16 value encodes to itself, fp16 agrees with numpy's float64 ->
+    float16 conversion and bf16 with torch's float32 -> bfloat16 conversion
+    (on values exact in float32, midpoints included), and the format
+    boundaries (overflow to infinity, subnormals) follow the definitions.
 """
 from __future__ import annotations
 
@@ -231,9 +236,73 @@ def pin_degenerate(lib):
         _full(lib, 2, 2, 3, 1.0, False, np.zeros(6, np.uint16), 2, np.zeros(6, np.uint16), 3, "bf16")
 
 
+def _encode(lib, x, dt):
+    return oracle.encode(np.asarray(x, dtype=np.float64), dt, lib=lib)
+
+
+def pin_encode_roundtrip(lib):
+    """Every finite value of each format encodes to its own bits (signed zeros too)."""
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        bits = np.arange(1 << 16, dtype=np.uint16)
+        vals = torch.from_numpy(bits.view(np.int16).copy()).view(tdt).to(torch.float64).numpy()
+        fin = np.isfinite(vals)
+        assert np.array_equal(_encode(lib, vals[fin], dt), bits[fin]), dt
+
+
+def _neighbour_midpoints(tdt):
+    """Midpoints between consecutive positive finite values of a 16-bit format,
+    and points a quarter-spacing on either side of them."""
+    bits = np.arange(0x0000, 0x7C00 if tdt == torch.float16 else 0x7F80, dtype=np.int16)
+    v = torch.from_numpy(bits).view(tdt).to(torch.float64).numpy()
+    lo, hi = v[:-1], v[1:]
+    mid = (lo + hi) / 2
+    q = (hi - lo) / 4
+    return np.concatenate([mid, mid - q, mid + q, -mid])
+
+
+def pin_encode_f16_vs_numpy(lib):
+    """fp16 rounding of fp64 values agrees with numpy's float64 -> float16 cast."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([_neighbour_midpoints(torch.float16),
+                        rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000)),
+                        [65504.0, 65519.999, 65520.0, 70000.0, 2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.0001,
+                         3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25]])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(_encode(lib, x, "f16"), want)
+
+
+def pin_encode_bf16_vs_torch(lib):
+    """bf16 rounding agrees with torch's float32 -> bfloat16 cast on values that
+    are exact in float32 (midpoints between bf16 neighbours have 9 significant
+    bits, so they are)."""
+    rng = np.random.default_rng(8)
+    mids = _neighbour_midpoints(torch.bfloat16)
+    mids = mids[np.isfinite(mids.astype(np.float32)) & (mids.astype(np.float32).astype(np.float64) == mids)]
+    x = np.concatenate([mids, rng.standard_normal(20000).astype(np.float32).astype(np.float64)])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(_encode(lib, x, "bf16"), want)
+
+
+def pin_encode_golden(lib):
+    """Boundary cases read off the format definitions."""
+    cases = {
+        "f16": [(65504.0, 0x7BFF), (65519.99, 0x7BFF), (65520.0, 0x7C00), (-1e6, 0xFC00),
+                (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000), (1.5 * 2.0 ** -24, 0x0002),
+                (2.0 ** -14, 0x0400), (1.0 + 2.0 ** -11, 0x3C00), (1.0 + 3 * 2.0 ** -11, 0x3C02)],
+        "bf16": [(1.0 + 2.0 ** -8, 0x3F80), (1.0 + 3 * 2.0 ** -8, 0x3F82), (2.0 ** -133, 0x0001),
+                 (2.0 ** -134, 0x0000), (2.0 ** -126, 0x0080), (3.0e38, 0x7F62), (3.4e38, 0x7F80),
+                 (-2.5, 0xC020)],
+    }
+    for dt, pairs in cases.items():
+        got = _encode(lib, [v for v, _ in pairs], dt)
+        assert [int(g) for g in got] == [b for _, b in pairs], (dt, [hex(int(g)) for g in got])
+
+
 PINS = [pin_decode_golden, pin_decode_all_patterns, pin_permutation, pin_identity, pin_rank1,
         pin_small_integers, pin_tiny_rational, pin_zero_padded_k, pin_nan_padding_unread,
-        pin_alpha_then_relu, pin_entries_and_column_ranges, pin_degenerate]
+        pin_alpha_then_relu, pin_entries_and_column_ranges, pin_degenerate,
+        pin_encode_roundtrip, pin_encode_f16_vs_numpy, pin_encode_bf16_vs_torch, pin_encode_golden]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -256,6 +325,11 @@ MUTATIONS = {
     "mag_signed": ("t += fabs(p);", "t += p;"),
     "sign_flip": ("s += p;", "s -= p;"),
     "relu_inverted": ("if (relu && r < 0.0) r = 0.0;", "if (relu && r > 0.0) r = 0.0;"),
+    "encode_ties_away": ("nearbyint(a / ulp)", "floor(a / ulp + 0.5)"),
+    "encode_truncate": ("nearbyint(a / ulp)", "trunc(a / ulp)"),
+    "encode_no_subnormal_range": ("if (E < emin) E = emin;", ""),
+    "encode_saturate": ("if (v > maxf) return (uint16_t)(sign | exp_all);",
+                        "if (v > maxf) return (uint16_t)(sign | (exp_all - (1u << mant_bits)) | ((1u << mant_bits) - 1u));"),
 }
 
 
@@ -278,6 +352,39 @@ def test_planted_mistakes(tmp_path, name):
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name!r}"
+
+
+def test_out_tolerance_admits_rounded_fp32_results():
+    """The low-precision bound admits the nearest bf16/fp16 value of a genuine
+    fp32 accumulation, and rejects the same result one output unit off."""
+    M, N, K = 16, 16, 1024
+    A, B = si.operands(M, N, K, "bf16", "normal_invsqrtk", 63, 64)
+    ref, mag = oracle.gemm(M, N, K, 0.5, False, _bits(A), K, _bits(B), K, "bf16")
+    a32, b32 = A.float().numpy(), B.float().numpy()
+    acc = np.zeros((N, M), dtype=np.float32)
+    for k in range(K):
+        acc += np.outer(b32[:, k], a32[:, k]).astype(np.float32)
+    v = np.float32(0.5) * acc
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        d = torch.from_numpy(v).to(tdt).to(torch.float64).numpy()
+        ok, ratio = oracle.check_out(d, ref, mag, K, dt)
+        assert ok and ratio <= 1.0, (dt, ratio)
+    # exact products far above the fp32 bound: the nearest output value passes,
+    # its neighbour one unit up does not
+    M, N, K = 16, 16, 4
+    a = torch.tensor([[10.0 + m] * K for m in range(M)], dtype=torch.bfloat16)
+    b = torch.tensor([[25.0 + n] * K for n in range(N)], dtype=torch.bfloat16)
+    ref, mag = oracle.gemm(M, N, K, 1.0, False, _bits(a), K, _bits(b), K, "bf16")
+    assert ref.min() >= 1000 and ref.max() < 4096
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        near = torch.from_numpy(ref.astype(np.float32)).to(tdt)
+        ok, _ = oracle.check_out(near.to(torch.float64).numpy(), ref, mag, K, dt)
+        assert ok, dt
+        up = (near.view(torch.int16) + 1).view(tdt).to(torch.float64).numpy()
+        moved = up != near.to(torch.float64).numpy()
+        assert moved.all()
+        ok, _ = oracle.check_out(np.where(ref % 3 == 0, up, near.to(torch.float64).numpy()), ref, mag, K, dt)
+        assert not ok, dt
 
 
 def test_tolerance_bound_holds_for_fp32_accumulation():
