@@ -97,13 +97,22 @@ def main() -> int:
     A_st, B_st = si.workload_operands(w)
     A, B = A_st.to(dev), B_st.to(dev)
     out_torch = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.out_dtype]
-    D = si.out_storage(w.M, w.N, w.ldd).to(out_torch).to(dev)
-    Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
-    plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
+    D = si.out_storage(w.M, w.batch * w.N, w.ldd).to(out_torch).to(dev)
+    if w.batch == 1:
+        Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
+        plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
+        launch = tg.gemm
+    else:
+        # stacked matrices: (batch, M, K), (batch, K, N), (batch, M, N) views
+        Av = A.view(w.batch, w.M, w.lda)[:, :, :w.K]
+        Bv = B.view(w.batch, w.N, w.ldb)[:, :, :w.K].transpose(1, 2)
+        Dv = D.view(w.batch, w.N, w.ldd)[:, :, :w.M].transpose(1, 2)
+        plan = tg.plan_for_batched(Av, Bv, Dv, args.kernel_id)
+        launch = tg.gemm_batched
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
-        tg.gemm(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
+        launch(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
     torch.cuda.synchronize()
     # one event before every launch and one after the last, all on the stream
     # the kernel runs on: the whole-region average is the launch duration used
@@ -112,7 +121,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i].record(stream)
-        tg.gemm(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
+        launch(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
     ev[args.steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -137,7 +146,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                    "ldd": w.ldd, "alpha": w.alpha, "relu": w.relu, "dist": w.dist,
-                   "out_dtype": args.out_dtype,
+                   "out_dtype": args.out_dtype, "batch": w.batch,
                    "kernel_id": plan.kernel_id,
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},
@@ -160,7 +169,7 @@ def main() -> int:
 
         import oracle
 
-        cols = min(args.cpu_cols, w.N)
+        cols = min(args.cpu_cols, w.N)  # of the first matrix of a batch
         threads = oracle.default_threads()
         t0 = time.perf_counter()
         ref, mag = oracle.gemm(w.M, w.N, w.K, w.alpha, w.relu, si.bits(A_st), w.lda, si.bits(B_st), w.ldb,
@@ -172,7 +181,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"output columns n < {cols} of the {w.M}x{w.N}x{w.K} workload (all m, full K), "
+            "sample": f"output columns n < {cols} of the {w.M}x{w.N}x{w.K} workload"
+                      f"{' (first product of the batch)' if w.batch > 1 else ''} (all m, full K), "
                       f"fp64; {cpu_s:.2f} s wall",
         }
         if args.out_dtype == "f32":

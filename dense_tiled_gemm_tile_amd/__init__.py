@@ -61,6 +61,10 @@ _SIGNATURES = {
                              _ptr, _int]),
     "tile_gemm_query_plan": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int,
                                     ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_batched": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64,
+                                 _i64, _i64, _int, _int, _ptr, _int]),
+    "tile_gemm_query_plan_batched": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _i64, _ptr, _i64, _i64, _ptr,
+                                            _i64, _i64, _i64, _int, _int, ctypes.POINTER(PlanInfo)]),
     "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                         ctypes.POINTER(PlanInfo)]),
     "tile_gemm_kernel_count": (_int, []),
@@ -120,6 +124,13 @@ def tile_gemm_out(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype
                   kernel_id=-1) -> int:
     return load_library().tile_gemm_out(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd,
                                         dtype, out_dtype, stream, kernel_id)
+
+
+def tile_gemm_batched(M, N, K, alpha, relu, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d, batch,
+                      dtype, out_dtype=F32, stream=None, kernel_id=-1) -> int:
+    return load_library().tile_gemm_batched(M, N, K, alpha, int(bool(relu)), A, lda, stride_a, B, ldb,
+                                            stride_b, D, ldd, stride_d, batch, dtype, out_dtype, stream,
+                                            kernel_id)
 
 
 def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1, out_dtype=F32) -> PlanInfo:
@@ -197,6 +208,48 @@ def gemm(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, kernel_id
             rc = tile_gemm_out(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb,
                                D.data_ptr(), ldd, dt, ot, stream.cuda_stream, kernel_id)
         _check(rc)
+    return D
+
+
+def _batched_args(A, B, D):
+    if A.dim() != 3 or B.dim() != 3 or D.dim() != 3:
+        raise ValueError("A, B and D must be 3-D (batch, rows, cols) views")
+    batch = D.shape[0]
+    if A.shape[0] != batch or B.shape[0] != batch:
+        raise ValueError(f"batch mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A[0] if batch else A.new_empty(A.shape[1:]),
+                                                   B[0] if batch else B.new_empty(B.shape[1:]),
+                                                   D[0] if batch else D.new_empty(D.shape[1:]))
+    sa, sb, sd = (A.stride(0), B.stride(0), D.stride(0)) if batch > 1 else (0, 0, 0)
+    return M, N, K, lda, ldb, ldd, sa, sb, sd, batch, dt, ot
+
+
+def plan_for_batched(A, B, D, kernel_id: int = -1) -> PlanInfo:
+    """The plan ``gemm_batched`` would launch (grid counts every product)."""
+    M, N, K, lda, ldb, ldd, sa, sb, sd, batch, dt, ot = _batched_args(A, B, D)
+    info = PlanInfo()
+    _check(load_library().tile_gemm_query_plan_batched(M, N, K, dt, A.data_ptr(), lda, sa, B.data_ptr(), ldb,
+                                                       sb, D.data_ptr(), ldd, sd, batch, ot, kernel_id,
+                                                       ctypes.byref(info)))
+    return info
+
+
+def gemm_batched(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, kernel_id: int = -1):
+    """D[b] = alpha*A[b]@B[b] (+ReLU) for every b, in one launch; returns D.
+
+    A: (batch, M, K) view with strides (stride_a, lda, 1); B: (batch, K, N) with
+    strides (stride_b, 1, ldb); D: (batch, M, N) with strides (stride_d, 1, ldd),
+    float32, bfloat16 or float16.  A batch stride of 0 (``expand``) reuses one
+    operand for every product.
+    """
+    import torch
+
+    M, N, K, lda, ldb, ldd, sa, sb, sd, batch, dt, ot = _batched_args(A, B, D)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.device(D.device):
+        _check(tile_gemm_batched(M, N, K, float(alpha), relu, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
+                                 D.data_ptr(), ldd, sd, batch, dt, ot, stream.cuda_stream, kernel_id))
     return D
 
 

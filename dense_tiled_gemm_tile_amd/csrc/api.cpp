@@ -22,6 +22,14 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxGrid = int64_t(1) << 24;
+constexpr int64_t kMaxBatch = 65535;              // grid y
+constexpr int64_t kMaxBatchStride = int64_t(1) << 40;
+
+// Matrices of a batched call: batch >= 1, element distances between
+// consecutive A, B and D matrices (0 = the same matrix for every entry).
+struct Batch {
+    int64_t batch = 1, stride_a = 0, stride_b = 0, stride_d = 0;
+};
 constexpr int kCusPerGpu = 256;
 
 int elem_size(int dtype) {
@@ -36,36 +44,47 @@ int elem_size(int dtype) {
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
 int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-             int64_t ldb, const void* D, int64_t ldd, int dtype, int out_dtype) {
+             int64_t ldb, const void* D, int64_t ldd, int dtype, int out_dtype, const Batch& bt) {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TG_ERR_DIMS;
+    if (bt.batch < 0 || bt.batch > kMaxBatch) return TG_ERR_DIMS;
     const int es = elem_size(dtype);
     const int os = elem_size(out_dtype);
     if (!es || !os) return TG_ERR_DTYPE;
     const int64_t kmin = K > 1 ? K : 1;
     if (lda < kmin || ldb < kmin || ldd < (M > 1 ? M : 1)) return TG_ERR_LD;
-    if (M == 0 || N == 0) return TG_OK;
+    if (bt.stride_a < 0 || bt.stride_b < 0 || bt.stride_d < 0 || bt.stride_a > kMaxBatchStride ||
+        bt.stride_b > kMaxBatchStride || bt.stride_d > kMaxBatchStride)
+        return TG_ERR_LD;
+    if (M == 0 || N == 0 || bt.batch == 0) return TG_OK;
+    // the output matrices of a batch must not overlap one another
+    if (bt.batch > 1 && bt.stride_d < (N - 1) * ldd + M) return TG_ERR_LD;
     const bool reads = K > 0;
     if (!D || (reads && (!A || !B))) return TG_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(D) & uintptr_t(os - 1)) ||
         (reads && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & uintptr_t(es - 1))))
         return TG_ERR_ALIGN;
     if (reads) {
+        // whole spans of the batch (conservative for interleaved layouts)
+        const int64_t last = bt.batch - 1;
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
-        const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
+        const uintptr_t d1 = d0 + uintptr_t(last * bt.stride_d + (N - 1) * ldd + M) * uintptr_t(os);
         const uintptr_t a0 = reinterpret_cast<uintptr_t>(A);
-        const uintptr_t a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
+        const uintptr_t a1 = a0 + uintptr_t(last * bt.stride_a + (M - 1) * lda + K) * uintptr_t(es);
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(B);
-        const uintptr_t b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
+        const uintptr_t b1 = b0 + uintptr_t(last * bt.stride_b + (N - 1) * ldb + K) * uintptr_t(es);
         if (overlaps(d0, d1, a0, a1) || overlaps(d0, d1, b0, b1)) return TG_ERR_ALIAS;
     }
     return TG_OK;
 }
 
-// Byte alignment class shared by every operand row start: 16, 4 or 2.
-int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, int64_t ldb, int es) {
+// Byte alignment class shared by every operand row start (of every matrix of
+// a batch): 16, 4 or 2.
+int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, int64_t ldb, int es,
+              const Batch& bt) {
     uintptr_t bits = reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B);
     if (M > 1) bits |= uintptr_t(lda * es);
     if (N > 1) bits |= uintptr_t(ldb * es);
+    if (bt.batch > 1) bits |= uintptr_t(bt.stride_a * es) | uintptr_t(bt.stride_b * es);
     if ((bits & 15u) == 0) return 16;
     if ((bits & 3u) == 0) return 4;
     return 2;
@@ -76,8 +95,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Relative cost of a plan: each CU works through ceil(tiles / CUs) tiles one
 // after another (co-resident workgroups share the CU's MFMA pipes), each tile
 // costing its area divided by the instance's expected MFMA efficiency.
-double plan_cost(const TgKernelDesc& k, int64_t M, int64_t N) {
-    const int64_t tiles = cdiv(M, k.block_m) * cdiv(N, k.block_n);
+double plan_cost(const TgKernelDesc& k, int64_t M, int64_t N, int64_t batch) {
+    const int64_t tiles = cdiv(M, k.block_m) * cdiv(N, k.block_n) * (batch > 1 ? batch : 1);
     return double(cdiv(tiles, kCusPerGpu)) * double(k.block_m) * double(k.block_n) / (0.01 * k.eff_pct);
 }
 
@@ -85,14 +104,14 @@ bool usable(const TgKernelDesc& k, int dtype, int cls, int64_t row_stride) {
     return k.dtype == dtype && cls >= k.load_class && (k.max_row_stride == 0 || row_stride <= k.max_row_stride);
 }
 
-int choose(int64_t M, int64_t N, int dtype, int cls, int64_t row_stride) {
+int choose(int64_t M, int64_t N, int64_t batch, int dtype, int cls, int64_t row_stride) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tg_kernel_table_size; ++i) {
         const TgKernelDesc& k = tg_kernel_table[i];
         if (!usable(k, dtype, cls, row_stride)) continue;
         // among equal costs prefer the instance that needs the strongest alignment
-        const double c = plan_cost(k, M, N) * (1.0 + 0.001 / k.load_class);
+        const double c = plan_cost(k, M, N, batch) * (1.0 + 0.001 / k.load_class);
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
     }
     return best;
@@ -123,15 +142,16 @@ void describe(const TgKernelDesc& k, int64_t M, int64_t N, tile_gemm_plan_info* 
 }
 
 int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
-         int64_t ldb, const void* D, int64_t ldd, int out_dtype, int kernel_id, tile_gemm_plan_info* out) {
-    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype);
+         int64_t ldb, const void* D, int64_t ldd, int out_dtype, int kernel_id, tile_gemm_plan_info* out,
+         const Batch& bt = Batch()) {
+    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, bt);
     if (rc) return rc;
     const int es = elem_size(dtype);
-    const int cls = row_class(M, N, A, lda, B, ldb, es);
+    const int cls = row_class(M, N, A, lda, B, ldb, es, bt);
     const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
     int id = kernel_id;
     if (id < 0) {
-        id = choose(M, N, dtype, cls, row_stride);
+        id = choose(M, N, bt.batch, dtype, cls, row_stride);
         if (id < 0) return TG_ERR_PLAN;
     } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls, row_stride)) {
         return TG_ERR_PLAN;
@@ -177,6 +197,21 @@ int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype, const void*
     return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, TG_F32, kernel_id, out);
 }
 
+int tile_gemm_query_plan_batched(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                                 int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
+                                 const void* D, int64_t ldd, int64_t stride_d, int64_t batch, int out_dtype,
+                                 int kernel_id, tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    Batch bt;
+    bt.batch = batch;
+    bt.stride_a = stride_a;
+    bt.stride_b = stride_b;
+    bt.stride_d = stride_d;
+    const int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out, bt);
+    if (rc == TG_OK) out->grid *= (batch > 0 ? batch : 0);
+    return rc;
+}
+
 int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
                              const void* B, int64_t ldb, const void* D, int64_t ldd, int out_dtype,
                              int kernel_id, tile_gemm_plan_info* out) {
@@ -184,13 +219,19 @@ int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype, const v
     return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out);
 }
 
-int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
-                  int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int dtype,
-                  int out_dtype, void* stream, int kernel_id) {
+int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
+                      int64_t lda, int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
+                      void* D, int64_t ldd, int64_t stride_d, int64_t batch, int dtype, int out_dtype,
+                      void* stream, int kernel_id) {
+    Batch bt;
+    bt.batch = batch;
+    bt.stride_a = stride_a;
+    bt.stride_b = stride_b;
+    bt.stride_d = stride_d;
     tile_gemm_plan_info pl;
-    int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, &pl);
+    int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, &pl, bt);
     if (rc) return rc;
-    if (M == 0 || N == 0) return TG_OK;
+    if (M == 0 || N == 0 || batch == 0) return TG_OK;
     rc = device_ok();
     if (rc) return rc;
     const int es = elem_size(dtype);
@@ -210,8 +251,19 @@ int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const 
     a.tiles_n = static_cast<int>(pl.tiles_n);
     a.group_m = pl.group_m;
     a.out_dtype = out_dtype;
-    const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<hipStream_t>(stream));
+    a.batch_a_b = stride_a * es;
+    a.batch_b_b = stride_b * es;
+    a.batch_d_b = stride_d * elem_size(out_dtype);
+    const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<int>(batch),
+                                                                static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
+                  int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int dtype,
+                  int out_dtype, void* stream, int kernel_id) {
+    return tile_gemm_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype,
+                             stream, kernel_id);
 }
 
 int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,

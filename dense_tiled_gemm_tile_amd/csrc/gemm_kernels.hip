@@ -160,6 +160,16 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
     }
 }
 
+// Batched calls (grid y = matrix index; cuTile.jl tutorial "Matrix
+// Multiplication", "Where to go from here": batched operands): move the
+// operand and output bases to this workgroup's matrix.
+__device__ __forceinline__ void select_batch(GemmArgs& p) {
+    const int64_t b = blockIdx.y;
+    p.A += b * p.batch_a_b;
+    p.B += b * p.batch_b_b;
+    p.D = static_cast<char*>(p.D) + b * p.batch_d_b;
+}
+
 // Run f with the output type as a compile-time constant (one uniform branch
 // per kernel, outside the unrolled store loops).
 template <typename F>
@@ -176,6 +186,7 @@ __device__ __forceinline__ void with_out_type(int out, F&& f) {
 
 template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES>
 __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
+    select_batch(p);
     constexpr int ES = (DT == TG_F32) ? 4 : 2;  // element bytes
     constexpr int EPC = 16 / ES;                    // elements per 16-byte chunk
     constexpr int BKE = kRowBytes / ES;             // K elements per stage
@@ -419,6 +430,7 @@ __device__ __forceinline__ void slab_with_side(f32x16 (&acc)[FN][FM], const u32x
 
 template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
 __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kernel(GemmArgs p) {
+    select_batch(p);
     constexpr int NW = WM * WN;                 // waves per workgroup
     constexpr int NT = 64 * NW;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
@@ -604,8 +616,9 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
 }
 
 template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
-static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>), dim3(static_cast<unsigned>(grid)),
+static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>),
+                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
                        dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
@@ -647,6 +660,7 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, hipStream_t str
 // lines.
 template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
+    select_batch(p);
     constexpr int BM = 256, BN = 256, WM = 2;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
     constexpr int EPC = 16 / ES;
@@ -958,8 +972,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
 }
 
 template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
-static hipError_t launch_wide(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+static hipError_t launch_wide(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>),
+                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1001,6 +1016,7 @@ __device__ __forceinline__ void mfma16_drain() {
 
 template <int DT, int S, int P>
 __global__ __launch_bounds__(256, 1) void gemm_hybrid_kernel(GemmArgs p) {
+    select_batch(p);
     static_assert(DT == TG_BF16 || DT == TG_F16, "16-bit operands");
     constexpr int BM = 256, BN = 256;
     constexpr int EPC = 8;                   // elements per 16-byte chunk
@@ -1194,17 +1210,17 @@ __global__ __launch_bounds__(256, 1) void gemm_hybrid_kernel(GemmArgs p) {
 }
 
 template <int DT, int S, int P>
-static hipError_t launch_hybrid(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_hybrid_kernel<DT, S, P>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       stream, a);
+static hipError_t launch_hybrid(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_hybrid_kernel<DT, S, P>), dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
+                       dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- table
 
 template <int DT, int BM, int BN, int LC, int MW>
-static hipError_t launch(const GemmArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, LC, MW>), dim3(static_cast<unsigned>(grid)),
+static hipError_t launch(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, LC, MW>), dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -20,9 +20,10 @@ struct GemmArgs {
     int relu;
     int tiles_m, tiles_n, group_m;
     int out_dtype;   // element type of D: TG_F32, TG_BF16 or TG_F16
+    int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
 };
 
-typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, hipStream_t stream);
+typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, int batch, hipStream_t stream);
 
 struct TgKernelDesc {
     int id;

@@ -133,6 +133,24 @@ int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                   void* stream, int kernel_id);
 
 /*
+ * Batched: `batch` independent products D_b = alpha*A_b*B_b (+ReLU), b = 0 ..
+ * batch-1, in one launch (cuTile.jl tutorial "Matrix Multiplication", "Where to
+ * go from here": batched operands).  Matrix b of A starts stride_a elements
+ * after matrix b-1 (likewise B with stride_b, D with stride_d, in elements of
+ * their own types); a stride of 0 reuses one A or B for every product.  Each
+ * product is exactly the tile_gemm_out product of its matrices.
+ * Extra checks: 0 <= batch <= 65535 (TG_ERR_DIMS); strides >= 0 and at most
+ * 2^40, and with batch > 1, stride_d >= (N-1)*ldd + M so the outputs do not
+ * overlap (TG_ERR_LD); D's whole span must not overlap A's or B's whole span
+ * (TG_ERR_ALIAS).  batch = 0 is a no-op.
+ */
+int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                      const void* A, int64_t lda, int64_t stride_a,
+                      const void* B, int64_t ldb, int64_t stride_b,
+                      void* D, int64_t ldd, int64_t stride_d, int64_t batch,
+                      int dtype, int out_dtype, void* stream, int kernel_id);
+
+/*
  * Host-only: validate the arguments exactly as tile_gemm does and describe the
  * plan it would launch (no HIP call is made; pointers are only inspected for
  * alignment and overlap).  kernel_id -1 = automatic choice.
@@ -149,6 +167,14 @@ int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype,
                              const void* D, int64_t ldd, int out_dtype, int kernel_id,
                              tile_gemm_plan_info* out);
 
+/* Host-only: the plan of a tile_gemm_batched call; `grid` counts the
+ * workgroups of all products (tiles_m * tiles_n * batch). */
+int tile_gemm_query_plan_batched(int64_t M, int64_t N, int64_t K, int dtype,
+                                 const void* A, int64_t lda, int64_t stride_a,
+                                 const void* B, int64_t ldb, int64_t stride_b,
+                                 const void* D, int64_t ldd, int64_t stride_d, int64_t batch,
+                                 int out_dtype, int kernel_id, tile_gemm_plan_info* out);
+
 /* Number of compiled kernel instances (valid kernel ids are 0 .. count-1). */
 int tile_gemm_kernel_count(void);
 
@@ -161,7 +187,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 2
+#define TILE_GEMM_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -48,16 +48,17 @@ class Workload:
     seed_a: int
     seed_b: int
     notes: str = field(default="", compare=False)
+    batch: int = 1        # independent products, stored back to back (one launch)
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.N * self.K * self.batch
 
 
-def _w(name, M, N, K, dtype, dist, alpha, relu, seed_base, pad_ab=0, pad_d=0, notes=""):
+def _w(name, M, N, K, dtype, dist, alpha, relu, seed_base, pad_ab=0, pad_d=0, notes="", batch=1):
     return Workload(name, M, N, K, dtype, dist, alpha, relu,
                     lda=K + pad_ab, ldb=K + pad_ab, ldd=M + pad_d,
-                    seed_a=seed_base + 1, seed_b=seed_base + 2, notes=notes)
+                    seed_a=seed_base + 1, seed_b=seed_base + 2, notes=notes, batch=batch)
 
 
 # The five measured/parity workloads, in order; the large square comes in both
@@ -77,6 +78,11 @@ WORKLOADS = {
                                               12289, 5003, 4099, "bf16", "uniform_pm1",
                                               2.0, True, 5000, pad_ab=8, pad_d=16,
                                               notes="lda=ldb=K+8, ldd=M+16"),
+    # batched products (the batched GEMM of the cuTile tutorial's closing
+    # section): 16 independent 1024^3 products, matrices stored back to back
+    "batched_16x1024_bf16": _w("batched_16x1024_bf16", 1024, 1024, 1024, "bf16", "uniform_pm1",
+                               1.0, True, 6000, batch=16,
+                               notes="16 products; A (16*M, lda), B (16*N, ldb), D (16*N, ldd) storages"),
 }
 
 
@@ -109,7 +115,16 @@ def operands(M, N, K, dtype, dist, seed_a, seed_b, lda=None, ldb=None, pad=float
 
 
 def workload_operands(w: Workload, pad=float("nan")):
-    return operands(w.M, w.N, w.K, w.dtype, w.dist, w.seed_a, w.seed_b, w.lda, w.ldb, pad)
+    """A and B storages; a batched workload stacks its matrices: A is
+    (batch*M, lda), matrix b in rows b*M .. b*M+M-1 (B likewise with N)."""
+    if w.batch == 1:
+        return operands(w.M, w.N, w.K, w.dtype, w.dist, w.seed_a, w.seed_b, w.lda, w.ldb, pad)
+    ga = torch.Generator().manual_seed(int(w.seed_a))
+    gb = torch.Generator().manual_seed(int(w.seed_b))
+    a = _draw(w.batch * w.M, w.K, w.dist, w.K, ga)
+    b = _draw(w.batch * w.N, w.K, w.dist, w.K, gb)
+    return (_stored(w.batch * w.M, w.K, w.lda, a, w.dtype, pad),
+            _stored(w.batch * w.N, w.K, w.ldb, b, w.dtype, pad))
 
 
 def int_operands(M, N, K, dtype, seed, lda=None, ldb=None, lo=-3, hi=3, pad=float("nan")):

@@ -17,10 +17,11 @@ GOLDEN = Path(__file__).resolve().parent / "golden"
 def test_library_exports_every_declared_function():
     lib = tg.load_library()
     declared = tg.header_functions()
-    assert {"tile_gemm", "tile_gemm_out", "tile_gemm_query_plan", "tile_gemm_strerror"} <= set(declared)
+    assert {"tile_gemm", "tile_gemm_out", "tile_gemm_batched", "tile_gemm_query_plan",
+            "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 2
+    assert tg.abi_version() == 3
 
 
 def test_strerror_covers_every_status():
@@ -178,3 +179,43 @@ def test_row_stride_limited_instances_are_refused_for_huge_strides():
     assert small_plan.kernel_id in refused  # the default for ordinary strides is one of them
     p = tg.query_plan(512, 512, W.K, tg.BF16, a, huge, b, huge, d, 512, -1)
     assert p.kernel_id not in refused and p.load_class == 16
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(batch=-1), -1), (dict(batch=65536), -1),
+    (dict(sa=-1), -2), (dict(sb=-64), -2), (dict(sd=-1), -2), (dict(sa=(1 << 40) + 1), -2),
+    (dict(sd=64 * 47 + 63), -2),                # outputs of consecutive products would overlap
+    (dict(sd=64 * 48), None), (dict(sa=0, sb=0), None), (dict(batch=1, sd=0), None),
+    (dict(batch=0, A=0, B=0, D=0), 0),          # nothing to do
+    (dict(sa=4 * 64 * 64, D=A + 4 * 64 * 64 * 2 + 4096), -6),  # A's span reaches into D's
+    (dict(sa=64 * 64 + 3), None),               # a batch stride that breaks 16-byte rows is legal
+])
+def test_batched_validation(args, code):
+    """tile_gemm_batched's extra checks (batch range, strides, non-overlapping
+    outputs, whole-span aliasing), before any HIP call."""
+    import torch
+
+    p = dict(M=64, N=48, K=64, A=A, B=B, D=D, sa=64 * 64, sb=48 * 64, sd=64 * 48 + 16, batch=4)
+    p.update(args)
+    rc = tg.tile_gemm_batched(p["M"], p["N"], p["K"], 1.0, 0, p["A"], 64, p["sa"], p["B"], 64, p["sb"],
+                              p["D"], 64, p["sd"], p["batch"], 1, 3, None, -1)
+    if code is None:
+        if torch.cuda.is_available():
+            pytest.skip("fake pointers cannot be launched on a GPU")
+        code = -8
+    assert rc == code, tg.STATUS.get(rc, rc)
+
+
+def test_batched_plan_counts_every_product():
+    """The plan of a batch weighs all its workgroups: 16 products of 1024^3
+    bf16 fill the chip with 256x256 tiles (16 tiles each)."""
+    w = si.WORKLOADS["batched_16x1024_bf16"]
+    info = tg.PlanInfo()
+    D2 = 0x7F4000000000
+    rc = tg.load_library().tile_gemm_query_plan_batched(
+        w.M, w.N, w.K, tg.BF16, A, w.lda, w.M * w.lda, B, w.ldb, w.N * w.ldb, D2, w.ldd, w.N * w.ldd,
+        w.batch, tg.F32, -1, ctypes.byref(info))
+    assert rc == 0
+    assert (info.block_m, info.block_n, info.grid) == (256, 256, 256)
+    single = _plan(si.WORKLOADS["full_tile_1024_bf16"])
+    assert (single.block_m, single.block_n) == (128, 128)
