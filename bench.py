@@ -68,6 +68,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square_8192_bf16_relu")
     ap.add_argument("--kernel-id", type=int, default=-1)
+    ap.add_argument("--splits", type=int, default=1,
+                    help="split K into this many ranges (tile_gemm_splitk, 0 = automatic; workspace allocated "
+                         "up front)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="element type of D (bf16/f16: fp32 epilogue rounded on the way out)")
     ap.add_argument("--cpu-cols", type=int, default=4096,
@@ -102,6 +105,13 @@ def main() -> int:
         Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
         plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
         launch = tg.gemm
+        if args.splits != 1:
+            ws = torch.empty(max(tg.splitk_workspace_bytes(w.M, w.N, args.splits), 16), dtype=torch.uint8,
+                             device=dev)
+
+            def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
+                return tg.gemm_splitk(A_, B_, D_, alpha, relu, splits=args.splits, workspace=ws, stream=stream,
+                                      kernel_id=kernel_id)
     else:
         # stacked matrices: (batch, M, K), (batch, K, N), (batch, M, N) views
         Av = A.view(w.batch, w.M, w.lda)[:, :, :w.K]
@@ -146,7 +156,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                    "ldd": w.ldd, "alpha": w.alpha, "relu": w.relu, "dist": w.dist,
-                   "out_dtype": args.out_dtype, "batch": w.batch,
+                   "out_dtype": args.out_dtype, "batch": w.batch, "splits": args.splits,
                    "kernel_id": plan.kernel_id,
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},

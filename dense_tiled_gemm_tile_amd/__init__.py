@@ -30,7 +30,7 @@ DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32}
 TG_OK = 0
 STATUS = {0: "TG_OK", -1: "TG_ERR_DIMS", -2: "TG_ERR_LD", -3: "TG_ERR_NULL", -4: "TG_ERR_ALIGN",
           -5: "TG_ERR_DTYPE", -6: "TG_ERR_ALIAS", -7: "TG_ERR_LAUNCH", -8: "TG_ERR_DEVICE",
-          -9: "TG_ERR_PLAN"}
+          -9: "TG_ERR_PLAN", -10: "TG_ERR_WORKSPACE"}
 
 
 class TileGemmError(RuntimeError):
@@ -65,6 +65,9 @@ _SIGNATURES = {
                                  _i64, _i64, _int, _int, _ptr, _int]),
     "tile_gemm_query_plan_batched": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _i64, _ptr, _i64, _i64, _ptr,
                                             _i64, _i64, _i64, _int, _int, ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_splitk": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _int,
+                                _ptr, _i64, _ptr, _int]),
+    "tile_gemm_splitk_workspace_bytes": (_i64, [_i64, _i64, _int]),
     "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                         ctypes.POINTER(PlanInfo)]),
     "tile_gemm_kernel_count": (_int, []),
@@ -131,6 +134,16 @@ def tile_gemm_batched(M, N, K, alpha, relu, A, lda, stride_a, B, ldb, stride_b, 
     return load_library().tile_gemm_batched(M, N, K, alpha, int(bool(relu)), A, lda, stride_a, B, ldb,
                                             stride_b, D, ldd, stride_d, batch, dtype, out_dtype, stream,
                                             kernel_id)
+
+
+def tile_gemm_splitk(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, splits, workspace,
+                     workspace_bytes, stream=None, kernel_id=-1) -> int:
+    return load_library().tile_gemm_splitk(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd, dtype,
+                                           out_dtype, splits, workspace, workspace_bytes, stream, kernel_id)
+
+
+def splitk_workspace_bytes(M, N, splits) -> int:
+    return load_library().tile_gemm_splitk_workspace_bytes(M, N, splits)
 
 
 def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1, out_dtype=F32) -> PlanInfo:
@@ -250,6 +263,29 @@ def gemm_batched(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, k
     with torch.cuda.device(D.device):
         _check(tile_gemm_batched(M, N, K, float(alpha), relu, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
                                  D.data_ptr(), ldd, sd, batch, dt, ot, stream.cuda_stream, kernel_id))
+    return D
+
+
+def gemm_splitk(A, B, D, alpha: float = 1.0, relu: bool = False, splits: int = 0, workspace=None,
+                stream=None, kernel_id: int = -1):
+    """As ``gemm``, with K split into `splits` ranges whose fp32 partial
+    products are summed in split order before the epilogue (splits = 0: the
+    library's automatic choice, within the workspace).  `workspace` is a
+    device tensor of at least ``splitk_workspace_bytes(M, N, splits)`` bytes
+    (allocated here through torch when omitted; the library itself allocates
+    nothing)."""
+    import torch
+
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
+    need = splitk_workspace_bytes(M, N, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=D.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.device(D.device):
+        _check(tile_gemm_splitk(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(),
+                                ldd, dt, ot, splits, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), stream.cuda_stream, kernel_id))
     return D
 
 

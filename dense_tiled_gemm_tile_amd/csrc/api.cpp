@@ -24,6 +24,8 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxGrid = int64_t(1) << 24;
 constexpr int64_t kMaxBatch = 65535;              // grid y
 constexpr int64_t kMaxBatchStride = int64_t(1) << 40;
+constexpr int kMaxSplits = 256;
+constexpr int kAutoSplitMax = 64;
 
 // Matrices of a batched call: batch >= 1, element distances between
 // consecutive A, B and D matrices (0 = the same matrix for every entry).
@@ -143,7 +145,7 @@ void describe(const TgKernelDesc& k, int64_t M, int64_t N, tile_gemm_plan_info* 
 
 int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
          int64_t ldb, const void* D, int64_t ldd, int out_dtype, int kernel_id, tile_gemm_plan_info* out,
-         const Batch& bt = Batch()) {
+         const Batch& bt = Batch(), int64_t splits = 1) {
     const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, bt);
     if (rc) return rc;
     const int es = elem_size(dtype);
@@ -151,7 +153,7 @@ int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
     const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
     int id = kernel_id;
     if (id < 0) {
-        id = choose(M, N, bt.batch, dtype, cls, row_stride);
+        id = choose(M, N, bt.batch * splits, dtype, cls, row_stride);
         if (id < 0) return TG_ERR_PLAN;
     } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls, row_stride)) {
         return TG_ERR_PLAN;
@@ -235,7 +237,7 @@ int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, co
     rc = device_ok();
     if (rc) return rc;
     const int es = elem_size(dtype);
-    GemmArgs a;
+    GemmArgs a{};  // every field starts at zero (split_k = 0: no split)
     a.A = static_cast<const char*>(A);
     a.B = static_cast<const char*>(B);
     a.D = D;
@@ -256,6 +258,94 @@ int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, co
     a.batch_d_b = stride_d * elem_size(out_dtype);
     const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<int>(batch),
                                                                 static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+int64_t tile_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || splits < 0 || splits > kMaxSplits) return -1;
+    if (splits == 0) splits = kAutoSplitMax;
+    if (splits <= 1 || M == 0 || N == 0) return 0;
+    return int64_t(splits) * M * N * 4;
+}
+
+int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, int splits,
+                     void* workspace, int64_t workspace_bytes, void* stream, int kernel_id) {
+    if (splits < 0 || splits > kMaxSplits) return TG_ERR_DIMS;
+    if (splits == 0) {
+        // automatic: split only when the output has fewer tiles than the chip
+        // has CUs and every split keeps at least 16 stages of K; aim at two
+        // workgroups per CU
+        tile_gemm_plan_info p1;
+        const int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, &p1);
+        if (rc) return rc;
+        const int64_t tiles = p1.tiles_m * p1.tiles_n, stages = p1.block_k ? K / p1.block_k : 0;
+        int64_t s = 1;
+        if (tiles > 0 && tiles < kCusPerGpu && stages >= 64) {
+            s = 2 * kCusPerGpu / tiles;
+            if (s > stages / 16) s = stages / 16;
+            if (s > kAutoSplitMax) s = kAutoSplitMax;
+            // never more than the workspace holds
+            const int64_t fit = (M > 0 && N > 0 && workspace) ? workspace_bytes / (M * N * 4) : 0;
+            if (s > fit) s = fit;
+        }
+        splits = static_cast<int>(s < 1 ? 1 : s);
+    }
+    if (splits == 1)
+        return tile_gemm_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype,
+                                 stream, kernel_id);
+    // the first launch is a batch of `splits` products over K ranges; the
+    // plan weighs all their workgroups
+    tile_gemm_plan_info pl;
+    int rc = plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, &pl, Batch(), splits);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return TG_OK;
+    const int64_t bk = pl.block_k;
+    const int64_t stages = cdiv(K, bk);
+    const int64_t chunk = cdiv(stages, splits) * bk;         // K elements per split, whole stages
+    const int64_t used = K > 0 ? cdiv(K, chunk) : 1;        // splits that get at least one element
+    const int64_t need = used * M * N * 4;
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u))
+        return TG_ERR_WORKSPACE;
+    {
+        const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uintptr_t(need);
+        const int es = elem_size(dtype), os = elem_size(out_dtype);
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(D), d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(B), b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
+        if (overlaps(w0, w1, d0, d1) || (K > 0 && (overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1))))
+            return TG_ERR_ALIAS;
+    }
+    rc = device_ok();
+    if (rc) return rc;
+    const int es = elem_size(dtype);
+    GemmArgs a{};  // every field starts at zero (split_k = 0: no split)
+    a.A = static_cast<const char*>(A);
+    a.B = static_cast<const char*>(B);
+    a.D = workspace;
+    a.lda_b = lda * es;
+    a.ldb_b = ldb * es;
+    a.ldd = M;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.alpha = 1.0f;
+    a.relu = 0;
+    a.tiles_m = static_cast<int>(pl.tiles_m);
+    a.tiles_n = static_cast<int>(pl.tiles_n);
+    a.group_m = pl.group_m;
+    a.out_dtype = TG_F32;
+    a.batch_a_b = chunk * es;
+    a.batch_b_b = chunk * es;
+    a.batch_d_b = M * N * 4;
+    a.split_k = static_cast<int>(chunk);
+    hipError_t err = hipSuccess;
+    if (K > 0)
+        err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<int>(used), static_cast<hipStream_t>(stream));
+    if (err == hipSuccess)
+        err = tg_splitk_reduce(static_cast<const float*>(workspace), K > 0 ? static_cast<int>(used) : 0,
+                               static_cast<int>(M), static_cast<int>(N), D, ldd, alpha, relu ? 1 : 0, out_dtype,
+                               static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
@@ -298,6 +388,7 @@ const char* tile_gemm_strerror(int code) {
         case TG_ERR_LAUNCH: return "HIP kernel launch failed";
         case TG_ERR_DEVICE: return "no current gfx950 HIP device";
         case TG_ERR_PLAN: return "kernel instance unknown or not valid for these operands";
+        case TG_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
         default: return "unknown status";
     }
 }

@@ -163,11 +163,15 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
 // Batched calls (grid y = matrix index; cuTile.jl tutorial "Matrix
 // Multiplication", "Where to go from here": batched operands): move the
 // operand and output bases to this workgroup's matrix.
+// A split-K launch is the same mechanism with the operand bases stepping
+// along K: split s covers k in [s*split_k, min((s+1)*split_k, K)) and writes
+// its fp32 partial product to its own workspace matrix.
 __device__ __forceinline__ void select_batch(GemmArgs& p) {
     const int64_t b = blockIdx.y;
     p.A += b * p.batch_a_b;
     p.B += b * p.batch_b_b;
     p.D = static_cast<char*>(p.D) + b * p.batch_d_b;
+    if (p.split_k) p.K = min(p.split_k, p.K - static_cast<int>(b) * p.split_k);
 }
 
 // Run f with the output type as a compile-time constant (one uniform branch
@@ -1225,7 +1229,68 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, int batch, hipStream_t
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- split-K reduction
+//
+// One thread per 4 consecutive m of one output column n: the fp32 partial
+// products of the splits are added in split order (so every launch gives the
+// same bits), then alpha, the clamp and the conversion of the output type.
+// Workspace layout: split s, element (m, n) at ws[s*M*N + n*M + m].
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, int M,
+                                                            int N, void* D, int64_t ldd, float alpha, int relu) {
+    const int mq = (M + 3) / 4;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= static_cast<int64_t>(mq) * N) return;
+    const int n = static_cast<int>(t / mq);
+    const int m = static_cast<int>(t % mq) * 4;
+    const int64_t plane = static_cast<int64_t>(M) * N;
+    const float* src = ws + static_cast<int64_t>(n) * M + m;
+    const int cnt = min(4, M - m);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if ((M & 3) == 0) {
+        // whole 16-byte groups (the workspace base is 16-byte aligned)
+        for (int s = 0; s < splits; ++s) {
+            const f32x4 q = *reinterpret_cast<const f32x4*>(src + s * plane);
+            acc[0] += q.x;
+            acc[1] += q.y;
+            acc[2] += q.z;
+            acc[3] += q.w;
+        }
+    } else {
+        for (int s = 0; s < splits; ++s) {
+            const float* q = src + s * plane;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < cnt) acc[e] += q[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e < cnt) {
+            float v = acc[e] * alpha;
+            if (relu) v = fmaxf(v, 0.0f);
+            store_out<OUT>(D, static_cast<int64_t>(n) * ldd + m + e, v);
+        }
+    }
+}
+
 }  // namespace tg
+
+hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, int64_t ldd, float alpha,
+                            int relu, int out_dtype, hipStream_t stream) {
+    const int64_t threads = static_cast<int64_t>((M + 3) / 4) * N;
+    const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+    if (out_dtype == TG_BF16)
+        hipLaunchKernelGGL(tg::splitk_reduce_kernel<TG_BF16>, grid, dim3(256), 0, stream, ws, splits, M, N, D, ldd,
+                           alpha, relu);
+    else if (out_dtype == TG_F16)
+        hipLaunchKernelGGL(tg::splitk_reduce_kernel<TG_F16>, grid, dim3(256), 0, stream, ws, splits, M, N, D, ldd,
+                           alpha, relu);
+    else
+        hipLaunchKernelGGL(tg::splitk_reduce_kernel<TG_F32>, grid, dim3(256), 0, stream, ws, splits, M, N, D, ldd,
+                           alpha, relu);
+    return hipGetLastError();
+}
 
 // Kernel instances.
 //   register-staged: (id, dtype, BM, BN, min row alignment class, min waves per SIMD, group_m, eff%)
@@ -1241,7 +1306,12 @@ static hipError_t launch(const GemmArgs& a, int64_t grid, int batch, hipStream_t
     X(7, TG_BF16, 128, 128, 2, 2, 4, 45)        \
     X(8, TG_F16, 128, 128, 4, 2, 4, 45)         \
     X(9, TG_F16, 128, 128, 2, 2, 4, 45)         \
-    X(10, TG_F32, 128, 128, 4, 2, 4, 45)
+    X(10, TG_F32, 128, 128, 4, 2, 4, 45)        \
+    X(30, TG_BF16, 64, 64, 4, 2, 4, 25)         \
+    X(31, TG_F16, 64, 64, 4, 2, 4, 25)          \
+    X(32, TG_F32, 64, 64, 4, 2, 4, 25)          \
+    X(33, TG_BF16, 64, 64, 2, 2, 4, 25)         \
+    X(34, TG_F16, 64, 64, 2, 2, 4, 25)
 #define TG_STREAM_LIST(X)                       \
     X(0, TG_BF16, 256, 256, 2, 4, 4, 4, 100)    \
     X(1, TG_F16, 256, 256, 2, 4, 4, 4, 100)     \

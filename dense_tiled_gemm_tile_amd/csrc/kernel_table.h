@@ -21,7 +21,13 @@ struct GemmArgs {
     int tiles_m, tiles_n, group_m;
     int out_dtype;   // element type of D: TG_F32, TG_BF16 or TG_F16
     int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
+    int split_k;     // split-K partial products: K elements per split (grid y = split), 0 = off
 };
+
+// Second phase of a split-K call: D = epilogue(sum over splits of the fp32
+// partial products), summed in split order.
+hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, int64_t ldd, float alpha,
+                            int relu, int out_dtype, hipStream_t stream);
 
 typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, int batch, hipStream_t stream);
 

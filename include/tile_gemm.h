@@ -70,7 +70,8 @@ enum tile_gemm_status {
     TG_ERR_ALIAS = -6,  /* D's byte range overlaps A's or B's */
     TG_ERR_LAUNCH = -7, /* the HIP launch failed (hipGetLastError) */
     TG_ERR_DEVICE = -8, /* no current HIP device, or it is not gfx950 */
-    TG_ERR_PLAN = -9    /* requested kernel id unknown or not valid for the call */
+    TG_ERR_PLAN = -9,   /* requested kernel id unknown or not valid for the call */
+    TG_ERR_WORKSPACE = -10 /* split-K workspace missing, misaligned or too small */
 };
 
 /* The host plan for one call (what the kernel will be launched with). */
@@ -151,6 +152,37 @@ int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                       int dtype, int out_dtype, void* stream, int kernel_id);
 
 /*
+ * Split-K (for problems with few output tiles and a long K): K is cut into
+ * `splits` contiguous ranges of whole pipeline stages; each range's fp32
+ * partial product goes to the caller's workspace in a first launch, and a
+ * second launch on the same stream adds the partials in split order (so the
+ * result is the same bits on every call), applies alpha and the clamp and
+ * stores D in out_dtype.  The epilogue thus runs after the reduction, never on
+ * partial sums.
+ *
+ * splits: 1 .. 256 requested (fewer are used when K has fewer stages; 1 is the
+ * plain product), or 0 for an automatic choice (no split unless the output
+ * has fewer tiles than the GPU has CUs and K has at least 64 stages; then
+ * about two workgroups per CU, at least 16 stages per split, at most 64
+ * splits, and never more than `workspace_bytes` holds); workspace: device
+ * memory of at least
+ * tile_gemm_splitk_workspace_bytes(M, N, splits) bytes, 16-byte aligned, not
+ * overlapping A, B or D, owned by the caller and reusable once the stream has
+ * passed the call (its prior contents are irrelevant).  The library still
+ * allocates nothing.  Errors as tile_gemm_out, plus TG_ERR_DIMS for splits out
+ * of range and TG_ERR_WORKSPACE for a missing, misaligned or short workspace.
+ */
+int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                     const void* A, int64_t lda, const void* B, int64_t ldb,
+                     void* D, int64_t ldd, int dtype, int out_dtype, int splits,
+                     void* workspace, int64_t workspace_bytes, void* stream, int kernel_id);
+
+/* Workspace a split-K call needs: splits * M * N * 4 bytes (0 for splits = 1
+ * or an empty output; splits = 0: enough for any automatic choice, i.e. 64
+ * splits; -1 for negative or oversized arguments). */
+int64_t tile_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
+
+/*
  * Host-only: validate the arguments exactly as tile_gemm does and describe the
  * plan it would launch (no HIP call is made; pointers are only inspected for
  * alignment and overlap).  kernel_id -1 = automatic choice.
@@ -187,7 +219,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 3
+#define TILE_GEMM_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

@@ -78,6 +78,9 @@ WORKLOADS = {
                                               12289, 5003, 4099, "bf16", "uniform_pm1",
                                               2.0, True, 5000, pad_ab=8, pad_d=16,
                                               notes="lda=ldb=K+8, ldd=M+16"),
+    # few output tiles and a long K: the shape split-K is for
+    "tall_k_512x512x16384_bf16": _w("tall_k_512x512x16384_bf16", 512, 512, 16384, "bf16", "normal_invsqrtk",
+                                    1.0, True, 7000),
     # batched products (the batched GEMM of the cuTile tutorial's closing
     # section): 16 independent 1024^3 products, matrices stored back to back
     "batched_16x1024_bf16": _w("batched_16x1024_bf16", 1024, 1024, 1024, "bf16", "uniform_pm1",

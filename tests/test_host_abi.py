@@ -21,7 +21,7 @@ def test_library_exports_every_declared_function():
             "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 3
+    assert tg.abi_version() == 4
 
 
 def test_strerror_covers_every_status():
@@ -113,10 +113,11 @@ def test_plans_for_the_workloads():
     assert _plan(W["square_8192_f16_relu"]).dtype == tg.F16
     ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
     assert ragged.load_class == 2 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
+    # small problems take small tiles so that more CUs get work
     tiny = _plan(W["tiny_bounded_65x97x73_bf16"])
-    assert tiny.load_class == 2 and tiny.grid == 1
+    assert tiny.load_class == 2 and (tiny.block_m, tiny.grid) == (64, 4)
     mid = _plan(W["full_tile_1024_bf16"])
-    assert (mid.block_m, mid.block_n, mid.grid) == (128, 128, 64)
+    assert (mid.block_m, mid.block_n, mid.grid) == (64, 64, 256)
     f32 = _plan(W["fp32_2048"])
     assert f32.dtype == tg.F32 and f32.grid == 256 and f32.block_k == 32
 
@@ -218,4 +219,35 @@ def test_batched_plan_counts_every_product():
     assert rc == 0
     assert (info.block_m, info.block_n, info.grid) == (256, 256, 256)
     single = _plan(si.WORKLOADS["full_tile_1024_bf16"])
-    assert (single.block_m, single.block_n) == (128, 128)
+    assert (single.block_m, single.block_n) == (64, 64)
+
+
+def test_splitk_workspace_size_and_validation():
+    """Split-K: workspace size, the splits range and the workspace checks, all
+    before any HIP call."""
+    import torch
+
+    assert tg.splitk_workspace_bytes(1024, 512, 4) == 4 * 1024 * 512 * 4
+    assert tg.splitk_workspace_bytes(1024, 512, 1) == 0
+    assert tg.splitk_workspace_bytes(0, 512, 4) == 0
+    assert tg.splitk_workspace_bytes(-1, 5, 2) == -1 and tg.splitk_workspace_bytes(5, 5, 257) == -1
+    W = 0x7F8000000000
+    M, N, K = 256, 128, 1024
+    need = tg.splitk_workspace_bytes(M, N, 4)
+
+    def call(splits=4, ws=W, ws_bytes=need, **kw):
+        p = dict(A=A, B=B, D=D, lda=K)
+        p.update(kw)
+        return tg.tile_gemm_splitk(M, N, K, 1.0, 1, p["A"], p["lda"], p["B"], K, p["D"], M, tg.BF16, tg.F32,
+                                   splits, ws, ws_bytes, None, -1)
+    no_gpu = 0 if torch.cuda.is_available() else -8
+    assert call(splits=-1) == -1 and call(splits=257) == -1
+    assert tg.splitk_workspace_bytes(1024, 512, 0) == 64 * 1024 * 512 * 4
+    assert call(ws=0) == -10 and call(ws_bytes=need - 1) == -10 and call(ws=W + 8) == -10
+    assert call(ws=D) == -6                   # workspace on top of D
+    assert call(lda=K - 1) == -2              # ordinary validation still applies
+    if no_gpu:
+        assert call() == -8
+        # K with fewer stages than splits: the unused splits need no workspace
+        assert tg.tile_gemm_splitk(M, N, 100, 1.0, 0, A, 100, B, 100, D, M, tg.BF16, tg.F32, 8, W,
+                                   tg.splitk_workspace_bytes(M, N, 2), None, -1) == -8
