@@ -71,6 +71,8 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=1,
                     help="split K into this many ranges (tile_gemm_splitk, 0 = automatic; workspace allocated "
                          "up front)")
+    ap.add_argument("--epilogue", choices=["pointwise", "softmax"], default="pointwise",
+                    help="pointwise alpha/ReLU (tile_gemm) or a row softmax over N (tile_gemm_softmax)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="element type of D (bf16/f16: fp32 epilogue rounded on the way out)")
     ap.add_argument("--cpu-cols", type=int, default=4096,
@@ -105,6 +107,9 @@ def main() -> int:
         Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
         plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
         launch = tg.gemm
+        if args.epilogue == "softmax":
+            def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
+                return tg.gemm_softmax(A_, B_, D_, alpha, stream=stream, kernel_id=kernel_id)
         if args.splits != 1:
             ws = torch.empty(max(tg.splitk_workspace_bytes(w.M, w.N, args.splits), 16), dtype=torch.uint8,
                              device=dev)
@@ -157,6 +162,7 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb,
                    "ldd": w.ldd, "alpha": w.alpha, "relu": w.relu, "dist": w.dist,
                    "out_dtype": args.out_dtype, "batch": w.batch, "splits": args.splits,
+                   "epilogue": args.epilogue,  # softmax: kernel_id below is the pointwise plan
                    "kernel_id": plan.kernel_id,
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},
@@ -179,23 +185,45 @@ def main() -> int:
 
         import oracle
 
-        cols = min(args.cpu_cols, w.N)  # of the first matrix of a batch
         threads = oracle.default_threads()
-        t0 = time.perf_counter()
-        ref, mag = oracle.gemm(w.M, w.N, w.K, w.alpha, w.relu, si.bits(A_st), w.lda, si.bits(B_st), w.ldb,
-                               w.dtype, n0=0, n1=cols, threads=threads)
-        cpu_s = time.perf_counter() - t0
-        cpu_flops = 2.0 * w.M * cols * w.K
+        if args.epilogue == "softmax":
+            # whole rows (every n) for rows m < rows
+            rows = max(1, min(w.M, args.cpu_cols * 8))
+            ms = np.repeat(np.arange(rows, dtype=np.int64)[None, :], w.N, axis=0).reshape(-1)
+            ns = np.repeat(np.arange(w.N, dtype=np.int64), rows)
+            t0 = time.perf_counter()
+            ref, mag = oracle.gemm_entries(w.M, w.N, w.K, w.alpha, False, si.bits(A_st), w.lda, si.bits(B_st),
+                                           w.ldb, w.dtype, ms, ns, threads=threads)
+            cpu_s = time.perf_counter() - t0
+            cpu_flops = 2.0 * rows * w.N * w.K
+            ref, mag = ref.reshape(w.N, rows), mag.reshape(w.N, rows)
+            cols = w.N
+        else:
+            cols = min(args.cpu_cols, w.N)  # of the first matrix of a batch
+            t0 = time.perf_counter()
+            ref, mag = oracle.gemm(w.M, w.N, w.K, w.alpha, w.relu, si.bits(A_st), w.lda, si.bits(B_st), w.ldb,
+                                   w.dtype, n0=0, n1=cols, threads=threads)
+            cpu_s = time.perf_counter() - t0
+            cpu_flops = 2.0 * w.M * cols * w.K
         result["cpu_baseline"] = {
             "value": round(cpu_flops / cpu_s / 1e12, 6),
             "unit": "TFLOP/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"output columns n < {cols} of the {w.M}x{w.N}x{w.K} workload"
-                      f"{' (first product of the batch)' if w.batch > 1 else ''} (all m, full K), "
-                      f"fp64; {cpu_s:.2f} s wall",
+            "sample": (f"rows m < {rows}, every n, of the {w.M}x{w.N}x{w.K} logits (full K), fp64; "
+                       f"{cpu_s:.2f} s wall" if args.epilogue == "softmax" else
+                       f"output columns n < {cols} of the {w.M}x{w.N}x{w.K} workload"
+                       f"{' (first product of the batch)' if w.batch > 1 else ''} (all m, full K), "
+                       f"fp64; {cpu_s:.2f} s wall"),
         }
-        if args.out_dtype == "f32":
+        if args.epilogue == "softmax":
+            sub = D[:w.N, :rows]
+            if args.out_dtype == "f32":
+                d = sub.double().cpu().numpy()
+            else:
+                d = oracle.decode(sub.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), args.out_dtype)
+            ok, ratio = oracle.check_softmax(d, ref, mag, w.K, args.out_dtype)
+        elif args.out_dtype == "f32":
             d = D[:cols, :w.M].double().cpu().numpy()
             ok, ratio = oracle.check(d, ref, mag, w.K)
         else:

@@ -68,6 +68,7 @@ _SIGNATURES = {
     "tile_gemm_splitk": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _int,
                                 _ptr, _i64, _ptr, _int]),
     "tile_gemm_splitk_workspace_bytes": (_i64, [_i64, _i64, _int]),
+    "tile_gemm_softmax": (_int, [_i64, _i64, _i64, _f32, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr, _int]),
     "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                         ctypes.POINTER(PlanInfo)]),
     "tile_gemm_kernel_count": (_int, []),
@@ -140,6 +141,12 @@ def tile_gemm_splitk(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dt
                      workspace_bytes, stream=None, kernel_id=-1) -> int:
     return load_library().tile_gemm_splitk(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd, dtype,
                                            out_dtype, splits, workspace, workspace_bytes, stream, kernel_id)
+
+
+def tile_gemm_softmax(M, N, K, alpha, A, lda, B, ldb, D, ldd, dtype, out_dtype=F32, stream=None,
+                      kernel_id=-1) -> int:
+    return load_library().tile_gemm_softmax(M, N, K, alpha, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream,
+                                            kernel_id)
 
 
 def splitk_workspace_bytes(M, N, splits) -> int:
@@ -286,6 +293,19 @@ def gemm_splitk(A, B, D, alpha: float = 1.0, relu: bool = False, splits: int = 0
         _check(tile_gemm_splitk(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(),
                                 ldd, dt, ot, splits, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), stream.cuda_stream, kernel_id))
+    return D
+
+
+def gemm_softmax(A, B, D, alpha: float = 1.0, stream=None, kernel_id: int = -1):
+    """D[m, :] = softmax over n of alpha*A@B (row m), through tile_gemm_softmax."""
+    import torch
+
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.device(D.device):
+        _check(tile_gemm_softmax(M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd,
+                                 dt, ot, stream.cuda_stream, kernel_id))
     return D
 
 

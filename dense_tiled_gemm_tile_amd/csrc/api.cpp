@@ -349,6 +349,64 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
+int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
+                      int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id) {
+    int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    if (rc) return rc;
+    if (M == 0 || N == 0) return TG_OK;
+    const int es = elem_size(dtype);
+    const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
+    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    // fused: an instance whose tile spans all of N
+    int id = -1;
+    if (kernel_id >= 0) {
+        if (kernel_id >= tg_kernel_table_size) return TG_ERR_PLAN;
+        const TgKernelDesc& k = tg_kernel_table[kernel_id];
+        if (!usable(k, dtype, cls, row_stride) || !k.softmax || k.block_n < N) return TG_ERR_PLAN;
+        id = kernel_id;
+    } else {
+        double best = 0;
+        for (int i = 0; i < tg_kernel_table_size; ++i) {
+            const TgKernelDesc& k = tg_kernel_table[i];
+            if (!usable(k, dtype, cls, row_stride) || !k.softmax || k.block_n < N) continue;
+            const double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+            if (id < 0 || c < best) { id = i; best = c; }
+        }
+    }
+    if (id < 0) {
+        // two passes: the logits alpha*S into an fp32 D, then the row softmax in place
+        if (out_dtype != TG_F32) return TG_ERR_DIMS;
+        rc = tile_gemm_out(M, N, K, alpha, 0, A, lda, B, ldb, D, ldd, dtype, TG_F32, stream, -1);
+        if (rc) return rc;
+        const hipError_t err = tg_softmax_rows(static_cast<float*>(D), static_cast<int>(M), static_cast<int>(N), ldd,
+                                               static_cast<hipStream_t>(stream));
+        return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+    }
+    rc = device_ok();
+    if (rc) return rc;
+    const TgKernelDesc& k = tg_kernel_table[id];
+    GemmArgs a{};
+    a.A = static_cast<const char*>(A);
+    a.B = static_cast<const char*>(B);
+    a.D = D;
+    a.lda_b = lda * es;
+    a.ldb_b = ldb * es;
+    a.ldd = ldd;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.alpha = alpha;
+    a.tiles_m = static_cast<int>(cdiv(M, k.block_m));
+    a.tiles_n = 1;
+    a.group_m = k.group_m;
+    a.out_dtype = out_dtype;
+    a.epi = TG_EPI_SOFTMAX;
+    const int64_t grid = a.tiles_m;
+    if (grid > kMaxGrid) return TG_ERR_DIMS;
+    const hipError_t err = k.launch(a, grid, 1, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
 int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
                   int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int dtype,
                   int out_dtype, void* stream, int kernel_id) {

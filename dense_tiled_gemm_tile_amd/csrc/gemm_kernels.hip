@@ -186,6 +186,84 @@ __device__ __forceinline__ void with_out_type(int out, F&& f) {
         f(std::integral_constant<int, TG_F32>{});
 }
 
+// Softmax over n of x = alpha*S for every row m of a 2 x 2-wave tile whose
+// n range spans all of N (n0 = 0, N <= BN); `acc` as the kernels hold it
+// (block (i, j), register r: m = m0 + wave_m*WTM + 32j + acc_col(lane),
+// n = wave_n*WTN + 32i + acc_row(lane, r)).  Row statistics are reduced
+// within a lane (its FN*16 values), across the two half-waves (lanes l and
+// l^32 hold the other n of each block) and across the two waves along n
+// through LDS -- the collective a row-wise epilogue needs (Tylo.jl manual,
+// "Walk through GEMM", section 5).  Every reduction runs in a fixed order, so
+// results repeat bit for bit.  `smem` needs 2*BM floats and must be free.
+template <int BM, int WTM, int WTN, int FM, int FN>
+__device__ __forceinline__ void softmax_epilogue(f32x16 (&acc)[FN][FM], const GemmArgs& p, int m0, int wave_m,
+                                                 int wave_n, int lane, char* smem) {
+    const float alpha = p.alpha;
+    const int M = p.M, N = p.N;
+    float* red = reinterpret_cast<float*>(smem);  // [2][BM]: one value per (wave_n, m)
+    const float neg_inf = -__builtin_huge_valf();
+    float stat[FM];
+    __syncthreads();  // the LDS stages are no longer read
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        float mx = neg_inf;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = wave_n * WTN + 32 * i + acc_row(lane, r);
+                const float x = acc[i][j][r] * alpha;
+                acc[i][j][r] = x;
+                if (n < N) mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (lane < 32) red[wave_n * BM + wave_m * WTM + 32 * j + lane] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int idx = wave_m * WTM + 32 * j + acc_col(lane);
+        stat[j] = fmaxf(red[idx], red[BM + idx]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = wave_n * WTN + 32 * i + acc_row(lane, r);
+                const float e = (n < N) ? expf(acc[i][j][r] - stat[j]) : 0.0f;
+                acc[i][j][r] = e;
+                sum += e;
+            }
+        const float other = __shfl_xor(sum, 32);
+        sum = (lane < 32) ? sum + other : other + sum;  // same order on both halves
+        if (lane < 32) red[wave_n * BM + wave_m * WTM + 32 * j + lane] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int idx = wave_m * WTM + 32 * j + acc_col(lane);
+        stat[j] = red[idx] + red[BM + idx];
+    }
+    with_out_type(p.out_dtype, [&](auto out) {
+        constexpr int OUT = decltype(out)::value;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = wave_n * WTN + 32 * i + acc_row(lane, r);
+                    if (m < M && n < N) store_out<OUT>(p.D, static_cast<int64_t>(n) * p.ldd + m, acc[i][j][r] / stat[j]);
+                }
+            }
+    });
+}
+
 // ---------------------------------------------------------------- kernel
 
 template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES>
@@ -331,6 +409,10 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     //   n = n0 + wave_n*WTN + 32*i + 8*(r/4) + 4*(l/32) + (r%4).
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
+    if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
+        softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
+        return;
+    }
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
     with_out_type(p.out_dtype, [&](auto out) {
         constexpr int OUT = decltype(out)::value;
@@ -857,6 +939,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         }
     }
 
+    if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
+        softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
+        return;
+    }
+
     // epilogue: alpha, then ReLU, in registers
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
@@ -1276,6 +1363,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 }  // namespace tg
 
+// Row softmax over n of an fp32 D in place: one thread per m (consecutive
+// threads read consecutive m of each row n, so every pass is coalesced); max,
+// then the sum of exponentials, then the normalised values, each pass in
+// increasing n.
+__global__ __launch_bounds__(256) void tg_softmax_rows_kernel(float* D, int M, int N, int64_t ldd) {
+    const int m = blockIdx.x * 256 + threadIdx.x;
+    if (m >= M) return;
+    float mx = -__builtin_huge_valf();
+    for (int n = 0; n < N; ++n) mx = fmaxf(mx, D[static_cast<int64_t>(n) * ldd + m]);
+    float sum = 0.0f;
+    for (int n = 0; n < N; ++n) sum += expf(D[static_cast<int64_t>(n) * ldd + m] - mx);
+    for (int n = 0; n < N; ++n) {
+        float* d = D + static_cast<int64_t>(n) * ldd + m;
+        *d = expf(*d - mx) / sum;
+    }
+}
+
+hipError_t tg_softmax_rows(float* D, int M, int N, int64_t ldd, hipStream_t stream) {
+    hipLaunchKernelGGL(tg_softmax_rows_kernel, dim3(static_cast<unsigned>((M + 255) / 256)), dim3(256), 0, stream, D,
+                       M, N, ldd);
+    return hipGetLastError();
+}
+
 hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, int64_t ldd, float alpha,
                             int relu, int out_dtype, hipStream_t stream) {
     const int64_t threads = static_cast<int64_t>((M + 3) / 4) * N;
@@ -1358,7 +1468,7 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 #define TG_ES(DT) ((DT) == TG_F32 ? 4 : 2)
 #define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, EFF)                                                \
     {id, DT, BM, BN, 128 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,    \
-     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW>},
+     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW>, 0, 1},
 #define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF)                                         \
     {id, DT, BM, BN, 64 / TG_ES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,           \
      (S) * ((BM) + (BN)) * 64, ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                    \
@@ -1371,7 +1481,7 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 #define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                    \
     {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
-     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0},
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, 1},
 
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
                                              TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};

@@ -22,7 +22,14 @@ struct GemmArgs {
     int out_dtype;   // element type of D: TG_F32, TG_BF16 or TG_F16
     int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
     int split_k;     // split-K partial products: K elements per split (grid y = split), 0 = off
+    int epi;         // epilogue: 0 = alpha then optional ReLU per element, 1 = softmax over n
 };
+
+enum { TG_EPI_POINTWISE = 0, TG_EPI_SOFTMAX = 1 };
+
+// Row softmax over n of an fp32 D, in place (second pass when one tile
+// cannot span N).
+hipError_t tg_softmax_rows(float* D, int M, int N, int64_t ldd, hipStream_t stream);
 
 // Second phase of a split-K call: D = epilogue(sum over splits of the fp32
 // partial products), summed in split order.
@@ -46,6 +53,7 @@ struct TgKernelDesc {
     int eff_pct;       // expected MFMA efficiency, weighs tiles in the plan chooser
     TgLaunchFn launch;
     int64_t max_row_stride;  // largest lda/ldb in bytes the instance can address (0: any)
+    int softmax;             // 1: the epilogue can also take a softmax over n (N <= block_n)
 };
 
 // Indexed by kernel id.

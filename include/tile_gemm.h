@@ -177,6 +177,27 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      void* D, int64_t ldd, int dtype, int out_dtype, int splits,
                      void* workspace, int64_t workspace_bytes, void* stream, int kernel_id);
 
+/*
+ * Softmax over n (a row-wise epilogue; Tylo.jl manual, "Walk through GEMM",
+ * section 5, on replacing the pointwise ReLU by a softmax, which needs a
+ * reduction across the waves that share a row):
+ *
+ *     x[m,n] = alpha * S[m,n]  (fp32),
+ *     d[m,n] = exp(x[m,n] - max_n' x[m,n']) / sum_n' exp(x[m,n'] - max_n' x[m,n'])
+ *
+ * for every row m, over the N columns.  When one tile of a softmax-capable
+ * instance spans N (N <= 256 for 16-bit operands, N <= 128 for fp32), it is
+ * fused into the GEMM's epilogue and D may be fp32, bf16 or fp16
+ * (out_dtype).  Otherwise it runs as two launches on the stream -- the fp32
+ * logits into D, then the row softmax in place -- which needs out_dtype
+ * TG_F32 (else TG_ERR_DIMS).  kernel_id forces a fused instance (-1 = auto).
+ * Other rules as tile_gemm_out.
+ */
+int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
+                      const void* A, int64_t lda, const void* B, int64_t ldb,
+                      void* D, int64_t ldd, int dtype, int out_dtype,
+                      void* stream, int kernel_id);
+
 /* Workspace a split-K call needs: splits * M * N * 4 bytes (0 for splits = 1
  * or an empty output; splits = 0: enough for any automatic choice, i.e. 64
  * splits; -1 for negative or oversized arguments). */
@@ -219,7 +240,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 4
+#define TILE_GEMM_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -223,3 +223,45 @@ def check(d: np.ndarray, ref: np.ndarray, mag: np.ndarray, K: int):
     ratio = float(np.max(err / tol)) if err.size else 0.0
     ok = bool(np.all(err <= tol)) and not bool(np.any(np.isnan(d)))
     return ok, ratio
+
+
+def softmax_rows(ref: np.ndarray) -> np.ndarray:
+    """Softmax over n for every row m of the logits ``ref`` = alpha*S (fp64,
+    shape (N, M) as returned by ``gemm`` with relu off): y = exp(x - max_n x) /
+    sum_n exp(x - max_n x) (the row-wise epilogue of the Tylo.jl manual,
+    "Walk through GEMM", section 5).  numpy's exp and sum serve as the steps."""
+    x = np.asarray(ref, dtype=np.float64)
+    e = np.exp(x - x.max(axis=0, keepdims=True))
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def softmax_tolerance(K: int, mag: np.ndarray, ref: np.ndarray, out_dtype="f32") -> np.ndarray:
+    """Bound for a softmax computed from fp32 logits.
+
+    Logits within T of the exact ones (T = the row's largest fp32 bound) move
+    each probability by at most a factor exp(+-2T); evaluating in fp32 adds
+    about one rounding of (x - max) relative to its magnitude inside exp, and
+    about N + 8 roundings for the sum, the exponential and the division.  A
+    16-bit output adds half a unit of its format."""
+    x = np.asarray(ref, dtype=np.float64)
+    y = softmax_rows(x)
+    T = tolerance(K, mag).max(axis=0, keepdims=True)
+    N = x.shape[0]
+    rel = np.expm1(2.0 * T) + 2.0 ** -24 * (np.abs(x - x.max(axis=0, keepdims=True)) + N + 8)
+    tol = y * rel + 1e-37
+    if _code(out_dtype) != F32:
+        p, emin = _FORMAT[_code(out_dtype)]
+        _, e = np.frexp(y + tol)
+        tol = tol + 0.5 * np.ldexp(1.0, np.maximum(e - 1, emin) - (p - 1))
+    return tol
+
+
+def check_softmax(d: np.ndarray, ref: np.ndarray, mag: np.ndarray, K: int, out_dtype="f32"):
+    """Return (ok, worst_ratio) of a GPU softmax d (fp64, shape (N, M))."""
+    d = np.asarray(d, dtype=np.float64)
+    y = softmax_rows(ref)
+    tol = softmax_tolerance(K, mag, ref, out_dtype)
+    err = np.abs(d - y)
+    ratio = float(np.max(err / tol)) if err.size else 0.0
+    ok = bool(np.all(err <= tol)) and not bool(np.any(np.isnan(d)))
+    return ok, ratio

@@ -81,6 +81,10 @@ WORKLOADS = {
     # few output tiles and a long K: the shape split-K is for
     "tall_k_512x512x16384_bf16": _w("tall_k_512x512x16384_bf16", 512, 512, 16384, "bf16", "normal_invsqrtk",
                                     1.0, True, 7000),
+    # a row softmax over N fused into the epilogue (one 256-wide tile spans N)
+    "softmax_65536x256x4096_bf16": _w("softmax_65536x256x4096_bf16", 65536, 256, 4096, "bf16",
+                                      "normal_invsqrtk", 1.0, False, 8000,
+                                      notes="measured with tile_gemm_softmax"),
     # batched products (the batched GEMM of the cuTile tutorial's closing
     # section): 16 independent 1024^3 products, matrices stored back to back
     "batched_16x1024_bf16": _w("batched_16x1024_bf16", 1024, 1024, 1024, "bf16", "uniform_pm1",

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_function():
             "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 4
+    assert tg.abi_version() == 5
 
 
 def test_strerror_covers_every_status():
@@ -251,3 +251,25 @@ def test_splitk_workspace_size_and_validation():
         # K with fewer stages than splits: the unused splits need no workspace
         assert tg.tile_gemm_splitk(M, N, 100, 1.0, 0, A, 100, B, 100, D, M, tg.BF16, tg.F32, 8, W,
                                    tg.splitk_workspace_bytes(M, N, 2), None, -1) == -8
+
+
+def test_softmax_validation_without_gpu():
+    """tile_gemm_softmax validates like tile_gemm_out; the fused path needs an
+    instance whose tile spans N, the two-pass path an fp32 D."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    call = lambda N, out, kid=-1, lda=64: tg.tile_gemm_softmax(256, N, 64, 1.0, A, lda, B, 64, D, 256, tg.BF16,
+                                                               out, None, kid)
+    assert call(256, tg.BF16) == -8       # fused, valid: no device here
+    assert call(1000, tg.F32) == -8       # two passes, valid
+    assert call(1000, tg.BF16) == -1      # two passes need an fp32 D
+    assert call(256, tg.BF16, lda=63) == -2
+    assert call(256, 9) == -5
+    big = [k for k in range(tg.kernel_count()) if tg.kernel_info(k).block_n == 256
+           and tg.kernel_info(k).dtype == tg.BF16 and tg.kernel_info(k).load_class != 16]
+    wide = [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 16
+            and tg.kernel_info(k).dtype == tg.BF16]
+    assert call(256, tg.F32, big[0]) == -8
+    assert call(256, tg.F32, wide[0]) == -9   # streaming instances have no softmax epilogue

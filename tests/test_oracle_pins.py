@@ -406,3 +406,42 @@ def test_tolerance_bound_holds_for_fp32_accumulation():
     ref1, mag1 = oracle.gemm(M, N, K, 1.0, False, ones, K, ones[:N], K, "bf16")
     ok, _ = oracle.check(ref1 - 64.0, ref1, mag1, K)
     assert not ok
+
+
+def test_softmax_reference():
+    """The row softmax of the oracle: probabilities sum to one and are
+    nonnegative, a constant added to a row changes nothing, equal logits give
+    exactly 1/N, zero B gives uniform rows through the GEMM, and the result
+    matches scipy's softmax."""
+    from scipy.special import softmax as scipy_softmax
+
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((37, 11)) * 5          # (N, M): 37 columns n, 11 rows m
+    y = oracle.softmax_rows(x)
+    assert np.all(y >= 0) and np.allclose(y.sum(axis=0), 1.0, rtol=0, atol=1e-15)
+    assert np.allclose(oracle.softmax_rows(x + rng.standard_normal((1, 11)) * 100), y, rtol=1e-12, atol=0)
+    assert np.allclose(y, scipy_softmax(x, axis=0), rtol=1e-13, atol=0)
+    assert np.array_equal(oracle.softmax_rows(np.full((8, 3), 2.5)), np.full((8, 3), 0.125))
+    A = torch.ones(5, 7, dtype=torch.bfloat16)
+    B = torch.zeros(16, 7, dtype=torch.bfloat16)
+    ref, mag = oracle.gemm(5, 16, 7, 3.0, False, _bits(A), 7, _bits(B), 7, "bf16")
+    assert np.array_equal(oracle.softmax_rows(ref), np.full((16, 5), 1.0 / 16))
+
+
+def test_softmax_tolerance_admits_fp32_evaluation():
+    """The softmax bound admits a float32 evaluation of the softmax of float32
+    logits (a genuine fp32 accumulation) and rejects probabilities off by 1 %."""
+    M, N, K = 16, 200, 512
+    A, B = si.operands(M, N, K, "bf16", "normal_invsqrtk", 65, 66)
+    ref, mag = oracle.gemm(M, N, K, 4.0, False, _bits(A), K, _bits(B), K, "bf16")
+    a32, b32 = A.float().numpy(), B.float().numpy()
+    acc = np.zeros((N, M), dtype=np.float32)
+    for k in range(K):
+        acc += np.outer(b32[:, k], a32[:, k]).astype(np.float32)
+    x = np.float32(4.0) * acc
+    e = np.exp(x - x.max(axis=0, keepdims=True))
+    d = e / e.sum(axis=0, keepdims=True, dtype=np.float32)
+    ok, ratio = oracle.check_softmax(d, ref, mag, K)
+    assert ok and ratio < 0.5, ratio
+    ok, _ = oracle.check_softmax(d * 1.01, ref, mag, K)
+    assert not ok
