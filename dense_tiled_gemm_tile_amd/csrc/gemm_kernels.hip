@@ -743,7 +743,8 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 // each store writes a whole 1 KiB row run (measured no faster: the D write
 // burst at the end of a tile is bound by memory bandwidth either way), bit 2 =
 // the same for bf16/fp16 D, whose direct stores would write 64-byte halves of
-// lines.
+// lines; bit 3 = the instance also carries the softmax epilogue (kept out of
+// the plain instances, whose epilogue it would bloat).
 template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     select_batch(p);
@@ -939,9 +940,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         }
     }
 
-    if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
-        softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
-        return;
+    if constexpr ((EPI & 8) != 0) {
+        if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
+            softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
+            return;
+        }
     }
 
     // epilogue: alpha, then ReLU, in registers
@@ -961,20 +964,36 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     const bool trans32 = (EPI & 2) && p.out_dtype == TG_F32 && interior && aligned16 && (p.ldd & 3) == 0;
     const bool trans16 = (EPI & 4) && p.out_dtype != TG_F32 && interior && aligned16 && (p.ldd & 7) == 0;
     if (!trans32 && !trans16) {
-        // store by ownership: each instruction writes 2 x 32 consecutive m
+        // store by ownership: each instruction writes 2 x 32 consecutive m.
+        // Interior tiles store without per-element checks; the row offsets
+        // of a block's 16 registers are wave-uniform multiples of ldd.
         with_out_type(p.out_dtype, [&](auto out) {
             constexpr int OUT = decltype(out)::value;
+            const int64_t ldd = p.ldd;
+            const int64_t lane_off = static_cast<int64_t>(n0 + wave_n * WTN + acc_row(lane, 0)) * ldd +
+                                     (m0 + wave_m * WTM + acc_col(lane));
+            if (interior) {
 #pragma unroll
-            for (int i = 0; i < FN; ++i) {
+                for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
-                    const int nbase = n0 + wave_n * WTN + 32 * i;
+                    for (int j = 0; j < FM; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int n = nbase + acc_row(lane, r);
-                        if (interior || (m < M && n < N))
-                            store_out<OUT, (EPI & 1) != 0>(p.D, static_cast<int64_t>(n) * p.ldd + m, acc[i][j][r]);
+                        for (int r = 0; r < 16; ++r)
+                            store_out<OUT, (EPI & 1) != 0>(
+                                p.D, lane_off + (32 * i + 8 * (r >> 2) + (r & 3)) * ldd + 32 * j, acc[i][j][r]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+                        const int nbase = n0 + wave_n * WTN + 32 * i;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int n = nbase + acc_row(lane, r);
+                            if (m < M && n < N)
+                                store_out<OUT, (EPI & 1) != 0>(p.D, static_cast<int64_t>(n) * ldd + m, acc[i][j][r]);
+                        }
                     }
                 }
             }
@@ -1447,7 +1466,9 @@ hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, 
     X(26, TG_BF16, 4, 5, 16, 1, 1, 0, 10)       \
     X(27, TG_BF16, 4, 5, 16, 1, 1, 2, 10)       \
     X(28, TG_BF16, 4, 5, 16, 1, 1, 3, 10)       \
-    X(29, TG_BF16, 4, 5, 16, 1, 1, 1, 10)
+    X(29, TG_BF16, 4, 5, 16, 1, 1, 1, 10)       \
+    X(35, TG_BF16, 4, 5, 16, 1, 1, 13, 106)     \
+    X(36, TG_F16, 4, 5, 16, 1, 1, 13, 106)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
@@ -1481,7 +1502,7 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 #define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                    \
     {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
-     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, 1},
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, ((EPI) & 8) ? 1 : 0},
 
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
                                              TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};
