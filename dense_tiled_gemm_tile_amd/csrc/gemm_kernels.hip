@@ -266,7 +266,8 @@ __device__ __forceinline__ void softmax_epilogue(f32x16 (&acc)[FN][FM], const Ge
 
 // ---------------------------------------------------------------- kernel
 
-template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES>
+// SM = 1: the instance also carries the softmax epilogue.
+template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES, int SM>
 __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     select_batch(p);
     constexpr int ES = (DT == TG_F32) ? 4 : 2;  // element bytes
@@ -409,13 +410,32 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     //   n = n0 + wave_n*WTN + 32*i + 8*(r/4) + 4*(l/32) + (r%4).
     const float alpha = p.alpha;
     const bool relu = p.relu != 0;
-    if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
-        softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
-        return;
+    if constexpr (SM != 0) {
+        if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
+            softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
+            return;
+        }
     }
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
     with_out_type(p.out_dtype, [&](auto out) {
         constexpr int OUT = decltype(out)::value;
+        const int64_t ldd = p.ldd;
+        if (interior) {
+            // no per-element checks; row offsets are wave-uniform multiples of ldd
+            const int64_t lane_off = static_cast<int64_t>(n0 + wave_n * WTN + acc_row(lane, 0)) * ldd +
+                                     (m0 + wave_m * WTM + acc_col(lane));
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float v = acc[i][j][r] * alpha;
+                        if (relu) v = fmaxf(v, 0.0f);
+                        store_out<OUT>(p.D, lane_off + (32 * i + 8 * (r >> 2) + (r & 3)) * ldd + 32 * j, v);
+                    }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
 #pragma unroll
@@ -427,7 +447,7 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
                     const int n = nb + acc_row(lane, r);
                     float v = acc[i][j][r] * alpha;
                     if (relu) v = fmaxf(v, 0.0f);
-                    if (interior || (m < M && n < N)) store_out<OUT>(p.D, static_cast<int64_t>(n) * p.ldd + m, v);
+                    if (m < M && n < N) store_out<OUT>(p.D, static_cast<int64_t>(n) * ldd + m, v);
                 }
             }
         }
@@ -1328,9 +1348,9 @@ static hipError_t launch_hybrid(const GemmArgs& a, int64_t grid, int batch, hipS
 
 // ---------------------------------------------------------------- table
 
-template <int DT, int BM, int BN, int LC, int MW>
+template <int DT, int BM, int BN, int LC, int MW, int SM>
 static hipError_t launch(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, LC, MW>), dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, LC, MW, SM>), dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -1427,20 +1447,24 @@ hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, 
 //   hybrid:          (id, dtype, A stages in LDS, B prefetch stages, group_m, eff%), 256 x 256
 // eff% is the expected MFMA efficiency the host plan chooser weighs tiles by.
 #define TG_RS_LIST(X)                           \
-    X(2, TG_BF16, 256, 256, 4, 1, 4, 70)        \
-    X(3, TG_BF16, 256, 256, 2, 1, 4, 70)        \
-    X(4, TG_F16, 256, 256, 4, 1, 4, 70)         \
-    X(5, TG_F16, 256, 256, 2, 1, 4, 70)         \
-    X(6, TG_BF16, 128, 128, 4, 2, 4, 45)        \
-    X(7, TG_BF16, 128, 128, 2, 2, 4, 45)        \
-    X(8, TG_F16, 128, 128, 4, 2, 4, 45)         \
-    X(9, TG_F16, 128, 128, 2, 2, 4, 45)         \
-    X(10, TG_F32, 128, 128, 4, 2, 4, 45)        \
-    X(30, TG_BF16, 64, 64, 4, 2, 4, 25)         \
-    X(31, TG_F16, 64, 64, 4, 2, 4, 25)          \
-    X(32, TG_F32, 64, 64, 4, 2, 4, 25)          \
-    X(33, TG_BF16, 64, 64, 2, 2, 4, 25)         \
-    X(34, TG_F16, 64, 64, 2, 2, 4, 25)
+    X(2, TG_BF16, 256, 256, 4, 1, 4, 0, 70)     \
+    X(3, TG_BF16, 256, 256, 2, 1, 4, 0, 70)     \
+    X(4, TG_F16, 256, 256, 4, 1, 4, 0, 70)      \
+    X(5, TG_F16, 256, 256, 2, 1, 4, 0, 70)      \
+    X(6, TG_BF16, 128, 128, 4, 2, 4, 1, 45)     \
+    X(7, TG_BF16, 128, 128, 2, 2, 4, 1, 45)     \
+    X(8, TG_F16, 128, 128, 4, 2, 4, 1, 45)      \
+    X(9, TG_F16, 128, 128, 2, 2, 4, 1, 45)      \
+    X(10, TG_F32, 128, 128, 4, 2, 4, 1, 45)     \
+    X(30, TG_BF16, 64, 64, 4, 2, 4, 1, 25)      \
+    X(31, TG_F16, 64, 64, 4, 2, 4, 1, 25)       \
+    X(32, TG_F32, 64, 64, 4, 2, 4, 1, 25)       \
+    X(33, TG_BF16, 64, 64, 2, 2, 4, 1, 25)      \
+    X(34, TG_F16, 64, 64, 2, 2, 4, 1, 25)       \
+    X(37, TG_BF16, 256, 256, 4, 1, 4, 1, 69)    \
+    X(38, TG_BF16, 256, 256, 2, 1, 4, 1, 69)    \
+    X(39, TG_F16, 256, 256, 4, 1, 4, 1, 69)     \
+    X(40, TG_F16, 256, 256, 2, 1, 4, 1, 69)
 #define TG_STREAM_LIST(X)                       \
     X(0, TG_BF16, 256, 256, 2, 4, 4, 4, 100)    \
     X(1, TG_F16, 256, 256, 2, 4, 4, 4, 100)     \
@@ -1471,8 +1495,8 @@ hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, 
     X(36, TG_F16, 4, 5, 16, 1, 1, 13, 106)
 
 // Explicit instantiation, seen by both the device and the host pass.
-#define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, EFF) \
-    template __global__ void tg::gemm_kernel<DT, BM, BN, LC, MW>(GemmArgs);
+#define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \
+    template __global__ void tg::gemm_kernel<DT, BM, BN, LC, MW, SM>(GemmArgs);
 #define TG_INSTANTIATE_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF) \
     template __global__ void tg::gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>(GemmArgs);
 #define TG_INSTANTIATE_HYBRID(id, DT, S, P, GM, EFF) \
@@ -1487,9 +1511,9 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 // The table holds host launch functions, so it exists only in the host pass.
 #ifndef __HIP_DEVICE_COMPILE__
 #define TG_ES(DT) ((DT) == TG_F32 ? 4 : 2)
-#define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, EFF)                                                \
+#define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF)                                            \
     {id, DT, BM, BN, 128 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,    \
-     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW>, 0, 1},
+     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW, SM>, 0, SM},
 #define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF)                                         \
     {id, DT, BM, BN, 64 / TG_ES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,           \
      (S) * ((BM) + (BN)) * 64, ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                    \

@@ -271,5 +271,6 @@ def test_softmax_validation_without_gpu():
            and tg.kernel_info(k).dtype == tg.BF16 and tg.kernel_info(k).load_class != 16]
     wide = [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 16
             and tg.kernel_info(k).dtype == tg.BF16]
-    assert call(256, tg.F32, big[0]) == -8
+    codes = {call(256, tg.F32, k) for k in big}
+    assert codes == {-8, -9}                # some 256-wide instances carry the softmax epilogue, some not
     assert call(256, tg.F32, wide[0]) == -9   # streaming instances have no softmax epilogue
