@@ -44,6 +44,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // 16-byte vector that only promises 4-byte alignment: still one dwordx4 access.
 typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -764,7 +767,12 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 // burst at the end of a tile is bound by memory bandwidth either way), bit 2 =
 // the same for bf16/fp16 D, whose direct stores would write 64-byte halves of
 // lines; bit 3 = the instance also carries the softmax epilogue (kept out of
-// the plain instances, whose epilogue it would bloat).
+// the plain instances, whose epilogue it would bloat); bit 4 = interior tiles
+// transpose 4 x 4 register groups across lane quads and store 4 consecutive m
+// per lane as one 8-byte vector for 16-bit D (measured: the bf16-D epilogue
+// drops from about 31k to 21k cycles against the LDS transpose), bit 5 = the
+// same for fp32 D as 16-byte vectors (measured slower than direct stores:
+// fp32 D is bound by the write burst, and the shuffles add VALU work).
 template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     select_batch(p);
@@ -983,7 +991,66 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     const bool aligned16 = (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
     const bool trans32 = (EPI & 2) && p.out_dtype == TG_F32 && interior && aligned16 && (p.ldd & 3) == 0;
     const bool trans16 = (EPI & 4) && p.out_dtype != TG_F32 && interior && aligned16 && (p.ldd & 7) == 0;
-    if (!trans32 && !trans16) {
+    const bool quad = (EPI & 16) && (p.out_dtype != TG_F32 || (EPI & 32)) && interior && (p.ldd & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.D) & (p.out_dtype == TG_F32 ? 15u : 7u)) == 0;
+    if (quad) {
+        // Interior tile: transpose each 4 x 4 group (4 lanes of a quad = 4
+        // consecutive m, 4 registers = 4 consecutive n) in registers with two
+        // DPP butterfly steps, so each lane holds 4 consecutive m of one n and
+        // stores them as one 16-byte (fp32) or 8-byte (16-bit) vector: a
+        // quarter of the store instructions, each writing whole 128-byte
+        // (fp32) or 64-byte (16-bit) row pieces.
+        const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+        auto dpp = [](float v, int ctrl_is_pair) {
+            const int x = __builtin_bit_cast(int, v);
+            return __builtin_bit_cast(float, ctrl_is_pair ? __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true)
+                                                          : __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+        };
+        const int64_t ldd = p.ldd;
+        const int64_t lane_off = static_cast<int64_t>(n0 + wave_n * WTN + 4 * (lane >> 5) + (lane & 3)) * ldd +
+                                 (m0 + wave_m * WTM + 4 * ((lane & 31) >> 2));
+        with_out_type(p.out_dtype, [&](auto out) {
+            constexpr int OUT = decltype(out)::value;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float x[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+#pragma unroll
+                        for (int q = 0; q < 4; q += 2) {  // swap within lane pairs
+                            const float r = dpp(b0 ? x[q] : x[q + 1], 1);
+                            x[q] = b0 ? r : x[q];
+                            x[q + 1] = b0 ? x[q + 1] : r;
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {  // swap between lane pairs
+                            const float r = dpp(b1 ? x[q] : x[q + 2], 0);
+                            x[q] = b1 ? r : x[q];
+                            x[q + 2] = b1 ? x[q + 2] : r;
+                        }
+                        const int64_t idx = lane_off + (32 * i + 8 * g) * ldd + 32 * j;
+                        if constexpr (OUT == TG_F32) {
+                            const f32x4 v = {x[0], x[1], x[2], x[3]};
+                            f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(p.D) + idx);
+                            if constexpr (EPI & 1) __builtin_nontemporal_store(v, d); else *d = v;
+                        } else {
+                            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                            u32x2 v;
+                            if constexpr (OUT == TG_BF16) {
+                                v.x = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2));
+                                v.y = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2));
+                            } else {
+                                v.x = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[0], x[1]}, f16x2));
+                                v.y = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[2], x[3]}, f16x2));
+                            }
+                            u32x2* d = reinterpret_cast<u32x2*>(static_cast<unsigned short*>(p.D) + idx);
+                            if constexpr (EPI & 1) __builtin_nontemporal_store(v, d); else *d = v;
+                        }
+                    }
+        });
+    } else if (!trans32 && !trans16) {
         // store by ownership: each instruction writes 2 x 32 consecutive m.
         // Interior tiles store without per-element checks; the row offsets
         // of a block's 16 registers are wave-uniform multiples of ldd.
@@ -1483,16 +1550,18 @@ hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, 
     X(19, TG_BF16, 4, 5, 8, 0, 0, 0, 10)        \
     X(20, TG_BF16, 4, 5, 8, 1, 0, 0, 10)        \
     X(21, TG_BF16, 4, 5, 16, 1, 0, 0, 10)       \
-    X(22, TG_BF16, 4, 5, 16, 1, 1, 5, 107)      \
+    X(22, TG_BF16, 4, 5, 16, 1, 1, 17, 107)     \
     X(23, TG_BF16, 4, 5, 8, 1, 1, 5, 10)        \
-    X(24, TG_F16, 4, 5, 16, 1, 1, 5, 107)       \
+    X(24, TG_F16, 4, 5, 16, 1, 1, 17, 107)      \
     X(25, TG_F32, 4, 5, 16, 1, 1, 5, 41)        \
     X(26, TG_BF16, 4, 5, 16, 1, 1, 0, 10)       \
     X(27, TG_BF16, 4, 5, 16, 1, 1, 2, 10)       \
     X(28, TG_BF16, 4, 5, 16, 1, 1, 3, 10)       \
     X(29, TG_BF16, 4, 5, 16, 1, 1, 1, 10)       \
     X(35, TG_BF16, 4, 5, 16, 1, 1, 13, 106)     \
-    X(36, TG_F16, 4, 5, 16, 1, 1, 13, 106)
+    X(36, TG_F16, 4, 5, 16, 1, 1, 13, 106)      \
+    X(41, TG_BF16, 4, 5, 16, 1, 1, 49, 10)      \
+    X(42, TG_F16, 4, 5, 16, 1, 1, 5, 10)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \
