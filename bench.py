@@ -164,6 +164,7 @@ def main() -> int:
                    "out_dtype": args.out_dtype, "batch": w.batch, "splits": args.splits,
                    "epilogue": args.epilogue,  # softmax: kernel_id below is the pointwise plan
                    "kernel_id": plan.kernel_id,
+                   "staged": bool(plan.staged),  # A and B copied into aligned rows first (one more launch)
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),

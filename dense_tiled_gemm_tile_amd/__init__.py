@@ -46,11 +46,11 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "kernel_id", "dtype", "block_m", "block_n", "block_k", "waves_m", "waves_n",
         "wave_tile_m", "wave_tile_n", "threads", "stages", "lds_bytes", "acc_per_lane",
-        "load_class", "group_m", "reserved")] + [
+        "load_class", "group_m", "staged")] + [
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _i64, _ptr, _int, _f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -68,6 +68,10 @@ _SIGNATURES = {
     "tile_gemm_splitk": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _int,
                                 _ptr, _i64, _ptr, _int]),
     "tile_gemm_splitk_workspace_bytes": (_i64, [_i64, _i64, _int]),
+    "tile_gemm_staged": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr,
+                                _i64, _ptr, _int]),
+    "tile_gemm_staged_workspace_bytes": (_i64, [_i64, _i64, _i64, _int]),
+    "tile_gemm_release_staging": (_int, []),
     "tile_gemm_softmax": (_int, [_i64, _i64, _i64, _f32, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr, _int]),
     "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                         ctypes.POINTER(PlanInfo)]),
@@ -151,6 +155,21 @@ def tile_gemm_softmax(M, N, K, alpha, A, lda, B, ldb, D, ldd, dtype, out_dtype=F
 
 def splitk_workspace_bytes(M, N, splits) -> int:
     return load_library().tile_gemm_splitk_workspace_bytes(M, N, splits)
+
+
+def tile_gemm_staged(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, workspace, workspace_bytes,
+                     stream=None, mode=-1) -> int:
+    return load_library().tile_gemm_staged(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd, dtype,
+                                           out_dtype, workspace, workspace_bytes, stream, mode)
+
+
+def staged_workspace_bytes(M, N, K, dtype) -> int:
+    return load_library().tile_gemm_staged_workspace_bytes(M, N, K, dtype)
+
+
+def release_staging() -> None:
+    """Free the library's own staging buffers (tile_gemm_release_staging)."""
+    _check(load_library().tile_gemm_release_staging())
 
 
 def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1, out_dtype=F32) -> PlanInfo:
@@ -293,6 +312,26 @@ def gemm_splitk(A, B, D, alpha: float = 1.0, relu: bool = False, splits: int = 0
         _check(tile_gemm_splitk(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(),
                                 ldd, dt, ot, splits, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), stream.cuda_stream, kernel_id))
+    return D
+
+
+def gemm_staged(A, B, D, alpha: float = 1.0, relu: bool = False, workspace=None, mode: int = 1, stream=None):
+    """As ``gemm``, through tile_gemm_staged: A and B are first copied into
+    16-byte aligned rows padded with zeros to whole K stages (mode 1: always;
+    -1: when the plan says it pays; 0: never).  `workspace` is a device tensor
+    of at least ``staged_workspace_bytes(M, N, K, dtype)`` bytes (allocated
+    here through torch when omitted)."""
+    import torch
+
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
+    if workspace is None:
+        workspace = torch.empty(max(staged_workspace_bytes(M, N, K, dt), 256), dtype=torch.uint8, device=D.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.device(D.device):
+        _check(tile_gemm_staged(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd,
+                                dt, ot, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                stream.cuda_stream, mode))
     return D
 
 

@@ -14,6 +14,8 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "kernel_table.h"
 #include "tile_gemm.h"
@@ -33,6 +35,13 @@ struct Batch {
     int64_t batch = 1, stride_a = 0, stride_b = 0, stride_d = 0;
 };
 constexpr int kCusPerGpu = 256;
+
+// Time model of the staging decision: seconds per unit of plan_cost per K
+// stage (fitted to the 256x256 streaming kernel on an 8192^3 bf16 product),
+// the HBM rate of the staging copy, and the cost of one more launch.
+constexpr double kSecondsPerCostStage = 2.5e-11;
+constexpr double kCopyBytesPerSecond = 4.0e12;
+constexpr double kLaunchSeconds = 6e-6;
 
 int elem_size(int dtype) {
     switch (dtype) {
@@ -143,14 +152,74 @@ void describe(const TgKernelDesc& k, int64_t M, int64_t N, tile_gemm_plan_info* 
     }
 }
 
+// Staged operands: A and B copied into rows of staged_row_bytes (a whole
+// number of 128-byte K stages, zeros past K) that start 16-byte aligned.
+int64_t staged_row_bytes(int64_t K, int es) { return cdiv(K * es, 128) * 128; }
+
+int64_t staged_b_offset(int64_t M, int64_t K, int es) { return cdiv(M * staged_row_bytes(K, es), 256) * 256; }
+
+int64_t staged_bytes(int64_t M, int64_t N, int64_t K, int es) {
+    return staged_b_offset(M, K, es) + N * staged_row_bytes(K, es);
+}
+
+double plan_seconds(const TgKernelDesc& k, int64_t M, int64_t N, int64_t K) {
+    return kSecondsPerCostStage * plan_cost(k, M, N, 1) * double(cdiv(K, k.block_k));
+}
+
+struct Staging {
+    bool on = false;
+    int staged_id = -1;     // instance for the staged operands
+    int64_t row_bytes = 0;  // bytes per staged row
+};
+
+// Whether a single product runs on staged copies of its operands (mode 1:
+// always; -1: when the operand rows are not all 16-byte aligned and the
+// staged plan plus the copy is expected to beat the direct plan).  The copy
+// costs one read and one write of both operands at HBM speed and a launch.
+Staging decide_staging(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, int mode) {
+    Staging st;
+    if (mode == 0 || M == 0 || N == 0 || K == 0) return st;
+    const int es = elem_size(dtype);
+    const int64_t rb = staged_row_bytes(K, es);
+    if (rb / es > kMaxDim) return st;
+    const int sid = choose(M, N, 1, dtype, 16, rb);
+    if (sid < 0) return st;
+    if (mode != 1) {
+        const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
+        if (cls == 16) return st;
+        const int did = choose(M, N, 1, dtype, cls, (lda > ldb ? lda : ldb) * es);
+        if (did >= 0) {
+            const double copy = double((M + N) * (K * es + rb)) / kCopyBytesPerSecond + kLaunchSeconds;
+            const double staged = plan_seconds(tg_kernel_table[sid], M, N, rb / es) + copy;
+            if (staged >= plan_seconds(tg_kernel_table[did], M, N, K)) return st;
+        }
+    }
+    st.on = true;
+    st.staged_id = sid;
+    st.row_bytes = rb;
+    return st;
+}
+
+// staging: report the staged plan when the automatic choice of a single
+// product would stage its operands (the library's own staging buffer assumed
+// available).
 int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
          int64_t ldb, const void* D, int64_t ldd, int out_dtype, int kernel_id, tile_gemm_plan_info* out,
-         const Batch& bt = Batch(), int64_t splits = 1) {
+         const Batch& bt = Batch(), int64_t splits = 1, bool staging = false) {
     const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, bt);
     if (rc) return rc;
     const int es = elem_size(dtype);
     const int cls = row_class(M, N, A, lda, B, ldb, es, bt);
     const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    if (staging && kernel_id < 0 && bt.batch == 1 && splits == 1) {
+        const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, -1);
+        if (st.on) {
+            describe(tg_kernel_table[st.staged_id], M, N, out);
+            out->staged = 1;
+            return out->grid > kMaxGrid ? TG_ERR_DIMS : TG_OK;
+        }
+    }
     int id = kernel_id;
     if (id < 0) {
         id = choose(M, N, bt.batch * splits, dtype, cls, row_stride);
@@ -188,6 +257,115 @@ int device_ok() {
     return ok ? TG_OK : TG_ERR_DEVICE;
 }
 
+// The library's staging buffers: one per (device, stream), grown on demand
+// and kept until tile_gemm_release_staging.  Work on one stream runs in
+// order, so a buffer is never used by two calls at once.
+struct StagingBuffer {
+    int dev;
+    void* stream;
+    void* ptr;
+    int64_t bytes;
+};
+std::mutex g_staging_mu;
+std::vector<StagingBuffer> g_staging;
+constexpr int64_t kStagingGranule = int64_t(32) << 20;
+
+// At least `need` bytes of the current device's buffer for `stream`, or
+// nullptr (the stream is being captured into a graph, or allocation failed):
+// the caller then runs the direct plan.
+char* library_staging(void* stream, int64_t need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_staging_mu);
+    StagingBuffer* buf = nullptr;
+    for (StagingBuffer& b : g_staging)
+        if (b.dev == dev && b.stream == stream) buf = &b;
+    if (buf && buf->bytes >= need) return static_cast<char*>(buf->ptr);
+    if (!buf) {
+        g_staging.push_back(StagingBuffer{dev, stream, nullptr, 0});
+        buf = &g_staging.back();
+    }
+    if (buf->ptr) {
+        // earlier work on the stream may still read the old buffer
+        const bool ok = hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess &&
+                        hipFree(buf->ptr) == hipSuccess;
+        buf->ptr = nullptr;
+        buf->bytes = 0;
+        if (!ok) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+    }
+    const int64_t size = cdiv(need, kStagingGranule) * kStagingGranule;
+    if (hipMalloc(&buf->ptr, static_cast<size_t>(size)) != hipSuccess) {
+        (void)hipGetLastError();
+        buf->ptr = nullptr;
+        return nullptr;
+    }
+    buf->bytes = size;
+    return static_cast<char*>(buf->ptr);
+}
+
+int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                   int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
+                   int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id);
+
+// A single product, on staged operand copies when `mode` and the plan say so
+// (workspace: the caller's, or nullptr for the library's own buffer).
+int gemm_single(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda, const void* B,
+                int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id,
+                void* workspace, int64_t workspace_bytes, int mode, bool library) {
+    if (kernel_id >= 0 || mode == 0)
+        return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                              kernel_id);
+    int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    if (rc) return rc;
+    const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, mode);
+    if (!st.on)
+        return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                              -1);
+    const int es = elem_size(dtype);
+    const int64_t need = staged_bytes(M, N, K, es);
+    char* buf = nullptr;
+    if (!library) {
+        if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) {
+            if (mode == 1) return TG_ERR_WORKSPACE;
+        } else {
+            const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uintptr_t(need);
+            const int os = elem_size(out_dtype);
+            const uintptr_t d0 = reinterpret_cast<uintptr_t>(D), d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
+            const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
+            const uintptr_t b0 = reinterpret_cast<uintptr_t>(B), b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
+            if (overlaps(w0, w1, d0, d1) || overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1)) return TG_ERR_ALIAS;
+            buf = static_cast<char*>(workspace);
+        }
+    }
+    rc = device_ok();
+    if (rc) return rc;
+    if (library) buf = library_staging(stream, need);
+    if (!buf)
+        return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                              -1);
+    char* sa = buf;
+    char* sb = buf + staged_b_offset(M, K, es);
+    const hipError_t err = tg_stage_operands(static_cast<const char*>(A), lda * es, M, static_cast<const char*>(B),
+                                             ldb * es, N, static_cast<int>(K), es, st.row_bytes, sa, sb,
+                                             static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return TG_ERR_LAUNCH;
+    const int64_t kp = st.row_bytes / es;  // the padding holds exact zeros
+    return launch_batched(M, N, kp, alpha, relu, sa, kp, 0, sb, kp, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                          st.staged_id);
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,7 +374,7 @@ int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype, const void*
                          const void* B, int64_t ldb, const float* D, int64_t ldd, int kernel_id,
                          tile_gemm_plan_info* out) {
     if (!out) return TG_ERR_NULL;
-    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, TG_F32, kernel_id, out);
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, TG_F32, kernel_id, out, Batch(), 1, true);
 }
 
 int tile_gemm_query_plan_batched(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
@@ -218,13 +396,24 @@ int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype, const v
                              const void* B, int64_t ldb, const void* D, int64_t ldd, int out_dtype,
                              int kernel_id, tile_gemm_plan_info* out) {
     if (!out) return TG_ERR_NULL;
-    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out);
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out, Batch(), 1, true);
 }
 
 int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
                       int64_t lda, int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b,
                       void* D, int64_t ldd, int64_t stride_d, int64_t batch, int dtype, int out_dtype,
                       void* stream, int kernel_id) {
+    return launch_batched(M, N, K, alpha, relu, A, lda, stride_a, B, ldb, stride_b, D, ldd, stride_d, batch, dtype,
+                          out_dtype, stream, kernel_id);
+}
+
+}  // extern "C"
+
+namespace {
+
+int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                   int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
+                   int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id) {
     Batch bt;
     bt.batch = batch;
     bt.stride_a = stride_a;
@@ -260,6 +449,10 @@ int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, co
                                                                 static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
 
 int64_t tile_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {
     if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || splits < 0 || splits > kMaxSplits) return -1;
@@ -410,8 +603,36 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* 
 int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
                   int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int dtype,
                   int out_dtype, void* stream, int kernel_id) {
-    return tile_gemm_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype,
-                             stream, kernel_id);
+    return gemm_single(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream, kernel_id, nullptr,
+                       0, -1, true);
+}
+
+int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* workspace,
+                     int64_t workspace_bytes, void* stream, int mode) {
+    if (mode < -1 || mode > 1) return TG_ERR_PLAN;
+    return gemm_single(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream, -1, workspace,
+                       workspace_bytes, mode, false);
+}
+
+int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype) {
+    const int es = elem_size(dtype);
+    if (!es || M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    return staged_bytes(M, N, K, es);
+}
+
+int tile_gemm_release_staging(void) {
+    std::lock_guard<std::mutex> lock(g_staging_mu);
+    int rc = TG_OK;
+    for (StagingBuffer& b : g_staging) {
+        if (b.ptr && hipFree(b.ptr) != hipSuccess) {  // hipFree waits for work still using it
+            (void)hipGetLastError();
+            rc = TG_ERR_LAUNCH;
+        }
+    }
+    g_staging.clear();
+    return rc;
 }
 
 int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
@@ -446,7 +667,7 @@ const char* tile_gemm_strerror(int code) {
         case TG_ERR_LAUNCH: return "HIP kernel launch failed";
         case TG_ERR_DEVICE: return "no current gfx950 HIP device";
         case TG_ERR_PLAN: return "kernel instance unknown or not valid for these operands";
-        case TG_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
+        case TG_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         default: return "unknown status";
     }
 }

@@ -1467,6 +1467,45 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+
+// ---------------------------------------------------------------- staged operand copy
+//
+// Rows of A (rows [0, M)) and then of B (rows [M, rows)) copied into dense
+// rows of cpr 16-byte chunks each, so that every copied row starts 16-byte
+// aligned and holds a whole number of 128-byte K stages; the elements from K
+// to the end of a copied row are exact zeros.  One wave per row at a time,
+// lanes on consecutive chunks (1 KiB per wave instruction on both sides).
+// A chunk that lies wholly below K takes the shifting 16-byte load (a
+// source row is only element-aligned); the chunk that straddles K reads its
+// elements one by one.
+template <int ES>
+__global__ __launch_bounds__(256) void stage_rows_kernel(const char* __restrict__ A, int64_t lda_b, int64_t M,
+                                                         const char* __restrict__ B, int64_t ldb_b, int64_t rows,
+                                                         int K, int64_t cpr, char* __restrict__ dstA,
+                                                         char* __restrict__ dstB) {
+    constexpr int EPC = 16 / ES;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+    const int64_t full = K / EPC;  // chunks entirely below K
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); r < rows; r += nwaves) {
+        const bool in_a = r < M;
+        const int64_t rr = in_a ? r : r - M;
+        const char* src = in_a ? A + rr * lda_b : B + rr * ldb_b;
+        char* dst = (in_a ? dstA : dstB) + rr * cpr * 16;
+        for (int64_t c = lane; c < cpr; c += 64) {
+            u32x4 v;
+            if (c < full) {
+                v = load_chunk<(ES == 2 ? 2 : 4)>(src + c * 16);
+            } else if (c * EPC < K) {
+                v = load_chunk_bounded<ES>(src, static_cast<int>(c * EPC), K);
+            } else {
+                v.x = v.y = v.z = v.w = 0u;
+            }
+            *reinterpret_cast<u32x4*>(dst + c * 16) = v;
+        }
+    }
+}
+
 }  // namespace tg
 
 // Row softmax over n of an fp32 D in place: one thread per m (consecutive
@@ -1508,30 +1547,47 @@ hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, 
     return hipGetLastError();
 }
 
+hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char* B, int64_t ldb_b, int64_t N, int K,
+                             int es, int64_t row_bytes, char* dstA, char* dstB, hipStream_t stream) {
+    const int64_t rows = M + N;
+    const int64_t blocks = (rows + 3) / 4;
+    const dim3 grid(static_cast<unsigned>(blocks < 65536 ? blocks : 65536));
+    const int64_t cpr = row_bytes / 16;
+    if (es == 2)
+        hipLaunchKernelGGL(tg::stage_rows_kernel<2>, grid, dim3(256), 0, stream, A, lda_b, M, B, ldb_b, rows, K, cpr,
+                           dstA, dstB);
+    else
+        hipLaunchKernelGGL(tg::stage_rows_kernel<4>, grid, dim3(256), 0, stream, A, lda_b, M, B, ldb_b, rows, K, cpr,
+                           dstA, dstB);
+    return hipGetLastError();
+}
+
 // Kernel instances.
 //   register-staged: (id, dtype, BM, BN, min row alignment class, min waves per SIMD, group_m, eff%)
 //   streaming:       (id, dtype, BM, BN, waves along m, waves along n, LDS stages, group_m, eff%)
 //   hybrid:          (id, dtype, A stages in LDS, B prefetch stages, group_m, eff%), 256 x 256
-// eff% is the expected MFMA efficiency the host plan chooser weighs tiles by.
+// eff% is the expected MFMA efficiency the host plan chooser weighs tiles by
+// (instances with the 2-byte shifting loader measure about 0.8x their 4-byte
+// twins).
 #define TG_RS_LIST(X)                           \
     X(2, TG_BF16, 256, 256, 4, 1, 4, 0, 70)     \
-    X(3, TG_BF16, 256, 256, 2, 1, 4, 0, 70)     \
+    X(3, TG_BF16, 256, 256, 2, 1, 4, 0, 56)     \
     X(4, TG_F16, 256, 256, 4, 1, 4, 0, 70)      \
-    X(5, TG_F16, 256, 256, 2, 1, 4, 0, 70)      \
+    X(5, TG_F16, 256, 256, 2, 1, 4, 0, 56)      \
     X(6, TG_BF16, 128, 128, 4, 2, 4, 1, 45)     \
-    X(7, TG_BF16, 128, 128, 2, 2, 4, 1, 45)     \
+    X(7, TG_BF16, 128, 128, 2, 2, 4, 1, 36)     \
     X(8, TG_F16, 128, 128, 4, 2, 4, 1, 45)      \
-    X(9, TG_F16, 128, 128, 2, 2, 4, 1, 45)      \
+    X(9, TG_F16, 128, 128, 2, 2, 4, 1, 36)      \
     X(10, TG_F32, 128, 128, 4, 2, 4, 1, 45)     \
     X(30, TG_BF16, 64, 64, 4, 2, 4, 1, 25)      \
     X(31, TG_F16, 64, 64, 4, 2, 4, 1, 25)       \
     X(32, TG_F32, 64, 64, 4, 2, 4, 1, 25)       \
-    X(33, TG_BF16, 64, 64, 2, 2, 4, 1, 25)      \
-    X(34, TG_F16, 64, 64, 2, 2, 4, 1, 25)       \
+    X(33, TG_BF16, 64, 64, 2, 2, 4, 1, 20)      \
+    X(34, TG_F16, 64, 64, 2, 2, 4, 1, 20)       \
     X(37, TG_BF16, 256, 256, 4, 1, 4, 1, 69)    \
-    X(38, TG_BF16, 256, 256, 2, 1, 4, 1, 69)    \
+    X(38, TG_BF16, 256, 256, 2, 1, 4, 1, 55)    \
     X(39, TG_F16, 256, 256, 4, 1, 4, 1, 69)     \
-    X(40, TG_F16, 256, 256, 2, 1, 4, 1, 69)
+    X(40, TG_F16, 256, 256, 2, 1, 4, 1, 55)
 #define TG_STREAM_LIST(X)                       \
     X(0, TG_BF16, 256, 256, 2, 4, 4, 4, 100)    \
     X(1, TG_F16, 256, 256, 2, 4, 4, 4, 100)     \

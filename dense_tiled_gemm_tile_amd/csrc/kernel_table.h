@@ -36,6 +36,12 @@ hipError_t tg_softmax_rows(float* D, int M, int N, int64_t ldd, hipStream_t stre
 hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, int64_t ldd, float alpha,
                             int relu, int out_dtype, hipStream_t stream);
 
+// Staged operand copy: the M rows of A (byte stride lda_b) and the N rows of B
+// (ldb_b), K elements of es bytes each, into dense rows of row_bytes (a
+// multiple of 128) at dstA and dstB (16-byte aligned), zero past K.
+hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char* B, int64_t ldb_b, int64_t N, int K,
+                             int es, int64_t row_bytes, char* dstA, char* dstB, hipStream_t stream);
+
 typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, int batch, hipStream_t stream);
 
 struct TgKernelDesc {

@@ -28,15 +28,22 @@
  * multiple of the tile shape").
  *
  * Ownership: A, B and D are device pointers owned by the caller and only
- * borrowed for the duration of the enqueued kernel.  The library allocates no
- * device memory, keeps no pointer after the call returns and does not
- * synchronise: the kernel is enqueued on `stream` (a hipStream_t; NULL means
- * the default stream) and the call returns after the enqueue.  D must not
- * overlap A or B.  Calls are thread-safe.
+ * borrowed for the duration of the enqueued kernels.  The library keeps no
+ * pointer of the caller's after the call returns and does not synchronise:
+ * the kernels are enqueued on `stream` (a hipStream_t; NULL means the default
+ * stream) and the call returns after the enqueue.  D must not overlap A or B.
+ * Calls are thread-safe.
  *
  * Alignment: pointers must be aligned to their element size.  Nothing
- * stronger is required: rows whose byte offsets are not 16-byte aligned (odd
- * lda/ldb) take a narrower load path automatically.
+ * stronger is required.  When the operand rows are not all 16-byte aligned
+ * (odd lda/ldb, offset views), the automatic plan of a single product either
+ * runs a kernel with a narrower load path or, for large products, first
+ * copies A and B into 16-byte aligned rows padded with zeros to a whole
+ * number of 128-byte K stages (the staged plan, see tile_gemm_staged).  Only
+ * then does the library hold device memory of its own: one staging buffer per
+ * (device, stream), grown on demand, kept until tile_gemm_release_staging (the
+ * first call that grows it synchronises that stream).  Under stream capture
+ * the library allocates nothing and runs the direct plan instead.
  *
  * Errors: every entry point returns 0 on success or one of the negative
  * tile_gemm_status codes below; no exception or abort crosses the ABI.
@@ -71,7 +78,7 @@ enum tile_gemm_status {
     TG_ERR_LAUNCH = -7, /* the HIP launch failed (hipGetLastError) */
     TG_ERR_DEVICE = -8, /* no current HIP device, or it is not gfx950 */
     TG_ERR_PLAN = -9,   /* requested kernel id unknown or not valid for the call */
-    TG_ERR_WORKSPACE = -10 /* split-K workspace missing, misaligned or too small */
+    TG_ERR_WORKSPACE = -10 /* workspace missing, misaligned or too small */
 };
 
 /* The host plan for one call (what the kernel will be launched with). */
@@ -91,7 +98,7 @@ typedef struct tile_gemm_plan_info {
     int32_t acc_per_lane;  /* fp32 accumulators held by each lane */
     int32_t load_class;    /* 16, 4 or 2: byte alignment of every operand row start */
     int32_t group_m;       /* tile-rows per group in the grouped tile order */
-    int32_t reserved;
+    int32_t staged;        /* 1: A and B are first copied into aligned staging rows */
     int64_t tiles_m;       /* ceil(M / block_m) */
     int64_t tiles_n;       /* ceil(N / block_n) */
     int64_t grid;          /* workgroups launched = tiles_m * tiles_n */
@@ -198,6 +205,45 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
                       void* D, int64_t ldd, int dtype, int out_dtype,
                       void* stream, int kernel_id);
 
+/*
+ * A single product on staged operand copies: a first launch copies the M rows
+ * of A and the N rows of B into `workspace`, each row starting 16-byte aligned
+ * and holding K rounded up to a whole 128-byte K stage (64 bf16/fp16 or 32
+ * fp32 elements) with exact zeros past K; the product then runs on the copies
+ * with the widest loads, and the zero padding adds exact zeros to every sum
+ * (the same zero-fill of the ragged K edge the bounded path does in place;
+ * cuTile.jl tutorial "Matrix Multiplication", section "Sizes that are not a
+ * multiple of the tile shape"; Tylo.jl manual, "Walk through GEMM", section 3:
+ * the vector width a kernel may use depends on the alignment of the rows it
+ * reads).  Layout of the workspace: A's copy at byte 0 (row m at
+ * m*row_bytes), B's copy at the next 256-byte boundary after M*row_bytes,
+ * row_bytes = 128*ceil(K*s/128).
+ *
+ * mode 1: always stage (TG_ERR_WORKSPACE when workspace is NULL, not 256-byte
+ * aligned or shorter than tile_gemm_staged_workspace_bytes); mode -1: stage
+ * only when the operand rows are not all 16-byte aligned and the time model
+ * of the plan says the copy pays for itself, and run the direct plan when the
+ * workspace does not suffice; mode 0: never (as tile_gemm_out).  workspace:
+ * device memory owned by the caller, not overlapping A, B or D
+ * (TG_ERR_ALIAS), reusable once the stream has passed the call.  M, N or K
+ * = 0 never stages.  Other rules and errors as tile_gemm_out with kernel_id
+ * -1; tile_gemm, tile_gemm_ex and tile_gemm_out with kernel_id -1 behave as
+ * mode -1 with the library's own staging buffer.
+ */
+int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                     const void* A, int64_t lda, const void* B, int64_t ldb,
+                     void* D, int64_t ldd, int dtype, int out_dtype,
+                     void* workspace, int64_t workspace_bytes, void* stream, int mode);
+
+/* Workspace bytes tile_gemm_staged needs for these sizes (0 when M, N or K
+ * is 0; -1 for an unknown dtype or sizes out of range). */
+int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype);
+
+/* Free the library's staging buffers on every device (waits for the work
+ * that still reads them).  Returns TG_OK or TG_ERR_LAUNCH if a free failed.
+ * Later calls allocate again when they stage. */
+int tile_gemm_release_staging(void);
+
 /* Workspace a split-K call needs: splits * M * N * 4 bytes (0 for splits = 1
  * or an empty output; splits = 0: enough for any automatic choice, i.e. 64
  * splits; -1 for negative or oversized arguments). */
@@ -206,7 +252,9 @@ int64_t tile_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
 /*
  * Host-only: validate the arguments exactly as tile_gemm does and describe the
  * plan it would launch (no HIP call is made; pointers are only inspected for
- * alignment and overlap).  kernel_id -1 = automatic choice.
+ * alignment and overlap).  kernel_id -1 = automatic choice; when that choice
+ * stages the operands (staged = 1), the plan describes the product on the
+ * staged copies (load_class 16, K rounded up to whole stages).
  */
 int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype,
                          const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -240,7 +288,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 5
+#define TILE_GEMM_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_function():
             "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 5
+    assert tg.abi_version() == 6
 
 
 def test_strerror_covers_every_status():
@@ -111,11 +111,14 @@ def test_plans_for_the_workloads():
     assert big.lds_bytes <= 160 * 1024
     assert tg.kernel_info(big.kernel_id).load_class == 16  # a streaming instance
     assert _plan(W["square_8192_f16_relu"]).dtype == tg.F16
+    # 2-byte aligned rows: large enough that copying A and B into aligned
+    # staging rows first pays, and the product then runs the streaming kernel
     ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
-    assert ragged.load_class == 2 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
-    # small problems take small tiles so that more CUs get work
+    assert ragged.staged == 1 and ragged.load_class == 16 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
+    assert tg.kernel_info(ragged.kernel_id).block_m == 256 and big.staged == 0
+    # small problems take small tiles so that more CUs get work (and are not staged)
     tiny = _plan(W["tiny_bounded_65x97x73_bf16"])
-    assert tiny.load_class == 2 and (tiny.block_m, tiny.grid) == (64, 4)
+    assert tiny.staged == 0 and tiny.load_class == 2 and (tiny.block_m, tiny.grid) == (64, 4)
     mid = _plan(W["full_tile_1024_bf16"])
     assert (mid.block_m, mid.block_n, mid.grid) == (64, 64, 256)
     f32 = _plan(W["fp32_2048"])
@@ -124,8 +127,14 @@ def test_plans_for_the_workloads():
 
 def test_plan_alignment_classes_and_forced_instances():
     W = si.WORKLOADS["square_8192_bf16_relu"]
-    assert _plan(W, a=A + 4).load_class == 4
-    assert _plan(W, b=B + 2).load_class == 2
+    for off_a, off_b in ((4, 0), (0, 2)):
+        p = _plan(W, a=A + off_a, b=B + off_b)
+        assert p.staged == 1 and p.load_class == 16 and p.grid == 1024
+    w = si.Workload("mid", 300, 200, 130, "bf16", "uniform_pm1", 1.0, False, 130, 130, 300, 1, 2)
+    assert (_plan(w, a=A + 4).load_class, _plan(w, a=A + 4).staged) == (4, 0)
+    assert (_plan(w, b=B + 2).load_class, _plan(w, b=B + 2).staged) == (2, 0)
+    # a forced instance runs on the operands as given
+    assert _plan(W, b=B + 2, kernel_id=3).staged == 0
     # a 2-byte aligned operand cannot run an instance that needs 4-byte rows
     narrow = [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 4
               and tg.kernel_info(k).dtype == tg.BF16]
@@ -274,3 +283,41 @@ def test_softmax_validation_without_gpu():
     codes = {call(256, tg.F32, k) for k in big}
     assert codes == {-8, -9}                # some 256-wide instances carry the softmax epilogue, some not
     assert call(256, tg.F32, wide[0]) == -9   # streaming instances have no softmax epilogue
+
+
+def test_staged_workspace_size_and_validation():
+    """tile_gemm_staged: workspace size formula, and the argument checks that
+    happen before any HIP call."""
+    M, N, K = 12289, 5003, 4099
+    rb = -(-K * 2 // 128) * 128
+    assert rb == 8320
+    assert tg.staged_workspace_bytes(M, N, K, tg.BF16) == -(-M * rb // 256) * 256 + N * rb
+    assert tg.staged_workspace_bytes(M, N, 33, tg.F32) == -(-M * 256 // 256) * 256 + N * 256
+    assert tg.staged_workspace_bytes(M, N, 0, tg.BF16) == 0
+    assert tg.staged_workspace_bytes(0, N, K, tg.BF16) == 0
+    assert tg.staged_workspace_bytes(M, N, K, 9) == -1
+    assert tg.staged_workspace_bytes(-1, N, K, tg.BF16) == -1
+    m, n, k = 300, 200, 130
+    need = tg.staged_workspace_bytes(m, n, k, tg.BF16)
+    W = 0x7F4000000000  # far from A, B and D
+    call = lambda ws, nbytes, mode, d=D: tg.tile_gemm_staged(m, n, k, 1.0, 0, A + 2, k, B, k, d, m, tg.BF16, tg.F32,
+                                                             ws, nbytes, None, mode)
+    assert call(0, 0, 1) == -10            # mode 1 needs a workspace
+    assert call(W, need - 1, 1) == -10     # too short
+    assert call(W + 16, need, 1) == -10    # not 256-byte aligned
+    assert call(W, need, 2) == -9          # unknown mode
+    assert call(A - 256, need, 1) == -6    # overlaps A
+    assert call(W, need, 1, d=W + 512) == -6   # overlaps D
+    import torch
+    if not torch.cuda.is_available():
+        assert call(W, need, 1) == -8      # valid: only the device is missing
+        assert call(0, 0, -1) == -8        # automatic without a workspace: direct plan
+        assert call(0, 0, 0) == -8
+
+
+def test_staging_decision_scales_with_the_problem():
+    """Misaligned rows are staged only when the copy pays: 4096^3 yes, 1024^3 no."""
+    for n, staged in ((4096, 1), (1024, 0)):
+        w = si.Workload("sq", n, n, n, "bf16", "uniform_pm1", 1.0, False, n, n, n, 1, 2)
+        assert _plan(w, b=B + 2).staged == staged, n
+        assert _plan(w).staged == 0  # aligned rows never need it
