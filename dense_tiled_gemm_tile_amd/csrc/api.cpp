@@ -115,14 +115,27 @@ bool usable(const TgKernelDesc& k, int dtype, int cls, int64_t row_stride) {
     return k.dtype == dtype && cls >= k.load_class && (k.max_row_stride == 0 || row_stride <= k.max_row_stride);
 }
 
-int choose(int64_t M, int64_t N, int64_t batch, int dtype, int cls, int64_t row_stride) {
+// Whether every D column (and every D matrix of a batch) starts on a
+// 128-byte line, so that a tile's column pieces are whole lines.
+bool d_lines_aligned(const void* D, int64_t ldd, int os, const Batch& bt) {
+    uintptr_t bits = reinterpret_cast<uintptr_t>(D) | uintptr_t(ldd * os);
+    if (bt.batch > 1) bits |= uintptr_t(bt.stride_d * os);
+    return (bits & 127u) == 0;
+}
+
+// d_lines: D columns start on 128-byte lines.  When they do not, the tiles'
+// column pieces end in partial lines that a neighbouring tile completes
+// later, and nontemporal stores of them measure about 20 % slower on the whole
+// product than ordinary ones; such instances are then weighed down.
+int choose(int64_t M, int64_t N, int64_t batch, int dtype, int cls, int64_t row_stride, bool d_lines = true) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tg_kernel_table_size; ++i) {
         const TgKernelDesc& k = tg_kernel_table[i];
         if (!usable(k, dtype, cls, row_stride)) continue;
         // among equal costs prefer the instance that needs the strongest alignment
-        const double c = plan_cost(k, M, N, batch) * (1.0 + 0.001 / k.load_class);
+        double c = plan_cost(k, M, N, batch) * (1.0 + 0.001 / k.load_class);
+        if (k.nt_store && !d_lines) c *= 1.25;
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
     }
     return best;
@@ -177,18 +190,18 @@ struct Staging {
 // staged plan plus the copy is expected to beat the direct plan).  The copy
 // costs one read and one write of both operands at HBM speed and a launch.
 Staging decide_staging(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
-                       int64_t ldb, int mode) {
+                       int64_t ldb, bool d_lines, int mode) {
     Staging st;
     if (mode == 0 || M == 0 || N == 0 || K == 0) return st;
     const int es = elem_size(dtype);
     const int64_t rb = staged_row_bytes(K, es);
     if (rb / es > kMaxDim) return st;
-    const int sid = choose(M, N, 1, dtype, 16, rb);
+    const int sid = choose(M, N, 1, dtype, 16, rb, d_lines);
     if (sid < 0) return st;
     if (mode != 1) {
         const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
         if (cls == 16) return st;
-        const int did = choose(M, N, 1, dtype, cls, (lda > ldb ? lda : ldb) * es);
+        const int did = choose(M, N, 1, dtype, cls, (lda > ldb ? lda : ldb) * es, d_lines);
         if (did >= 0) {
             const double copy = double((M + N) * (K * es + rb)) / kCopyBytesPerSecond + kLaunchSeconds;
             const double staged = plan_seconds(tg_kernel_table[sid], M, N, rb / es) + copy;
@@ -212,8 +225,9 @@ int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
     const int es = elem_size(dtype);
     const int cls = row_class(M, N, A, lda, B, ldb, es, bt);
     const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), bt);
     if (staging && kernel_id < 0 && bt.batch == 1 && splits == 1) {
-        const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, -1);
+        const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, d_lines, -1);
         if (st.on) {
             describe(tg_kernel_table[st.staged_id], M, N, out);
             out->staged = 1;
@@ -222,7 +236,7 @@ int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
     }
     int id = kernel_id;
     if (id < 0) {
-        id = choose(M, N, bt.batch * splits, dtype, cls, row_stride);
+        id = choose(M, N, bt.batch * splits, dtype, cls, row_stride, d_lines);
         if (id < 0) return TG_ERR_PLAN;
     } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls, row_stride)) {
         return TG_ERR_PLAN;
@@ -329,7 +343,8 @@ int gemm_single(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
                               kernel_id);
     int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
     if (rc) return rc;
-    const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, mode);
+    const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb,
+                                      d_lines_aligned(D, ldd, elem_size(out_dtype), Batch()), mode);
     if (!st.on)
         return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
                               -1);

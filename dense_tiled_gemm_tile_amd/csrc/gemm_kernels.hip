@@ -762,7 +762,9 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 // resources with 32-bit offsets; SCHED 0 = copies in bursts in slabs 0 and 3,
 // 1 = one copy every 4 MFMAs over the whole stage (5 slots); EPI bit 0 =
 // nontemporal D stores (D lines then do not displace operand panels in L2,
-// measured ~2 % faster main loop), bit 1 = fp32 D through an LDS transpose so
+// measured ~2 % faster main loop when D columns start on 128-byte lines; when
+// they do not, the partial lines at the tile edges make them about 20 %
+// slower on the whole product, and the twins without the bit are used), bit 1 = fp32 D through an LDS transpose so
 // each store writes a whole 1 KiB row run (measured no faster: the D write
 // burst at the end of a tile is bound by memory bandwidth either way), bit 2 =
 // the same for bf16/fp16 D, whose direct stores would write 64-byte halves of
@@ -1617,7 +1619,9 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     X(35, TG_BF16, 4, 5, 16, 1, 1, 13, 106)     \
     X(36, TG_F16, 4, 5, 16, 1, 1, 13, 106)      \
     X(41, TG_BF16, 4, 5, 16, 1, 1, 49, 10)      \
-    X(42, TG_F16, 4, 5, 16, 1, 1, 5, 10)
+    X(42, TG_F16, 4, 5, 16, 1, 1, 5, 10)        \
+    X(43, TG_BF16, 4, 5, 16, 1, 1, 16, 107)     \
+    X(44, TG_F16, 4, 5, 16, 1, 1, 16, 107)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \
@@ -1651,7 +1655,8 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 #define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                    \
     {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
-     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, ((EPI) & 8) ? 1 : 0},
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, ((EPI) & 8) ? 1 : 0, \
+     (EPI) & 1},
 
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
                                              TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};

@@ -60,6 +60,7 @@ struct TgKernelDesc {
     TgLaunchFn launch;
     int64_t max_row_stride;  // largest lda/ldb in bytes the instance can address (0: any)
     int softmax;             // 1: the epilogue can also take a softmax over n (N <= block_n)
+    int nt_store;            // 1: D is written with nontemporal stores
 };
 
 // Indexed by kernel id.

@@ -116,6 +116,9 @@ def test_plans_for_the_workloads():
     ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
     assert ragged.staged == 1 and ragged.load_class == 16 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
     assert tg.kernel_info(ragged.kernel_id).block_m == 256 and big.staged == 0
+    # ldd*4 is not a multiple of 128 there: the instance writes D without
+    # nontemporal stores; with line-aligned D columns the default keeps them
+    assert ragged.kernel_id == 43 and big.kernel_id == 22
     # small problems take small tiles so that more CUs get work (and are not staged)
     tiny = _plan(W["tiny_bounded_65x97x73_bf16"])
     assert tiny.staged == 0 and tiny.load_class == 2 and (tiny.block_m, tiny.grid) == (64, 4)
