@@ -1570,7 +1570,12 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
 //   hybrid:          (id, dtype, A stages in LDS, B prefetch stages, group_m, eff%), 256 x 256
 // eff% is the expected MFMA efficiency the host plan chooser weighs tiles by
 // (instances with the 2-byte shifting loader measure about 0.8x their 4-byte
-// twins).
+// twins).  The 64 x 64 and 128 x 128 streaming instances (45-48) keep 7
+// stages of copies in flight and win where few tiles each run a long K
+// (kernel trace, bf16: 512x512x16384 64 us against 109 us for the
+// register-staged 64 x 64; 2048^3 26.5 us against 30.0 us for the
+// register-staged 128 x 128); their weights tie with or just beat those
+// register-staged twins, whose plans they take over for aligned rows.
 #define TG_RS_LIST(X)                           \
     X(2, TG_BF16, 256, 256, 4, 1, 4, 0, 70)     \
     X(3, TG_BF16, 256, 256, 2, 1, 4, 0, 56)     \
@@ -1594,7 +1599,11 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     X(0, TG_BF16, 256, 256, 2, 4, 4, 4, 100)    \
     X(1, TG_F16, 256, 256, 2, 4, 4, 4, 100)     \
     X(11, TG_BF16, 256, 256, 2, 2, 4, 4, 90)    \
-    X(12, TG_F16, 256, 256, 2, 2, 4, 4, 90)
+    X(12, TG_F16, 256, 256, 2, 2, 4, 4, 90)     \
+    X(45, TG_BF16, 64, 64, 2, 2, 8, 4, 25)      \
+    X(46, TG_F16, 64, 64, 2, 2, 8, 4, 25)       \
+    X(47, TG_BF16, 128, 128, 2, 2, 8, 4, 46)    \
+    X(48, TG_F16, 128, 128, 2, 2, 8, 4, 46)
 
 #define TG_HYBRID_LIST(X)                       \
     X(13, TG_BF16, 5, 2, 4, 75)                 \
