@@ -225,6 +225,35 @@ def _operand_args(A, B, D):
     return M, N, K, lda, ldb, ldd, codes[A.dtype], codes[D.dtype]
 
 
+def bound_gemm(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, kernel_id: int = -1):
+    """A no-argument callable that enqueues the same call as ``gemm`` with the
+    arguments marshalled once (for tight launch loops: each call is then one
+    foreign call into the library).  The views must stay alive and unchanged
+    while the callable is used, and D's device must be the current device
+    when it is called; it raises TileGemmError on a failed call."""
+    import torch
+
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    lib = load_library()
+    if ot == F32:
+        fn = lib.tile_gemm_ex
+        args = (M, N, K, float(alpha), int(bool(relu)), A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd, dt,
+                stream.cuda_stream, kernel_id)
+    else:
+        fn = lib.tile_gemm_out
+        args = (M, N, K, float(alpha), int(bool(relu)), A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(), ldd, dt,
+                ot, stream.cuda_stream, kernel_id)
+
+    def call():
+        rc = fn(*args)
+        if rc != TG_OK:
+            raise TileGemmError(rc, strerror(rc))
+
+    return call
+
+
 def gemm(A, B, D, alpha: float = 1.0, relu: bool = False, stream=None, kernel_id: int = -1):
     """D = alpha*A@B (+ReLU) on the GPU through the C ABI; returns D.
 

@@ -291,3 +291,28 @@ def test_invalid_arguments_return_codes_on_gpu():
     assert rc == -6
     with pytest.raises(ValueError):
         tg.gemm(A, A, D, 1.0)  # D is not M-contiguous
+
+
+def test_bound_gemm_repeats_the_same_call():
+    """The pre-marshalled callable enqueues exactly what gemm does (fp32 and
+    bf16 D), every time it is called."""
+    dev = torch.device("cuda:0")
+    M, N, K = 300, 200, 130
+    A_st, B_st = si.operands(M, N, K, "bf16", "normal_invsqrtk", 5, 6)
+    A, B = A_st.to(dev), B_st.to(dev)
+    for odt in (torch.float32, torch.bfloat16):
+        D1 = si.out_storage(M, N).to(odt).to(dev)
+        D2 = si.out_storage(M, N).to(odt).to(dev)
+        tg.gemm(A, B.t(), D1.t(), 0.5, True)
+        call = tg.bound_gemm(A, B.t(), D2.t(), 0.5, True)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(D1.cpu(), D2.cpu())
+        D2.fill_(si.D_SENTINEL)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(D1.cpu(), D2.cpu())
+    bad = tg.bound_gemm(A, B.t(), D1.t(), 0.5, True, kernel_id=tg.kernel_count())
+    with pytest.raises(tg.TileGemmError) as e:
+        bad()
+    assert e.value.code == -9
