@@ -324,3 +324,14 @@ def test_staging_decision_scales_with_the_problem():
         w = si.Workload("sq", n, n, n, "bf16", "uniform_pm1", 1.0, False, n, n, n, 1, 2)
         assert _plan(w, b=B + 2).staged == staged, n
         assert _plan(w).staged == 0  # aligned rows never need it
+
+
+def test_plan_choices_follow_the_kernel_trace_table():
+    """The automatic choice for aligned bf16 operands is the instance that was
+    fastest in the kernel trace for each of these shapes (small streaming 64^2
+    for long-K few-tile products, 128^2 at 2048^2, the wide kernel beyond)."""
+    A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
+    expect = {(1024, 1024, 1024): 45, (2048, 2048, 2048): 47, (512, 512, 16384): 45, (1024, 1024, 4096): 45,
+              (2048, 2048, 8192): 47, (4096, 4096, 1024): 22, (3072, 3072, 3072): 22}
+    for (M, N, K), kid in expect.items():
+        assert tg.query_plan(M, N, K, tg.BF16, A2, K, B2, K, D2, M).kernel_id == kid, (M, N, K)
