@@ -125,7 +125,7 @@ def test_plans_for_the_workloads():
     mid = _plan(W["full_tile_1024_bf16"])
     assert (mid.block_m, mid.block_n, mid.grid) == (64, 64, 256)
     f32 = _plan(W["fp32_2048"])
-    assert f32.dtype == tg.F32 and f32.grid == 256 and f32.block_k == 32
+    assert f32.dtype == tg.F32 and f32.grid == 256 and (f32.block_m, f32.block_k) == (128, 16)
 
 
 def test_plan_alignment_classes_and_forced_instances():
@@ -335,3 +335,15 @@ def test_plan_choices_follow_the_kernel_trace_table():
               (2048, 2048, 8192): 47, (4096, 4096, 1024): 22, (3072, 3072, 3072): 22}
     for (M, N, K), kid in expect.items():
         assert tg.query_plan(M, N, K, tg.BF16, A2, K, B2, K, D2, M).kernel_id == kid, (M, N, K)
+
+
+def test_fp32_plan_choices():
+    """fp32 operands: the wide kernel at 4096^3 (ids 25, or 17 with plain
+    stores when D columns are not line-aligned), the 128^2 streaming instance
+    at 2048^3, the register-staged 64^2 for 1024x1024x4096."""
+    A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
+    q = lambda M, N, K, ldd=None: tg.query_plan(M, N, K, tg.F32, A2, K, B2, K, D2, ldd or M).kernel_id
+    assert q(4096, 4096, 4096) == 25
+    assert q(4096, 4096, 4096, ldd=4097) == 17
+    assert q(2048, 2048, 2048) == 49
+    assert q(1024, 1024, 4096) == 32
