@@ -16,7 +16,9 @@ fp32 acceptance bound is stated in.
 Storage follows the Tylo manual, section 2: A is (M,K) stored K-contiguous with
 leading stride lda (element m*lda + k), B is (K,N) stored K-contiguous with
 leading stride ldb (element k + n*ldb).  Arrays passed here are the raw storage:
-``uint16`` bit patterns for bf16/fp16, ``float32`` for fp32.
+``uint16`` bit patterns for bf16/fp16, ``float32`` for fp32, ``uint8`` for the
+8-bit formats e4m3/e5m2, which may carry block scales (``ref_gemm.c`` states
+the formats and the scale reading).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, exact integer and rational arithmetic, and library decoders.
@@ -30,8 +32,8 @@ from pathlib import Path
 
 import numpy as np
 
-BF16, F16, F32 = 1, 2, 3
-_DTYPES = {"bf16": BF16, "f16": F16, "f32": F32}
+BF16, F16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
+_DTYPES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2}
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "ref_gemm.c"
@@ -69,12 +71,23 @@ def bind(path) -> ctypes.CDLL:
                                         _ptr, _i64, _ptr, _i64, ctypes.c_int,
                                         _i64, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
     lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_gemm_scaled.argtypes = [_i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                       _ptr, _i64, _ptr, _i64, ctypes.c_int, _ptr, _i64, _ptr, _i64,
+                                       _i64, _i64, _ptr, _ptr, _i64, ctypes.c_int]
+    lib.oracle_gemm_scaled.restype = ctypes.c_int
+    lib.oracle_gemm_entries_scaled.argtypes = [_i64, _i64, _i64, ctypes.c_float, ctypes.c_int,
+                                               _ptr, _i64, _ptr, _i64, ctypes.c_int, _ptr, _i64, _ptr, _i64,
+                                               _i64, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_gemm_entries_scaled.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_ptr, ctypes.c_int, _i64, _ptr]
     lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_encode.argtypes = [_ptr, ctypes.c_int, _i64, _ptr]
     lib.oracle_encode.restype = ctypes.c_int
     for name in ("oracle_decode_bf16", "oracle_decode_f16"):
         getattr(lib, name).argtypes = [ctypes.c_uint16]
+        getattr(lib, name).restype = ctypes.c_double
+    for name in ("oracle_decode_e4m3", "oracle_decode_e5m2", "oracle_decode_e8m0"):
+        getattr(lib, name).argtypes = [ctypes.c_uint8]
         getattr(lib, name).restype = ctypes.c_double
     return lib
 
@@ -102,7 +115,7 @@ def _code(dtype) -> int:
 
 
 def _storage(arr: np.ndarray, dtype: int) -> np.ndarray:
-    want = np.float32 if dtype == F32 else np.uint16
+    want = np.float32 if dtype == F32 else np.uint8 if dtype in (E4M3, E5M2) else np.uint16
     arr = np.ascontiguousarray(arr)
     if arr.dtype != want:
         raise TypeError(f"storage for dtype {dtype} must be {np.dtype(want)}, got {arr.dtype}")
@@ -110,7 +123,8 @@ def _storage(arr: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def decode(bits: np.ndarray, dtype, lib=None) -> np.ndarray:
-    """Decode raw storage (uint16 for bf16/fp16, float32 for fp32) to fp64."""
+    """Decode raw storage (uint16 for bf16/fp16, float32 for fp32, uint8 for
+    e4m3/e5m2) to fp64."""
     dt = _code(dtype)
     src = _storage(np.asarray(bits), dt)
     out = np.empty(src.shape, dtype=np.float64)
@@ -131,48 +145,74 @@ def encode(values: np.ndarray, dtype, lib=None) -> np.ndarray:
     return out
 
 
-def gemm(M, N, K, alpha, relu, A, lda, B, ldb, dtype, n0=0, n1=None, threads=None, lib=None):
+def _scales(sc, lds):
+    if sc is None:
+        return None, 0
+    arr = np.ascontiguousarray(np.asarray(sc), dtype=np.uint8)
+    return arr, int(lds)
+
+
+def decode_scale(bits, lib=None) -> np.ndarray:
+    """Block-scale exponents (uint8) to their values 2^(e - 127) (e = 255: NaN)."""
+    lib = lib or _load()
+    return np.array([lib.oracle_decode_e8m0(int(b)) for b in np.asarray(bits, dtype=np.uint8).ravel()],
+                    dtype=np.float64).reshape(np.shape(bits))
+
+
+def gemm(M, N, K, alpha, relu, A, lda, B, ldb, dtype, n0=0, n1=None, threads=None, lib=None,
+         scale_a=None, lds_a=0, scale_b=None, lds_b=0):
     """Columns n0..n1-1 of the oracle result.
 
     A is the raw storage of A (at least (M-1)*lda + K elements, row-major
-    (M, lda) is the usual shape), B likewise for B ((N, ldb)).  Returns
-    ``(ref, mag)``, both float64 arrays of shape (n1 - n0, M): row j holds
-    output column n0 + j, i.e. the M-contiguous storage of the result.
+    (M, lda) is the usual shape), B likewise for B ((N, ldb)).  For the
+    8-bit formats, scale_a / scale_b are optional block-scale exponents
+    (uint8, byte m*lds_a + k//32 for A row m, n*lds_b + k//32 for B column n).
+    Returns ``(ref, mag)``, both float64 arrays of shape (n1 - n0, M): row j
+    holds output column n0 + j, i.e. the M-contiguous storage of the result.
     """
     dt = _code(dtype)
     n1 = N if n1 is None else n1
     a = _storage(np.asarray(A), dt)
     b = _storage(np.asarray(B), dt)
+    sa, lds_a = _scales(scale_a, lds_a)
+    sb, lds_b = _scales(scale_b, lds_b)
     cols = max(0, n1 - n0)
     ref = np.zeros((cols, M), dtype=np.float64)
     mag = np.zeros((cols, M), dtype=np.float64)
-    rc = (lib or _load()).oracle_gemm(M, N, K, float(alpha), int(bool(relu)),
-                             a.ctypes.data if a.size else None, lda,
-                             b.ctypes.data if b.size else None, ldb, dt,
-                             n0, n1, ref.ctypes.data, mag.ctypes.data, max(M, 1),
-                             threads or default_threads())
+    rc = (lib or _load()).oracle_gemm_scaled(M, N, K, float(alpha), int(bool(relu)),
+                                    a.ctypes.data if a.size else None, lda,
+                                    b.ctypes.data if b.size else None, ldb, dt,
+                                    sa.ctypes.data if sa is not None and sa.size else None, lds_a,
+                                    sb.ctypes.data if sb is not None and sb.size else None, lds_b,
+                                    n0, n1, ref.ctypes.data, mag.ctypes.data, max(M, 1),
+                                    threads or default_threads())
     if rc:
         raise ValueError(f"oracle_gemm failed ({rc})")
     return ref, mag
 
 
-def gemm_entries(M, N, K, alpha, relu, A, lda, B, ldb, dtype, ms, ns, threads=None, lib=None):
+def gemm_entries(M, N, K, alpha, relu, A, lda, B, ldb, dtype, ms, ns, threads=None, lib=None,
+                 scale_a=None, lds_a=0, scale_b=None, lds_b=0):
     """Oracle result at the sampled coordinates (ms[i], ns[i]); returns (ref, mag)."""
     dt = _code(dtype)
     a = _storage(np.asarray(A), dt)
     b = _storage(np.asarray(B), dt)
+    sa, lds_a = _scales(scale_a, lds_a)
+    sb, lds_b = _scales(scale_b, lds_b)
     ms = np.ascontiguousarray(ms, dtype=np.int64)
     ns = np.ascontiguousarray(ns, dtype=np.int64)
     if ms.shape != ns.shape:
         raise ValueError("ms and ns must have the same shape")
     ref = np.zeros(ms.shape, dtype=np.float64)
     mag = np.zeros(ms.shape, dtype=np.float64)
-    rc = (lib or _load()).oracle_gemm_entries(M, N, K, float(alpha), int(bool(relu)),
-                                     a.ctypes.data if a.size else None, lda,
-                                     b.ctypes.data if b.size else None, ldb, dt,
-                                     ms.size, ms.ctypes.data, ns.ctypes.data,
-                                     ref.ctypes.data, mag.ctypes.data,
-                                     threads or default_threads())
+    rc = (lib or _load()).oracle_gemm_entries_scaled(M, N, K, float(alpha), int(bool(relu)),
+                                            a.ctypes.data if a.size else None, lda,
+                                            b.ctypes.data if b.size else None, ldb, dt,
+                                            sa.ctypes.data if sa is not None and sa.size else None, lds_a,
+                                            sb.ctypes.data if sb is not None and sb.size else None, lds_b,
+                                            ms.size, ms.ctypes.data, ns.ctypes.data,
+                                            ref.ctypes.data, mag.ctypes.data,
+                                            threads or default_threads())
     if rc:
         raise ValueError(f"oracle_gemm_entries failed ({rc})")
     return ref, mag

@@ -28,7 +28,22 @@
  *   fp16: IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 fraction
  *         bits), subnormals decoded exactly as fraction * 2^-24;
  *   fp32: IEEE binary32 as stored.
+ *   e4m3: 8-bit float, 1 sign, 4 exponent bits with bias 7, 3 fraction
+ *         bits; exponent 0 holds zero and subnormals (fraction * 2^-9);
+ *         exponent 15 with fraction 7 is NaN, every other code is finite
+ *         (largest 448); there is no infinity;
+ *   e5m2: 8-bit float, 1 sign, 5 exponent bits with bias 15, 2 fraction
+ *         bits; subnormals fraction * 2^-16; exponent 31 is infinity
+ *         (fraction 0) or NaN, as in the IEEE formats.
  * Every decoded value is exactly representable in fp64.
+ *
+ * Block scales (8-bit operands only; the pages name block-scaled 8-bit
+ * matmuls but do not define them, so the plain reading of the MX formats is
+ * taken): an optional unsigned 8-bit exponent per 32 consecutive k of every
+ * A row and every B column, value 2^(e - 127), e = 255 meaning NaN.  With
+ * scales, a[m,k] stands for decode(a[m,k]) * 2^(sa[m, k/32] - 127), and b
+ * likewise with sb[n, k/32]; the scale of A row m for k-block j is byte
+ * m*lds_a + j, that of B column n is byte n*lds_b + j.
  *
  * Built with plain -O2 (no fast-math), so the k order of each sum is kept.
  */
@@ -38,7 +53,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_F32 = 3 };
+enum { ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_F32 = 3, ORACLE_E4M3 = 4, ORACLE_E5M2 = 5 };
 
 double oracle_decode_bf16(uint16_t bits) {
     uint32_t word = (uint32_t)bits << 16;
@@ -67,14 +82,65 @@ double oracle_decode_f32(uint32_t bits) {
     return (double)f;
 }
 
+double oracle_decode_e4m3(uint8_t bits) {
+    int sign = (bits >> 7) & 1;
+    int expo = (bits >> 3) & 15;
+    int frac = bits & 7;
+    double v;
+    if (expo == 15 && frac == 7)
+        v = NAN;
+    else if (expo == 0)
+        v = ldexp((double)frac, -9);              /* zero and subnormals */
+    else
+        v = ldexp((double)(8 + frac), expo - 10); /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+double oracle_decode_e5m2(uint8_t bits) {
+    int sign = (bits >> 7) & 1;
+    int expo = (bits >> 2) & 31;
+    int frac = bits & 3;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -16);             /* zero and subnormals */
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(4 + frac), expo - 17); /* (1 + f/4) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Block scale: 2^(e - 127), e = 255 is NaN. */
+double oracle_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
 static int elem_size(int dtype) {
-    return dtype == ORACLE_F32 ? 4 : (dtype == ORACLE_BF16 || dtype == ORACLE_F16) ? 2 : 0;
+    switch (dtype) {
+        case ORACLE_F32: return 4;
+        case ORACLE_BF16:
+        case ORACLE_F16: return 2;
+        case ORACLE_E4M3:
+        case ORACLE_E5M2: return 1;
+        default: return 0;
+    }
 }
 
 static double decode_at(const void* base, int dtype, int64_t idx) {
-    if (dtype == ORACLE_BF16) return oracle_decode_bf16(((const uint16_t*)base)[idx]);
-    if (dtype == ORACLE_F16) return oracle_decode_f16(((const uint16_t*)base)[idx]);
-    return oracle_decode_f32(((const uint32_t*)base)[idx]);
+    switch (dtype) {
+        case ORACLE_BF16: return oracle_decode_bf16(((const uint16_t*)base)[idx]);
+        case ORACLE_F16: return oracle_decode_f16(((const uint16_t*)base)[idx]);
+        case ORACLE_E4M3: return oracle_decode_e4m3(((const uint8_t*)base)[idx]);
+        case ORACLE_E5M2: return oracle_decode_e5m2(((const uint8_t*)base)[idx]);
+        default: return oracle_decode_f32(((const uint32_t*)base)[idx]);
+    }
+}
+
+/* Element k of a row or column stored at base + rowoff, with its block scale
+ * (scales NULL: no scale). */
+static double scaled_at(const void* base, int dtype, int64_t rowoff, int64_t k, const uint8_t* scales,
+                        int64_t scale_off) {
+    double v = decode_at(base, dtype, rowoff + k);
+    if (scales) v *= oracle_decode_e8m0(scales[scale_off + k / 32]);
+    return v;
 }
 
 /* Decode `count` stored elements into fp64 (used by tests of the decoders). */
@@ -160,6 +226,9 @@ typedef struct {
     const int64_t* ms;
     const int64_t* ns;
     const void* A;
+    const uint8_t* sa;  /* block scales (NULL: none) */
+    const uint8_t* sb;
+    int64_t lds_a, lds_b;
 } job_t;
 
 static void* full_worker(void* arg) {
@@ -168,7 +237,7 @@ static void* full_worker(void* arg) {
     if (!bcol) return (void*)1;
     /* columns n0 + tid, n0 + tid + nthreads, ...: loop order n -> m -> k */
     for (int64_t n = j->n0 + j->tid; n < j->n1; n += j->nthreads) {
-        for (int64_t k = 0; k < j->K; ++k) bcol[k] = decode_at(j->B, j->dtype, k + n * j->ldb);
+        for (int64_t k = 0; k < j->K; ++k) bcol[k] = scaled_at(j->B, j->dtype, n * j->ldb, k, j->sb, n * j->lds_b);
         for (int64_t m = 0; m < j->M; ++m) {
             int64_t o = (n - j->n0) * j->ldr + m;
             one_entry(m, n, j->K, j->alpha, j->relu, j->a + m * j->K, bcol, &j->ref[o], &j->mag[o]);
@@ -187,8 +256,8 @@ static void* entry_worker(void* arg) {
     for (int64_t i = j->tid; i < j->count; i += j->nthreads) {
         int64_t m = j->ms[i], n = j->ns[i];
         for (int64_t k = 0; k < j->K; ++k) {
-            arow[k] = decode_at(j->A, j->dtype, m * j->lda + k);
-            bcol[k] = decode_at(j->B, j->dtype, k + n * j->ldb);
+            arow[k] = scaled_at(j->A, j->dtype, m * j->lda, k, j->sa, m * j->lds_a);
+            bcol[k] = scaled_at(j->B, j->dtype, n * j->ldb, k, j->sb, n * j->lds_b);
         }
         one_entry(m, n, j->K, j->alpha, j->relu, arow, bcol, &j->ref[i], &j->mag[i]);
     }
@@ -203,6 +272,16 @@ static int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t ld
     if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1)) return -2;
     if (!elem_size(dtype)) return -5;
     if (K > 0 && ((M > 0 && !A) || (N > 0 && !B))) return -3;
+    return 0;
+}
+
+/* Scales are for 8-bit operands only; each row holds ceil(K/32) of them. */
+static int check_scales(int64_t K, int dtype, const uint8_t* sa, int64_t lds_a, const uint8_t* sb,
+                        int64_t lds_b) {
+    if (!sa && !sb) return 0;
+    if (elem_size(dtype) != 1) return -5;
+    const int64_t blocks = (K + 31) / 32;
+    if ((sa && lds_a < blocks) || (sb && lds_b < blocks)) return -2;
     return 0;
 }
 
@@ -235,10 +314,12 @@ static int run_threads(job_t* proto, int nthreads, void* (*fn)(void*)) {
  * ref and mag are (n1 - n0) columns of ldr >= M doubles each.
  * Returns 0, or a negative code for bad arguments / allocation failure.
  */
-int oracle_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu,
-                const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
-                int64_t n0, int64_t n1, double* ref, double* mag, int64_t ldr, int nthreads) {
+int oracle_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                       const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                       const uint8_t* sa, int64_t lds_a, const uint8_t* sb, int64_t lds_b,
+                       int64_t n0, int64_t n1, double* ref, double* mag, int64_t ldr, int nthreads) {
     int rc = check_args(M, N, K, A, lda, B, ldb, dtype);
+    if (!rc) rc = check_scales(K, dtype, sa, lds_a, sb, lds_b);
     if (rc) return rc;
     if (n0 < 0 || n1 > N || n0 > n1 || ldr < M) return -2;
     if (M == 0 || n1 == n0) return 0;
@@ -247,25 +328,35 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu,
         a = (double*)malloc(sizeof(double) * (size_t)M * (size_t)K);
         if (!a) return -9;
         for (int64_t m = 0; m < M; ++m)
-            for (int64_t k = 0; k < K; ++k) a[m * K + k] = decode_at(A, dtype, m * lda + k);
+            for (int64_t k = 0; k < K; ++k) a[m * K + k] = scaled_at(A, dtype, m * lda, k, sa, m * lds_a);
     }
     job_t p;
     memset(&p, 0, sizeof p);
     p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.n0 = n0; p.n1 = n1; p.ldr = ldr;
     p.alpha = (double)alpha; p.relu = relu; p.dtype = dtype;
     p.a = a; p.B = B; p.ref = ref; p.mag = mag;
+    p.sb = sb; p.lds_b = lds_b;
     int64_t cols = n1 - n0;
     rc = run_threads(&p, nthreads > cols ? (int)cols : nthreads, full_worker);
     free(a);
     return rc;
 }
 
+int oracle_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                int64_t n0, int64_t n1, double* ref, double* mag, int64_t ldr, int nthreads) {
+    return oracle_gemm_scaled(M, N, K, alpha, relu, A, lda, B, ldb, dtype, NULL, 0, NULL, 0, n0, n1, ref, mag, ldr,
+                              nthreads);
+}
+
 /* Sampled entries (ms[i], ns[i]), i < count, into ref[i] and mag[i]. */
-int oracle_gemm_entries(int64_t M, int64_t N, int64_t K, float alpha, int relu,
-                        const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
-                        int64_t count, const int64_t* ms, const int64_t* ns,
-                        double* ref, double* mag, int nthreads) {
+int oracle_gemm_entries_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                               const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                               const uint8_t* sa, int64_t lds_a, const uint8_t* sb, int64_t lds_b,
+                               int64_t count, const int64_t* ms, const int64_t* ns,
+                               double* ref, double* mag, int nthreads) {
     int rc = check_args(M, N, K, A, lda, B, ldb, dtype);
+    if (!rc) rc = check_scales(K, dtype, sa, lds_a, sb, lds_b);
     if (rc) return rc;
     for (int64_t i = 0; i < count; ++i)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
@@ -276,5 +367,14 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K, float alpha, int relu,
     p.alpha = (double)alpha; p.relu = relu; p.dtype = dtype;
     p.A = A; p.B = B; p.ref = ref; p.mag = mag;
     p.count = count; p.ms = ms; p.ns = ns;
+    p.sa = sa; p.lds_a = lds_a; p.sb = sb; p.lds_b = lds_b;
     return run_threads(&p, nthreads > count ? (int)count : nthreads, entry_worker);
+}
+
+int oracle_gemm_entries(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
+                        int64_t count, const int64_t* ms, const int64_t* ns,
+                        double* ref, double* mag, int nthreads) {
+    return oracle_gemm_entries_scaled(M, N, K, alpha, relu, A, lda, B, ldb, dtype, NULL, 0, NULL, 0, count, ms, ns,
+                                      ref, mag, nthreads);
 }

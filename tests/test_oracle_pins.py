@@ -299,10 +299,81 @@ def pin_encode_golden(lib):
         assert [int(g) for g in got] == [b for _, b in pairs], (dt, [hex(int(g)) for g in got])
 
 
+def pin_fp8_decode_vs_torch(lib):
+    """Every code of e4m3, e5m2 and the e8m0 block scale decodes to torch's
+    value for float8_e4m3fn, float8_e5m2 and float8_e8m0fnu (NaN codes alike)."""
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes)
+    for dt, tdt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        got = oracle.decode(codes, dt, lib=lib)
+        want = t.view(tdt).double().numpy()
+        assert np.array_equal(got, want, equal_nan=True), dt
+    got = oracle.decode_scale(codes, lib=lib)
+    want = t.view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(got, want, equal_nan=True)
+    # golden values read off the format definitions
+    g = oracle.decode(np.array([0x7E, 0x08, 0x01, 0xFE], dtype=np.uint8), "e4m3", lib=lib)
+    assert list(g) == [448.0, 2.0 ** -6, 2.0 ** -9, -448.0]
+    g = oracle.decode(np.array([0x7B, 0x04, 0x01, 0x7C], dtype=np.uint8), "e5m2", lib=lib)
+    assert list(g) == [57344.0, 2.0 ** -14, 2.0 ** -16, np.inf]
+
+
+def _fp8_values(codes, dt):
+    tdt = torch.float8_e4m3fn if dt == "e4m3" else torch.float8_e5m2
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(tdt).double().numpy()
+
+
+def pin_fp8_gemm_brute_force(lib):
+    """8-bit products, with and without block scales, against values decoded
+    by torch and summed by numpy.  Unscaled, every value and sum is exact in
+    fp64 (e4m3 codes are multiples of 2^-9 below 512, e5m2 codes come from a
+    narrow exponent range), so the results must be equal; with scales
+    (2^-7..2^7) the sums may round, and the two summation orders must agree
+    within 2^-50 of the summed magnitudes."""
+    rng = np.random.default_rng(11)
+    M, N, K = 5, 6, 70
+    for dt in ("e4m3", "e5m2"):
+        if dt == "e4m3":
+            pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+        else:
+            pool = np.array([c for c in range(256) if 10 <= ((c >> 2) & 31) <= 20], dtype=np.uint8)
+        lda, ldb = K + 3, K + 1
+        A = rng.choice(pool, size=(M, lda)).astype(np.uint8)
+        B = rng.choice(pool, size=(N, ldb)).astype(np.uint8)
+        a, b = _fp8_values(A[:, :K], dt), _fp8_values(B[:, :K], dt)
+        ref, mag = oracle.gemm(M, N, K, 0.75, False, A, lda, B, ldb, dt, lib=lib)
+        want = 0.75 * (a @ b.T)
+        assert np.array_equal(ref, want.T), dt
+        assert np.array_equal(mag, (0.75 * (np.abs(a) @ np.abs(b).T)).T), dt
+        # block scales: 3 blocks of 32 cover K = 70
+        lds_a, lds_b = 4, 5
+        sa = rng.integers(120, 135, size=(M, lds_a)).astype(np.uint8)
+        sb = rng.integers(120, 135, size=(N, lds_b)).astype(np.uint8)
+        blk = np.arange(K) // 32
+        a_s = a * np.exp2(sa[:, blk].astype(np.float64) - 127)
+        b_s = b * np.exp2(sb[:, blk].astype(np.float64) - 127)
+        ref, mag = oracle.gemm(M, N, K, 0.75, True, A, lda, B, ldb, dt, lib=lib, scale_a=sa, lds_a=lds_a,
+                               scale_b=sb, lds_b=lds_b)
+        want = np.maximum(0.75 * (a_s @ b_s.T), 0).T
+        assert np.all(np.abs(ref - want) <= 2.0 ** -50 * (0.75 * (np.abs(a_s) @ np.abs(b_s).T)).T), dt
+        assert np.array_equal(mag, (0.75 * (np.abs(a_s) @ np.abs(b_s).T)).T) or \
+            np.allclose(mag, (0.75 * (np.abs(a_s) @ np.abs(b_s).T)).T, rtol=2.0 ** -50, atol=0), dt
+        ms, ns = np.array([0, 4, 2]), np.array([5, 0, 3])
+        e, _ = oracle.gemm_entries(M, N, K, 0.75, True, A, lda, B, ldb, dt, ms, ns, lib=lib, scale_a=sa,
+                                   lds_a=lds_a, scale_b=sb, lds_b=lds_b)
+        assert np.array_equal(e, ref[ns, ms]), dt
+        # a NaN scale poisons exactly the row it scales
+        sa2 = sa.copy()
+        sa2[2, 1] = 255
+        ref2, _ = oracle.gemm(M, N, K, 0.75, False, A, lda, B, ldb, dt, lib=lib, scale_a=sa2, lds_a=lds_a)
+        assert np.isnan(ref2[:, 2]).all() and np.isfinite(np.delete(ref2, 2, axis=1)).all()
+
+
 PINS = [pin_decode_golden, pin_decode_all_patterns, pin_permutation, pin_identity, pin_rank1,
         pin_small_integers, pin_tiny_rational, pin_zero_padded_k, pin_nan_padding_unread,
         pin_alpha_then_relu, pin_entries_and_column_ranges, pin_degenerate,
-        pin_encode_roundtrip, pin_encode_f16_vs_numpy, pin_encode_bf16_vs_torch, pin_encode_golden]
+        pin_encode_roundtrip, pin_encode_f16_vs_numpy, pin_encode_bf16_vs_torch, pin_encode_golden,
+        pin_fp8_decode_vs_torch, pin_fp8_gemm_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -317,8 +388,14 @@ def test_oracle_pin(pin):
 MUTATIONS = {
     "drop_last_k": ("for (int64_t k = 0; k < K; ++k) {\n        double p", "for (int64_t k = 0; k + 1 < K; ++k) {\n        double p"),
     "relu_before_alpha": ("double r = alpha * s;\n    if (relu && r < 0.0) r = 0.0;", "double r = s;\n    if (relu && r < 0.0) r = 0.0;\n    r *= alpha;"),
-    "b_transposed": ("decode_at(j->B, j->dtype, k + n * j->ldb)", "decode_at(j->B, j->dtype, n + k * j->ldb)"),
-    "a_stride_is_k": ("decode_at(A, dtype, m * lda + k)", "decode_at(A, dtype, m * K + k)"),
+    "b_transposed": ("scaled_at(j->B, j->dtype, n * j->ldb, k, j->sb", "scaled_at(j->B, j->dtype, k * j->ldb, n, j->sb"),
+    "a_stride_is_k": ("scaled_at(A, dtype, m * lda, k, sa", "scaled_at(A, dtype, m * K, k, sa"),
+    "e4m3_bias_8": ("expo - 10);", "expo - 11);"),
+    "e4m3_no_nan": ("if (expo == 15 && frac == 7)", "if (0)"),
+    "e5m2_subnormal_scale": ("ldexp((double)frac, -16)", "ldexp((double)frac, -15)"),
+    "scale_block_16": ("scales[scale_off + k / 32]", "scales[scale_off + k / 16]"),
+    "scale_b_dropped": ("p.sb = sb; p.lds_b = lds_b;\n    int64_t cols", "p.lds_b = lds_b;\n    int64_t cols"),
+    "e8m0_bias_128": ("(int)e - 127", "(int)e - 128"),
     "f16_subnormal_flush": ("v = ldexp((double)frac, -24);", "v = 0.0;"),
     "f16_bias_off_by_one": ("expo - 25", "expo - 24"),
     "bf16_wrong_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
