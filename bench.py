@@ -24,7 +24,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "TFLOP/s (2MNK/t) bf16 GEMM+ReLU at 8192³; % of dense MFMA peak"
 # MI355X dense peaks (no sparsity): 256 CUs at 2.4 GHz
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "e4m3": 5033.2, "e5m2": 5033.2}
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 SOURCES = ["dense_tiled_gemm_tile_amd/csrc/gemm_kernels.hip", "dense_tiled_gemm_tile_amd/csrc/tile_math.h"]
 

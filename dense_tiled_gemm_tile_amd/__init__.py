@@ -24,8 +24,8 @@ _PKG = Path(__file__).resolve().parent
 LIB_PATH = _PKG / "_lib" / "libtile_gemm.so"
 HEADER_PATH = _PKG.parent / "include" / "tile_gemm.h"
 
-BF16, F16, F32 = 1, 2, 3
-DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32}
+BF16, F16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
+DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2}
 
 TG_OK = 0
 STATUS = {0: "TG_OK", -1: "TG_ERR_DIMS", -2: "TG_ERR_LD", -3: "TG_ERR_NULL", -4: "TG_ERR_ALIGN",
@@ -71,6 +71,8 @@ _SIGNATURES = {
     "tile_gemm_staged": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr,
                                 _i64, _ptr, _int]),
     "tile_gemm_staged_workspace_bytes": (_i64, [_i64, _i64, _i64, _int]),
+    "tile_gemm_scaled": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
+                                _i64, _int, _int, _ptr, _int]),
     "tile_gemm_release_staging": (_int, []),
     "tile_gemm_softmax": (_int, [_i64, _i64, _i64, _f32, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr, _int]),
     "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
@@ -163,6 +165,12 @@ def tile_gemm_staged(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dt
                                            out_dtype, workspace, workspace_bytes, stream, mode)
 
 
+def tile_gemm_scaled(M, N, K, alpha, relu, A, lda, scale_a, lds_a, B, ldb, scale_b, lds_b, D, ldd, dtype,
+                     out_dtype=F32, stream=None, kernel_id=-1) -> int:
+    return load_library().tile_gemm_scaled(M, N, K, alpha, int(bool(relu)), A, lda, scale_a, lds_a, B, ldb, scale_b,
+                                           lds_b, D, ldd, dtype, out_dtype, stream, kernel_id)
+
+
 def staged_workspace_bytes(M, N, K, dtype) -> int:
     return load_library().tile_gemm_staged_workspace_bytes(M, N, K, dtype)
 
@@ -204,7 +212,9 @@ def abi_version() -> int:
 def _operand_args(A, B, D):
     import torch
 
-    codes = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
+    codes = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32,
+             torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
+    out_codes = (BF16, F16, F32)
     if A.dim() != 2 or B.dim() != 2 or D.dim() != 2:
         raise ValueError("A, B and D must be 2-D views")
     M, K = A.shape
@@ -213,8 +223,8 @@ def _operand_args(A, B, D):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
     if A.dtype != B.dtype or A.dtype not in codes:
         raise TypeError(f"A and B must share a dtype in {list(codes)}; got {A.dtype}, {B.dtype}")
-    if D.dtype not in codes:
-        raise TypeError(f"D must have a dtype in {list(codes)}; got {D.dtype}")
+    if D.dtype not in codes or codes[D.dtype] not in out_codes:
+        raise TypeError(f"D must be float32, bfloat16 or float16; got {D.dtype}")
     if not (A.is_cuda and B.is_cuda and D.is_cuda):
         raise ValueError("A, B and D must be device tensors")
     if (K > 1 and A.stride(1) != 1) or (K > 1 and B.stride(0) != 1) or (M > 1 and D.stride(0) != 1):
@@ -341,6 +351,33 @@ def gemm_splitk(A, B, D, alpha: float = 1.0, relu: bool = False, splits: int = 0
         _check(tile_gemm_splitk(M, N, K, float(alpha), relu, A.data_ptr(), lda, B.data_ptr(), ldb, D.data_ptr(),
                                 ldd, dt, ot, splits, workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), stream.cuda_stream, kernel_id))
+    return D
+
+
+def gemm_scaled(A, B, D, scale_a=None, scale_b=None, alpha: float = 1.0, relu: bool = False, stream=None,
+                kernel_id: int = -1):
+    """As ``gemm`` for 8-bit operands (torch.float8_e4m3fn / float8_e5m2 views)
+    with block scales: scale_a a (M, lds_a) uint8 view (row stride lds_a,
+    element [m, j] the exponent of k-block j of A row m), scale_b (N, lds_b)
+    likewise for B's columns; either may be None."""
+    import torch
+
+    M, N, K, lda, ldb, ldd, dt, ot = _operand_args(A, B, D)
+
+    def sc(t, rows):
+        if t is None:
+            return None, 0
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[0] != rows or (rows > 1 and t.stride(1) != 1):
+            raise ValueError("scales must be a (rows, lds) uint8 view with unit column stride")
+        return t.data_ptr(), (t.stride(0) if rows > 1 else t.shape[1])
+
+    pa, la = sc(scale_a, M)
+    pb, lb = sc(scale_b, N)
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.device(D.device):
+        _check(tile_gemm_scaled(M, N, K, float(alpha), relu, A.data_ptr(), lda, pa, la, B.data_ptr(), ldb, pb, lb,
+                                D.data_ptr(), ldd, dt, ot, stream.cuda_stream, kernel_id))
     return D
 
 

@@ -45,12 +45,17 @@ constexpr double kLaunchSeconds = 6e-6;
 
 int elem_size(int dtype) {
     switch (dtype) {
+        case TG_E4M3:
+        case TG_E5M2: return 1;
         case TG_BF16:
         case TG_F16: return 2;
         case TG_F32: return 4;
         default: return 0;
     }
 }
+
+// Types D may have.
+bool out_type_ok(int dtype) { return dtype == TG_F32 || dtype == TG_BF16 || dtype == TG_F16; }
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
@@ -59,7 +64,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TG_ERR_DIMS;
     if (bt.batch < 0 || bt.batch > kMaxBatch) return TG_ERR_DIMS;
     const int es = elem_size(dtype);
-    const int os = elem_size(out_dtype);
+    const int os = out_type_ok(out_dtype) ? elem_size(out_dtype) : 0;
     if (!es || !os) return TG_ERR_DTYPE;
     const int64_t kmin = K > 1 ? K : 1;
     if (lda < kmin || ldb < kmin || ldd < (M > 1 ? M : 1)) return TG_ERR_LD;
@@ -89,7 +94,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
 }
 
 // Byte alignment class shared by every operand row start (of every matrix of
-// a batch): 16, 4 or 2.
+// a batch): 16, 4, 2 or (8-bit operands) 1.
 int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, int64_t ldb, int es,
               const Batch& bt) {
     uintptr_t bits = reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B);
@@ -98,7 +103,8 @@ int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, i
     if (bt.batch > 1) bits |= uintptr_t(bt.stride_a * es) | uintptr_t(bt.stride_b * es);
     if ((bits & 15u) == 0) return 16;
     if ((bits & 3u) == 0) return 4;
-    return 2;
+    if ((bits & 1u) == 0) return 2;
+    return 1;
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -329,9 +335,17 @@ char* library_staging(void* stream, int64_t need) {
     return static_cast<char*>(buf->ptr);
 }
 
+// Block scales of 8-bit operands (none when both pointers are null).
+struct Scales {
+    const unsigned char* a = nullptr;
+    const unsigned char* b = nullptr;
+    int64_t lds_a = 0, lds_b = 0;
+};
+
 int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
                    int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
-                   int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id);
+                   int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id,
+                   const Scales& sc = Scales());
 
 // A single product, on staged operand copies when `mode` and the plan say so
 // (workspace: the caller's, or nullptr for the library's own buffer).
@@ -428,7 +442,8 @@ namespace {
 
 int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
                    int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b, void* D, int64_t ldd,
-                   int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id) {
+                   int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id,
+                   const Scales& sc) {
     Batch bt;
     bt.batch = batch;
     bt.stride_a = stride_a;
@@ -460,6 +475,10 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
     a.batch_a_b = stride_a * es;
     a.batch_b_b = stride_b * es;
     a.batch_d_b = stride_d * elem_size(out_dtype);
+    a.scale_a = sc.a;
+    a.scale_b = sc.b;
+    a.lds_a = sc.lds_a;
+    a.lds_b = sc.lds_b;
     const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<int>(batch),
                                                                 static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
@@ -628,6 +647,40 @@ int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
     if (mode < -1 || mode > 1) return TG_ERR_PLAN;
     return gemm_single(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream, -1, workspace,
                        workspace_bytes, mode, false);
+}
+
+int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                     const void* scale_a, int64_t lds_a, const void* B, int64_t ldb, const void* scale_b,
+                     int64_t lds_b, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id) {
+    int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    if (rc) return rc;
+    Scales sc;
+    if (scale_a || scale_b) {
+        if (elem_size(dtype) != 1) return TG_ERR_DTYPE;
+        // whole dwords per 128-k stage: 4*ceil(K/128) bytes per row, 4-byte aligned
+        const int64_t need = 4 * cdiv(K, 128);
+        if ((scale_a && (lds_a < need || (lds_a & 3))) || (scale_b && (lds_b < need || (lds_b & 3))))
+            return TG_ERR_LD;
+        if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & 3u) return TG_ERR_ALIGN;
+        if (M > 0 && N > 0 && K > 0) {
+            const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
+            const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(elem_size(out_dtype));
+            if (scale_a) {
+                const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale_a), s1 = s0 + uintptr_t((M - 1) * lds_a + need);
+                if (overlaps(d0, d1, s0, s1)) return TG_ERR_ALIAS;
+            }
+            if (scale_b) {
+                const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale_b), s1 = s0 + uintptr_t((N - 1) * lds_b + need);
+                if (overlaps(d0, d1, s0, s1)) return TG_ERR_ALIAS;
+            }
+        }
+        sc.a = static_cast<const unsigned char*>(scale_a);
+        sc.b = static_cast<const unsigned char*>(scale_b);
+        sc.lds_a = lds_a;
+        sc.lds_b = lds_b;
+    }
+    return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                          kernel_id, sc);
 }
 
 int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype) {

@@ -60,9 +60,10 @@ __device__ __forceinline__ u32x4 load_chunk(const char* p) {
     if constexpr (LOADCLASS >= 4) {
         return *reinterpret_cast<const u32x4_a4*>(p);
     } else {
-        // 2-byte aligned rows: load the dword-aligned 16 bytes at or below p
-        // plus, when p sits mid-dword, the next dword, then shift by 2 bytes.
-        const uintptr_t sub = reinterpret_cast<uintptr_t>(p) & 2u;
+        // 2-byte (or, for 8-bit elements, 1-byte) aligned rows: load the
+        // dword-aligned 16 bytes at or below p plus, when p sits mid-dword, the
+        // next dword (which starts inside the chunk), then shift by the offset.
+        const uintptr_t sub = reinterpret_cast<uintptr_t>(p) & (LOADCLASS == 1 ? 3u : 2u);
         const unsigned* q = reinterpret_cast<const unsigned*>(p - sub);
         u32x4 lo = *reinterpret_cast<const u32x4_a4*>(q);
         unsigned hi = 0;
@@ -82,7 +83,19 @@ __device__ __forceinline__ u32x4 load_chunk(const char* p) {
 template <int ES>
 __device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int K) {
     unsigned w[4];
-    if constexpr (ES == 2) {
+    if constexpr (ES == 1) {
+        const unsigned char* r = reinterpret_cast<const unsigned char*>(row);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            unsigned v = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = k0 + 4 * d + e;
+                if (k < K) v |= static_cast<unsigned>(r[k]) << (8 * e);
+            }
+            w[d] = v;
+        }
+    } else if constexpr (ES == 2) {
         const unsigned short* r = reinterpret_cast<const unsigned short*>(row);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -130,6 +143,25 @@ __device__ __forceinline__ f32x16 mfma_slab(u32x4 nfrag, u32x4 mfrag, f32x16 acc
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(nv.w, mv.w, acc, 0, 0, 0);
         return acc;
     }
+}
+
+// 8-bit operands: one 32x32x64 MFMA per pair of 16-byte chunks.  Lane l
+// supplies row l & 31; bytes 0-15 of half-wave h = l >> 5 are k [16h, 16h+16)
+// of the 64 and bytes 16-31 are k [32 + 16h, 48 + 16h), for both operands
+// alike.  Half-wave h also supplies the block-scale exponent of k-block h of
+// its row (low byte of sn for the n side, sm for the m side); 127 means a
+// scale of 1.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_f8(const u32x4 (&n)[2], const u32x4 (&m)[2], f32x16 acc, int sn, int sm) {
+    constexpr int FMT = (DT == TG_E4M3) ? 0 : 1;  // operand format codes: 0 e4m3, 1 e5m2
+    const i32x8 a = {static_cast<int>(n[0].x), static_cast<int>(n[0].y), static_cast<int>(n[0].z),
+                     static_cast<int>(n[0].w), static_cast<int>(n[1].x), static_cast<int>(n[1].y),
+                     static_cast<int>(n[1].z), static_cast<int>(n[1].w)};
+    const i32x8 b = {static_cast<int>(m[0].x), static_cast<int>(m[0].y), static_cast<int>(m[0].z),
+                     static_cast<int>(m[0].w), static_cast<int>(m[1].x), static_cast<int>(m[1].y),
+                     static_cast<int>(m[1].z), static_cast<int>(m[1].w)};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, FMT, FMT, 0, sn, 0, sm);
 }
 
 // ---------------------------------------------------------------- output
@@ -273,7 +305,8 @@ __device__ __forceinline__ void softmax_epilogue(f32x16 (&acc)[FN][FM], const Ge
 template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES, int SM>
 __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     select_batch(p);
-    constexpr int ES = (DT == TG_F32) ? 4 : 2;  // element bytes
+    constexpr bool F8 = (DT == TG_E4M3 || DT == TG_E5M2);
+    constexpr int ES = (DT == TG_F32) ? 4 : F8 ? 1 : 2;  // element bytes
     constexpr int EPC = 16 / ES;                    // elements per 16-byte chunk
     constexpr int BKE = kRowBytes / ES;             // K elements per stage
     constexpr int WTM = BM / 2, WTN = BN / 2;       // 2 x 2 waves
@@ -316,6 +349,59 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
         nread[q] = (BM + wave_n * WTN) * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
     }
 
+    // 8-bit operands: pair p of a stage covers k [64p, 64p + 64); half-wave h
+    // supplies chunks 4p + h (bytes 0-15) and 4p + 2 + h (bytes 16-31) of its
+    // row, which the MFMA takes as k [16h, 16h + 16) and [32 + 16h, 48 + 16h)
+    // of the 64: so k-block 2p (the first 32) sits in bytes 0-15 of both
+    // halves and takes its scale from half 0, block 2p + 1 from half 1
+    // (measured with one-hot operands and distinct scales per block)
+    int mread8[2][2], nread8[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int ch = 4 * q + 2 * e + (lane >> 5);
+            mread8[q][e] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), ch);
+            nread8[q][e] = (BM + wave_n * WTN) * kRowBytes + lds_chunk_offset(frag_row(lane), ch);
+        }
+    // block scales of the lane's rows: one dword per row and stage (the four
+    // 32-k blocks of the stage's 128 k), for the stage being consumed (cur)
+    // and the one being loaded (nxt)
+    unsigned scm_cur[FM], scn_cur[FN], scm_nxt[FM], scn_nxt[FN];
+    const int nblk = (K + 31) / 32;
+    auto load_scales = [&](int s) {
+        if constexpr (F8) {
+            if (p.scale_a) {
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int m = min(m0 + wave_m * WTM + 32 * j + frag_row(lane), M - 1);
+                    scm_nxt[j] = *reinterpret_cast<const unsigned*>(p.scale_a + m * p.lds_a + 4 * s);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FM; ++j) scm_nxt[j] = 0x7F7F7F7Fu;
+            }
+            if (p.scale_b) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const int n = min(n0 + wave_n * WTN + 32 * i + frag_row(lane), N - 1);
+                    scn_nxt[i] = *reinterpret_cast<const unsigned*>(p.scale_b + n * p.lds_b + 4 * s);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) scn_nxt[i] = 0x7F7F7F7Fu;
+            }
+        }
+    };
+    auto next_scales = [&]() {
+        if constexpr (F8) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j) scm_cur[j] = scm_nxt[j];
+#pragma unroll
+            for (int i = 0; i < FN; ++i) scn_cur[i] = scn_nxt[i];
+        }
+    };
+
     f32x16 acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -331,6 +417,7 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
 
     u32x4 sa[RA], sb[RB];
     auto load_full = [&](int s) {
+        load_scales(s);
         const int kb = s * kRowBytes + c * 16;
 #pragma unroll
         for (int i = 0; i < RA; ++i) sa[i] = load_chunk<LOADCLASS>(arow[i] + kb);
@@ -338,6 +425,7 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
         for (int i = 0; i < RB; ++i) sb[i] = load_chunk<LOADCLASS>(brow[i] + kb);
     };
     auto load_ragged = [&](int s) {
+        load_scales(s);
         const int k0 = s * BKE + c * EPC;
 #pragma unroll
         for (int i = 0; i < RA; ++i) sa[i] = load_chunk_bounded<ES>(arow[i], k0, K);
@@ -362,7 +450,45 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
         for (int i = 0; i < FN; ++i)
             nf[i] = *reinterpret_cast<const u32x4*>(base + nread[q] + i * 32 * kRowBytes);
     };
-    auto compute = [&](int buf) {
+    // 8-bit operands, stage s in buffer buf: two MFMAs of 64 k per block;
+    // scale blocks past the last one of K (their data is zero) count as 1
+    auto compute8 = [&](int buf, int s) {
+        const char* base = smem + buf * STAGE;
+        u32x4 mf[2][FM][2], nf[2][FN][2];
+        auto read_pair = [&](int q, u32x4 (&m8)[FM][2], u32x4 (&n8)[FN][2]) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    m8[j][e] = *reinterpret_cast<const u32x4*>(base + mread8[q][e] + j * 32 * kRowBytes);
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+                    n8[i][e] = *reinterpret_cast<const u32x4*>(base + nread8[q][e] + i * 32 * kRowBytes);
+            }
+        };
+        read_pair(0, mf[0], nf[0]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (q == 0) read_pair(1, mf[1], nf[1]);
+            const int sub = 2 * q + (lane >> 5);      // block within the stage
+            const bool live = 4 * s + sub < nblk;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int sn = live ? static_cast<int>(scn_cur[i] >> (8 * sub)) : 127;
+                    const int sm = live ? static_cast<int>(scm_cur[j] >> (8 * sub)) : 127;
+                    acc[i][j] = mfma_f8<DT>(nf[q][i], mf[q][j], acc[i][j], sn & 0xFF, sm & 0xFF);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto compute = [&](int buf, int s) {
+        if constexpr (F8) {
+            compute8(buf, s);
+            return;
+        }
         const char* base = smem + buf * STAGE;
         u32x4 mf[2][FM], nf[2][FN];
         read_frags(base, 0, mf[0], nf[0]);
@@ -391,20 +517,23 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
         store_stage(0);
         __syncthreads();
         for (; s + 1 < nfull; ++s) {
+            next_scales();
             load_full(s + 1);
             __builtin_amdgcn_sched_barrier(0);  // keep the global loads ahead of the MFMAs
-            compute(s & 1);
+            compute(s & 1, s);
             store_stage((s + 1) & 1);
             __syncthreads();
         }
         if (s + 1 < nk) {  // the ragged stage is still to come
+            next_scales();
             load_ragged(s + 1);
-            compute(s & 1);
+            compute(s & 1, s);
             store_stage((s + 1) & 1);
             __syncthreads();
             ++s;
         }
-        compute(s & 1);
+        next_scales();
+        compute(s & 1, s);
     }
 
     // ---- epilogue: alpha, optional ReLU, store by ownership.
@@ -1497,7 +1626,7 @@ __global__ __launch_bounds__(256) void stage_rows_kernel(const char* __restrict_
         for (int64_t c = lane; c < cpr; c += 64) {
             u32x4 v;
             if (c < full) {
-                v = load_chunk<(ES == 2 ? 2 : 4)>(src + c * 16);
+                v = load_chunk<(ES == 1 ? 1 : ES == 2 ? 2 : 4)>(src + c * 16);
             } else if (c * EPC < K) {
                 v = load_chunk_bounded<ES>(src, static_cast<int>(c * EPC), K);
             } else {
@@ -1555,7 +1684,10 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     const int64_t blocks = (rows + 3) / 4;
     const dim3 grid(static_cast<unsigned>(blocks < 65536 ? blocks : 65536));
     const int64_t cpr = row_bytes / 16;
-    if (es == 2)
+    if (es == 1)
+        hipLaunchKernelGGL(tg::stage_rows_kernel<1>, grid, dim3(256), 0, stream, A, lda_b, M, B, ldb_b, rows, K, cpr,
+                           dstA, dstB);
+    else if (es == 2)
         hipLaunchKernelGGL(tg::stage_rows_kernel<2>, grid, dim3(256), 0, stream, A, lda_b, M, B, ldb_b, rows, K, cpr,
                            dstA, dstB);
     else
@@ -1598,7 +1730,17 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     X(37, TG_BF16, 256, 256, 4, 1, 4, 1, 69)    \
     X(38, TG_BF16, 256, 256, 2, 1, 4, 1, 55)    \
     X(39, TG_F16, 256, 256, 4, 1, 4, 1, 69)     \
-    X(40, TG_F16, 256, 256, 2, 1, 4, 1, 55)
+    X(40, TG_F16, 256, 256, 2, 1, 4, 1, 55)     \
+    X(50, TG_E4M3, 256, 256, 4, 1, 4, 0, 70)    \
+    X(51, TG_E4M3, 256, 256, 1, 1, 4, 0, 56)    \
+    X(52, TG_E4M3, 128, 128, 4, 2, 4, 0, 45)    \
+    X(53, TG_E4M3, 64, 64, 4, 2, 4, 0, 25)      \
+    X(54, TG_E4M3, 64, 64, 1, 2, 4, 0, 20)      \
+    X(55, TG_E5M2, 256, 256, 4, 1, 4, 0, 70)    \
+    X(56, TG_E5M2, 256, 256, 1, 1, 4, 0, 56)    \
+    X(57, TG_E5M2, 128, 128, 4, 2, 4, 0, 45)    \
+    X(58, TG_E5M2, 64, 64, 4, 2, 4, 0, 25)      \
+    X(59, TG_E5M2, 64, 64, 1, 2, 4, 0, 20)
 #define TG_STREAM_LIST(X)                       \
     X(0, TG_BF16, 256, 256, 2, 4, 4, 4, 100)    \
     X(1, TG_F16, 256, 256, 2, 4, 4, 4, 100)     \
@@ -1653,7 +1795,7 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 
 // The table holds host launch functions, so it exists only in the host pass.
 #ifndef __HIP_DEVICE_COMPILE__
-#define TG_ES(DT) ((DT) == TG_F32 ? 4 : 2)
+#define TG_ES(DT) ((DT) == TG_F32 ? 4 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 1 : 2)
 #define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF)                                            \
     {id, DT, BM, BN, 128 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,    \
      ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW, SM>, 0, SM},

@@ -23,6 +23,12 @@ struct GemmArgs {
     int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
     int split_k;     // split-K partial products: K elements per split (grid y = split), 0 = off
     int epi;         // epilogue: 0 = alpha then optional ReLU per element, 1 = softmax over n
+    // 8-bit operands: block-scale exponents (2^(e-127) per 32 consecutive k),
+    // byte m*lds_a + k/32 for A row m and n*lds_b + k/32 for B column n;
+    // nullptr = no scales
+    const unsigned char* scale_a;
+    const unsigned char* scale_b;
+    int64_t lds_a, lds_b;
 };
 
 enum { TG_EPI_POINTWISE = 0, TG_EPI_SOFTMAX = 1 };

@@ -9,7 +9,7 @@
  *     D = alpha * A * B,  optionally followed by D = max(D, 0)  (ReLU)
  *
  * with FP32 accumulation.  All coordinates are zero-based; s is the operand
- * element size (2 for bf16/fp16, 4 for fp32):
+ * element size (1 for the 8-bit formats, 2 for bf16/fp16, 4 for fp32):
  *
  *   A is logically (M,K), stored K-contiguous:  a[m,k] at byte A + (m*lda + k)*s
  *   B is logically (K,N), stored K-contiguous:  b[k,n] at byte B + (k + n*ldb)*s
@@ -64,7 +64,9 @@ extern "C" {
 enum tile_gemm_dtype {
     TG_BF16 = 1, /* bfloat16 operands, bf16 MFMA */
     TG_F16 = 2,  /* IEEE binary16 operands, fp16 MFMA */
-    TG_F32 = 3   /* IEEE binary32 operands, fp32 MFMA (full fp32 products) */
+    TG_F32 = 3,  /* IEEE binary32 operands, fp32 MFMA (full fp32 products) */
+    TG_E4M3 = 4, /* 8-bit float operands (1-4-3, bias 7, no infinity), 8-bit MFMA */
+    TG_E5M2 = 5  /* 8-bit float operands (1-5-2, bias 15, IEEE-style), 8-bit MFMA */
 };
 
 enum tile_gemm_status {
@@ -230,6 +232,32 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
  * -1; tile_gemm, tile_gemm_ex and tile_gemm_out with kernel_id -1 behave as
  * mode -1 with the library's own staging buffer.
  */
+/*
+ * 8-bit operands (TG_E4M3, TG_E5M2) with optional block scales: every 32
+ * consecutive k of an A row (and of a B column) share one unsigned 8-bit
+ * exponent e, and the elements of that block stand for their decoded value
+ * times 2^(e - 127) (e = 255: NaN).  The pages name block-scaled 8-bit
+ * matmuls (cuTile.jl tutorial "Matrix Multiplication", "Where to go from
+ * here") without defining them; this is the plain reading of the MX
+ * formats, and the product then is
+ *
+ *     d[m,n] = epilogue(alpha * sum_k a[m,k]*sa[m,k/32] * b[k,n]*sb[n,k/32])
+ *
+ * accumulated in fp32 on the 8-bit MFMA (which applies the scales itself).
+ * Scale of A row m, block j: byte scale_a[m*lds_a + j]; of B column n:
+ * scale_b[n*lds_b + j].  lds_a, lds_b >= 4*ceil(K/128) and multiples of 4,
+ * scale pointers 4-byte aligned (TG_ERR_LD / TG_ERR_ALIGN): the kernel reads
+ * the four scales of each 128-k stage as one dword; scales of blocks past
+ * ceil(K/32) are read but ignored.  Either pointer may be NULL (no scale on
+ * that side); scales with 16-bit or fp32 operands give TG_ERR_DTYPE; the
+ * scales must not overlap D (TG_ERR_ALIAS).  kernel_id as tile_gemm_ex.
+ * Other rules as tile_gemm_out (this call never stages its operands).
+ */
+int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                     const void* A, int64_t lda, const void* scale_a, int64_t lds_a,
+                     const void* B, int64_t ldb, const void* scale_b, int64_t lds_b,
+                     void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id);
+
 int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      const void* A, int64_t lda, const void* B, int64_t ldb,
                      void* D, int64_t ldd, int dtype, int out_dtype,

@@ -27,7 +27,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
+                "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 D_SENTINEL = -7777.0  # value planted in D storage that the product must never write
 
 
@@ -85,6 +86,11 @@ WORKLOADS = {
     "softmax_65536x256x4096_bf16": _w("softmax_65536x256x4096_bf16", 65536, 256, 4096, "bf16",
                                       "normal_invsqrtk", 1.0, False, 8000,
                                       notes="measured with tile_gemm_softmax"),
+    # 8-bit operands (the block-scaled 8-bit matmul the cuTile tutorial's
+    # closing section points to, here without scales): uniform values in
+    # [-1, 1) rounded to e4m3, alpha 2^-13 keeps D near unit scale
+    "square_8192_e4m3_relu": _w("square_8192_e4m3_relu", 8192, 8192, 8192, "e4m3", "uniform_pm1",
+                                2.0 ** -13, True, 9000),
     # batched products (the batched GEMM of the cuTile tutorial's closing
     # section): 16 independent 1024^3 products, matrices stored back to back
     "batched_16x1024_bf16": _w("batched_16x1024_bf16", 1024, 1024, 1024, "bf16", "uniform_pm1",
@@ -151,8 +157,11 @@ def out_storage(M, N, ldd=None, sentinel=D_SENTINEL) -> torch.Tensor:
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw storage of a CPU tensor as numpy: uint16 for bf16/fp16, float32 for fp32."""
+    """Raw storage of a CPU tensor as numpy: uint16 for bf16/fp16, float32 for
+    fp32, uint8 for the 8-bit formats."""
     t = t.contiguous()
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        return t.view(torch.uint8).numpy()
     if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:

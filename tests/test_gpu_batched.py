@@ -14,6 +14,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +35,8 @@ def run_batched(A_all, B_all, M, N, K, lda, ldb, ldd, sa, sb, sd, batch, alpha, 
     A, B = A_all.to(dev), B_all.to(dev)
     rows_d = (batch - 1) * sd // ldd + N + 1
     D = si.out_storage(M, rows_d, ldd).to({"f32": torch.float32, "bf16": torch.bfloat16}[out]).to(dev)
-    dt = {torch.bfloat16: tg.BF16, torch.float16: tg.F16, torch.float32: tg.F32}[A_all.dtype]
+    dt = {torch.bfloat16: tg.BF16, torch.float16: tg.F16, torch.float32: tg.F32, torch.float8_e4m3fn: tg.E4M3,
+          torch.float8_e5m2: tg.E5M2}[A_all.dtype]
     ot = {"f32": tg.F32, "bf16": tg.BF16}[out]
     rc = tg.tile_gemm_batched(M, N, K, alpha, relu, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
                               D.data_ptr(), ldd, sd, batch, dt, ot, torch.cuda.current_stream().cuda_stream,
@@ -98,10 +100,10 @@ def test_every_instance_batched(kid):
     """Three products with gaps between them, every instance forced: exact on
     integer data with alpha < 0 and ReLU."""
     info = tg.kernel_info(kid)
-    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
-    es = 4 if dt == "f32" else 2
+    dt = dtype_name(info)
+    es = ELEM_SIZE[dt]
     M, N, K = info.block_m + 21, info.block_n + 45, 2 * info.block_k + 5
-    lda, ldb = _strides(info.load_class, M, N, K, es)
+    lda, ldb = strides_for_class(info.load_class, K, es)
     batch, ldd = 3, M + 3
     parts_a, parts_b = [], []
     for b in range(batch):

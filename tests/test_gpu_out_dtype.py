@@ -16,6 +16,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
 
 pytestmark = pytest.mark.gpu
 
@@ -84,18 +85,11 @@ def test_every_instance_low_precision_output(kid, out):
     enough sums that the output format has to round), within the bound on
     random data."""
     info = tg.kernel_info(kid)
-    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
-    es = 4 if dt == "f32" else 2
+    dt = dtype_name(info)
+    es = ELEM_SIZE[dt]
     M, N = info.block_m + 37, 2 * info.block_n + 11
     K = 3 * info.block_k + 9
-    if info.load_class == 2:
-        lda, ldb = K + 2, K + 4
-    elif info.load_class == 4:
-        lda = K + (2 - K) % 8 if es == 2 else K + (1 - K) % 4
-        ldb = lda + 8 if es == 2 else lda + 4
-    else:
-        lda = K + (-K) % (16 // es)
-        ldb = lda + 16 // es
+    lda, ldb = strides_for_class(info.load_class, K, es)
     _log(f"[out {out}] instance {kid} ({dt}, {info.block_m}x{info.block_n}): {M}x{N}x{K}")
     A_st, B_st = si.int_operands(M, N, K, dt, seed=300 + kid, lda=lda, ldb=ldb)
     D_st = run_out(A_st, B_st, M, N, K, -1.5, True, out, M + 3, kernel_id=kid)

@@ -16,6 +16,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
 
 pytestmark = pytest.mark.gpu
 
@@ -121,21 +122,14 @@ def test_every_kernel_instance(kid):
     """Each compiled instance, forced, on a problem spanning several tiles with
     ragged M, N and K, at the narrowest row alignment it accepts."""
     info = tg.kernel_info(kid)
-    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
+    dt = dtype_name(info)
     M, N = 2 * info.block_m + 37, 2 * info.block_n + 11
     K = 3 * info.block_k + 9
-    es = 4 if dt == "f32" else 2
-    # narrowest accepted row alignment: odd element strides for class 2,
-    # strides with lda*es = 4 (mod 16) for class 4
-    if info.load_class == 2:
-        lda, ldb = K + 2, K + 4  # K is odd here
-    elif info.load_class == 4:
-        lda = K + (2 - K) % 8 if es == 2 else K + (1 - K) % 4
-        ldb = lda + 8 if es == 2 else lda + 4
-    else:
-        lda = K + (-K) % (16 // es)
-        ldb = lda + 16 // es
-    want = {2: (2, 6, 10, 14), 4: (4, 12), 16: (0,)}[info.load_class]
+    es = ELEM_SIZE[dt]
+    # narrowest accepted row alignment: lda*es odd for class 1, 2 (mod 4)
+    # for class 2, 4 (mod 16) for class 4
+    lda, ldb = strides_for_class(info.load_class, K, es)
+    want = {1: tuple(range(1, 16, 2)), 2: (2, 6, 10, 14), 4: (4, 12), 16: (0,)}[info.load_class]
     assert (lda * es) % 16 in want
     _log(f"[instance {kid}] {dt} {info.block_m}x{info.block_n} class {info.load_class}: {M}x{N}x{K} lda={lda} ldb={ldb}")
     A_st, B_st = si.int_operands(M, N, K, dt, seed=kid, lda=lda, ldb=ldb)
@@ -158,7 +152,7 @@ def test_stream_instance_k_sweep(kid):
     """The streaming instances across K: fewer full stages than pipeline
     depth, exact multiples of the stage, and ragged tails."""
     info = tg.kernel_info(kid)
-    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
+    dt = dtype_name(info)
     bk = info.block_k
     M, N = info.block_m + 45, 2 * info.block_n - 3
     Ks = sorted({1, bk // 2, bk - 1, bk, bk + 1, 2 * bk, 2 * bk + 7, 3 * bk, 3 * bk + 1,

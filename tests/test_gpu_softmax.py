@@ -15,6 +15,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
 
 pytestmark = pytest.mark.gpu
 
@@ -92,11 +93,9 @@ def _softmax_instances():
     ids = []
     for k in range(tg.kernel_count()):
         info = tg.kernel_info(k)
-        dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
+        dt = dtype_name(info)
         M, N, K = 2 * info.block_m + 7, info.block_n - 3, 2 * info.block_k + 5
-        es = 4 if dt == "f32" else 2
-        lda = K + (-K) % (16 // es) if info.load_class == 16 else (K + 2 if info.load_class == 2 else
-                                                                    K + (2 - K) % 8 if es == 2 else K + (1 - K) % 4)
+        lda, _ = strides_for_class(info.load_class, K, ELEM_SIZE[dt])
         try:
             tg.query_plan(M, N, K, info.dtype, 0x7F0000000000, lda, 0x7F4000000000, lda, 0x7F8000000000, M, k)
         except tg.TileGemmError:
@@ -110,7 +109,7 @@ def test_every_softmax_instance(kid):
     """Every instance, forced into the softmax epilogue when it accepts the
     call (instances without one answer TG_ERR_PLAN)."""
     info = tg.kernel_info(kid)
-    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
+    dt = dtype_name(info)
     M, N, K = 2 * info.block_m + 7, info.block_n - 3, 2 * info.block_k + 5
     A_st, B_st = si.operands(M, N, K, dt, "normal_invsqrtk", 120 + kid, 130 + kid)
     try:

@@ -15,6 +15,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
 
 pytestmark = pytest.mark.gpu
 
@@ -64,17 +65,10 @@ def check(D_st, A_st, B_st, M, N, K, alpha, relu, dt, exact, out="f32"):
 def test_every_instance_splitk(kid):
     """Every instance as the partial-product kernel, 3 splits of a ragged K, exact."""
     info = tg.kernel_info(kid)
-    dt = {tg.BF16: "bf16", tg.F16: "f16", tg.F32: "f32"}[info.dtype]
-    es = 4 if dt == "f32" else 2
+    dt = dtype_name(info)
+    es = ELEM_SIZE[dt]
     M, N, K = info.block_m + 19, info.block_n + 3, 5 * info.block_k + 7
-    if info.load_class == 2:
-        lda, ldb = K + 2, K + 4
-    elif info.load_class == 4:
-        lda = K + (2 - K) % 8 if es == 2 else K + (1 - K) % 4
-        ldb = lda + 8 if es == 2 else lda + 4
-    else:
-        lda = K + (-K) % (16 // es)
-        ldb = lda + 16 // es
+    lda, ldb = strides_for_class(info.load_class, K, es)
     _log(f"[split-K] instance {kid} ({dt}): {M}x{N}x{K}, 3 splits")
     A_st, B_st = si.int_operands(M, N, K, dt, seed=900 + kid, lda=lda, ldb=ldb)
     D_st = run_splitk(A_st, B_st, M, N, K, -1.5, True, 3, ldd=M + 2, kernel_id=kid)

@@ -164,7 +164,7 @@ def test_every_instance_has_consistent_ownership_arithmetic():
         assert info.threads == 64 * info.waves_m * info.waves_n
         assert info.wave_tile_m * info.waves_m == info.block_m
         assert info.wave_tile_n * info.waves_n == info.block_n
-        es = 4 if info.dtype == tg.F32 else 2
+        es = {tg.F32: 4, tg.E4M3: 1, tg.E5M2: 1}.get(info.dtype, 2)
         row_bytes = info.block_k * es
         assert row_bytes in (64, 128)
         # every instance keeps at least its A stages in LDS, within the 160 KiB of a CU
@@ -347,3 +347,26 @@ def test_fp32_plan_choices():
     assert q(4096, 4096, 4096, ldd=4097) == 17
     assert q(2048, 2048, 2048) == 49
     assert q(1024, 1024, 4096) == 32
+
+
+def test_scaled_entry_point_validation():
+    """tile_gemm_scaled: scales only with 8-bit operands, whole dwords of
+    scales per 128-k stage, 4-byte aligned, not overlapping D."""
+    M, N, K = 300, 200, 300
+    S = 0x7F4000000000  # far from A, B and D
+    need = 4 * -(-K // 128)
+    call = lambda dt, sa, la, sb, lb, d=D: tg.tile_gemm_scaled(M, N, K, 1.0, 0, A, K, sa, la, B, K, sb, lb, d, M, dt,
+                                                               tg.F32, None, -1)
+    assert call(tg.BF16, S, need, 0, 0) == -5
+    assert call(tg.E4M3, S, need - 4, 0, 0) == -2
+    assert call(tg.E4M3, 0, 0, S, need + 2, ) == -2
+    assert call(tg.E4M3, S + 2, need, 0, 0) == -4
+    assert call(tg.E4M3, S, need, 0, 0, d=S + 64) == -6
+    import torch
+    if not torch.cuda.is_available():
+        assert call(tg.E4M3, S, need, S + (1 << 20), need) == -8
+        assert call(tg.E5M2, 0, 0, 0, 0) == -8
+    # 8-bit plans: rows aligned to a single byte take the 1-byte class
+    p = tg.query_plan(M, N, K, tg.E4M3, A + 1, K, B, K, D, M)
+    assert p.load_class == 1 and tg.kernel_info(p.kernel_id).dtype == tg.E4M3
+    assert tg.query_plan(8192, 8192, 8192, tg.E4M3, A, 8192, B, 8192, D, 8192).block_k == 128
