@@ -678,6 +678,22 @@ int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
         sc.b = static_cast<const unsigned char*>(scale_b);
         sc.lds_a = lds_a;
         sc.lds_b = lds_b;
+        // only instances that apply block scales may run the call
+        const int es = elem_size(dtype);
+        const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
+        const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+        if (kernel_id >= 0) {
+            if (kernel_id >= tg_kernel_table_size || !tg_kernel_table[kernel_id].block_scales) return TG_ERR_PLAN;
+        } else {
+            double best = 0;
+            for (int i = 0; i < tg_kernel_table_size; ++i) {
+                const TgKernelDesc& k = tg_kernel_table[i];
+                if (!k.block_scales || !usable(k, dtype, cls, row_stride)) continue;
+                const double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+                if (kernel_id < 0 || c < best) { kernel_id = i; best = c; }
+            }
+            if (kernel_id < 0) return TG_ERR_PLAN;
+        }
     }
     return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
                           kernel_id, sc);

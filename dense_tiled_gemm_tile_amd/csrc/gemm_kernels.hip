@@ -908,7 +908,8 @@ template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     select_batch(p);
     constexpr int BM = 256, BN = 256, WM = 2;
-    constexpr int ES = (DT == TG_F32) ? 4 : 2;
+    constexpr bool F8 = (DT == TG_E4M3 || DT == TG_E5M2);
+    constexpr int ES = (DT == TG_F32) ? 4 : F8 ? 1 : 2;
     constexpr int EPC = 16 / ES;
     constexpr int BKE = kRowBytes / ES;          // K elements per stage
     constexpr int WTM = 128, WTN = 128;          // output owned by one wave
@@ -1008,94 +1009,183 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nfull = K / BKE;
-    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-
-    if (nfull > 0) {
-        // prologue: half-stages 0 .. NS-2 (a stage index past the last full
-        // stage reloads that stage, so the copy counts stay uniform)
-        constexpr int PRO = (SCHED == 0) ? (NS - 1) * NC : 3 * NC + NC / 2;  // prologue copies
+    if constexpr (F8) {
+        // 8-bit operands: a stage (128 k) is two 32x32x64 MFMAs per block.
+        // The fragments of slabs 2p and 2p + 1 (chunks 4p + h and 4p + 2 + h
+        // of half-wave h) together feed MFMA pair p; pair 0 runs while slabs
+        // 2 and 3 are read and the copies of slabs 0-2 of the 16-bit schedule
+        // go out (12), pair 1 after the barrier while slabs 0 and 1 of the
+        // next stage are read and the last 4 copies go out, so the copy
+        // order and the wait counts are those of the 16-bit schedule.
+        static_assert(SCHED == 1 && NS == 5, "the 8-bit schedule follows the spread copy schedule");
+        u32x4 g[4][FM], h[4][FN];
+        auto pair = [&](int pp, auto&& side) {
 #pragma unroll
-        for (int c = 0; c < PRO; ++c) {
-            const int h = c / NC;
-            copy(h & 1, c % NC, min(h >> 1, nfull - 1), h);
-        }
-        wait_vm<PRO - 2 * NC>();
-        barrier();
+            for (int m = 0; m < MF; ++m) {
+                const int i = m / FM, j = m % FM;
+                const u32x4 nn[2] = {h[2 * pp][i], h[2 * pp + 1][i]};
+                const u32x4 mm[2] = {g[2 * pp][j], g[2 * pp + 1][j]};
+                acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], 127, 127);
+                side(m);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (nfull > 0) {
+            constexpr int PRO = 3 * NC + NC / 2;  // prologue copies, as in the 16-bit schedule
 #pragma unroll
-        for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
-
-        constexpr int H0 = NS - 1;                 // half-stage copied in slab 0, minus 2s
-        int slot0 = 0;                             // slot of stage s's A half, (2s) % NS
-        for (int s = 0; s < nfull; ++s) {
-            const int sa = slot0, sb = wrap(slot0 + 1);
-            const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
-            const int t0 = min(s + (H0 >> 1), nfull - 1);       // stage of half-stage 2s + H0
-            const int t3 = min(s + ((H0 + 1) >> 1), nfull - 1); // stage of half-stage 2s + H0 + 1
-            const int slot_h0 = wrap(slot0 + NS - 1);
-            // SCHED 1 (5 slots): one copy every 4 MFMAs through the whole stage --
-            // the second half of B(s+1) in slab 0, A(s+2) in slabs 1-2 and the
-            // first half of B(s+2) in slab 3 -- instead of bursts in slabs 0 and 3
-            const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
-            slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
-                reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
-                if constexpr (SCHED == 0) {
-                    if (m & 1) copy(H0 & 1, m >> 1, t0, slot_h0);
-                } else {
-                    if ((m & 3) == 1) copy(1, NC / 2 + (m >> 2), t1, nb);
-                }
-            });
-            slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
-                reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); });
-                if constexpr (SCHED == 1) {
-                    if ((m & 3) == 1) copy(0, m >> 2, t2, slot_h0);
-                }
-            });
-            slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
-                reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); });
-                if constexpr (SCHED == 1) {
-                    if ((m & 3) == 1) copy(0, NC / 2 + (m >> 2), t2, slot_h0);
-                }
-            });
-            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-            wait_vm<(NS - 4) * NC>();
+            for (int c = 0; c < PRO; ++c) {
+                const int hs = c / NC;
+                copy(hs & 1, c % NC, min(hs >> 1, nfull - 1), hs);
+            }
+            wait_vm<PRO - 2 * NC>();
             barrier();
-            // on the last stage the reads below fetch values that go unused
-            slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
-                reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
-                if constexpr (SCHED == 0) {
-                    if (m & 1) copy((H0 + 1) & 1, m >> 1, t3, sa);
-                } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                read(r, 0, 0, 1, g[0], h[0]);
+                read(r, 1, 0, 1, g[1], h[1]);
+            }
+            int slot0 = 0;
+            for (int s = 0; s < nfull; ++s) {
+                const int sa = slot0, sb = wrap(slot0 + 1);
+                const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
+                const int slot_h0 = wrap(slot0 + NS - 1);
+                const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
+                pair(0, [&](int m) {
+                    if (m < NR) read(m, 2, sa, sb, g[2], h[2]); else read(m - NR, 3, sa, sb, g[3], h[3]);
+                    if ((m & 3) != 3) {
+                        const int c = m - (m >> 2);  // 0 .. 11
+                        if (c < 4) copy(1, NC / 2 + c, t1, nb);
+                        else if (c < 8) copy(0, c - 4, t2, slot_h0);
+                        else copy(0, NC / 2 + c - 8, t2, slot_h0);
+                    }
+                });
+                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+                wait_vm<(NS - 4) * NC>();
+                barrier();
+                // on the last stage the reads below fetch values that go unused
+                pair(1, [&](int m) {
+                    if (m < NR) read(m, 0, na, nb, g[0], h[0]); else read(m - NR, 1, na, nb, g[1], h[1]);
                     if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
+                });
+                slot0 = na;
+            }
+            wait_vm<0>();  // no copy outlives the loop
+        }
+        if (K % BKE != 0) {
+            // ragged last stage through registers into slots 0 (A) and 1 (B)
+            __syncthreads();
+            const int c = stage_chunk(tid);
+            const int k0 = nfull * BKE + c * EPC;
+#pragma unroll
+            for (int i = 0; i < BM / 32; ++i) {
+                const int r = stage_row(tid, i);
+                const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+                const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) =
+                    load_chunk_bounded<ES>(brow, k0, K);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    read(r, 2 * pp, 0, 1, g[2 * pp], h[2 * pp]);
+                    read(r, 2 * pp + 1, 0, 1, g[2 * pp + 1], h[2 * pp + 1]);
                 }
-            });
-            slot0 = na;
+                pair(pp, [](int) {});
+            }
         }
-        wait_vm<0>();  // no copy outlives the loop
-    }
+    } else {
+        u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
-    if (K % BKE != 0) {
-        // ragged last stage through registers into slots 0 (A) and 1 (B);
-        // k >= K become exact zeros
-        __syncthreads();
-        const int c = stage_chunk(tid);
-        const int k0 = nfull * BKE + c * EPC;
-#pragma unroll
-        for (int i = 0; i < BM / 32; ++i) {
-            const int r = stage_row(tid, i);
-            const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
-            const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
-            *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
-            *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+        if (nfull > 0) {
+            // prologue: half-stages 0 .. NS-2 (a stage index past the last full
+            // stage reloads that stage, so the copy counts stay uniform)
+            constexpr int PRO = (SCHED == 0) ? (NS - 1) * NC : 3 * NC + NC / 2;  // prologue copies
+    #pragma unroll
+            for (int c = 0; c < PRO; ++c) {
+                const int h = c / NC;
+                copy(h & 1, c % NC, min(h >> 1, nfull - 1), h);
+            }
+            wait_vm<PRO - 2 * NC>();
+            barrier();
+    #pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
+
+            constexpr int H0 = NS - 1;                 // half-stage copied in slab 0, minus 2s
+            int slot0 = 0;                             // slot of stage s's A half, (2s) % NS
+            for (int s = 0; s < nfull; ++s) {
+                const int sa = slot0, sb = wrap(slot0 + 1);
+                const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
+                const int t0 = min(s + (H0 >> 1), nfull - 1);       // stage of half-stage 2s + H0
+                const int t3 = min(s + ((H0 + 1) >> 1), nfull - 1); // stage of half-stage 2s + H0 + 1
+                const int slot_h0 = wrap(slot0 + NS - 1);
+                // SCHED 1 (5 slots): one copy every 4 MFMAs through the whole stage --
+                // the second half of B(s+1) in slab 0, A(s+2) in slabs 1-2 and the
+                // first half of B(s+2) in slab 3 -- instead of bursts in slabs 0 and 3
+                const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
+                slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
+                    if constexpr (SCHED == 0) {
+                        if (m & 1) copy(H0 & 1, m >> 1, t0, slot_h0);
+                    } else {
+                        if ((m & 3) == 1) copy(1, NC / 2 + (m >> 2), t1, nb);
+                    }
+                });
+                slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); });
+                    if constexpr (SCHED == 1) {
+                        if ((m & 3) == 1) copy(0, m >> 2, t2, slot_h0);
+                    }
+                });
+                slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); });
+                    if constexpr (SCHED == 1) {
+                        if ((m & 3) == 1) copy(0, NC / 2 + (m >> 2), t2, slot_h0);
+                    }
+                });
+                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+                wait_vm<(NS - 4) * NC>();
+                barrier();
+                // on the last stage the reads below fetch values that go unused
+                slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
+                    if constexpr (SCHED == 0) {
+                        if (m & 1) copy((H0 + 1) & 1, m >> 1, t3, sa);
+                    } else {
+                        if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
+                    }
+                });
+                slot0 = na;
+            }
+            wait_vm<0>();  // no copy outlives the loop
         }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+
+        if (K % BKE != 0) {
+            // ragged last stage through registers into slots 0 (A) and 1 (B);
+            // k >= K become exact zeros
+            __syncthreads();
+            const int c = stage_chunk(tid);
+            const int k0 = nfull * BKE + c * EPC;
+    #pragma unroll
+            for (int i = 0; i < BM / 32; ++i) {
+                const int r = stage_row(tid, i);
+                const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+                const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+            }
+            __syncthreads();
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
+    #pragma unroll
+                for (int i = 0; i < FN; ++i)
+    #pragma unroll
+                    for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+            }
         }
     }
 
@@ -1777,7 +1867,9 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     X(41, TG_BF16, 4, 5, 16, 1, 1, 49, 10)      \
     X(42, TG_F16, 4, 5, 16, 1, 1, 5, 10)        \
     X(43, TG_BF16, 4, 5, 16, 1, 1, 16, 107)     \
-    X(44, TG_F16, 4, 5, 16, 1, 1, 16, 107)
+    X(44, TG_F16, 4, 5, 16, 1, 1, 16, 107)      \
+    X(60, TG_E4M3, 4, 5, 16, 1, 1, 17, 107)     \
+    X(61, TG_E5M2, 4, 5, 16, 1, 1, 17, 107)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \
@@ -1798,7 +1890,8 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 #define TG_ES(DT) ((DT) == TG_F32 ? 4 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 1 : 2)
 #define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF)                                            \
     {id, DT, BM, BN, 128 / TG_ES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,    \
-     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW, SM>, 0, SM},
+     ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch<DT, BM, BN, LC, MW, SM>, 0, SM, 0,               \
+     ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 1 : 0},
 #define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF)                                         \
     {id, DT, BM, BN, 64 / TG_ES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,           \
      (S) * ((BM) + (BN)) * 64, ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                    \

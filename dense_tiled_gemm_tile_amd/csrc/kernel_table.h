@@ -67,6 +67,7 @@ struct TgKernelDesc {
     int64_t max_row_stride;  // largest lda/ldb in bytes the instance can address (0: any)
     int softmax;             // 1: the epilogue can also take a softmax over n (N <= block_n)
     int nt_store;            // 1: D is written with nontemporal stores
+    int block_scales;        // 1: 8-bit instance that applies block scales (GemmArgs::scale_a/b)
 };
 
 // Indexed by kernel id.

@@ -68,7 +68,12 @@ def test_block_scaled_exact(dt, shape):
         A_st, B_st = si.int_operands(M, N, K, dt, seed=M + K + kid, lda=lda, ldb=ldb)
         ref, _ = oracle.gemm(M, N, K, -0.75, True, si.bits(A_st), lda, si.bits(B_st), ldb, dt,
                              scale_a=sa, lds_a=lda_s, scale_b=sb, lds_b=ldb_s)
-        D_st = run(A_st, B_st, M, N, K, -0.75, True, sa, sb, ldd=M + 2, kernel_id=kid)
+        try:
+            D_st = run(A_st, B_st, M, N, K, -0.75, True, sa, sb, ldd=M + 2, kernel_id=kid)
+        except tg.TileGemmError as e:
+            # the streaming instance takes no block scales and must say so
+            assert e.code == -9 and tg.kernel_info(kid).load_class == 16, (kid, e.code)
+            continue
         d = D_st[:, :M].double().numpy()
         bad = np.argwhere(d != ref)
         assert bad.size == 0, f"instance {kid}: {len(bad)} mismatches, first {tuple(bad[0])}: " \

@@ -159,7 +159,7 @@ def test_stream_instance_k_sweep(kid):
                  4 * bk, 5 * bk - 1, 9 * bk, 9 * bk + 3})
     _log(f"[stream K sweep] instance {kid}: K in {Ks}")
     for K in Ks:
-        lda = K + (-K) % 8
+        lda = K + (-K) % (16 // ELEM_SIZE[dt])  # 16-byte aligned rows
         A_st, B_st = si.int_operands(M, N, K, dt, seed=K, lda=lda, ldb=lda)
         D_st = run(A_st, B_st, M, N, K, 1.0, False, M + 5, kernel_id=kid)
         check_full(D_st, A_st, B_st, M, N, K, 1.0, False, dt, exact=True)
