@@ -20,7 +20,7 @@ import seeded_inputs as si
 
 pytestmark = pytest.mark.gpu
 
-DT = {"bf16": tg.BF16, "f16": tg.F16, "f32": tg.F32}
+DT = {"bf16": tg.BF16, "f16": tg.F16, "f32": tg.F32, "e4m3": tg.E4M3, "e5m2": tg.E5M2}
 
 
 def _log(msg):
@@ -31,7 +31,11 @@ def _device_operand(st: torch.Tensor, off: int):
     """Device copy of a row-major storage starting `off` elements into a flat
     buffer (so that off = 1 makes every row start misaligned)."""
     dev = torch.device("cuda:0")
-    flat = torch.zeros(st.numel() + off + 8, dtype=st.dtype, device=dev)
+    n = st.numel() + off + 8
+    if st.element_size() == 1:  # 8-bit formats: zero bytes, viewed as the format
+        flat = torch.zeros(n, dtype=torch.uint8, device=dev).view(st.dtype)
+    else:
+        flat = torch.zeros(n, dtype=st.dtype, device=dev)
     flat[off:off + st.numel()] = st.reshape(-1).to(dev)
     return flat, flat.data_ptr() + off * flat.element_size()
 
@@ -82,7 +86,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}" for s in SHAPES])
-@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32", "e4m3", "e5m2"])
 def test_staged_exact_on_integer_data(dt, shape):
     """mode 1 (always stage): misaligned rows, odd strides, K below, at and
     past one stage; exact against the oracle with alpha < 0 and ReLU."""
