@@ -75,6 +75,9 @@ def main() -> int:
                     help="pointwise alpha/ReLU (tile_gemm) or a row softmax over N (tile_gemm_softmax)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="element type of D (bf16/f16: fp32 epilogue rounded on the way out)")
+    ap.add_argument("--block-scales", action="store_true",
+                    help="8-bit workloads: seeded block scales (one exponent per 32 k of every A row and B "
+                         "column) through tile_gemm_scaled")
     ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns the CPU-baseline oracle computes (all rows, full K)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,11 +108,27 @@ def main() -> int:
     D = si.out_storage(w.M, w.batch * w.N, w.ldd).to(out_torch).to(dev)
     if w.batch == 1:
         Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
+        if args.block_scales and args.kernel_id < 0:
+            # the 256 x 256 register-staged 8-bit instance applies block scales
+            code = tg.DTYPE_CODES[w.dtype]
+            args.kernel_id = next(k for k in range(tg.kernel_count())
+                                  if tg.kernel_info(k).dtype == code and tg.kernel_info(k).block_m == 256
+                                  and tg.kernel_info(k).load_class == 4)
         plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
         launch = tg.gemm
         if args.epilogue == "softmax":
             def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
                 return tg.gemm_softmax(A_, B_, D_, alpha, stream=stream, kernel_id=kernel_id)
+        if args.block_scales:
+            if w.dtype not in ("e4m3", "e5m2"):
+                print("--block-scales needs an 8-bit workload", file=sys.stderr)
+                return 2
+            sc_a_np = si.block_scales(w.M, w.K, w.seed_a + 50)
+            sc_b_np = si.block_scales(w.N, w.K, w.seed_b + 50)
+            sc_a, sc_b = torch.from_numpy(sc_a_np).to(dev), torch.from_numpy(sc_b_np).to(dev)
+
+            def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
+                return tg.gemm_scaled(A_, B_, D_, sc_a, sc_b, alpha, relu, stream=stream, kernel_id=kernel_id)
         if args.splits != 1:
             ws = torch.empty(max(tg.splitk_workspace_bytes(w.M, w.N, args.splits), 16), dtype=torch.uint8,
                              device=dev)
@@ -170,6 +189,7 @@ def main() -> int:
                    "ldd": w.ldd, "alpha": w.alpha, "relu": w.relu, "dist": w.dist,
                    "out_dtype": args.out_dtype, "batch": w.batch, "splits": args.splits,
                    "epilogue": args.epilogue,  # softmax: kernel_id below is the pointwise plan
+                   "block_scales": bool(args.block_scales),
                    "kernel_id": plan.kernel_id,
                    "staged": bool(plan.staged),  # A and B copied into aligned rows first (one more launch)
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
@@ -209,8 +229,11 @@ def main() -> int:
         else:
             cols = min(args.cpu_cols, w.N)  # of the first matrix of a batch
             t0 = time.perf_counter()
+            extra = {}
+            if args.block_scales:
+                extra = dict(scale_a=sc_a_np, lds_a=sc_a_np.shape[1], scale_b=sc_b_np, lds_b=sc_b_np.shape[1])
             ref, mag = oracle.gemm(w.M, w.N, w.K, w.alpha, w.relu, si.bits(A_st), w.lda, si.bits(B_st), w.ldb,
-                                   w.dtype, n0=0, n1=cols, threads=threads)
+                                   w.dtype, n0=0, n1=cols, threads=threads, **extra)
             cpu_s = time.perf_counter() - t0
             cpu_flops = 2.0 * w.M * cols * w.K
         result["cpu_baseline"] = {

@@ -150,6 +150,18 @@ def int_operands(M, N, K, dtype, seed, lda=None, ldb=None, lo=-3, hi=3, pad=floa
     return _stored(M, K, lda, a, dtype, pad), _stored(N, K, ldb, b, dtype, pad)
 
 
+def block_scales(rows: int, K: int, seed: int, lo: int = 124, hi: int = 130, pad: int = 0) -> np.ndarray:
+    """Seeded block-scale exponents for 8-bit operands: (rows, lds) uint8 with
+    lds = 4*ceil(K/128) + pad (whole dwords per 128-k stage), exponents in
+    [lo, hi] for the ceil(K/32) live blocks and 127 elsewhere."""
+    nblk = -(-K // 32)
+    lds = 4 * -(-K // 128) + pad
+    g = np.random.default_rng(int(seed))
+    s = np.full((rows, max(lds, 4)), 127, dtype=np.uint8)
+    s[:, :nblk] = g.integers(lo, hi + 1, size=(rows, nblk), dtype=np.uint8)
+    return s
+
+
 def out_storage(M, N, ldd=None, sentinel=D_SENTINEL) -> torch.Tensor:
     """D storage: row-major (N, ldd) fp32 pre-filled with a sentinel."""
     ldd = M if ldd is None else ldd
