@@ -27,7 +27,7 @@ def strides_for_class(cls: int, K: int, es: int):
         lda = smallest(4)
         return lda, smallest(4) + 16 // es
     if cls == 2:
-        lda = smallest(2 if es <= 2 else 0) if es == 2 else smallest(6)
+        lda = smallest(2 if es == 2 else 6)  # 16-bit: 2 (mod 16); 8-bit: 6 (mod 16)
         return lda, lda + 8 // es
     lda = smallest(1 if es == 1 else 0)
     return lda, lda + 2
