@@ -893,9 +893,11 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 // nontemporal D stores (D lines then do not displace operand panels in L2,
 // measured ~2 % faster main loop when D columns start on 128-byte lines; when
 // they do not, the partial lines at the tile edges make them about 20 %
-// slower on the whole product, and the twins without the bit are used), bit 1 = fp32 D through an LDS transpose so
-// each store writes a whole 1 KiB row run (measured no faster: the D write
-// burst at the end of a tile is bound by memory bandwidth either way), bit 2 =
+// slower on the whole product, and the twins without the bit are used), bit 1 =
+// fp32 D through an LDS transpose so each store writes a whole 1 KiB row run
+// (no faster for line-aligned D, where the write burst at the end of a tile
+// is bound by memory bandwidth either way; 2.5 % faster when D columns are
+// only 4-byte aligned, so the plain-store twins 43/44 carry it), bit 2 =
 // the same for bf16/fp16 D, whose direct stores would write 64-byte halves of
 // lines; bit 3 = the instance also carries the softmax epilogue (kept out of
 // the plain instances, whose epilogue it would bloat); bit 4 = interior tiles
@@ -1210,7 +1212,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             }
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
     const bool aligned16 = (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
-    const bool trans32 = (EPI & 2) && p.out_dtype == TG_F32 && interior && aligned16 && (p.ldd & 3) == 0;
+    const bool trans32 = (EPI & 2) && p.out_dtype == TG_F32 && interior;
     const bool trans16 = (EPI & 4) && p.out_dtype != TG_F32 && interior && aligned16 && (p.ldd & 7) == 0;
     const bool quad = (EPI & 16) && (p.out_dtype != TG_F32 || (EPI & 32)) && interior && (p.ldd & 3) == 0 &&
                       (reinterpret_cast<uintptr_t>(p.D) & (p.out_dtype == TG_F32 ? 15u : 7u)) == 0;
@@ -1349,12 +1351,15 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             }
         });
     } else {
-        // interior tile with 16-byte aligned D rows: transpose through LDS so
-        // that each store instruction writes one whole 1 KiB row run of the
-        // tile (256 consecutive m), which the memory system drains faster
-        // than scattered 128-byte pieces.  Two passes of 128 rows (n); the
-        // row pitch of 1056 bytes keeps the two half-waves of each LDS write
-        // on disjoint banks.
+        // interior tile: transpose through LDS so that each store instruction
+        // writes one whole 1 KiB row run of the tile (256 consecutive m).
+        // With line-aligned D columns this is no faster than the direct
+        // stores; with columns only 4-byte aligned (odd ldd) it touches 9
+        // lines per run instead of two lines per 128-byte piece and measured
+        // 2.5 % faster on the whole product.  The 16-byte stores only assume
+        // 4-byte alignment.  Two passes of 128 rows (n); the row pitch of
+        // 1056 bytes keeps the two half-waves of each LDS write on disjoint
+        // banks.
         constexpr int PITCH = 1056;
         static_assert(EPI < 2 || 128 * PITCH <= NS * SLOT, "transpose buffer fits the ring");
         __syncthreads();  // every wave is done with the ring
@@ -1376,9 +1381,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
 #pragma unroll
             for (int q = 0; q < 32; ++q) {
                 const int nl = 32 * wave + q;
-                const f32x4 v = *reinterpret_cast<const f32x4*>(smem + nl * PITCH + lane * 16);
-                f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.D) +
-                                                      static_cast<int64_t>(n0 + 128 * pass + nl) * p.ldd + m0) + lane;
+                typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+                const f32x4_a4 v = *reinterpret_cast<const f32x4*>(smem + nl * PITCH + lane * 16);
+                f32x4_a4* dst = reinterpret_cast<f32x4_a4*>(static_cast<float*>(p.D) +
+                                                            static_cast<int64_t>(n0 + 128 * pass + nl) * p.ldd +
+                                                            m0) + lane;
                 if constexpr (EPI & 1)
                     __builtin_nontemporal_store(v, dst);
                 else
@@ -1866,8 +1873,8 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     X(36, TG_F16, 4, 5, 16, 1, 1, 13, 106)      \
     X(41, TG_BF16, 4, 5, 16, 1, 1, 49, 10)      \
     X(42, TG_F16, 4, 5, 16, 1, 1, 5, 10)        \
-    X(43, TG_BF16, 4, 5, 16, 1, 1, 16, 107)     \
-    X(44, TG_F16, 4, 5, 16, 1, 1, 16, 107)      \
+    X(43, TG_BF16, 4, 5, 16, 1, 1, 18, 107)     \
+    X(44, TG_F16, 4, 5, 16, 1, 1, 18, 107)      \
     X(60, TG_E4M3, 4, 5, 16, 1, 1, 17, 107)     \
     X(61, TG_E5M2, 4, 5, 16, 1, 1, 17, 107)
 
