@@ -108,12 +108,6 @@ def main() -> int:
     D = si.out_storage(w.M, w.batch * w.N, w.ldd).to(out_torch).to(dev)
     if w.batch == 1:
         Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
-        if args.block_scales and args.kernel_id < 0:
-            # the 256 x 256 register-staged 8-bit instance applies block scales
-            code = tg.DTYPE_CODES[w.dtype]
-            args.kernel_id = next(k for k in range(tg.kernel_count())
-                                  if tg.kernel_info(k).dtype == code and tg.kernel_info(k).block_m == 256
-                                  and tg.kernel_info(k).load_class == 4)
         plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
         launch = tg.gemm
         if args.epilogue == "softmax":
@@ -190,7 +184,8 @@ def main() -> int:
                    "out_dtype": args.out_dtype, "batch": w.batch, "splits": args.splits,
                    "epilogue": args.epilogue,  # softmax: kernel_id below is the pointwise plan
                    "block_scales": bool(args.block_scales),
-                   "kernel_id": plan.kernel_id,
+                   # with block scales tile_gemm_scaled picks among the instances that apply them
+                   "kernel_id": None if args.block_scales else plan.kernel_id,
                    "staged": bool(plan.staged),  # A and B copied into aligned rows first (one more launch)
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},

@@ -905,7 +905,10 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 // per lane as one 8-byte vector for 16-bit D (measured: the bf16-D epilogue
 // drops from about 31k to 21k cycles against the LDS transpose), bit 5 = the
 // same for fp32 D as 16-byte vectors (measured slower than direct stores:
-// fp32 D is bound by the write burst, and the shuffles add VALU work).
+// fp32 D is bound by the write burst, and the shuffles add VALU work), bit 6 =
+// 8-bit operands with block scales (their loads sit in the main loop, and the
+// waits the compiler puts before their use also wait for copies, so the
+// instances without scales do not carry them).
 template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     select_batch(p);
@@ -1018,16 +1021,60 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         // 2 and 3 are read and the copies of slabs 0-2 of the 16-bit schedule
         // go out (12), pair 1 after the barrier while slabs 0 and 1 of the
         // next stage are read and the last 4 copies go out, so the copy
-        // order and the wait counts are those of the 16-bit schedule.
+        // order and the wait counts are those of the 16-bit schedule.  Block
+        // scales (when given) come from the lane's rows, as in the
+        // register-staged kernel.
         static_assert(SCHED == 1 && NS == 5, "the 8-bit schedule follows the spread copy schedule");
+        constexpr bool SC = (EPI & 64) != 0;  // the instance applies block scales
+        const int nk = nfull + ((K % BKE) != 0 ? 1 : 0);  // stages including a ragged one
         u32x4 g[4][FM], h[4][FN];
-        auto pair = [&](int pp, auto&& side) {
+        // block scales of the lane's rows for the stage being consumed: one
+        // dword per row (the stage's four 32-k blocks), loaded at the end of
+        // the previous stage, after its copies, so that the waits the
+        // compiler puts in front of their first use only also cover copies
+        // issued a stage earlier
+        unsigned scm[FM], scn[FN];
+        const int nblk = (K + 31) / 32;
+        auto load_scales = [&](int t) {
+            if constexpr (!SC) return;
+            if (p.scale_a) {
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int m = min(m0 + wave_m * WTM + 32 * j + frag_row(lane), M - 1);
+                    scm[j] = *reinterpret_cast<const unsigned*>(p.scale_a + m * p.lds_a + 4 * t);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FM; ++j) scm[j] = 0x7F7F7F7Fu;
+            }
+            if (p.scale_b) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const int n = min(n0 + wave_n * WTN + 32 * i + frag_row(lane), N - 1);
+                    scn[i] = *reinterpret_cast<const unsigned*>(p.scale_b + n * p.lds_b + 4 * t);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) scn[i] = 0x7F7F7F7Fu;
+            }
+        };
+        // pair pp of stage t; scale blocks past the last one of K count as 1
+        auto pair = [&](int pp, int t, auto&& side) {
+            const int sub = 2 * pp + (lane >> 5);
+            const bool live = 4 * t + sub < nblk;
+            (void)live;
 #pragma unroll
             for (int m = 0; m < MF; ++m) {
                 const int i = m / FM, j = m % FM;
                 const u32x4 nn[2] = {h[2 * pp][i], h[2 * pp + 1][i]};
                 const u32x4 mm[2] = {g[2 * pp][j], g[2 * pp + 1][j]};
-                acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], 127, 127);
+                if constexpr (SC) {
+                    const int sn = live ? static_cast<int>((scn[i] >> (8 * sub)) & 0xFFu) : 127;
+                    const int sm = live ? static_cast<int>((scm[j] >> (8 * sub)) & 0xFFu) : 127;
+                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], sn, sm);
+                } else {
+                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], 127, 127);
+                }
                 side(m);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1046,13 +1093,14 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 read(r, 0, 0, 1, g[0], h[0]);
                 read(r, 1, 0, 1, g[1], h[1]);
             }
+            load_scales(0);
             int slot0 = 0;
             for (int s = 0; s < nfull; ++s) {
                 const int sa = slot0, sb = wrap(slot0 + 1);
                 const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
                 const int slot_h0 = wrap(slot0 + NS - 1);
                 const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
-                pair(0, [&](int m) {
+                pair(0, s, [&](int m) {
                     if (m < NR) read(m, 2, sa, sb, g[2], h[2]); else read(m - NR, 3, sa, sb, g[3], h[3]);
                     if ((m & 3) != 3) {
                         const int c = m - (m >> 2);  // 0 .. 11
@@ -1065,10 +1113,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 wait_vm<(NS - 4) * NC>();
                 barrier();
                 // on the last stage the reads below fetch values that go unused
-                pair(1, [&](int m) {
+                pair(1, s, [&](int m) {
                     if (m < NR) read(m, 0, na, nb, g[0], h[0]); else read(m - NR, 1, na, nb, g[1], h[1]);
                     if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
                 });
+                if (s + 1 < nk) load_scales(s + 1);
                 slot0 = na;
             }
             wait_vm<0>();  // no copy outlives the loop
@@ -1087,6 +1136,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) =
                     load_chunk_bounded<ES>(brow, k0, K);
             }
+            if (nfull == 0) load_scales(0);  // otherwise loaded at the end of the last full stage
             __syncthreads();
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
@@ -1095,7 +1145,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                     read(r, 2 * pp, 0, 1, g[2 * pp], h[2 * pp]);
                     read(r, 2 * pp + 1, 0, 1, g[2 * pp + 1], h[2 * pp + 1]);
                 }
-                pair(pp, [](int) {});
+                pair(pp, nfull, [](int) {});
             }
         }
     } else {
@@ -1876,7 +1926,9 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
     X(43, TG_BF16, 4, 5, 16, 1, 1, 18, 107)     \
     X(44, TG_F16, 4, 5, 16, 1, 1, 18, 107)      \
     X(60, TG_E4M3, 4, 5, 16, 1, 1, 17, 107)     \
-    X(61, TG_E5M2, 4, 5, 16, 1, 1, 17, 107)
+    X(61, TG_E5M2, 4, 5, 16, 1, 1, 17, 107)     \
+    X(62, TG_E4M3, 4, 5, 16, 1, 1, 81, 90)      \
+    X(63, TG_E5M2, 4, 5, 16, 1, 1, 81, 90)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \
@@ -1912,7 +1964,7 @@ TG_WIDE_LIST(TG_INSTANTIATE_WIDE)
 #define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                    \
     {id, DT, 256, 256, 128 / TG_ES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,   \
      &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, ((EPI) & 8) ? 1 : 0, \
-     (EPI) & 1},
+     (EPI) & 1, ((EPI) & 64) ? 1 : 0},
 
 static const TgKernelDesc kUnsorted[] = {TG_STREAM_LIST(TG_ENTRY_STREAM) TG_RS_LIST(TG_ENTRY_RS)
                                              TG_HYBRID_LIST(TG_ENTRY_HYBRID) TG_WIDE_LIST(TG_ENTRY_WIDE)};
