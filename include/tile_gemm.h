@@ -316,7 +316,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 6
+#define TILE_GEMM_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -140,3 +140,17 @@ def test_fp8_workload_sampled():
     ok, r = oracle.check(d, ref, mag, w.K)
     assert ok, f"worst ratio {r}"
     _log(f"[fp8 workload] {w.name}: {ms.size} sampled entries, worst ratio {r:.3g}")
+
+
+def test_softmax_over_8bit_logits():
+    """Row softmax of an 8-bit product: no 8-bit instance carries the fused
+    softmax, so the fp32 logits are written and normalised in a second pass."""
+    M, N, K = 300, 300, 256
+    A_st, B_st = si.operands(M, N, K, "e4m3", "uniform_pm1", 31, 32)
+    dev = torch.device("cuda:0")
+    D = si.out_storage(M, N, M + 1).to(dev)
+    tg.gemm_softmax(A_st.to(dev), B_st.to(dev).t(), D[:, :M].t(), 0.25)
+    torch.cuda.synchronize()
+    ref, mag = oracle.gemm(M, N, K, 0.25, False, si.bits(A_st), K, si.bits(B_st), K, "e4m3")
+    ok, r = oracle.check_softmax(D.cpu()[:, :M].double().numpy(), ref, mag, K)
+    assert ok, f"worst ratio {r}"

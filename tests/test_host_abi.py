@@ -21,7 +21,7 @@ def test_library_exports_every_declared_function():
             "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 6
+    assert tg.abi_version() == 7
 
 
 def test_strerror_covers_every_status():
@@ -370,3 +370,15 @@ def test_scaled_entry_point_validation():
     p = tg.query_plan(M, N, K, tg.E4M3, A + 1, K, B, K, D, M)
     assert p.load_class == 1 and tg.kernel_info(p.kernel_id).dtype == tg.E4M3
     assert tg.query_plan(8192, 8192, 8192, tg.E4M3, A, 8192, B, 8192, D, 8192).block_k == 128
+
+
+def test_8bit_staging_and_streaming_plans():
+    """8-bit operands: aligned rows run the streaming 8-bit instance; a large
+    product with 1-byte aligned rows is staged onto it; a small one is not."""
+    A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
+    p = tg.query_plan(4096, 4096, 4096, tg.E4M3, A2, 4096, B2, 4096, D2, 4096)
+    assert p.staged == 0 and p.kernel_id == 60 and p.block_k == 128
+    p = tg.query_plan(4096, 4096, 4096, tg.E5M2, A2 + 1, 4097, B2, 4097, D2, 4096)
+    assert p.staged == 1 and p.kernel_id == 61
+    p = tg.query_plan(300, 200, 130, tg.E4M3, A2 + 1, 131, B2, 131, D2, 300)
+    assert p.staged == 0 and p.load_class == 1
