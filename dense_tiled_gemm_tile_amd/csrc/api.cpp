@@ -685,11 +685,13 @@ int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
         if (kernel_id >= 0) {
             if (kernel_id >= tg_kernel_table_size || !tg_kernel_table[kernel_id].block_scales) return TG_ERR_PLAN;
         } else {
+            const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
             double best = 0;
             for (int i = 0; i < tg_kernel_table_size; ++i) {
                 const TgKernelDesc& k = tg_kernel_table[i];
                 if (!k.block_scales || !usable(k, dtype, cls, row_stride)) continue;
-                const double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+                double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+                if (k.nt_store && !d_lines) c *= 1.25;
                 if (kernel_id < 0 || c < best) { kernel_id = i; best = c; }
             }
             if (kernel_id < 0) return TG_ERR_PLAN;
