@@ -684,12 +684,18 @@ int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
         const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
         if (kernel_id >= 0) {
             if (kernel_id >= tg_kernel_table_size || !tg_kernel_table[kernel_id].block_scales) return TG_ERR_PLAN;
+            const TgKernelDesc& k = tg_kernel_table[kernel_id];
+            if (k.max_row_stride && ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
+                return TG_ERR_PLAN;
         } else {
             const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
             double best = 0;
             for (int i = 0; i < tg_kernel_table_size; ++i) {
                 const TgKernelDesc& k = tg_kernel_table[i];
                 if (!k.block_scales || !usable(k, dtype, cls, row_stride)) continue;
+                // instances with 32-bit row offsets also address 256 rows of scales that way
+                if (k.max_row_stride && ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
+                    continue;
                 double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
                 if (k.nt_store && !d_lines) c *= 1.25;
                 if (kernel_id < 0 || c < best) { kernel_id = i; best = c; }
