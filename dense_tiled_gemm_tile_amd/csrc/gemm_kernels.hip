@@ -1035,11 +1035,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         // issued a stage earlier
         unsigned scm[FM], scn[FN];
         const int nblk = (K + 31) / 32;
-        // scale loads through buffer resources over the tile's scale rows: one
-        // VGPR of per-lane offset per operand and the rest in SGPRs, which
-        // keeps the loop free of spills (a spill reload waits for every copy
-        // in flight).  Rows past M or N fall outside the range and read 0,
-        // i.e. a tiny scale on rows whose data loads as zeros.
+        // scale loads through buffer resources over the tile's scale rows:
+        // 32-bit per-lane offsets and the rest in SGPRs, which keeps the loop
+        // free of spills (a spill reload waits for every copy in flight).
+        // Rows past M or N fall outside the range and read 0, i.e. a tiny
+        // scale on rows whose data loads as zeros.
         // (an absent operand gets an empty range and is never loaded)
         const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
             p.scale_a ? const_cast<unsigned char*>(p.scale_a + static_cast<int64_t>(m0) * p.lds_a) : p.D,
@@ -1049,16 +1049,19 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             p.scale_b ? const_cast<unsigned char*>(p.scale_b + static_cast<int64_t>(n0) * p.lds_b) : p.D,
             static_cast<short>(0), p.scale_b ? static_cast<int>(static_cast<unsigned>(min(BN, N - n0) * p.lds_b)) : 0,
             0x00020000);
-        const unsigned vo_a = static_cast<unsigned>(frag_row(lane) * p.lds_a);
-        const unsigned vo_b = static_cast<unsigned>(frag_row(lane) * p.lds_b);
+        // the whole row offset sits in the per-lane offset, which is what the
+        // range check looks at (the scalar offset only carries the stage)
+        unsigned vo_a[FM], vo_b[FN];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) vo_a[j] = static_cast<unsigned>((wave_m * WTM + 32 * j + frag_row(lane)) * p.lds_a);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) vo_b[i] = static_cast<unsigned>((wave_n * WTN + 32 * i + frag_row(lane)) * p.lds_b);
         auto load_scales = [&](int t) {
             if constexpr (!SC) return;
             if (p.scale_a) {
 #pragma unroll
                 for (int j = 0; j < FM; ++j)
-                    scm[j] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rs_a, static_cast<int>(vo_a),
-                        static_cast<int>(static_cast<unsigned>((wave_m * WTM + 32 * j) * p.lds_a + 4 * t)), 0);
+                    scm[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_a, static_cast<int>(vo_a[j]), 4 * t, 0);
             } else {
 #pragma unroll
                 for (int j = 0; j < FM; ++j) scm[j] = 0x7F7F7F7Fu;
@@ -1066,9 +1069,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             if (p.scale_b) {
 #pragma unroll
                 for (int i = 0; i < FN; ++i)
-                    scn[i] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rs_b, static_cast<int>(vo_b),
-                        static_cast<int>(static_cast<unsigned>((wave_n * WTN + 32 * i) * p.lds_b + 4 * t)), 0);
+                    scn[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, static_cast<int>(vo_b[i]), 4 * t, 0);
             } else {
 #pragma unroll
                 for (int i = 0; i < FN; ++i) scn[i] = 0x7F7F7F7Fu;
