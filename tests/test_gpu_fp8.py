@@ -154,3 +154,20 @@ def test_softmax_over_8bit_logits():
     ref, mag = oracle.gemm(M, N, K, 0.25, False, si.bits(A_st), K, si.bits(B_st), K, "e4m3")
     ok, r = oracle.check_softmax(D.cpu()[:, :M].double().numpy(), ref, mag, K)
     assert ok, f"worst ratio {r}"
+
+
+def test_block_scaled_workload_sampled():
+    """The measured 8-bit workload with seeded block scales (as bench.py
+    --block-scales draws them), full size, sampled entries (edges included)."""
+    w = si.WORKLOADS["square_8192_e4m3_relu"]
+    A_st, B_st = si.workload_operands(w)
+    sa = si.block_scales(w.M, w.K, w.seed_a + 50)
+    sb = si.block_scales(w.N, w.K, w.seed_b + 50)
+    D_st = run(A_st, B_st, w.M, w.N, w.K, w.alpha, w.relu, sa, sb, ldd=w.ldd)
+    ms, ns = si.sample_coords(w.M, w.N, 2000, 19)
+    ref, mag = oracle.gemm_entries(w.M, w.N, w.K, w.alpha, w.relu, si.bits(A_st), w.lda, si.bits(B_st), w.ldb,
+                                   w.dtype, ms, ns, scale_a=sa, lds_a=sa.shape[1], scale_b=sb, lds_b=sb.shape[1])
+    d = D_st[torch.from_numpy(ns), torch.from_numpy(ms)].double().numpy()
+    ok, r = oracle.check(d, ref, mag, w.K)
+    assert ok, f"worst ratio {r}"
+    _log(f"[fp8 scaled workload] {w.name}: {ms.size} sampled entries, worst ratio {r:.3g}")
