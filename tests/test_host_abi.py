@@ -382,3 +382,17 @@ def test_8bit_staging_and_streaming_plans():
     assert p.staged == 1 and p.kernel_id == 61
     p = tg.query_plan(300, 200, 130, tg.E4M3, A2 + 1, 131, B2, 131, D2, 300)
     assert p.staged == 0 and p.load_class == 1
+
+
+def test_scaled_call_refuses_instances_without_scales():
+    """A forced instance that does not apply block scales (the plain 8-bit
+    streaming one) is refused before any device call, as is a scaled
+    streaming instance whose scale rows are too long for its 32-bit offsets."""
+    A2, B2, D2, S2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000
+    M = N = K = 4096
+    need = 4 * (K // 128)
+    rc = tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, K, S2, need, B2, K, 0, 0, D2, M, tg.E4M3, tg.F32, None, 60)
+    assert rc == -9
+    big = 1 << 24  # bytes per scale row, beyond 8 MiB
+    rc = tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, K, S2, big, B2, K, 0, 0, D2, M, tg.E4M3, tg.F32, None, 62)
+    assert rc == -9
