@@ -682,24 +682,58 @@ int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
         const int es = elem_size(dtype);
         const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
         const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+        const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
+        // the cheapest instance with scales for rows of class c and stride rs
+        auto pick = [&](int c, int64_t rs) {
+            int best_id = -1;
+            double best = 0;
+            for (int i = 0; i < tg_kernel_table_size; ++i) {
+                const TgKernelDesc& k = tg_kernel_table[i];
+                if (!k.block_scales || !usable(k, dtype, c, rs)) continue;
+                // instances with 32-bit row offsets also address 256 rows of scales that way
+                if (k.max_row_stride &&
+                    ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
+                    continue;
+                double cost = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+                if (k.nt_store && !d_lines) cost *= 1.25;
+                if (best_id < 0 || cost < best) { best_id = i; best = cost; }
+            }
+            return best_id;
+        };
+        if (kernel_id < 0 && cls < 16 && M > 0 && N > 0 && K > 0) {
+            // misaligned rows: copy A and B into aligned rows first when the
+            // streaming instance plus the copy beats the direct plan (as for
+            // tile_gemm); the product keeps the true K, so the scale blocks
+            // past ceil(K/32) stay unused
+            const int64_t rb = staged_row_bytes(K, es);
+            const int sid = pick(16, rb), did = pick(cls, row_stride);
+            if (sid >= 0 && did >= 0) {
+                const double copy = double((M + N) * (K * es + rb)) / kCopyBytesPerSecond + kLaunchSeconds;
+                const double staged = plan_seconds(tg_kernel_table[sid], M, N, K) + copy;
+                if (staged < plan_seconds(tg_kernel_table[did], M, N, K)) {
+                    rc = device_ok();
+                    if (rc) return rc;
+                    char* buf = library_staging(stream, staged_bytes(M, N, K, es));
+                    if (buf) {
+                        char* sa = buf;
+                        char* sb = buf + staged_b_offset(M, K, es);
+                        const hipError_t err = tg_stage_operands(
+                            static_cast<const char*>(A), lda * es, M, static_cast<const char*>(B), ldb * es, N,
+                            static_cast<int>(K), es, rb, sa, sb, static_cast<hipStream_t>(stream));
+                        if (err != hipSuccess) return TG_ERR_LAUNCH;
+                        return launch_batched(M, N, K, alpha, relu, sa, rb / es, 0, sb, rb / es, 0, D, ldd, 0, 1,
+                                              dtype, out_dtype, stream, sid, sc);
+                    }
+                }
+            }
+        }
         if (kernel_id >= 0) {
             if (kernel_id >= tg_kernel_table_size || !tg_kernel_table[kernel_id].block_scales) return TG_ERR_PLAN;
             const TgKernelDesc& k = tg_kernel_table[kernel_id];
             if (k.max_row_stride && ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
                 return TG_ERR_PLAN;
         } else {
-            const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
-            double best = 0;
-            for (int i = 0; i < tg_kernel_table_size; ++i) {
-                const TgKernelDesc& k = tg_kernel_table[i];
-                if (!k.block_scales || !usable(k, dtype, cls, row_stride)) continue;
-                // instances with 32-bit row offsets also address 256 rows of scales that way
-                if (k.max_row_stride && ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
-                    continue;
-                double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
-                if (k.nt_store && !d_lines) c *= 1.25;
-                if (kernel_id < 0 || c < best) { kernel_id = i; best = c; }
-            }
+            kernel_id = pick(cls, row_stride);
             if (kernel_id < 0) return TG_ERR_PLAN;
         }
     }

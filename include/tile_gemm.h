@@ -250,8 +250,11 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
  * the four scales of each 128-k stage as one dword; scales of blocks past
  * ceil(K/32) are read but ignored.  Either pointer may be NULL (no scale on
  * that side); scales with 16-bit or fp32 operands give TG_ERR_DTYPE; the
- * scales must not overlap D (TG_ERR_ALIAS).  kernel_id as tile_gemm_ex.
- * Other rules as tile_gemm_out (this call never stages its operands).
+ * scales must not overlap D (TG_ERR_ALIAS).  kernel_id as tile_gemm_ex
+ * (only instances that apply block scales accept scales; others give
+ * TG_ERR_PLAN).  With kernel_id -1, large products whose operand rows are not
+ * 16-byte aligned are staged as by tile_gemm (library staging buffer; the
+ * scales are read in place).  Other rules as tile_gemm_out.
  */
 int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      const void* A, int64_t lda, const void* scale_a, int64_t lds_a,

@@ -171,3 +171,24 @@ def test_block_scaled_workload_sampled():
     ok, r = oracle.check(d, ref, mag, w.K)
     assert ok, f"worst ratio {r}"
     _log(f"[fp8 scaled workload] {w.name}: {ms.size} sampled entries, worst ratio {r:.3g}")
+
+
+def test_block_scaled_misaligned_rows_are_staged():
+    """A large block-scaled product with 1-byte aligned rows: the automatic
+    plan stages the operands (the scales stay in place) and must match the
+    oracle on sampled entries, as must the direct register-staged instance."""
+    M = N = K = 4096
+    A_st, B_st = si.operands(M, N, K, "e4m3", "uniform_pm1", 41, 42, lda=K + 1, ldb=K + 3)
+    sa = si.block_scales(M, K, 43, pad=4)
+    sb = si.block_scales(N, K, 44, pad=8)
+    ms, ns = si.sample_coords(M, N, 1500, 23)
+    ref, mag = oracle.gemm_entries(M, N, K, 0.01, True, si.bits(A_st), K + 1, si.bits(B_st), K + 3, "e4m3", ms, ns,
+                                   scale_a=sa, lds_a=sa.shape[1], scale_b=sb, lds_b=sb.shape[1])
+    direct = [k for k in _fp8_instances("e4m3") if tg.kernel_info(k).load_class == 1 and tg.kernel_info(k).block_m == 256]
+    for kid in [-1] + direct:
+        D_st = run(A_st, B_st, M, N, K, 0.01, True, sa, sb, kernel_id=kid)
+        d = D_st[torch.from_numpy(ns), torch.from_numpy(ms)].double().numpy()
+        ok, r = oracle.check(d, ref, mag, K)
+        assert ok, f"instance {kid}: worst ratio {r}"
+        _log(f"[fp8 scaled misaligned] instance {kid}: worst ratio {r:.3g}")
+    tg.release_staging()
