@@ -15,6 +15,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import sys
 import time
 from pathlib import Path
@@ -25,27 +26,165 @@ sys.path.insert(0, str(ROOT))
 METRIC = "TFLOP/s (2MNK/t) bf16 GEMM+ReLU at 8192³; % of dense MFMA peak"
 # MI355X dense peaks (no sparsity): 256 CUs at 2.4 GHz
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "e4m3": 5033.2, "e5m2": 5033.2}
-TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
-SOURCES = ["dense_tiled_gemm_tile_amd/csrc/gemm_kernels.hip", "dense_tiled_gemm_tile_amd/csrc/tile_math.h"]
+COUNTERS_FILE = ROOT / "profiles" / "counters.json"
+PROFILES = ROOT / "profiles"
+KERNEL_SOURCES = ROOT / "dense_tiled_gemm_tile_amd" / "csrc"
+XCDS, SIMDS, SPEC_GHZ = 8, 1024, 2.4  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs, 2.4 GHz peak engine clock
 
 
-def kernel_source_hash() -> str:
+def kernel_sources(kernel_name: str) -> list[Path]:
+    """The device sources one compiled kernel is built from (its instance unit
+    and the headers every kernel unit includes)."""
+    family = {"gemm_wide_kernel": ["gemm_wide.h", "gemm_wide16.hip", "gemm_wide32.hip", "gemm_wide8.hip"],
+              "gemm_stream_kernel": ["gemm_stream.hip"], "gemm_kernel": ["gemm_rs.hip"],
+              "splitk_reduce_kernel": ["gemm_aux.hip"], "stage_rows_kernel": ["gemm_aux.hip"]}
+    base = ["gemm_common.h", "tile_math.h", "kernel_table.h"]
+    for key, files in family.items():
+        if f"::{key}<" in kernel_name or kernel_name.startswith(f"{key}<"):
+            return [KERNEL_SOURCES / f for f in base + files]
+    return sorted(p for p in KERNEL_SOURCES.iterdir() if p.suffix in (".hip", ".h"))
+
+
+def kernel_source_hash(kernel_name: str = "") -> str:
+    """Hash of the device sources of one kernel (all of them when unnamed)."""
     h = hashlib.sha256()
-    for rel in SOURCES:
-        h.update((ROOT / rel).read_bytes())
+    for path in kernel_sources(kernel_name):
+        h.update(path.name.encode())
+        h.update(path.read_bytes())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str, kernel_id: int):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; otherwise None."""
-    if not TRAFFIC_FILE.exists():
+def counters_for(key: str, kernel_id: int):
+    """The committed counter summary of this workload's kernel, if it was taken
+    on the current sources of that kernel and the same instance; else None."""
+    if not COUNTERS_FILE.exists():
         return None
-    data = json.loads(TRAFFIC_FILE.read_text())
-    entry = data.get(workload)
-    if not entry or entry.get("source_hash") != kernel_source_hash() or entry.get("kernel_id") != kernel_id:
+    entry = json.loads(COUNTERS_FILE.read_text()).get(key)
+    if (not entry or entry.get("kernel_id") != kernel_id
+            or entry.get("source_hash") != kernel_source_hash(entry.get("kernel", ""))):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry
+
+
+def _csv_rows(path: Path) -> list[dict]:
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(pmc_dir: Path, kernel: str) -> list[dict]:
+    """Counter values and duration of every dispatch of `kernel` in one
+    rocprofv3 --pmc output directory."""
+    by = {}
+    for r in _csv_rows(next(pmc_dir.rglob("*counter_collection.csv"))):
+        if r["Kernel_Name"] != kernel:
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["duration_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    return [by[k] for k in sorted(by)]
+
+
+def summarize_profile(prof: Path, key: str, flops: float, alg_bytes: float, peak: float, command: str) -> dict:
+    """Turn one workload's rocprofv3 outputs (kernel trace, counter passes
+    pmc_A/pmc_B/pmc_FETCH_SIZE/pmc_WRITE_SIZE, and the copy calibration next
+    to it) into a counters.json entry and a Markdown summary under profiles/.
+    Dispatch 1 of each counter pass is the first launch in its process (cold
+    TLBs and caches) and is left out of the means."""
+    stats = _csv_rows(next((prof / "trace").rglob("*kernel_stats.csv")))
+    top = max(stats, key=lambda r: float(r["TotalDurationNs"]))
+    kernel = top["Name"]
+    avg_ns = float(top["AverageNs"])
+    warm = lambda rows: rows[1:] if len(rows) > 1 else rows
+    a = warm(_per_dispatch(prof / "pmc_A", kernel))
+    b = warm(_per_dispatch(prof / "pmc_B", kernel))
+    mean = lambda rows, c: sum(r[c] for r in rows) / len(rows)
+    clocks = [r["GRBM_GUI_ACTIVE"] / XCDS / r["duration_s"] / 1e9 for r in a]
+    busy = [r["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * r["GRBM_GUI_ACTIVE"] / XCDS) for r in a]
+    frac = [bz * ck / SPEC_GHZ for bz, ck in zip(busy, clocks)]
+    frac_time = [flops / r["duration_s"] / 1e12 / peak for r in a]
+    copy = prof.parent
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = [r for r in _csv_rows(next((copy / f"copy_{c}").rglob("*counter_collection.csv")))
+                if r["Counter_Name"] == c]
+        # the largest dispatches of the calibration run are the 256 MiB copies
+        vals = sorted(float(r["Counter_Value"]) for r in rows)[-3:]
+        scale[c] = 268435456 / (1024 * sum(vals) / len(vals))
+    fetch = mean(warm(_per_dispatch(prof / "pmc_FETCH_SIZE", kernel)), "FETCH_SIZE")
+    write = mean(warm(_per_dispatch(prof / "pmc_WRITE_SIZE", kernel)), "WRITE_SIZE")
+    rd, wr = fetch * 1024 * scale["FETCH_SIZE"], write * 1024 * scale["WRITE_SIZE"]
+    mops = [c for c in a[0] if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
+    mfma_flops = sum(mean(a, c) for c in mops) * 512
+    entry = {
+        "kernel": kernel, "source_hash": kernel_source_hash(kernel),
+        "sources": [p.name for p in kernel_sources(kernel)],
+        "trace_average_ns": round(avg_ns), "trace_calls": int(top["Calls"]),
+        "effective_sclk_ghz": round(sum(clocks) / len(clocks), 3),
+        "mfma_busy_frac": round(sum(busy) / len(busy), 4),
+        "mfma_util_pct_rocprof": round(mean(b, "MfmaUtil"), 2) if b and "MfmaUtil" in b[0] else None,
+        "frac_from_counters": round(sum(frac) / len(frac), 4),
+        "frac_from_duration": round(sum(frac_time) / len(frac_time), 4),
+        "mfma_flops_counted": mfma_flops, "flops_2mnk": flops,
+        "mfma_insts": mean(a, "SQ_INSTS_MFMA"), "valu_insts": mean(a, "SQ_INSTS_VALU"),
+        "salu_insts": mean(a, "SQ_INSTS_SALU"), "lds_bank_conflict_cycles": mean(a, "SQ_LDS_BANK_CONFLICT"),
+        "lds_insts": mean(b, "SQ_INSTS_LDS") if b and "SQ_INSTS_LDS" in b[0] else None,
+        "read_bytes": round(rd), "write_bytes": round(wr), "hbm_bytes_per_launch": round(rd + wr),
+        "algorithmic_bytes": alg_bytes, "fetch_scale": round(scale["FETCH_SIZE"], 4),
+        "write_scale": round(scale["WRITE_SIZE"], 4),
+        "per_dispatch": [{"ms": round(r["duration_s"] * 1e3, 4), "sclk_ghz": round(ck, 3), "mfma_busy": round(bz, 4)}
+                         for r, ck, bz in zip(a, clocks, busy)],
+    }
+    name = re.sub(r"[^A-Za-z0-9]+", "_", kernel.split("(")[0].replace("void tg::", "")).strip("_")
+    md = PROFILES / f"{name}__{key.replace(':', '_')}.md"
+    entry["summary"] = str(md.relative_to(ROOT))
+    lines = [
+        f"# `{kernel}` — {key}", "",
+        f"Kernel trace (`rocprofv3 --kernel-trace --stats`): {entry['trace_calls']} dispatches, average "
+        f"{avg_ns:.0f} ns, min {float(top['MinNs']):.0f} ns, max {float(top['MaxNs']):.0f} ns; "
+        f"{flops / avg_ns / 1e3:.1f} TFLOP/s at the average (2MNK/t), {flops / avg_ns / 1e3 / peak:.4f} of "
+        f"the {peak} TFLOP/s dense peak.", "",
+        "Counters per dispatch (the first launch of each counter run left out):", "",
+        "| dispatch ms | effective SCLK GHz (GRBM_GUI_ACTIVE / 8 XCDs / duration) | MFMA busy "
+        "(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)) | busy x SCLK / 2.4 GHz | 2MNK / t / peak |",
+        "|---|---|---|---|---|",
+    ]
+    for r, ck, bz, fr, ft in zip(a, clocks, busy, frac, frac_time):
+        lines.append(f"| {r['duration_s'] * 1e3:.3f} | {ck:.3f} | {bz:.4f} | {fr:.4f} | {ft:.4f} |")
+    lines += [
+        "", "| quantity | value |", "|---|---|",
+        f"| MFMA instructions (SQ_INSTS_MFMA) | {entry['mfma_insts']:.4g} |",
+        f"| MFMA flops counted (MOPS x 512) / 2MNK | {mfma_flops / flops:.4f} |",
+        f"| rocprof MfmaUtil (%) | {entry['mfma_util_pct_rocprof']} |",
+        f"| VALU instructions incl. MFMA (SQ_INSTS_VALU) | {entry['valu_insts']:.4g} |",
+        f"| SALU instructions (SQ_INSTS_SALU) | {entry['salu_insts']:.4g} |",
+        f"| LDS instructions (SQ_INSTS_LDS) | {entry['lds_insts']} |",
+        f"| LDS bank-conflict cycles (SQ_LDS_BANK_CONFLICT) | {entry['lds_bank_conflict_cycles']:.4g} |",
+        f"| FETCH_SIZE x {scale['FETCH_SIZE']:.3f} (read bytes / launch) | {rd:.4g} |",
+        f"| WRITE_SIZE x {scale['WRITE_SIZE']:.3f} (written bytes / launch) | {wr:.4g} |",
+        f"| algorithmic bytes (A, B read once, D written once) | {alg_bytes:.4g} |", "",
+        "FETCH_SIZE and WRITE_SIZE are scaled by what the same counters read for a plain 256 MiB device "
+        "copy (`bench.py --copy-calibration 268435456`).", "",
+        "Commands (from /tmp with TMPDIR=/tmp; `$R` is the repository root, `$O` the output folder):", "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d $O/trace -o run -- python3 $R/bench.py {command} "
+        "--steps 20 --warmup 5 --no-cpu-baseline",
+        f"rocprofv3 --pmc {' '.join(sorted(k for k in a[0] if k != 'duration_s'))} --output-format csv -d $O/pmc_A "
+        f"-o run -- python3 $R/bench.py {command} --steps 3 --warmup 1 --no-cpu-baseline",
+        f"rocprofv3 --pmc {' '.join(sorted(k for k in b[0] if k != 'duration_s'))} --output-format csv -d $O/pmc_B "
+        f"-o run -- python3 $R/bench.py {command} --steps 3 --warmup 1 --no-cpu-baseline" if b else "",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $O/pmc_FETCH_SIZE -o run -- python3 $R/bench.py {command} "
+        "--steps 3 --warmup 1 --no-cpu-baseline   (then WRITE_SIZE the same way)",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $O/../copy_FETCH_SIZE -o run -- python3 $R/bench.py "
+        "--copy-calibration 268435456   (then WRITE_SIZE the same way)",
+        "```", "",
+    ]
+    md.write_text("\n".join(line for line in lines if line is not None) + "\n")
+    data = json.loads(COUNTERS_FILE.read_text()) if COUNTERS_FILE.exists() else {}
+    data[key] = {"kernel_id": None, **entry}
+    COUNTERS_FILE.write_text(json.dumps(data, indent=1, sort_keys=True) + "\n")
+    return data[key]
 
 
 def copy_calibration(nbytes: int) -> None:
@@ -80,9 +219,17 @@ def main() -> int:
                          "column) through tile_gemm_scaled")
     ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns the CPU-baseline oracle computes (all rows, full K)")
+    ap.add_argument("--staged", action="store_true",
+                    help="single products through tile_gemm_staged (mode -1) with a workspace allocated up front "
+                         "through torch: misaligned rows are first copied into aligned rows when that pays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="host only: summarise the rocprofv3 outputs in DIR (trace/, pmc_*/; the copy calibration "
+                         "in DIR/..) of this workload into profiles/ and profiles/counters.json")
+    ap.add_argument("--profile-kernel-id", type=int, default=None,
+                    help="with --summarize-profile: the instance the profiled run launched")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -92,6 +239,23 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return 0
+    if args.summarize_profile:
+        import seeded_inputs as si
+
+        w = si.WORKLOADS[args.workload]
+        os_ = {"f32": 4, "bf16": 2, "f16": 2}[args.out_dtype]
+        es = {"bf16": 2, "f16": 2, "f32": 4, "e4m3": 1, "e5m2": 1}[w.dtype]
+        alg = float(w.batch * ((w.M * w.K + w.K * w.N) * es + w.M * w.N * os_))
+        key = w.name if args.out_dtype == "f32" else f"{w.name}:out_{args.out_dtype}"
+        cmd = f"--workload {w.name}" + (f" --out-dtype {args.out_dtype}" if args.out_dtype != "f32" else "")
+        entry = summarize_profile(Path(args.summarize_profile), key, w.flops, alg, PEAK_TFLOPS[w.dtype], cmd)
+        if args.profile_kernel_id is not None:
+            data = json.loads(COUNTERS_FILE.read_text())
+            data[key]["kernel_id"] = args.profile_kernel_id
+            COUNTERS_FILE.write_text(json.dumps(data, indent=1, sort_keys=True) + "\n")
+        print(json.dumps({k: entry[k] for k in ("kernel", "effective_sclk_ghz", "mfma_busy_frac",
+                                                "frac_from_counters", "frac_from_duration", "summary")}))
         return 0
 
     import torch
@@ -123,6 +287,15 @@ def main() -> int:
 
             def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
                 return tg.gemm_scaled(A_, B_, D_, sc_a, sc_b, alpha, relu, stream=stream, kernel_id=kernel_id)
+        if args.staged:
+            ws_bytes = max(tg.staged_workspace_bytes(w.M, w.N, w.K, tg.DTYPE_CODES[w.dtype]), 256)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            plan = tg.query_plan_staged(w.M, w.N, w.K, tg.DTYPE_CODES[w.dtype], Av.data_ptr(), w.lda, Bv.data_ptr(),
+                                        w.ldb, Dv.data_ptr(), w.ldd, tg.DTYPE_CODES[args.out_dtype] if args.out_dtype
+                                        != "f32" else tg.F32, ws.data_ptr(), ws_bytes, -1)
+
+            def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
+                return tg.gemm_staged(A_, B_, D_, alpha, relu, workspace=ws, mode=-1, stream=stream)
         if args.splits != 1:
             ws = torch.empty(max(tg.splitk_workspace_bytes(w.M, w.N, args.splits), 16), dtype=torch.uint8,
                              device=dev)
@@ -186,7 +359,9 @@ def main() -> int:
                    "block_scales": bool(args.block_scales),
                    # with block scales tile_gemm_scaled picks among the instances that apply them
                    "kernel_id": None if args.block_scales else plan.kernel_id,
-                   "staged": bool(plan.staged),  # A and B copied into aligned rows first (one more launch)
+                   # A and B copied into aligned rows of a workspace first (one more launch)
+                   "staged": bool(plan.staged),
+                   "workspace_bytes": (ws_bytes if args.staged else None),
                    "tile": f"{plan.block_m}x{plan.block_n}x{plan.block_k}", "grid": plan.grid,
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
@@ -198,9 +373,21 @@ def main() -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": traffic_for(w.name if args.out_dtype == "f32" else f"{w.name}:out_{args.out_dtype}",
-                                   plan.kernel_id),
+            "traffic": None,
         },
+    }
+    # counters from the committed rocprofv3 summary of this kernel (null when
+    # the kernel sources changed since they were taken)
+    key = w.name if args.out_dtype == "f32" else f"{w.name}:out_{args.out_dtype}"
+    cnt = None if (args.staged or args.block_scales or args.splits != 1 or args.epilogue != "pointwise") else \
+        counters_for(key, plan.kernel_id)
+    if cnt:
+        result["roofline"]["traffic"] = cnt.get("hbm_bytes_per_launch")
+    result["counters"] = None if not cnt else {
+        "effective_sclk_ghz": cnt.get("effective_sclk_ghz"),
+        "mfma_busy_frac": cnt.get("mfma_busy_frac"),
+        "frac_from_counters": cnt.get("frac_from_counters"),
+        "summary": cnt.get("summary"),
     }
 
     if not args.no_cpu_baseline:
@@ -209,6 +396,7 @@ def main() -> int:
         import oracle
 
         threads = oracle.default_threads()
+        cores = oracle.affinity_cores()
         if args.epilogue == "softmax":
             # whole rows (every n) for rows m < rows
             rows = max(1, min(w.M, args.cpu_cols * 8))
@@ -234,7 +422,9 @@ def main() -> int:
         result["cpu_baseline"] = {
             "value": round(cpu_flops / cpu_s / 1e12, 6),
             "unit": "TFLOP/s",
-            "cores": threads,
+            "cores": cores,
+            "threads": threads,
+            "cpu_quota": oracle.cpu_quota(),
             "kind": "oracle",
             "sample": (f"rows m < {rows}, every n, of the {w.M}x{w.N}x{w.K} logits (full K), fp64; "
                        f"{cpu_s:.2f} s wall" if args.epilogue == "softmax" else

@@ -59,7 +59,7 @@ _SIGNATURES = {
     "tile_gemm_ex": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _int]),
     "tile_gemm_out": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                              _ptr, _int]),
-    "tile_gemm_query_plan": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int,
+    "tile_gemm_query_plan": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64,
                                     ctypes.POINTER(PlanInfo)]),
     "tile_gemm_batched": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64,
                                  _i64, _i64, _int, _int, _ptr, _int]),
@@ -73,10 +73,15 @@ _SIGNATURES = {
     "tile_gemm_staged_workspace_bytes": (_i64, [_i64, _i64, _i64, _int]),
     "tile_gemm_scaled": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr,
                                 _i64, _int, _int, _ptr, _int]),
-    "tile_gemm_release_staging": (_int, []),
     "tile_gemm_softmax": (_int, [_i64, _i64, _i64, _f32, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr, _int]),
     "tile_gemm_query_plan_out": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                         ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_query_plan_softmax": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                                            ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_query_plan_scaled": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64,
+                                           _ptr, _i64, _int, _int, ctypes.POINTER(PlanInfo)]),
+    "tile_gemm_query_plan_staged": (_int, [_i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr,
+                                           _i64, _int, ctypes.POINTER(PlanInfo)]),
     "tile_gemm_kernel_count": (_int, []),
     "tile_gemm_kernel_info": (_int, [_int, ctypes.POINTER(PlanInfo)]),
     "tile_gemm_strerror": (ctypes.c_char_p, [_int]),
@@ -175,21 +180,41 @@ def staged_workspace_bytes(M, N, K, dtype) -> int:
     return load_library().tile_gemm_staged_workspace_bytes(M, N, K, dtype)
 
 
-def release_staging() -> None:
-    """Free the library's own staging buffers (tile_gemm_release_staging)."""
-    _check(load_library().tile_gemm_release_staging())
-
-
 def query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id=-1, out_dtype=F32) -> PlanInfo:
     """Host-only plan query; raises TileGemmError on invalid arguments."""
     info = PlanInfo()
-    if out_dtype == F32:
-        rc = load_library().tile_gemm_query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, kernel_id,
-                                                 ctypes.byref(info))
+    if out_dtype == F32 and kernel_id == -1:
+        rc = load_library().tile_gemm_query_plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, ctypes.byref(info))
     else:
         rc = load_library().tile_gemm_query_plan_out(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype,
                                                      kernel_id, ctypes.byref(info))
     _check(rc)
+    return info
+
+
+def query_plan_softmax(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype=F32, kernel_id=-1) -> PlanInfo:
+    """Host-only plan of a tile_gemm_softmax call (kernel_id -1: two launches)."""
+    info = PlanInfo()
+    _check(load_library().tile_gemm_query_plan_softmax(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id,
+                                                       ctypes.byref(info)))
+    return info
+
+
+def query_plan_scaled(M, N, K, dtype, A, lda, scale_a, lds_a, B, ldb, scale_b, lds_b, D, ldd, out_dtype=F32,
+                      kernel_id=-1) -> PlanInfo:
+    """Host-only plan of a tile_gemm_scaled call."""
+    info = PlanInfo()
+    _check(load_library().tile_gemm_query_plan_scaled(M, N, K, dtype, A, lda, scale_a, lds_a, B, ldb, scale_b, lds_b,
+                                                      D, ldd, out_dtype, kernel_id, ctypes.byref(info)))
+    return info
+
+
+def query_plan_staged(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype=F32, workspace=None, workspace_bytes=0,
+                      mode=-1) -> PlanInfo:
+    """Host-only plan of a tile_gemm_staged call (staged = 1 when the copy runs)."""
+    info = PlanInfo()
+    _check(load_library().tile_gemm_query_plan_staged(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, workspace,
+                                                      workspace_bytes, mode, ctypes.byref(info)))
     return info
 
 

@@ -1,11 +1,17 @@
 """Build step for the HIP library: compiles csrc/ into an in-tree shared
-library for gfx950 with hipcc (run ``python -m dense_tiled_gemm_tile_amd.build``)."""
+library for gfx950 with hipcc (run ``python -m dense_tiled_gemm_tile_amd.build``).
+
+Every translation unit is compiled to its own object in parallel (the kernel
+instances are spread over several units for that reason), then the objects
+are linked into ``_lib/libtile_gemm.so``."""
 from __future__ import annotations
 
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -13,7 +19,10 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "_lib" / "libtile_gemm.so"
-SOURCES = [CSRC / "api.cpp", CSRC / "gemm_kernels.hip"]
+# host-side units first, then the kernel units (largest first, so the
+# parallel build ends sooner)
+SOURCES = [CSRC / "gemm_wide16.hip", CSRC / "gemm_rs.hip", CSRC / "gemm_wide8.hip", CSRC / "gemm_wide32.hip",
+           CSRC / "gemm_stream.hip", CSRC / "gemm_aux.hip", CSRC / "api.cpp", CSRC / "kernel_table.cpp"]
 ARCH = "gfx950"
 
 
@@ -31,23 +40,43 @@ def compile_flags() -> list[str]:
             "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+def _jobs() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n, len(SOURCES)))
+
+
 def build(verbose: bool = False) -> Path:
     """Compile every source for gfx950 and link the shared library (always rebuilds)."""
     LIB.parent.mkdir(parents=True, exist_ok=True)
-    tmp = LIB.with_name(LIB.name + ".tmp")
-    cmd = [hipcc(), *compile_flags(), "-shared", "-o", str(tmp), *map(str, SOURCES)]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    with tempfile.TemporaryDirectory(prefix="tg_build_") as tmpdir:
+        objs = [Path(tmpdir) / (src.name + ".o") for src in SOURCES]
+
+        def compile_one(pair):
+            src, obj = pair
+            cmd = [hipcc(), *compile_flags(), "-c", "-o", str(obj), str(src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            list(pool.map(compile_one, zip(SOURCES, objs)))
+        tmp = LIB.with_name(LIB.name + ".tmp")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", str(tmp), *map(str, objs)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
     return LIB
 
 
-def asm(out_dir: Path) -> list[Path]:
-    """Write the gfx950 assembly of the kernels (our own build) for inspection."""
+def asm(out_dir: Path, source: str = "gemm_wide16.hip") -> list[Path]:
+    """Write the gfx950 assembly of one kernel unit (our own build) for inspection."""
     out_dir.mkdir(parents=True, exist_ok=True)
-    out = out_dir / "gemm_kernels-gfx950.s"
-    cmd = [hipcc(), *compile_flags(), "--cuda-device-only", "-S", "-o", str(out), str(CSRC / "gemm_kernels.hip")]
+    out = out_dir / (Path(source).stem + "-gfx950.s")
+    cmd = [hipcc(), *compile_flags(), "--cuda-device-only", "-S", "-o", str(out), str(CSRC / source)]
     subprocess.run(cmd, check=True)
     return [out]
 

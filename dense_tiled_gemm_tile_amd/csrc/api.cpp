@@ -14,8 +14,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <mutex>
-#include <vector>
 
 #include "kernel_table.h"
 #include "tile_gemm.h"
@@ -136,8 +134,8 @@ bool d_lines_aligned(const void* D, int64_t ldd, int os, const Batch& bt) {
 int choose(int64_t M, int64_t N, int64_t batch, int dtype, int cls, int64_t row_stride, bool d_lines = true) {
     int best = -1;
     double best_cost = 0;
-    for (int i = 0; i < tg_kernel_table_size; ++i) {
-        const TgKernelDesc& k = tg_kernel_table[i];
+    for (int i = 0; i < tg_kernel_count(); ++i) {
+        const TgKernelDesc& k = tg_kernel(i);
         if (!usable(k, dtype, cls, row_stride)) continue;
         // among equal costs prefer the instance that needs the strongest alignment
         double c = plan_cost(k, M, N, batch) * (1.0 + 0.001 / k.load_class);
@@ -210,8 +208,8 @@ Staging decide_staging(int64_t M, int64_t N, int64_t K, int dtype, const void* A
         const int did = choose(M, N, 1, dtype, cls, (lda > ldb ? lda : ldb) * es, d_lines);
         if (did >= 0) {
             const double copy = double((M + N) * (K * es + rb)) / kCopyBytesPerSecond + kLaunchSeconds;
-            const double staged = plan_seconds(tg_kernel_table[sid], M, N, rb / es) + copy;
-            if (staged >= plan_seconds(tg_kernel_table[did], M, N, K)) return st;
+            const double staged = plan_seconds(tg_kernel(sid), M, N, rb / es) + copy;
+            if (staged >= plan_seconds(tg_kernel(did), M, N, K)) return st;
         }
     }
     st.on = true;
@@ -220,34 +218,24 @@ Staging decide_staging(int64_t M, int64_t N, int64_t K, int dtype, const void* A
     return st;
 }
 
-// staging: report the staged plan when the automatic choice of a single
-// product would stage its operands (the library's own staging buffer assumed
-// available).
+// The plan of a direct launch on the operands as given (no staging).
 int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
          int64_t ldb, const void* D, int64_t ldd, int out_dtype, int kernel_id, tile_gemm_plan_info* out,
-         const Batch& bt = Batch(), int64_t splits = 1, bool staging = false) {
+         const Batch& bt = Batch(), int64_t splits = 1) {
     const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, bt);
     if (rc) return rc;
     const int es = elem_size(dtype);
     const int cls = row_class(M, N, A, lda, B, ldb, es, bt);
     const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
     const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), bt);
-    if (staging && kernel_id < 0 && bt.batch == 1 && splits == 1) {
-        const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, d_lines, -1);
-        if (st.on) {
-            describe(tg_kernel_table[st.staged_id], M, N, out);
-            out->staged = 1;
-            return out->grid > kMaxGrid ? TG_ERR_DIMS : TG_OK;
-        }
-    }
     int id = kernel_id;
     if (id < 0) {
         id = choose(M, N, bt.batch * splits, dtype, cls, row_stride, d_lines);
         if (id < 0) return TG_ERR_PLAN;
-    } else if (id >= tg_kernel_table_size || !usable(tg_kernel_table[id], dtype, cls, row_stride)) {
+    } else if (id >= tg_kernel_count() || !usable(tg_kernel(id), dtype, cls, row_stride)) {
         return TG_ERR_PLAN;
     }
-    describe(tg_kernel_table[id], M, N, out);
+    describe(tg_kernel(id), M, N, out);
     out->load_class = cls;
     if (out->grid > kMaxGrid) return TG_ERR_DIMS;
     return TG_OK;
@@ -277,64 +265,6 @@ int device_ok() {
     return ok ? TG_OK : TG_ERR_DEVICE;
 }
 
-// The library's staging buffers: one per (device, stream), grown on demand
-// and kept until tile_gemm_release_staging.  Work on one stream runs in
-// order, so a buffer is never used by two calls at once.
-struct StagingBuffer {
-    int dev;
-    void* stream;
-    void* ptr;
-    int64_t bytes;
-};
-std::mutex g_staging_mu;
-std::vector<StagingBuffer> g_staging;
-constexpr int64_t kStagingGranule = int64_t(32) << 20;
-
-// At least `need` bytes of the current device's buffer for `stream`, or
-// nullptr (the stream is being captured into a graph, or allocation failed):
-// the caller then runs the direct plan.
-char* library_staging(void* stream, int64_t need) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    if (cs != hipStreamCaptureStatusNone) return nullptr;
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    std::lock_guard<std::mutex> lock(g_staging_mu);
-    StagingBuffer* buf = nullptr;
-    for (StagingBuffer& b : g_staging)
-        if (b.dev == dev && b.stream == stream) buf = &b;
-    if (buf && buf->bytes >= need) return static_cast<char*>(buf->ptr);
-    if (!buf) {
-        g_staging.push_back(StagingBuffer{dev, stream, nullptr, 0});
-        buf = &g_staging.back();
-    }
-    if (buf->ptr) {
-        // earlier work on the stream may still read the old buffer
-        const bool ok = hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess &&
-                        hipFree(buf->ptr) == hipSuccess;
-        buf->ptr = nullptr;
-        buf->bytes = 0;
-        if (!ok) {
-            (void)hipGetLastError();
-            return nullptr;
-        }
-    }
-    const int64_t size = cdiv(need, kStagingGranule) * kStagingGranule;
-    if (hipMalloc(&buf->ptr, static_cast<size_t>(size)) != hipSuccess) {
-        (void)hipGetLastError();
-        buf->ptr = nullptr;
-        return nullptr;
-    }
-    buf->bytes = size;
-    return static_cast<char*>(buf->ptr);
-}
-
 // Block scales of 8-bit operands (none when both pointers are null).
 struct Scales {
     const unsigned char* a = nullptr;
@@ -347,45 +277,54 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
                    int64_t stride_d, int64_t batch, int dtype, int out_dtype, void* stream, int kernel_id,
                    const Scales& sc = Scales());
 
-// A single product, on staged operand copies when `mode` and the plan say so
-// (workspace: the caller's, or nullptr for the library's own buffer).
-int gemm_single(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda, const void* B,
-                int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id,
-                void* workspace, int64_t workspace_bytes, int mode, bool library) {
-    if (kernel_id >= 0 || mode == 0)
-        return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
-                              kernel_id);
+// Whether tile_gemm_staged copies the operands (mode 1: always; -1: when the
+// plan says the copy pays and the workspace suffices; 0: never).  *rc gets
+// TG_ERR_WORKSPACE (mode 1 without a usable workspace) or TG_ERR_ALIAS (the
+// workspace overlaps an operand).
+Staging staged_decision(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        const void* D, int64_t ldd, int dtype, int out_dtype, const void* workspace,
+                        int64_t workspace_bytes, int mode, int* rc) {
+    *rc = TG_OK;
+    Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, d_lines_aligned(D, ldd, elem_size(out_dtype), Batch()),
+                                mode);
+    if (!st.on) return st;
+    const int es = elem_size(dtype);
+    const int64_t need = staged_bytes(M, N, K, es);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) {
+        if (mode == 1) *rc = TG_ERR_WORKSPACE;
+        st.on = false;
+        return st;
+    }
+    const int os = elem_size(out_dtype);
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uintptr_t(need);
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(D), d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(B), b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
+    if (overlaps(w0, w1, d0, d1) || overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1)) {
+        *rc = TG_ERR_ALIAS;
+        st.on = false;
+    }
+    return st;
+}
+
+// A single product on staged operand copies in the caller's workspace, when
+// `mode` and the plan say so; otherwise the direct plan.
+int gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda, const void* B,
+                int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, void* workspace,
+                int64_t workspace_bytes, int mode) {
     int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
     if (rc) return rc;
-    const Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb,
-                                      d_lines_aligned(D, ldd, elem_size(out_dtype), Batch()), mode);
+    const Staging st = staged_decision(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, workspace,
+                                       workspace_bytes, mode, &rc);
+    if (rc) return rc;
     if (!st.on)
         return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
                               -1);
-    const int es = elem_size(dtype);
-    const int64_t need = staged_bytes(M, N, K, es);
-    char* buf = nullptr;
-    if (!library) {
-        if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) {
-            if (mode == 1) return TG_ERR_WORKSPACE;
-        } else {
-            const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uintptr_t(need);
-            const int os = elem_size(out_dtype);
-            const uintptr_t d0 = reinterpret_cast<uintptr_t>(D), d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
-            const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
-            const uintptr_t b0 = reinterpret_cast<uintptr_t>(B), b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
-            if (overlaps(w0, w1, d0, d1) || overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1)) return TG_ERR_ALIAS;
-            buf = static_cast<char*>(workspace);
-        }
-    }
     rc = device_ok();
     if (rc) return rc;
-    if (library) buf = library_staging(stream, need);
-    if (!buf)
-        return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
-                              -1);
-    char* sa = buf;
-    char* sb = buf + staged_b_offset(M, K, es);
+    const int es = elem_size(dtype);
+    char* sa = static_cast<char*>(workspace);
+    char* sb = sa + staged_b_offset(M, K, es);
     const hipError_t err = tg_stage_operands(static_cast<const char*>(A), lda * es, M, static_cast<const char*>(B),
                                              ldb * es, N, static_cast<int>(K), es, st.row_bytes, sa, sb,
                                              static_cast<hipStream_t>(stream));
@@ -395,15 +334,98 @@ int gemm_single(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
                           st.staged_id);
 }
 
+// The fused softmax instance for a tile_gemm_softmax call (*id = -1: two
+// launches, the plain product and the row pass).
+int softmax_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                 const void* D, int64_t ldd, int dtype, int out_dtype, int kernel_id, int* id) {
+    *id = -1;
+    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    if (rc) return rc;
+    if (M == 0 || N == 0) return TG_OK;
+    const int es = elem_size(dtype);
+    const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
+    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    // fused: an instance whose tile spans all of N
+    if (kernel_id >= 0) {
+        if (kernel_id >= tg_kernel_count()) return TG_ERR_PLAN;
+        const TgKernelDesc& k = tg_kernel(kernel_id);
+        if (!usable(k, dtype, cls, row_stride) || !k.softmax || k.block_n < N) return TG_ERR_PLAN;
+        *id = kernel_id;
+    } else {
+        double best = 0;
+        for (int i = 0; i < tg_kernel_count(); ++i) {
+            const TgKernelDesc& k = tg_kernel(i);
+            if (!usable(k, dtype, cls, row_stride) || !k.softmax || k.block_n < N) continue;
+            const double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+            if (*id < 0 || c < best) { *id = i; best = c; }
+        }
+    }
+    if (*id < 0 && out_dtype != TG_F32) return TG_ERR_DIMS;  // the two-pass path writes fp32 logits
+    if (*id >= 0 && cdiv(M, tg_kernel(*id).block_m) > kMaxGrid) return TG_ERR_DIMS;
+    return TG_OK;
+}
+
+// Validation of a tile_gemm_scaled call and its instance: with block scales
+// only instances that apply them may run it (*kernel_id -1 = the cheapest such
+// instance); without scales the call is tile_gemm_out's.
+int scaled_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* scale_a, int64_t lds_a,
+                const void* B, int64_t ldb, const void* scale_b, int64_t lds_b, const void* D, int64_t ldd, int dtype,
+                int out_dtype, int* kernel_id, Scales* sc) {
+    const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    if (rc) return rc;
+    if (!scale_a && !scale_b) return TG_OK;
+    if (elem_size(dtype) != 1) return TG_ERR_DTYPE;
+    // whole dwords per 128-k stage: 4*ceil(K/128) bytes per row, 4-byte aligned
+    const int64_t need = 4 * cdiv(K, 128);
+    if ((scale_a && (lds_a < need || (lds_a & 3))) || (scale_b && (lds_b < need || (lds_b & 3)))) return TG_ERR_LD;
+    if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & 3u) return TG_ERR_ALIGN;
+    if (M > 0 && N > 0 && K > 0) {
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
+        const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(elem_size(out_dtype));
+        if (scale_a) {
+            const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale_a), s1 = s0 + uintptr_t((M - 1) * lds_a + need);
+            if (overlaps(d0, d1, s0, s1)) return TG_ERR_ALIAS;
+        }
+        if (scale_b) {
+            const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale_b), s1 = s0 + uintptr_t((N - 1) * lds_b + need);
+            if (overlaps(d0, d1, s0, s1)) return TG_ERR_ALIAS;
+        }
+    }
+    sc->a = static_cast<const unsigned char*>(scale_a);
+    sc->b = static_cast<const unsigned char*>(scale_b);
+    sc->lds_a = lds_a;
+    sc->lds_b = lds_b;
+    // instances with 32-bit row offsets also address 256 rows of scales that way
+    auto scale_rows_fit = [&](const TgKernelDesc& k) {
+        return !k.max_row_stride || !((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride));
+    };
+    if (*kernel_id >= 0) {
+        if (*kernel_id >= tg_kernel_count() || !tg_kernel(*kernel_id).block_scales) return TG_ERR_PLAN;
+        return scale_rows_fit(tg_kernel(*kernel_id)) ? TG_OK : TG_ERR_PLAN;
+    }
+    const int es = elem_size(dtype);
+    const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
+    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
+    double best = 0;
+    for (int i = 0; i < tg_kernel_count(); ++i) {
+        const TgKernelDesc& k = tg_kernel(i);
+        if (!k.block_scales || !usable(k, dtype, cls, row_stride) || !scale_rows_fit(k)) continue;
+        double cost = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
+        if (k.nt_store && !d_lines) cost *= 1.25;
+        if (*kernel_id < 0 || cost < best) { *kernel_id = i; best = cost; }
+    }
+    return *kernel_id < 0 ? TG_ERR_PLAN : TG_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
-                         const void* B, int64_t ldb, const float* D, int64_t ldd, int kernel_id,
-                         tile_gemm_plan_info* out) {
+                         const void* B, int64_t ldb, const float* D, int64_t ldd, tile_gemm_plan_info* out) {
     if (!out) return TG_ERR_NULL;
-    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, TG_F32, kernel_id, out, Batch(), 1, true);
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, TG_F32, -1, out);
 }
 
 int tile_gemm_query_plan_batched(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
@@ -425,7 +447,7 @@ int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype, const v
                              const void* B, int64_t ldb, const void* D, int64_t ldd, int out_dtype,
                              int kernel_id, tile_gemm_plan_info* out) {
     if (!out) return TG_ERR_NULL;
-    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out, Batch(), 1, true);
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out);
 }
 
 int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
@@ -479,7 +501,7 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
     a.scale_b = sc.b;
     a.lds_a = sc.lds_a;
     a.lds_b = sc.lds_b;
-    const hipError_t err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<int>(batch),
+    const hipError_t err = tg_kernel(pl.kernel_id).launch(a, pl.grid, static_cast<int>(batch),
                                                                 static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
@@ -568,7 +590,7 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
     a.split_k = static_cast<int>(chunk);
     hipError_t err = hipSuccess;
     if (K > 0)
-        err = tg_kernel_table[pl.kernel_id].launch(a, pl.grid, static_cast<int>(used), static_cast<hipStream_t>(stream));
+        err = tg_kernel(pl.kernel_id).launch(a, pl.grid, static_cast<int>(used), static_cast<hipStream_t>(stream));
     if (err == hipSuccess)
         err = tg_splitk_reduce(static_cast<const float*>(workspace), K > 0 ? static_cast<int>(used) : 0,
                                static_cast<int>(M), static_cast<int>(N), D, ldd, alpha, relu ? 1 : 0, out_dtype,
@@ -578,31 +600,12 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
 
 int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,
                       int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id) {
-    int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    int id = -1;
+    int rc = softmax_plan(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, kernel_id, &id);
     if (rc) return rc;
     if (M == 0 || N == 0) return TG_OK;
-    const int es = elem_size(dtype);
-    const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
-    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
-    // fused: an instance whose tile spans all of N
-    int id = -1;
-    if (kernel_id >= 0) {
-        if (kernel_id >= tg_kernel_table_size) return TG_ERR_PLAN;
-        const TgKernelDesc& k = tg_kernel_table[kernel_id];
-        if (!usable(k, dtype, cls, row_stride) || !k.softmax || k.block_n < N) return TG_ERR_PLAN;
-        id = kernel_id;
-    } else {
-        double best = 0;
-        for (int i = 0; i < tg_kernel_table_size; ++i) {
-            const TgKernelDesc& k = tg_kernel_table[i];
-            if (!usable(k, dtype, cls, row_stride) || !k.softmax || k.block_n < N) continue;
-            const double c = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
-            if (id < 0 || c < best) { id = i; best = c; }
-        }
-    }
     if (id < 0) {
         // two passes: the logits alpha*S into an fp32 D, then the row softmax in place
-        if (out_dtype != TG_F32) return TG_ERR_DIMS;
         rc = tile_gemm_out(M, N, K, alpha, 0, A, lda, B, ldb, D, ldd, dtype, TG_F32, stream, -1);
         if (rc) return rc;
         const hipError_t err = tg_softmax_rows(static_cast<float*>(D), static_cast<int>(M), static_cast<int>(N), ldd,
@@ -611,7 +614,8 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* 
     }
     rc = device_ok();
     if (rc) return rc;
-    const TgKernelDesc& k = tg_kernel_table[id];
+    const int es = elem_size(dtype);
+    const TgKernelDesc& k = tg_kernel(id);
     GemmArgs a{};
     a.A = static_cast<const char*>(A);
     a.B = static_cast<const char*>(B);
@@ -628,117 +632,81 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* 
     a.group_m = k.group_m;
     a.out_dtype = out_dtype;
     a.epi = TG_EPI_SOFTMAX;
-    const int64_t grid = a.tiles_m;
-    if (grid > kMaxGrid) return TG_ERR_DIMS;
-    const hipError_t err = k.launch(a, grid, 1, static_cast<hipStream_t>(stream));
+    const hipError_t err = k.launch(a, a.tiles_m, 1, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+int tile_gemm_query_plan_softmax(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, const void* D, int64_t ldd, int out_dtype,
+                                 int kernel_id, tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    memset(out, 0, sizeof *out);
+    int id = -1;
+    const int rc = softmax_plan(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, kernel_id, &id);
+    if (rc) return rc;
+    if (id >= 0) {
+        describe(tg_kernel(id), M, N, out);
+        out->tiles_n = 1;  // one tile spans N
+        out->grid = out->tiles_m;
+    } else {
+        out->kernel_id = -1;  // two launches: the plain product, then the row pass
+        out->dtype = dtype;
+    }
+    return TG_OK;
 }
 
 int tile_gemm_out(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
                   int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int dtype,
                   int out_dtype, void* stream, int kernel_id) {
-    return gemm_single(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream, kernel_id, nullptr,
-                       0, -1, true);
+    return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                          kernel_id);
 }
 
 int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
                      const void* B, int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, void* workspace,
                      int64_t workspace_bytes, void* stream, int mode) {
     if (mode < -1 || mode > 1) return TG_ERR_PLAN;
-    return gemm_single(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream, -1, workspace,
-                       workspace_bytes, mode, false);
+    return gemm_staged(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, stream, workspace,
+                       workspace_bytes, mode);
 }
 
 int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
                      const void* scale_a, int64_t lds_a, const void* B, int64_t ldb, const void* scale_b,
                      int64_t lds_b, void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id) {
-    int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
-    if (rc) return rc;
     Scales sc;
-    if (scale_a || scale_b) {
-        if (elem_size(dtype) != 1) return TG_ERR_DTYPE;
-        // whole dwords per 128-k stage: 4*ceil(K/128) bytes per row, 4-byte aligned
-        const int64_t need = 4 * cdiv(K, 128);
-        if ((scale_a && (lds_a < need || (lds_a & 3))) || (scale_b && (lds_b < need || (lds_b & 3))))
-            return TG_ERR_LD;
-        if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & 3u) return TG_ERR_ALIGN;
-        if (M > 0 && N > 0 && K > 0) {
-            const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
-            const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(elem_size(out_dtype));
-            if (scale_a) {
-                const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale_a), s1 = s0 + uintptr_t((M - 1) * lds_a + need);
-                if (overlaps(d0, d1, s0, s1)) return TG_ERR_ALIAS;
-            }
-            if (scale_b) {
-                const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale_b), s1 = s0 + uintptr_t((N - 1) * lds_b + need);
-                if (overlaps(d0, d1, s0, s1)) return TG_ERR_ALIAS;
-            }
-        }
-        sc.a = static_cast<const unsigned char*>(scale_a);
-        sc.b = static_cast<const unsigned char*>(scale_b);
-        sc.lds_a = lds_a;
-        sc.lds_b = lds_b;
-        // only instances that apply block scales may run the call
-        const int es = elem_size(dtype);
-        const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
-        const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
-        const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
-        // the cheapest instance with scales for rows of class c and stride rs
-        auto pick = [&](int c, int64_t rs) {
-            int best_id = -1;
-            double best = 0;
-            for (int i = 0; i < tg_kernel_table_size; ++i) {
-                const TgKernelDesc& k = tg_kernel_table[i];
-                if (!k.block_scales || !usable(k, dtype, c, rs)) continue;
-                // instances with 32-bit row offsets also address 256 rows of scales that way
-                if (k.max_row_stride &&
-                    ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
-                    continue;
-                double cost = plan_cost(k, M, N, 1) * (1.0 + 0.001 / k.load_class);
-                if (k.nt_store && !d_lines) cost *= 1.25;
-                if (best_id < 0 || cost < best) { best_id = i; best = cost; }
-            }
-            return best_id;
-        };
-        if (kernel_id < 0 && cls < 16 && M > 0 && N > 0 && K > 0) {
-            // misaligned rows: copy A and B into aligned rows first when the
-            // streaming instance plus the copy beats the direct plan (as for
-            // tile_gemm); the product keeps the true K, so the scale blocks
-            // past ceil(K/32) stay unused
-            const int64_t rb = staged_row_bytes(K, es);
-            const int sid = pick(16, rb), did = pick(cls, row_stride);
-            if (sid >= 0 && did >= 0) {
-                const double copy = double((M + N) * (K * es + rb)) / kCopyBytesPerSecond + kLaunchSeconds;
-                const double staged = plan_seconds(tg_kernel_table[sid], M, N, K) + copy;
-                if (staged < plan_seconds(tg_kernel_table[did], M, N, K)) {
-                    rc = device_ok();
-                    if (rc) return rc;
-                    char* buf = library_staging(stream, staged_bytes(M, N, K, es));
-                    if (buf) {
-                        char* sa = buf;
-                        char* sb = buf + staged_b_offset(M, K, es);
-                        const hipError_t err = tg_stage_operands(
-                            static_cast<const char*>(A), lda * es, M, static_cast<const char*>(B), ldb * es, N,
-                            static_cast<int>(K), es, rb, sa, sb, static_cast<hipStream_t>(stream));
-                        if (err != hipSuccess) return TG_ERR_LAUNCH;
-                        return launch_batched(M, N, K, alpha, relu, sa, rb / es, 0, sb, rb / es, 0, D, ldd, 0, 1,
-                                              dtype, out_dtype, stream, sid, sc);
-                    }
-                }
-            }
-        }
-        if (kernel_id >= 0) {
-            if (kernel_id >= tg_kernel_table_size || !tg_kernel_table[kernel_id].block_scales) return TG_ERR_PLAN;
-            const TgKernelDesc& k = tg_kernel_table[kernel_id];
-            if (k.max_row_stride && ((scale_a && lds_a > k.max_row_stride) || (scale_b && lds_b > k.max_row_stride)))
-                return TG_ERR_PLAN;
-        } else {
-            kernel_id = pick(cls, row_stride);
-            if (kernel_id < 0) return TG_ERR_PLAN;
-        }
-    }
+    const int rc = scaled_plan(M, N, K, A, lda, scale_a, lds_a, B, ldb, scale_b, lds_b, D, ldd, dtype, out_dtype,
+                               &kernel_id, &sc);
+    if (rc) return rc;
     return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
                           kernel_id, sc);
+}
+
+int tile_gemm_query_plan_scaled(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                                const void* scale_a, int64_t lds_a, const void* B, int64_t ldb, const void* scale_b,
+                                int64_t lds_b, const void* D, int64_t ldd, int out_dtype, int kernel_id,
+                                tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    Scales sc;
+    const int rc = scaled_plan(M, N, K, A, lda, scale_a, lds_a, B, ldb, scale_b, lds_b, D, ldd, dtype, out_dtype,
+                               &kernel_id, &sc);
+    if (rc) return rc;
+    return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, kernel_id, out);
+}
+
+int tile_gemm_query_plan_staged(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, const void* D, int64_t ldd, int out_dtype,
+                                const void* workspace, int64_t workspace_bytes, int mode, tile_gemm_plan_info* out) {
+    if (!out) return TG_ERR_NULL;
+    if (mode < -1 || mode > 1) return TG_ERR_PLAN;
+    int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
+    if (rc) return rc;
+    const Staging st = staged_decision(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, workspace,
+                                       workspace_bytes, mode, &rc);
+    if (rc) return rc;
+    if (!st.on) return plan(M, N, K, dtype, A, lda, B, ldb, D, ldd, out_dtype, -1, out);
+    describe(tg_kernel(st.staged_id), M, N, out);
+    out->staged = 1;
+    return out->grid > kMaxGrid ? TG_ERR_DIMS : TG_OK;
 }
 
 int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype) {
@@ -746,19 +714,6 @@ int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dt
     if (!es || M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
     if (M == 0 || N == 0 || K == 0) return 0;
     return staged_bytes(M, N, K, es);
-}
-
-int tile_gemm_release_staging(void) {
-    std::lock_guard<std::mutex> lock(g_staging_mu);
-    int rc = TG_OK;
-    for (StagingBuffer& b : g_staging) {
-        if (b.ptr && hipFree(b.ptr) != hipSuccess) {  // hipFree waits for work still using it
-            (void)hipGetLastError();
-            rc = TG_ERR_LAUNCH;
-        }
-    }
-    g_staging.clear();
-    return rc;
 }
 
 int tile_gemm_ex(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A,
@@ -772,12 +727,12 @@ int tile_gemm(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void
     return tile_gemm_out(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, TG_F32, stream, -1);
 }
 
-int tile_gemm_kernel_count(void) { return tg_kernel_table_size; }
+int tile_gemm_kernel_count(void) { return tg_kernel_count(); }
 
 int tile_gemm_kernel_info(int kernel_id, tile_gemm_plan_info* out) {
     if (!out) return TG_ERR_NULL;
-    if (kernel_id < 0 || kernel_id >= tg_kernel_table_size) return TG_ERR_PLAN;
-    describe(tg_kernel_table[kernel_id], 0, 0, out);
+    if (kernel_id < 0 || kernel_id >= tg_kernel_count()) return TG_ERR_PLAN;
+    describe(tg_kernel(kernel_id), 0, 0, out);
     return TG_OK;
 }
 

@@ -1,0 +1,625 @@
+// Wide-row streaming GEMM kernel for gfx950 (CDNA4): the default for large
+// products.  Included by the instance translation units (one per operand
+// width, compiled in parallel).
+#pragma once
+
+#include "gemm_common.h"
+
+namespace tg {
+
+// 256 x 256 tile, 4 waves of 128 x 128, stages of 128 bytes of K per operand
+// row copied global -> LDS by LDS-DMA.  Each group of 8 lanes of a copy reads
+// one whole 128-byte row segment (a full cache line), which halves the number
+// of memory requests per byte against 64-byte rows; the L2 -> LDS request rate
+// is what bounds the copy path of these kernels.  Per stage each wave runs four
+// slabs of 16 MFMAs (32 bytes of K each).
+//
+// LDS holds NS slots of 32 KiB; a slot holds one operand's half of a stage
+// (256 rows x 128 bytes).  Half-stage h (stage h/2, A if h is even, B if odd)
+// lives in slot h % NS.  NS = 4 is plain double buffering; NS = 5 fills the
+// 160 KiB of a CU and keeps one and a half stages of copies in flight.
+//
+// Schedule of stage s (barrier B_s sits between slabs 2 and 3):
+//   slab 0: read slab 1 fragments; copy half-stage 2s + NS - 1
+//   slab 1: read slab 2 fragments
+//   slab 2: read slab 3 fragments
+//   wait for this wave's reads and for its copies of stage s+1; B_s
+//   (stage s+1 is published, and every wave is done reading stage s)
+//   slab 3: read slab 0 of stage s+1; copy half-stage 2s + NS into the slot
+//   stage s's A half just left
+// A slot is refilled only after the barrier that ends the reads of the
+// half-stage NS places earlier, which the two copy points respect.
+//
+// Knobs: GM tile-order group; RS = the MFMAs of a slab over which its 8
+// fragment reads are spread; ADDR 0 = 64-bit per-lane addresses, 1 = buffer
+// resources with 32-bit offsets; SCHED 0 = copies in bursts in slabs 0 and 3,
+// 1 = one copy every 4 MFMAs over the whole stage (5 slots); EPI bit 0 =
+// nontemporal D stores (D lines then do not displace operand panels in L2,
+// measured ~2 % faster main loop when D columns start on 128-byte lines; when
+// they do not, the partial lines at the tile edges make them about 20 %
+// slower on the whole product, and the twins without the bit are used), bit 1 =
+// fp32 D through an LDS transpose so each store writes a whole 1 KiB row run
+// (no faster for line-aligned D, where the write burst at the end of a tile
+// is bound by memory bandwidth either way; 2.5 % faster when D columns are
+// only 4-byte aligned, so the plain-store twins carry it), bit 2 =
+// the same for bf16/fp16 D, whose direct stores would write 64-byte halves of
+// lines; bit 3 = the instance also carries the softmax epilogue (kept out of
+// the plain instances, whose epilogue it would bloat); bit 4 = interior tiles
+// transpose 4 x 4 register groups across lane quads and store 4 consecutive m
+// per lane as one 8-byte vector for 16-bit D (measured: the bf16-D epilogue
+// drops from about 31k to 21k cycles against the LDS transpose; the same for
+// fp32 D as 16-byte vectors measured slower than direct stores, since fp32 D
+// is bound by the write burst and the shuffles add VALU work), bit 6 =
+// 8-bit operands with block scales (their loads sit in the main loop, and the
+// waits the compiler puts before their use also wait for copies, so the
+// instances without scales do not carry them).
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
+    select_batch(p);
+    constexpr int BM = 256, BN = 256, WM = 2;
+    constexpr bool F8 = (DT == TG_E4M3 || DT == TG_E5M2);
+    constexpr int ES = (DT == TG_F32) ? 4 : F8 ? 1 : 2;
+    constexpr int EPC = 16 / ES;
+    constexpr int BKE = kRowBytes / ES;          // K elements per stage
+    constexpr int WTM = 128, WTN = 128;          // output owned by one wave
+    constexpr int FM = WTM / 32, FN = WTN / 32;  // 32 x 32 MFMA blocks per wave
+    constexpr int NC = BM / (8 * 4);             // 1 KiB copies per wave per half-stage
+    constexpr int NR = FM + FN;                  // fragment reads per slab
+    constexpr int MF = FM * FN;                  // MFMAs per slab
+    constexpr int SLOT = BM * kRowBytes;         // 32 KiB
+    static_assert(BM == BN && NC == 8 && MF == 16, "schedule assumes 8 copies per half-stage, 16 MFMAs a slab");
+    static_assert(NS == 4 || NS == 5, "4 or 5 half-stage slots");
+    static_assert(SCHED == 0 || NS == 5, "the spread copy schedule needs 5 slots");
+    static_assert(RS >= 1 && RS <= MF, "reads spread over at most one slab");
+
+    __shared__ __attribute__((aligned(1024))) char smem[NS * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave % WM, wave_n = wave / WM;
+
+    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
+    const int m0 = tile.tm * BM, n0 = tile.tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const unsigned lds_base = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
+
+    // copy sources.  ADDR 0: 64-bit addresses, rows past M or N clamp to
+    // the last row.  ADDR 1: buffer resources over the tile's valid rows, 32-bit
+    // row offsets (the plan keeps 256 * stride below 2^31); rows past M or N
+    // fall outside the range and load zeros.  Either way those rows only feed
+    // accumulators that are never stored.
+    const char* src[2][NC];
+    unsigned voff[2][NC];
+    i32x4 rsrc[2];
+    if constexpr (ADDR == 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int j = wave * NC + i;
+            src[0][i] = p.A + static_cast<int64_t>(min(m0 + dma128_row(j, lane), M - 1)) * p.lda_b +
+                        dma128_chunk(j, lane) * kChunkBytes;
+            src[1][i] = p.B + static_cast<int64_t>(min(n0 + dma128_row(j, lane), N - 1)) * p.ldb_b +
+                        dma128_chunk(j, lane) * kChunkBytes;
+        }
+    } else {
+        rsrc[0] = buffer_rsrc(p.A + static_cast<int64_t>(m0) * p.lda_b,
+                              static_cast<unsigned>(min(BM, M - m0) * p.lda_b));
+        rsrc[1] = buffer_rsrc(p.B + static_cast<int64_t>(n0) * p.ldb_b,
+                              static_cast<unsigned>(min(BN, N - n0) * p.ldb_b));
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int j = wave * NC + i;
+            voff[0][i] = static_cast<unsigned>(dma128_row(j, lane) * p.lda_b) + dma128_chunk(j, lane) * kChunkBytes;
+            voff[1][i] = static_cast<unsigned>(dma128_row(j, lane) * p.ldb_b) + dma128_chunk(j, lane) * kChunkBytes;
+        }
+    }
+    // copy i of operand o (0: A, 1: B) of stage t into slot `slot`
+    auto copy = [&](int o, int i, int t, int slot) {
+        const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + i) * 1024);
+        if constexpr (ADDR == 0)
+            dma16(src[o][i] + static_cast<int64_t>(t) * kRowBytes, dst);
+        else
+            dma16_buf(rsrc[o], voff[o][i], __builtin_amdgcn_readfirstlane(t * kRowBytes), dst);
+    };
+    auto wrap = [](int x) { return x >= NS ? x - NS : x; };
+
+    // fragment read offsets within a slot (block steps are 32 rows, which
+    // keep the swizzle)
+    int mread[4], nread[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        mread[q] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+        nread[q] = wave_n * WTN * kRowBytes + lds_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+    }
+    // read r of slab q from slots (sa, sb); m-side and n-side fragments alternate
+    auto read = [&](int r, int q, int sa, int sb, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
+        const int blk = r >> 1;
+        if ((r & 1) == 0)
+            fa[blk] = *reinterpret_cast<const u32x4*>(smem + sa * SLOT + mread[q] + blk * 32 * kRowBytes);
+        else
+            fb[blk] = *reinterpret_cast<const u32x4*>(smem + sb * SLOT + nread[q] + blk * 32 * kRowBytes);
+    };
+    // the NR fragment reads of a slab go out after the first RS of its MFMAs
+    auto reads_at = [&](int m, auto&& f) {
+        if (m < RS) {
+#pragma unroll
+            for (int k = (m * NR + RS - 1) / RS; k < ((m + 1) * NR + RS - 1) / RS; ++k) f(k);
+        }
+    };
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nfull = K / BKE;
+    if constexpr (F8) {
+        // 8-bit operands: a stage (128 k) is two 32x32x64 MFMAs per block.
+        // The fragments of slabs 2p and 2p + 1 (chunks 4p + h and 4p + 2 + h
+        // of half-wave h) together feed MFMA pair p; pair 0 runs while slabs
+        // 2 and 3 are read and the copies of slabs 0-2 of the 16-bit schedule
+        // go out (12), pair 1 after the barrier while slabs 0 and 1 of the
+        // next stage are read and the last 4 copies go out, so the copy
+        // order and the wait counts are those of the 16-bit schedule.  Block
+        // scales (when given) come from the lane's rows, as in the
+        // register-staged kernel.
+        static_assert(SCHED == 1 && NS == 5, "the 8-bit schedule follows the spread copy schedule");
+        constexpr bool SC = (EPI & 64) != 0;  // the instance applies block scales
+        const int nk = nfull + ((K % BKE) != 0 ? 1 : 0);  // stages including a ragged one
+        u32x4 g[4][FM], h[4][FN];
+        // block scales of the lane's rows for the stage being consumed: one
+        // dword per row (the stage's four 32-k blocks), loaded at the end of
+        // the previous stage, after its copies, so that the waits the
+        // compiler puts in front of their first use only also cover copies
+        // issued a stage earlier
+        unsigned scm[FM], scn[FN];
+        const int nblk = (K + 31) / 32;
+        // scale loads through buffer resources over the tile's scale rows:
+        // 32-bit per-lane offsets and the rest in SGPRs, which keeps the loop
+        // free of spills (a spill reload waits for every copy in flight).
+        // Rows past M or N fall outside the range and read 0, i.e. a tiny
+        // scale on rows whose data loads as zeros.
+        // (an absent operand gets an empty range and is never loaded)
+        const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+            p.scale_a ? const_cast<unsigned char*>(p.scale_a + static_cast<int64_t>(m0) * p.lds_a) : p.D,
+            static_cast<short>(0), p.scale_a ? static_cast<int>(static_cast<unsigned>(min(BM, M - m0) * p.lds_a)) : 0,
+            0x00020000);
+        const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+            p.scale_b ? const_cast<unsigned char*>(p.scale_b + static_cast<int64_t>(n0) * p.lds_b) : p.D,
+            static_cast<short>(0), p.scale_b ? static_cast<int>(static_cast<unsigned>(min(BN, N - n0) * p.lds_b)) : 0,
+            0x00020000);
+        // the whole row offset sits in the per-lane offset, which is what the
+        // range check looks at (the scalar offset only carries the stage)
+        unsigned vo_a[FM], vo_b[FN];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) vo_a[j] = static_cast<unsigned>((wave_m * WTM + 32 * j + frag_row(lane)) * p.lds_a);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) vo_b[i] = static_cast<unsigned>((wave_n * WTN + 32 * i + frag_row(lane)) * p.lds_b);
+        auto load_scales = [&](int t) {
+            if constexpr (!SC) return;
+            if (p.scale_a) {
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    scm[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_a, static_cast<int>(vo_a[j]), 4 * t, 0);
+            } else {
+#pragma unroll
+                for (int j = 0; j < FM; ++j) scm[j] = 0x7F7F7F7Fu;
+            }
+            if (p.scale_b) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+                    scn[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, static_cast<int>(vo_b[i]), 4 * t, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) scn[i] = 0x7F7F7F7Fu;
+            }
+        };
+        // pair pp of stage t; scale blocks past the last one of K count as 1
+        auto pair = [&](int pp, int t, auto&& side) {
+            const int sub = 2 * pp + (lane >> 5);
+            const bool live = 4 * t + sub < nblk;
+            (void)live;
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                const int i = m / FM, j = m % FM;
+                const u32x4 nn[2] = {h[2 * pp][i], h[2 * pp + 1][i]};
+                const u32x4 mm[2] = {g[2 * pp][j], g[2 * pp + 1][j]};
+                if constexpr (SC) {
+                    const int sn = live ? static_cast<int>((scn[i] >> (8 * sub)) & 0xFFu) : 127;
+                    const int sm = live ? static_cast<int>((scm[j] >> (8 * sub)) & 0xFFu) : 127;
+                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], sn, sm);
+                } else {
+                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], 127, 127);
+                }
+                side(m);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (nfull > 0) {
+            constexpr int PRO = 3 * NC + NC / 2;  // prologue copies, as in the 16-bit schedule
+#pragma unroll
+            for (int c = 0; c < PRO; ++c) {
+                const int hs = c / NC;
+                copy(hs & 1, c % NC, min(hs >> 1, nfull - 1), hs);
+            }
+            wait_vm<PRO - 2 * NC>();
+            barrier();
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                read(r, 0, 0, 1, g[0], h[0]);
+                read(r, 1, 0, 1, g[1], h[1]);
+            }
+            load_scales(0);
+            int slot0 = 0;
+            for (int s = 0; s < nfull; ++s) {
+                const int sa = slot0, sb = wrap(slot0 + 1);
+                const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
+                const int slot_h0 = wrap(slot0 + NS - 1);
+                const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
+                pair(0, s, [&](int m) {
+                    if (m < NR) read(m, 2, sa, sb, g[2], h[2]); else read(m - NR, 3, sa, sb, g[3], h[3]);
+                    if ((m & 3) != 3) {
+                        const int c = m - (m >> 2);  // 0 .. 11
+                        if (c < 4) copy(1, NC / 2 + c, t1, nb);
+                        else if (c < 8) copy(0, c - 4, t2, slot_h0);
+                        else copy(0, NC / 2 + c - 8, t2, slot_h0);
+                    }
+                });
+                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+                wait_vm<(NS - 4) * NC>();
+                barrier();
+                // on the last stage the reads below fetch values that go unused
+                pair(1, s, [&](int m) {
+                    if (m < NR) read(m, 0, na, nb, g[0], h[0]); else read(m - NR, 1, na, nb, g[1], h[1]);
+                    if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
+                });
+                if (s + 1 < nk) load_scales(s + 1);
+                slot0 = na;
+            }
+            wait_vm<0>();  // no copy outlives the loop
+        }
+        if (K % BKE != 0) {
+            // ragged last stage through registers into slots 0 (A) and 1 (B)
+            __syncthreads();
+            const int c = stage_chunk(tid);
+            const int k0 = nfull * BKE + c * EPC;
+#pragma unroll
+            for (int i = 0; i < BM / 32; ++i) {
+                const int r = stage_row(tid, i);
+                const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+                const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) =
+                    load_chunk_bounded<ES>(brow, k0, K);
+            }
+            if (nfull == 0) load_scales(0);  // otherwise loaded at the end of the last full stage
+            __syncthreads();
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    read(r, 2 * pp, 0, 1, g[2 * pp], h[2 * pp]);
+                    read(r, 2 * pp + 1, 0, 1, g[2 * pp + 1], h[2 * pp + 1]);
+                }
+                pair(pp, nfull, [](int) {});
+            }
+        }
+    } else {
+        u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+        if (nfull > 0) {
+            // prologue: half-stages 0 .. NS-2 (a stage index past the last full
+            // stage reloads that stage, so the copy counts stay uniform)
+            constexpr int PRO = (SCHED == 0) ? (NS - 1) * NC : 3 * NC + NC / 2;  // prologue copies
+    #pragma unroll
+            for (int c = 0; c < PRO; ++c) {
+                const int h = c / NC;
+                copy(h & 1, c % NC, min(h >> 1, nfull - 1), h);
+            }
+            wait_vm<PRO - 2 * NC>();
+            barrier();
+    #pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
+
+            constexpr int H0 = NS - 1;                 // half-stage copied in slab 0, minus 2s
+            int slot0 = 0;                             // slot of stage s's A half, (2s) % NS
+            for (int s = 0; s < nfull; ++s) {
+                const int sa = slot0, sb = wrap(slot0 + 1);
+                const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
+                const int t0 = min(s + (H0 >> 1), nfull - 1);       // stage of half-stage 2s + H0
+                const int t3 = min(s + ((H0 + 1) >> 1), nfull - 1); // stage of half-stage 2s + H0 + 1
+                const int slot_h0 = wrap(slot0 + NS - 1);
+                // SCHED 1 (5 slots): one copy every 4 MFMAs through the whole stage --
+                // the second half of B(s+1) in slab 0, A(s+2) in slabs 1-2 and the
+                // first half of B(s+2) in slab 3 -- instead of bursts in slabs 0 and 3
+                const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
+                slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
+                    if constexpr (SCHED == 0) {
+                        if (m & 1) copy(H0 & 1, m >> 1, t0, slot_h0);
+                    } else {
+                        if ((m & 3) == 1) copy(1, NC / 2 + (m >> 2), t1, nb);
+                    }
+                });
+                slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); });
+                    if constexpr (SCHED == 1) {
+                        if ((m & 3) == 1) copy(0, m >> 2, t2, slot_h0);
+                    }
+                });
+                slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); });
+                    if constexpr (SCHED == 1) {
+                        if ((m & 3) == 1) copy(0, NC / 2 + (m >> 2), t2, slot_h0);
+                    }
+                });
+                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+                wait_vm<(NS - 4) * NC>();
+                barrier();
+                // on the last stage the reads below fetch values that go unused
+                slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
+                    if constexpr (SCHED == 0) {
+                        if (m & 1) copy((H0 + 1) & 1, m >> 1, t3, sa);
+                    } else {
+                        if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
+                    }
+                });
+                slot0 = na;
+            }
+            wait_vm<0>();  // no copy outlives the loop
+        }
+
+        if (K % BKE != 0) {
+            // ragged last stage through registers into slots 0 (A) and 1 (B);
+            // k >= K become exact zeros
+            __syncthreads();
+            const int c = stage_chunk(tid);
+            const int k0 = nfull * BKE + c * EPC;
+    #pragma unroll
+            for (int i = 0; i < BM / 32; ++i) {
+                const int r = stage_row(tid, i);
+                const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+                const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+            }
+            __syncthreads();
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
+    #pragma unroll
+                for (int i = 0; i < FN; ++i)
+    #pragma unroll
+                    for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+            }
+        }
+    }
+
+    if constexpr ((EPI & 8) != 0) {
+        if (p.epi == TG_EPI_SOFTMAX) {  // the plan makes one tile span all of N
+            softmax_epilogue<BM, WTM, WTN, FM, FN>(acc, p, m0, wave_m, wave_n, lane, smem);
+            return;
+        }
+    }
+
+    // epilogue: alpha, then ReLU, in registers
+    const float alpha = p.alpha;
+    const bool relu = p.relu != 0;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = acc[i][j][r] * alpha;
+                acc[i][j][r] = relu ? fmaxf(v, 0.0f) : v;
+            }
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
+    const bool trans32 = (EPI & 2) && p.out_dtype == TG_F32 && interior;
+    const bool trans16 = (EPI & 4) && p.out_dtype != TG_F32 && interior && aligned16 && (p.ldd & 7) == 0;
+    const bool quad = (EPI & 16) && p.out_dtype != TG_F32 && interior && (p.ldd & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.D) & 7u) == 0;
+    if (quad) {
+        // Interior tile, 16-bit D: transpose each 4 x 4 group (4 lanes of a
+        // quad = 4 consecutive m, 4 registers = 4 consecutive n) in registers
+        // with two DPP butterfly steps, so each lane holds 4 consecutive m of
+        // one n and stores them as one 8-byte vector: a quarter of the store
+        // instructions, each writing whole 64-byte row pieces.
+        const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+        auto dpp = [](float v, int ctrl_is_pair) {
+            const int x = __builtin_bit_cast(int, v);
+            return __builtin_bit_cast(float, ctrl_is_pair ? __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true)
+                                                          : __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+        };
+        const int64_t ldd = p.ldd;
+        const int64_t lane_off = static_cast<int64_t>(n0 + wave_n * WTN + 4 * (lane >> 5) + (lane & 3)) * ldd +
+                                 (m0 + wave_m * WTM + 4 * ((lane & 31) >> 2));
+        with_out_type(p.out_dtype, [&](auto out) {
+            constexpr int OUT = decltype(out)::value;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float x[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+#pragma unroll
+                        for (int q = 0; q < 4; q += 2) {  // swap within lane pairs
+                            const float r = dpp(b0 ? x[q] : x[q + 1], 1);
+                            x[q] = b0 ? r : x[q];
+                            x[q + 1] = b0 ? x[q + 1] : r;
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {  // swap between lane pairs
+                            const float r = dpp(b1 ? x[q] : x[q + 2], 0);
+                            x[q] = b1 ? r : x[q];
+                            x[q + 2] = b1 ? x[q + 2] : r;
+                        }
+                        const int64_t idx = lane_off + (32 * i + 8 * g) * ldd + 32 * j;
+                        if constexpr (OUT != TG_F32) {
+                            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                            u32x2 v;
+                            if constexpr (OUT == TG_BF16) {
+                                v.x = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2));
+                                v.y = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2));
+                            } else {
+                                v.x = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[0], x[1]}, f16x2));
+                                v.y = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[2], x[3]}, f16x2));
+                            }
+                            u32x2* d = reinterpret_cast<u32x2*>(static_cast<unsigned short*>(p.D) + idx);
+                            if constexpr (EPI & 1) __builtin_nontemporal_store(v, d); else *d = v;
+                        }
+                    }
+        });
+    } else if (!trans32 && !trans16) {
+        // store by ownership: each instruction writes 2 x 32 consecutive m.
+        // Interior tiles store without per-element checks; the row offsets
+        // of a block's 16 registers are wave-uniform multiples of ldd.
+        with_out_type(p.out_dtype, [&](auto out) {
+            constexpr int OUT = decltype(out)::value;
+            const int64_t ldd = p.ldd;
+            const int64_t lane_off = static_cast<int64_t>(n0 + wave_n * WTN + acc_row(lane, 0)) * ldd +
+                                     (m0 + wave_m * WTM + acc_col(lane));
+            if (interior) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            store_out<OUT, (EPI & 1) != 0>(
+                                p.D, lane_off + (32 * i + 8 * (r >> 2) + (r & 3)) * ldd + 32 * j, acc[i][j][r]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        const int m = m0 + wave_m * WTM + 32 * j + acc_col(lane);
+                        const int nbase = n0 + wave_n * WTN + 32 * i;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int n = nbase + acc_row(lane, r);
+                            if (m < M && n < N)
+                                store_out<OUT, (EPI & 1) != 0>(p.D, static_cast<int64_t>(n) * ldd + m, acc[i][j][r]);
+                        }
+                    }
+                }
+            }
+        });
+    } else if (trans16) {
+        // 16-bit D, interior tile, 16-byte aligned rows: the whole rounded
+        // tile (256 x 256 x 2 bytes) goes through LDS in one pass and each
+        // store instruction writes two whole 512-byte row runs, instead of
+        // 64-byte pieces of lines that other instructions complete later.
+        constexpr int PITCH16 = 528;
+        static_assert((EPI & 4) == 0 || 256 * PITCH16 <= NS * SLOT, "16-bit tile fits the ring");
+        __syncthreads();  // every wave is done with the ring
+        with_out_type(p.out_dtype, [&](auto out) {
+            constexpr int OUT = decltype(out)::value;
+            if constexpr (OUT != TG_F32) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int nl = wave_n * WTN + 32 * i + acc_row(lane, r);
+                            const int ml = wave_m * WTM + 32 * j + acc_col(lane);
+                            const float v = acc[i][j][r];
+                            unsigned short h;
+                            if constexpr (OUT == TG_BF16)
+                                h = bf16_rne(v);
+                            else
+                                h = __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+                            *reinterpret_cast<unsigned short*>(smem + nl * PITCH16 + ml * 2) = h;
+                        }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 32; ++q) {
+                    const int nl = 64 * wave + 2 * q + (lane >> 5);
+                    const int c = lane & 31;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + nl * PITCH16 + c * 16);
+                    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<unsigned short*>(p.D) +
+                                                          static_cast<int64_t>(n0 + nl) * p.ldd + m0) + c;
+                    if constexpr (EPI & 1)
+                        __builtin_nontemporal_store(v, dst);
+                    else
+                        *dst = v;
+                }
+            }
+        });
+    } else {
+        // interior tile: transpose through LDS so that each store instruction
+        // writes one whole 1 KiB row run of the tile (256 consecutive m).
+        // With line-aligned D columns this is no faster than the direct
+        // stores; with columns only 4-byte aligned (odd ldd) it touches 9
+        // lines per run instead of two lines per 128-byte piece and measured
+        // 2.5 % faster on the whole product.  The 16-byte stores only assume
+        // 4-byte alignment.  Two passes of 128 rows (n); the row pitch of
+        // 1056 bytes keeps the two half-waves of each LDS write on disjoint
+        // banks.
+        constexpr int PITCH = 1056;
+        static_assert(EPI < 2 || 128 * PITCH <= NS * SLOT, "transpose buffer fits the ring");
+        __syncthreads();  // every wave is done with the ring
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if (wave_n == pass) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int nl = 32 * i + acc_row(lane, r);
+                            const int ml = wave_m * WTM + 32 * j + acc_col(lane);
+                            *reinterpret_cast<float*>(smem + nl * PITCH + ml * 4) = acc[i][j][r];
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                const int nl = 32 * wave + q;
+                typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+                const f32x4_a4 v = *reinterpret_cast<const f32x4*>(smem + nl * PITCH + lane * 16);
+                f32x4_a4* dst = reinterpret_cast<f32x4_a4*>(static_cast<float*>(p.D) +
+                                                            static_cast<int64_t>(n0 + 128 * pass + nl) * p.ldd +
+                                                            m0) + lane;
+                if constexpr (EPI & 1)
+                    __builtin_nontemporal_store(v, dst);
+                else
+                    *dst = v;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
+static hipError_t launch_wide(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>),
+                       dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace tg
+
+// Instance rows of the wide kernel: (id, dtype, group_m, slots NS, read spread
+// RS, ADDR, SCHED, EPI, eff%).  eff% weighs the instance's tiles in the host
+// plan chooser.  ADDR 1 instances address a tile through 32-bit byte offsets,
+// so they take operand row strides up to 8 MiB (256 rows x stride < 2^31); the
+// ADDR 0 twins cover longer rows.
+#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF) \
+    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>(GemmArgs);
+
+#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                             \
+    {id, DT, 256, 256, 128 / TG_ELEM_BYTES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,  \
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, ((EPI) & 8) ? 1 : 0, \
+     (EPI) & 1, ((EPI) & 64) ? 1 : 0},

@@ -70,6 +70,21 @@ struct TgKernelDesc {
     int block_scales;        // 1: 8-bit instance that applies block scales (GemmArgs::scale_a/b)
 };
 
-// Indexed by kernel id.
-extern "C" const TgKernelDesc* const tg_kernel_table;
-extern "C" const int tg_kernel_table_size;
+// Element bytes of an operand type.
+#define TG_ELEM_BYTES(DT) ((DT) == TG_F32 ? 4 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 1 : 2)
+
+// The instances each kernel translation unit contributes (host pass only).
+extern const TgKernelDesc tg_entries_wide16[];
+extern const int tg_entries_wide16_count;
+extern const TgKernelDesc tg_entries_wide32[];
+extern const int tg_entries_wide32_count;
+extern const TgKernelDesc tg_entries_wide8[];
+extern const int tg_entries_wide8_count;
+extern const TgKernelDesc tg_entries_stream[];
+extern const int tg_entries_stream_count;
+extern const TgKernelDesc tg_entries_rs[];
+extern const int tg_entries_rs_count;
+
+// The instance table, indexed by kernel id (ids are 0 .. tg_kernel_count()-1).
+int tg_kernel_count();
+const TgKernelDesc& tg_kernel(int id);

@@ -28,22 +28,26 @@
  * multiple of the tile shape").
  *
  * Ownership: A, B and D are device pointers owned by the caller and only
- * borrowed for the duration of the enqueued kernels.  The library keeps no
- * pointer of the caller's after the call returns and does not synchronise:
- * the kernels are enqueued on `stream` (a hipStream_t; NULL means the default
- * stream) and the call returns after the enqueue.  D must not overlap A or B.
- * Calls are thread-safe.
+ * borrowed for the duration of the enqueued kernels (Tylo.jl manual, "Walk
+ * through GEMM", section 2: the kernel's views borrow storage the caller
+ * owns).  The library allocates no device memory, never synchronises a
+ * stream or the device, and keeps no pointer of the caller's after the call
+ * returns: the kernels are enqueued on `stream` (a hipStream_t; NULL means
+ * the default stream) and the call returns after the enqueue (section 4:
+ * no hidden allocation).  Scratch space, where an entry point needs it
+ * (split-K partial products, staged operand copies), is a workspace the
+ * caller passes in.  D must not overlap A or B.  The library's only shared
+ * state is an immutable instance table and a per-device architecture check,
+ * so calls from several host threads may run concurrently; work enqueued on
+ * one stream runs in the order of the calls.
  *
  * Alignment: pointers must be aligned to their element size.  Nothing
  * stronger is required.  When the operand rows are not all 16-byte aligned
- * (odd lda/ldb, offset views), the automatic plan of a single product either
- * runs a kernel with a narrower load path or, for large products, first
- * copies A and B into 16-byte aligned rows padded with zeros to a whole
- * number of 128-byte K stages (the staged plan, see tile_gemm_staged).  Only
- * then does the library hold device memory of its own: one staging buffer per
- * (device, stream), grown on demand, kept until tile_gemm_release_staging (the
- * first call that grows it synchronises that stream).  Under stream capture
- * the library allocates nothing and runs the direct plan instead.
+ * (odd lda/ldb, offset views), the plan takes a kernel whose loads need only
+ * 4- or 2-byte aligned rows (Tylo.jl manual, "Walk through GEMM", section 3:
+ * the caller establishes the alignment and the plan must respect it);
+ * tile_gemm_staged can instead copy the operands into aligned rows in a
+ * caller workspace first.
  *
  * Errors: every entry point returns 0 on success or one of the negative
  * tile_gemm_status codes below; no exception or abort crosses the ABI.
@@ -100,7 +104,7 @@ typedef struct tile_gemm_plan_info {
     int32_t acc_per_lane;  /* fp32 accumulators held by each lane */
     int32_t load_class;    /* 16, 4 or 2: byte alignment of every operand row start */
     int32_t group_m;       /* tile-rows per group in the grouped tile order */
-    int32_t staged;        /* 1: A and B are first copied into aligned staging rows */
+    int32_t staged;        /* always 0 for a query (tile_gemm_staged decides per call) */
     int64_t tiles_m;       /* ceil(M / block_m) */
     int64_t tiles_n;       /* ceil(N / block_n) */
     int64_t grid;          /* workgroups launched = tiles_m * tiles_n */
@@ -208,6 +212,33 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
                       void* stream, int kernel_id);
 
 /*
+ * 8-bit operands (TG_E4M3, TG_E5M2) with optional block scales: every 32
+ * consecutive k of an A row (and of a B column) share one unsigned 8-bit
+ * exponent e, and the elements of that block stand for their decoded value
+ * times 2^(e - 127) (e = 255: NaN).  The pages name block-scaled 8-bit
+ * matmuls (cuTile.jl tutorial "Matrix Multiplication", "Where to go from
+ * here") without defining them; this is the plain reading of the MX
+ * formats, and the product then is
+ *
+ *     d[m,n] = epilogue(alpha * sum_k a[m,k]*sa[m,k/32] * b[k,n]*sb[n,k/32])
+ *
+ * accumulated in fp32 on the 8-bit MFMA (which applies the scales itself).
+ * Scale of A row m, block j: byte scale_a[m*lds_a + j]; of B column n:
+ * scale_b[n*lds_b + j].  lds_a, lds_b >= 4*ceil(K/128) and multiples of 4,
+ * scale pointers 4-byte aligned (TG_ERR_LD / TG_ERR_ALIGN): the kernel reads
+ * the four scales of each 128-k stage as one dword; scales of blocks past
+ * ceil(K/32) are read but ignored.  Either pointer may be NULL (no scale on
+ * that side); scales with 16-bit or fp32 operands give TG_ERR_DTYPE; the
+ * scales must not overlap D (TG_ERR_ALIAS).  kernel_id as tile_gemm_ex
+ * (only instances that apply block scales accept scales; others give
+ * TG_ERR_PLAN).  Other rules as tile_gemm_out.
+ */
+int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                     const void* A, int64_t lda, const void* scale_a, int64_t lds_a,
+                     const void* B, int64_t ldb, const void* scale_b, int64_t lds_b,
+                     void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id);
+
+/*
  * A single product on staged operand copies: a first launch copies the M rows
  * of A and the N rows of B into `workspace`, each row starting 16-byte aligned
  * and holding K rounded up to a whole 128-byte K stage (64 bf16/fp16 or 32
@@ -229,38 +260,8 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
  * device memory owned by the caller, not overlapping A, B or D
  * (TG_ERR_ALIAS), reusable once the stream has passed the call.  M, N or K
  * = 0 never stages.  Other rules and errors as tile_gemm_out with kernel_id
- * -1; tile_gemm, tile_gemm_ex and tile_gemm_out with kernel_id -1 behave as
- * mode -1 with the library's own staging buffer.
+ * -1.
  */
-/*
- * 8-bit operands (TG_E4M3, TG_E5M2) with optional block scales: every 32
- * consecutive k of an A row (and of a B column) share one unsigned 8-bit
- * exponent e, and the elements of that block stand for their decoded value
- * times 2^(e - 127) (e = 255: NaN).  The pages name block-scaled 8-bit
- * matmuls (cuTile.jl tutorial "Matrix Multiplication", "Where to go from
- * here") without defining them; this is the plain reading of the MX
- * formats, and the product then is
- *
- *     d[m,n] = epilogue(alpha * sum_k a[m,k]*sa[m,k/32] * b[k,n]*sb[n,k/32])
- *
- * accumulated in fp32 on the 8-bit MFMA (which applies the scales itself).
- * Scale of A row m, block j: byte scale_a[m*lds_a + j]; of B column n:
- * scale_b[n*lds_b + j].  lds_a, lds_b >= 4*ceil(K/128) and multiples of 4,
- * scale pointers 4-byte aligned (TG_ERR_LD / TG_ERR_ALIGN): the kernel reads
- * the four scales of each 128-k stage as one dword; scales of blocks past
- * ceil(K/32) are read but ignored.  Either pointer may be NULL (no scale on
- * that side); scales with 16-bit or fp32 operands give TG_ERR_DTYPE; the
- * scales must not overlap D (TG_ERR_ALIAS).  kernel_id as tile_gemm_ex
- * (only instances that apply block scales accept scales; others give
- * TG_ERR_PLAN).  With kernel_id -1, large products whose operand rows are not
- * 16-byte aligned are staged as by tile_gemm (library staging buffer; the
- * scales are read in place).  Other rules as tile_gemm_out.
- */
-int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
-                     const void* A, int64_t lda, const void* scale_a, int64_t lds_a,
-                     const void* B, int64_t ldb, const void* scale_b, int64_t lds_b,
-                     void* D, int64_t ldd, int dtype, int out_dtype, void* stream, int kernel_id);
-
 int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      const void* A, int64_t lda, const void* B, int64_t ldb,
                      void* D, int64_t ldd, int dtype, int out_dtype,
@@ -270,11 +271,6 @@ int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
  * is 0; -1 for an unknown dtype or sizes out of range). */
 int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype);
 
-/* Free the library's staging buffers on every device (waits for the work
- * that still reads them).  Returns TG_OK or TG_ERR_LAUNCH if a free failed.
- * Later calls allocate again when they stage. */
-int tile_gemm_release_staging(void);
-
 /* Workspace a split-K call needs: splits * M * N * 4 bytes (0 for splits = 1
  * or an empty output; splits = 0: enough for any automatic choice, i.e. 64
  * splits; -1 for negative or oversized arguments). */
@@ -283,17 +279,16 @@ int64_t tile_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
 /*
  * Host-only: validate the arguments exactly as tile_gemm does and describe the
  * plan it would launch (no HIP call is made; pointers are only inspected for
- * alignment and overlap).  kernel_id -1 = automatic choice; when that choice
- * stages the operands (staged = 1), the plan describes the product on the
- * staged copies (load_class 16, K rounded up to whole stages).
+ * alignment and overlap).  For tests and tuning.
  */
 int tile_gemm_query_plan(int64_t M, int64_t N, int64_t K, int dtype,
                          const void* A, int64_t lda, const void* B, int64_t ldb,
-                         const float* D, int64_t ldd, int kernel_id,
-                         tile_gemm_plan_info* out);
+                         const float* D, int64_t ldd, tile_gemm_plan_info* out);
 
 /* Host-only: as tile_gemm_query_plan, for a tile_gemm_out call with D of
- * element type out_dtype (the plan itself does not depend on out_dtype). */
+ * element type out_dtype and an explicit kernel instance (kernel_id -1 = the
+ * automatic choice; TG_ERR_PLAN as for tile_gemm_ex).  The plan does not
+ * depend on out_dtype except through the D line alignment it weighs. */
 int tile_gemm_query_plan_out(int64_t M, int64_t N, int64_t K, int dtype,
                              const void* A, int64_t lda, const void* B, int64_t ldb,
                              const void* D, int64_t ldd, int out_dtype, int kernel_id,
@@ -307,6 +302,32 @@ int tile_gemm_query_plan_batched(int64_t M, int64_t N, int64_t K, int dtype,
                                  const void* D, int64_t ldd, int64_t stride_d, int64_t batch,
                                  int out_dtype, int kernel_id, tile_gemm_plan_info* out);
 
+/* Host-only: the plan of a tile_gemm_softmax call after the same validation:
+ * the fused instance (grid = tiles along m; one tile spans N), or kernel_id
+ * -1 when the call runs as two launches (the fp32 logits, then the row pass). */
+int tile_gemm_query_plan_softmax(int64_t M, int64_t N, int64_t K, int dtype,
+                                 const void* A, int64_t lda, const void* B, int64_t ldb,
+                                 const void* D, int64_t ldd, int out_dtype, int kernel_id,
+                                 tile_gemm_plan_info* out);
+
+/* Host-only: the plan of a tile_gemm_scaled call after the same validation
+ * (with scales, the instance that applies them). */
+int tile_gemm_query_plan_scaled(int64_t M, int64_t N, int64_t K, int dtype,
+                                const void* A, int64_t lda, const void* scale_a, int64_t lds_a,
+                                const void* B, int64_t ldb, const void* scale_b, int64_t lds_b,
+                                const void* D, int64_t ldd, int out_dtype, int kernel_id,
+                                tile_gemm_plan_info* out);
+
+/* Host-only: the plan of a tile_gemm_staged call after the same validation:
+ * staged = 1 and the product on the staged copies (load_class 16, the instance
+ * chosen for rows of the rounded-up K) when the copy runs, else the direct
+ * plan. */
+int tile_gemm_query_plan_staged(int64_t M, int64_t N, int64_t K, int dtype,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                const void* D, int64_t ldd, int out_dtype,
+                                const void* workspace, int64_t workspace_bytes, int mode,
+                                tile_gemm_plan_info* out);
+
 /* Number of compiled kernel instances (valid kernel ids are 0 .. count-1). */
 int tile_gemm_kernel_count(void);
 
@@ -319,7 +340,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 7
+#define TILE_GEMM_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

@@ -101,13 +101,31 @@ def _load():
     return _lib
 
 
-def default_threads() -> int:
-    """Host threads the oracle uses: the process's CPU share, at most 16."""
+def affinity_cores() -> int:
+    """Cores in the process's CPU affinity mask."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def cpu_quota() -> float | None:
+    """CPUs the process's cgroup grants (cpu.max quota / period), or None."""
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        return None if quota == "max" else int(quota) / int(period)
+    except (OSError, ValueError):
+        return None
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: one per core of the affinity mask, no
+    more than the cgroup's CPU quota grants."""
+    n = affinity_cores()
+    q = cpu_quota()
+    if q is not None:
+        n = min(n, max(1, int(q)))
+    return max(1, n)
 
 
 def _code(dtype) -> int:

@@ -173,22 +173,33 @@ def test_block_scaled_workload_sampled():
     _log(f"[fp8 scaled workload] {w.name}: {ms.size} sampled entries, worst ratio {r:.3g}")
 
 
-def test_block_scaled_misaligned_rows_are_staged():
-    """A large block-scaled product with 1-byte aligned rows: the automatic
-    plan stages the operands (the scales stay in place) and must match the
-    oracle on sampled entries, as must the direct register-staged instance."""
-    M = N = K = 4096
-    A_st, B_st = si.operands(M, N, K, "e4m3", "uniform_pm1", 41, 42, lda=K + 1, ldb=K + 3)
+@pytest.mark.parametrize("K", [4096, 4099])
+def test_block_scaled_misaligned_rows(K):
+    """A large block-scaled product with 1-byte aligned rows (and a K that is
+    not a whole number of 128-k stages): the automatic plan runs a 1-byte
+    aligned instance that applies the scales, and it and every such instance
+    match the oracle on sampled entries."""
+    M = N = 4096
+    lda = K + 1 if (K + 1) % 2 else K + 2  # odd strides: rows 1-byte aligned
+    ldb = lda + 2
+    A_st, B_st = si.operands(M, N, K, "e4m3", "uniform_pm1", 41, 42, lda=lda, ldb=ldb)
     sa = si.block_scales(M, K, 43, pad=4)
     sb = si.block_scales(N, K, 44, pad=8)
     ms, ns = si.sample_coords(M, N, 1500, 23)
-    ref, mag = oracle.gemm_entries(M, N, K, 0.01, True, si.bits(A_st), K + 1, si.bits(B_st), K + 3, "e4m3", ms, ns,
+    ref, mag = oracle.gemm_entries(M, N, K, 0.01, True, si.bits(A_st), lda, si.bits(B_st), ldb, "e4m3", ms, ns,
                                    scale_a=sa, lds_a=sa.shape[1], scale_b=sb, lds_b=sb.shape[1])
-    direct = [k for k in _fp8_instances("e4m3") if tg.kernel_info(k).load_class == 1 and tg.kernel_info(k).block_m == 256]
+    dev = torch.device("cuda:0")
+    A, B = A_st.to(dev), B_st.to(dev)
+    D = torch.empty(N, M, device=dev)
+    ta, tb = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
+    plan = tg.query_plan_scaled(M, N, K, tg.E4M3, A.data_ptr(), lda, ta.data_ptr(), sa.shape[1], B.data_ptr(),
+                                ldb, tb.data_ptr(), sb.shape[1], D.data_ptr(), M)
+    assert plan.load_class == 1 and plan.staged == 0
+    direct = [k for k in _fp8_instances("e4m3") if tg.kernel_info(k).load_class == 1]
+    assert plan.kernel_id in direct
     for kid in [-1] + direct:
         D_st = run(A_st, B_st, M, N, K, 0.01, True, sa, sb, kernel_id=kid)
         d = D_st[torch.from_numpy(ns), torch.from_numpy(ms)].double().numpy()
         ok, r = oracle.check(d, ref, mag, K)
         assert ok, f"instance {kid}: worst ratio {r}"
-        _log(f"[fp8 scaled misaligned] instance {kid}: worst ratio {r:.3g}")
-    tg.release_staging()
+        _log(f"[fp8 scaled misaligned] K={K} instance {kid}: worst ratio {r:.3g}")

@@ -1,12 +1,11 @@
-"""Staged operand copies (tile_gemm_staged, and the automatic plan of
-tile_gemm) against the oracle, on the GPU.
+"""Staged operand copies (tile_gemm_staged, with the caller's workspace)
+against the oracle, on the GPU.
 
 The staging launch copies A and B into 16-byte aligned rows padded with zeros
 to whole K stages; the product of the copies must equal the oracle's result
-exactly on integer data (the padding adds exact zeros), leave D's padding
-alone, and give the same bits whether the workspace is the caller's or the
-library's own.  Operand storage carries NaN past K in every row, so a copy
-that read beyond K would show.
+exactly on integer data (the padding adds exact zeros) and leave D's padding
+alone.  Operand storage carries NaN past K in every row, so a copy that read
+beyond K would show.
 """
 from __future__ import annotations
 
@@ -122,40 +121,14 @@ def test_automatic_mode_and_short_workspace():
         assert ok, f"worst ratio {r}"
 
 
-def test_library_staging_buffer_grows_and_is_released():
-    """tile_gemm's automatic plan stages through the library's buffer; a larger
-    product grows it, a smaller one reuses it, release frees it; every result
-    has the bits of the same product staged in a caller workspace."""
-    dev = torch.device("cuda:0")
-    cases = [(4096, 4096, 4096), (4352, 4608, 5000), (4096, 4200, 4100)]
-    for i, (M, N, K) in enumerate(cases):
-        A_st, B_st = si.operands(M, N, K, "bf16", "normal_invsqrtk", 10 + i, 20 + i, lda=K + 1, ldb=K + 1)
-        A, B = A_st.to(dev), B_st.to(dev)
-        D = si.out_storage(M, N).to(dev)
-        plan = tg.plan_for(A[:, :K], B[:, :K].t(), D.t())
-        assert plan.staged == 1, (M, N, K)
-        tg.gemm(A[:, :K], B[:, :K].t(), D.t(), 0.5, True)
-        torch.cuda.synchronize()
-        ref = run(A_st, B_st, M, N, K, 0.5, True, "bf16", 1)
-        assert torch.equal(D.cpu(), ref), (M, N, K)
-        _log(f"[staged library buffer] {M}x{N}x{K}: same bits as the caller-workspace call")
-    tg.release_staging()
-    D2 = si.out_storage(M, N).to(dev)
-    tg.gemm(A[:, :K], B[:, :K].t(), D2.t(), 0.5, True)
-    torch.cuda.synchronize()
-    assert torch.equal(D2.cpu(), ref)
-    tg.release_staging()
-
-
-def test_graph_capture_runs_the_direct_plan():
-    """Under stream capture the library allocates nothing and runs the direct
-    plan; every replay equals the eager direct result."""
+def test_graph_capture_of_misaligned_rows():
+    """tile_gemm on misaligned rows, captured into a graph: the library only
+    enqueues kernels, so every replay equals the eager result."""
     dev = torch.device("cuda:0")
     M = N = K = 4096
     A_st, B_st = si.operands(M, N, K, "bf16", "normal_invsqrtk", 31, 32, lda=K + 1, ldb=K + 1)
     A, B = A_st.to(dev), B_st.to(dev)
     eager = run(A_st, B_st, M, N, K, 0.5, True, "bf16", 0, workspace=None)
-    tg.release_staging()
     D = si.out_storage(M, N).to(dev)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()

@@ -21,7 +21,29 @@ def test_library_exports_every_declared_function():
             "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 7
+    assert tg.abi_version() == 8
+
+
+def test_library_neither_allocates_nor_synchronises():
+    """The library borrows every buffer from the caller and only enqueues work
+    (Tylo.jl manual, "Walk through GEMM", sections 2 and 4: views borrow
+    storage, no hidden allocation or barrier): its dynamic symbol table
+    imports no HIP allocation, free or synchronisation routine."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", str(tg.LIB_PATH)], check=True, capture_output=True,
+                         text=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert "hipLaunchKernel" in imported  # the table really is the dynamic imports
+    forbidden = {name for name in imported
+                 if name.startswith(("hipMalloc", "hipFree", "hipExtMalloc", "hipHostMalloc", "hipMallocAsync",
+                                     "hipStreamSynchronize", "hipDeviceSynchronize", "hipEventSynchronize",
+                                     "hipStreamWaitEvent", "hipMemcpy", "hipMemset"))}
+    assert not forbidden, forbidden
 
 
 def test_strerror_covers_every_status():
@@ -51,7 +73,7 @@ def test_validation_codes(args, code):
     assert rc == code, tg.STATUS.get(rc, rc)
     info = tg.PlanInfo()
     rc2 = tg.load_library().tile_gemm_query_plan(p["M"], p["N"], p["K"], p["dtype"], p["A"], p["lda"],
-                                                 p["B"], p["ldb"], p["D"], p["ldd"], -1, ctypes.byref(info))
+                                                 p["B"], p["ldb"], p["D"], p["ldd"], ctypes.byref(info))
     assert rc2 == code
 
 
@@ -111,14 +133,11 @@ def test_plans_for_the_workloads():
     assert big.lds_bytes <= 160 * 1024
     assert tg.kernel_info(big.kernel_id).load_class == 16  # a streaming instance
     assert _plan(W["square_8192_f16_relu"]).dtype == tg.F16
-    # 2-byte aligned rows: large enough that copying A and B into aligned
-    # staging rows first pays, and the product then runs the streaming kernel
+    # 2-byte aligned rows run directly (tile_gemm never copies the operands)
     ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
-    assert ragged.staged == 1 and ragged.load_class == 16 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
+    assert ragged.staged == 0 and ragged.load_class == 2 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
     assert tg.kernel_info(ragged.kernel_id).block_m == 256 and big.staged == 0
-    # ldd*4 is not a multiple of 128 there: the instance writes D without
-    # nontemporal stores; with line-aligned D columns the default keeps them
-    assert ragged.kernel_id == 43 and big.kernel_id == 22
+    assert big.kernel_id == 0
     # small problems take small tiles so that more CUs get work (and are not staged)
     tiny = _plan(W["tiny_bounded_65x97x73_bf16"])
     assert tiny.staged == 0 and tiny.load_class == 2 and (tiny.block_m, tiny.grid) == (64, 4)
@@ -130,14 +149,12 @@ def test_plans_for_the_workloads():
 
 def test_plan_alignment_classes_and_forced_instances():
     W = si.WORKLOADS["square_8192_bf16_relu"]
-    for off_a, off_b in ((4, 0), (0, 2)):
+    for off_a, off_b, cls in ((4, 0, 4), (0, 2, 2)):
         p = _plan(W, a=A + off_a, b=B + off_b)
-        assert p.staged == 1 and p.load_class == 16 and p.grid == 1024
+        assert p.staged == 0 and p.load_class == cls and p.grid == 1024
     w = si.Workload("mid", 300, 200, 130, "bf16", "uniform_pm1", 1.0, False, 130, 130, 300, 1, 2)
     assert (_plan(w, a=A + 4).load_class, _plan(w, a=A + 4).staged) == (4, 0)
     assert (_plan(w, b=B + 2).load_class, _plan(w, b=B + 2).staged) == (2, 0)
-    # a forced instance runs on the operands as given
-    assert _plan(W, b=B + 2, kernel_id=3).staged == 0
     # a 2-byte aligned operand cannot run an instance that needs 4-byte rows
     narrow = [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 4
               and tg.kernel_info(k).dtype == tg.BF16]
@@ -319,11 +336,25 @@ def test_staged_workspace_size_and_validation():
 
 
 def test_staging_decision_scales_with_the_problem():
-    """Misaligned rows are staged only when the copy pays: 4096^3 yes, 1024^3 no."""
+    """tile_gemm_staged (mode -1) copies misaligned rows only when the copy
+    pays and the caller's workspace holds the copies: 4096^3 yes, 1024^3 no;
+    aligned rows never; mode 1 always (with a workspace), mode 0 never."""
+    A2, B2, D2, W2 = 0x100000000000, 0x200000000000, 0x300000000000, 0x400000000000
     for n, staged in ((4096, 1), (1024, 0)):
-        w = si.Workload("sq", n, n, n, "bf16", "uniform_pm1", 1.0, False, n, n, n, 1, 2)
-        assert _plan(w, b=B + 2).staged == staged, n
-        assert _plan(w).staged == 0  # aligned rows never need it
+        need = tg.staged_workspace_bytes(n, n, n, tg.BF16)
+        q = lambda b, mode=-1, ws=W2, nbytes=need: tg.query_plan_staged(n, n, n, tg.BF16, A2, n, b, n, D2, n, tg.F32,
+                                                                        ws, nbytes, mode)
+        p = q(B2 + 2)
+        assert p.staged == staged, n
+        if staged:
+            assert p.load_class == 16 and tg.kernel_info(p.kernel_id).load_class == 16
+        assert q(B2 + 2, ws=0, nbytes=0).staged == 0          # no workspace: the direct plan
+        assert q(B2 + 2, nbytes=need - 1).staged == 0         # too short: the direct plan
+        assert q(B2).staged == 0                              # aligned rows never need it
+        assert q(B2, mode=1).staged == 1 and q(B2 + 2, mode=0).staged == 0
+        with pytest.raises(tg.TileGemmError) as e:
+            q(B2, mode=1, ws=0, nbytes=0)
+        assert e.value.code == -10
 
 
 def test_plan_choices_follow_the_kernel_trace_table():
@@ -331,22 +362,22 @@ def test_plan_choices_follow_the_kernel_trace_table():
     fastest in the kernel trace for each of these shapes (small streaming 64^2
     for long-K few-tile products, 128^2 at 2048^2, the wide kernel beyond)."""
     A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
-    expect = {(1024, 1024, 1024): 45, (2048, 2048, 2048): 47, (512, 512, 16384): 45, (1024, 1024, 4096): 45,
-              (2048, 2048, 8192): 47, (4096, 4096, 1024): 22, (3072, 3072, 3072): 22}
+    expect = {(1024, 1024, 1024): 14, (2048, 2048, 2048): 16, (512, 512, 16384): 14, (1024, 1024, 4096): 14,
+              (2048, 2048, 8192): 16, (4096, 4096, 1024): 0, (3072, 3072, 3072): 0}
     for (M, N, K), kid in expect.items():
         assert tg.query_plan(M, N, K, tg.BF16, A2, K, B2, K, D2, M).kernel_id == kid, (M, N, K)
 
 
 def test_fp32_plan_choices():
-    """fp32 operands: the wide kernel at 4096^3 (ids 25, or 17 with plain
+    """fp32 operands: the wide kernel at 4096^3 (ids 8, or 9 with plain
     stores when D columns are not line-aligned), the 128^2 streaming instance
     at 2048^3, the register-staged 64^2 for 1024x1024x4096."""
     A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
     q = lambda M, N, K, ldd=None: tg.query_plan(M, N, K, tg.F32, A2, K, B2, K, D2, ldd or M).kernel_id
-    assert q(4096, 4096, 4096) == 25
-    assert q(4096, 4096, 4096, ldd=4097) == 17
-    assert q(2048, 2048, 2048) == 49
-    assert q(1024, 1024, 4096) == 32
+    assert q(4096, 4096, 4096) == 8
+    assert q(4096, 4096, 4096, ldd=4097) == 9
+    assert q(2048, 2048, 2048) == 18
+    assert q(1024, 1024, 4096) == 30
 
 
 def test_scaled_entry_point_validation():
@@ -374,12 +405,17 @@ def test_scaled_entry_point_validation():
 
 def test_8bit_staging_and_streaming_plans():
     """8-bit operands: aligned rows run the streaming 8-bit instance; a large
-    product with 1-byte aligned rows is staged onto it; a small one is not."""
-    A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
+    product with 1-byte aligned rows runs the 1-byte loader directly, or is
+    staged onto the streaming instance through tile_gemm_staged; a small one
+    is not staged."""
+    A2, B2, D2, W2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000
     p = tg.query_plan(4096, 4096, 4096, tg.E4M3, A2, 4096, B2, 4096, D2, 4096)
-    assert p.staged == 0 and p.kernel_id == 60 and p.block_k == 128
+    assert p.staged == 0 and p.kernel_id == 10 and p.block_k == 128
     p = tg.query_plan(4096, 4096, 4096, tg.E5M2, A2 + 1, 4097, B2, 4097, D2, 4096)
-    assert p.staged == 1 and p.kernel_id == 61
+    assert p.staged == 0 and p.load_class == 1
+    need = tg.staged_workspace_bytes(4096, 4096, 4096, tg.E5M2)
+    p = tg.query_plan_staged(4096, 4096, 4096, tg.E5M2, A2 + 1, 4097, B2, 4097, D2, 4096, tg.F32, W2, need)
+    assert p.staged == 1 and p.kernel_id == 11
     p = tg.query_plan(300, 200, 130, tg.E4M3, A2 + 1, 131, B2, 131, D2, 300)
     assert p.staged == 0 and p.load_class == 1
 
@@ -391,8 +427,58 @@ def test_scaled_call_refuses_instances_without_scales():
     A2, B2, D2, S2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000
     M = N = K = 4096
     need = 4 * (K // 128)
-    rc = tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, K, S2, need, B2, K, 0, 0, D2, M, tg.E4M3, tg.F32, None, 60)
+    rc = tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, K, S2, need, B2, K, 0, 0, D2, M, tg.E4M3, tg.F32, None, 10)
     assert rc == -9
     big = 1 << 24  # bytes per scale row, beyond 8 MiB
-    rc = tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, K, S2, big, B2, K, 0, 0, D2, M, tg.E4M3, tg.F32, None, 62)
+    rc = tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, K, S2, big, B2, K, 0, 0, D2, M, tg.E4M3, tg.F32, None, 12)
     assert rc == -9
+    # the automatic choice with scales is the scaled streaming instance
+    p = tg.query_plan_scaled(M, N, K, tg.E4M3, A2, K, S2, need, B2, K, 0, 0, D2, M)
+    assert p.kernel_id == 12 and tg.kernel_info(12).load_class == 16
+
+
+def _chosen_instances():
+    """Every instance some automatic plan picks, over a grid of shapes, dtypes,
+    row alignments, D line alignments and entry points."""
+    A2, B2, D2, S2, W2 = 0x100000000000, 0x200000000000, 0x300000000000, 0x400000000000, 0x500000000000
+    es_of = {tg.BF16: 2, tg.F16: 2, tg.F32: 4, tg.E4M3: 1, tg.E5M2: 1}
+    dims = [17, 65, 200, 512, 1024, 2048, 4096, 8192, 12289]
+    Ks = [9, 73, 1024, 4099, 8192, 16384]
+    chosen = set()
+
+    def stride(K, es, cls):
+        for ld in range(K, K + 64):
+            b = ld * es
+            c = 16 if b % 16 == 0 else 4 if b % 4 == 0 else 2 if b % 2 == 0 else 1
+            if c == cls:
+                return ld
+        return None
+
+    for dt, es in es_of.items():
+        classes = [c for c in (16, 4, 2, 1) if c >= es]
+        for M in dims:
+            for N in dims[::2]:
+                for K in Ks:
+                    for cls in classes:
+                        ld = stride(K, es, cls)
+                        for ldd in (-(-M // 32) * 32, M + 1):
+                            chosen.add(tg.query_plan(M, N, K, dt, A2, ld, B2, ld, D2, ldd, -1, tg.F32).kernel_id)
+                            if es == 1:
+                                sc = 4 * -(-K // 128)
+                                chosen.add(tg.query_plan_scaled(M, N, K, dt, A2, ld, S2, sc, B2, ld, 0, 0, D2,
+                                                                ldd).kernel_id)
+                            elif N <= 256:
+                                p = tg.query_plan_softmax(M, N, K, dt, A2, ld, B2, ld, D2, ldd)
+                                chosen.add(p.kernel_id)
+        # operand rows longer than 8 MiB
+        K = (1 << 23) // es + 64
+        chosen.add(tg.query_plan(8192, 8192, K, dt, A2, K, B2, K, D2, 8192, -1, tg.F32).kernel_id)
+    chosen.discard(-1)
+    return chosen
+
+
+def test_every_instance_is_chosen_by_some_plan():
+    """The instance table holds only instances that an automatic plan picks
+    for some call (no experiment variants ship)."""
+    chosen = _chosen_instances()
+    assert chosen == set(range(tg.kernel_count())), sorted(set(range(tg.kernel_count())) - chosen)
