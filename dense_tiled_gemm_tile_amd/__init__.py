@@ -68,6 +68,8 @@ _SIGNATURES = {
     "tile_gemm_splitk": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _int,
                                 _ptr, _i64, _ptr, _int]),
     "tile_gemm_splitk_workspace_bytes": (_i64, [_i64, _i64, _int]),
+    "tile_gemm_splitk_noalloc": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                                        _int, _ptr, _int]),
     "tile_gemm_staged": (_int, [_i64, _i64, _i64, _f32, _int, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr,
                                 _i64, _ptr, _int]),
     "tile_gemm_staged_workspace_bytes": (_i64, [_i64, _i64, _i64, _int]),
@@ -152,6 +154,12 @@ def tile_gemm_splitk(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dt
                      workspace_bytes, stream=None, kernel_id=-1) -> int:
     return load_library().tile_gemm_splitk(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd, dtype,
                                            out_dtype, splits, workspace, workspace_bytes, stream, kernel_id)
+
+
+def tile_gemm_splitk_noalloc(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, splits, stream=None,
+                             kernel_id=-1) -> int:
+    return load_library().tile_gemm_splitk_noalloc(M, N, K, alpha, int(bool(relu)), A, lda, B, ldb, D, ldd, dtype,
+                                                   out_dtype, splits, stream, kernel_id)
 
 
 def tile_gemm_softmax(M, N, K, alpha, A, lda, B, ldb, D, ldd, dtype, out_dtype=F32, stream=None,

@@ -517,9 +517,16 @@ int64_t tile_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {
     return int64_t(splits) * M * N * 4;
 }
 
-int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
-                     const void* B, int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, int splits,
-                     void* workspace, int64_t workspace_bytes, void* stream, int kernel_id) {
+}  // extern "C"
+
+namespace {
+
+// Split-K product; `use_static` puts the partials in the library's static
+// scratch array instead of `workspace` (whose checks then do not apply).
+int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda, const void* B,
+                int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, int splits, void* workspace,
+                int64_t workspace_bytes, void* stream, int kernel_id, bool use_static) {
+    if (use_static) workspace_bytes = kTgStaticScratchBytes;
     if (splits < 0 || splits > kMaxSplits) return TG_ERR_DIMS;
     if (splits == 0) {
         // automatic: split only when the output has fewer tiles than the chip
@@ -535,14 +542,14 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
             if (s > stages / 16) s = stages / 16;
             if (s > kAutoSplitMax) s = kAutoSplitMax;
             // never more than the workspace holds
-            const int64_t fit = (M > 0 && N > 0 && workspace) ? workspace_bytes / (M * N * 4) : 0;
+            const int64_t fit = (M > 0 && N > 0 && (workspace || use_static)) ? workspace_bytes / (M * N * 4) : 0;
             if (s > fit) s = fit;
         }
         splits = static_cast<int>(s < 1 ? 1 : s);
     }
     if (splits == 1)
-        return tile_gemm_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype,
-                                 stream, kernel_id);
+        return launch_batched(M, N, K, alpha, relu, A, lda, 0, B, ldb, 0, D, ldd, 0, 1, dtype, out_dtype, stream,
+                              kernel_id);
     // the first launch is a batch of `splits` products over K ranges; the
     // plan weighs all their workgroups
     tile_gemm_plan_info pl;
@@ -554,9 +561,11 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
     const int64_t chunk = cdiv(stages, splits) * bk;         // K elements per split, whole stages
     const int64_t used = K > 0 ? cdiv(K, chunk) : 1;        // splits that get at least one element
     const int64_t need = used * M * N * 4;
-    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u))
-        return TG_ERR_WORKSPACE;
-    {
+    if (use_static) {
+        if (need > kTgStaticScratchBytes) return TG_ERR_WORKSPACE;
+    } else {
+        if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u))
+            return TG_ERR_WORKSPACE;
         const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uintptr_t(need);
         const int es = elem_size(dtype), os = elem_size(out_dtype);
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(D), d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
@@ -567,6 +576,10 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
     }
     rc = device_ok();
     if (rc) return rc;
+    if (use_static && tg_static_scratch(&workspace) != hipSuccess) {
+        (void)hipGetLastError();
+        return TG_ERR_LAUNCH;
+    }
     const int es = elem_size(dtype);
     GemmArgs a{};  // every field starts at zero (split_k = 0: no split)
     a.A = static_cast<const char*>(A);
@@ -596,6 +609,25 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, con
                                static_cast<int>(M), static_cast<int>(N), D, ldd, alpha, relu ? 1 : 0, out_dtype,
                                static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, int splits,
+                     void* workspace, int64_t workspace_bytes, void* stream, int kernel_id) {
+    return splitk_impl(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, splits, workspace,
+                       workspace_bytes, stream, kernel_id, false);
+}
+
+int tile_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, float alpha, int relu, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, void* D, int64_t ldd, int dtype, int out_dtype, int splits,
+                             void* stream, int kernel_id) {
+    return splitk_impl(M, N, K, alpha, relu, A, lda, B, ldb, D, ldd, dtype, out_dtype, splits, nullptr, 0, stream,
+                       kernel_id, true);
 }
 
 int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B,

@@ -2,6 +2,9 @@
 // products added in split order, then the epilogue), the staged operand copy
 // (misaligned rows into 16-byte aligned, zero-padded rows) and the row
 // softmax over n of an fp32 D (the second pass when one tile cannot span N).
+#include <atomic>
+#include <mutex>
+
 #include "gemm_common.h"
 
 namespace tg {
@@ -147,4 +150,41 @@ hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char
         hipLaunchKernelGGL(tg::stage_rows_kernel<4>, grid, dim3(256), 0, stream, A, lda_b, M, B, ldb_b, rows, K, cpr,
                            dstA, dstB);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- static scratch
+//
+// Device memory the library itself holds, for callers that cannot allocate
+// (tile_gemm_splitk_noalloc keeps its fp32 partial products here): one array
+// per GPU, loaded with the library's code object and kept until the process
+// ends.  In host code the array's name is only a stand-in for the device
+// symbol, never a device address, so the address is looked up once per
+// device (with that device current) and only that address reaches kernels.
+// Every call on a GPU shares its array: calls that overlap on one GPU race.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kTgStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t tg_static_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }

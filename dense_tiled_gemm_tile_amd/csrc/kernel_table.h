@@ -48,6 +48,12 @@ hipError_t tg_splitk_reduce(const float* ws, int splits, int M, int N, void* D, 
 hipError_t tg_stage_operands(const char* A, int64_t lda_b, int64_t M, const char* B, int64_t ldb_b, int64_t N, int K,
                              int es, int64_t row_bytes, char* dstA, char* dstB, hipStream_t stream);
 
+// The library's static scratch array (one per GPU, for callers that cannot
+// allocate): its size, and its device address on the current device (looked
+// up once per device; no allocation).
+constexpr int64_t kTgStaticScratchBytes = int64_t(TILE_GEMM_STATIC_SCRATCH_BYTES);
+hipError_t tg_static_scratch(void** ptr);
+
 typedef hipError_t (*TgLaunchFn)(const GemmArgs&, int64_t grid, int batch, hipStream_t stream);
 
 struct TgKernelDesc {

@@ -191,6 +191,29 @@ int tile_gemm_splitk(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      void* workspace, int64_t workspace_bytes, void* stream, int kernel_id);
 
 /*
+ * As tile_gemm_splitk, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * allocation): the fp32 partial products live in the library's own static
+ * scratch array of TILE_GEMM_STATIC_SCRATCH_BYTES per GPU (part of the
+ * library's code object, held on each GPU it runs on until the process
+ * ends) instead of a caller workspace.  The call allocates nothing and
+ * synchronises nothing.  Every call on one GPU shares that GPU's array, so
+ * calls that can overlap on one GPU (several streams, several host threads)
+ * race and must be ordered by the caller; a call fully ordered after another
+ * on the stream is safe (each call writes every partial it reads).
+ * Errors as tile_gemm_splitk, and TG_ERR_WORKSPACE when the partials of the
+ * requested split (splits * M * N * 4 bytes for the splits that get work)
+ * exceed the scratch; splits = 0 chooses automatically within the scratch.
+ */
+int tile_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, float alpha, int relu,
+                             const void* A, int64_t lda, const void* B, int64_t ldb,
+                             void* D, int64_t ldd, int dtype, int out_dtype, int splits,
+                             void* stream, int kernel_id);
+
+/* Bytes of the static scratch array tile_gemm_splitk_noalloc uses (32 MiB). */
+#define TILE_GEMM_STATIC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
  * Softmax over n (a row-wise epilogue; Tylo.jl manual, "Walk through GEMM",
  * section 5, on replacing the pointwise ReLU by a softmax, which needs a
  * reduction across the waves that share a row):

@@ -482,3 +482,19 @@ def test_every_instance_is_chosen_by_some_plan():
     for some call (no experiment variants ship)."""
     chosen = _chosen_instances()
     assert chosen == set(range(tg.kernel_count())), sorted(set(range(tg.kernel_count())) - chosen)
+
+
+def test_noalloc_splitk_refuses_partials_beyond_the_static_scratch():
+    """tile_gemm_splitk_noalloc checks the partials against its static scratch
+    before any HIP call (no GPU here: a call that fits reports the device)."""
+    import torch
+
+    M = N = 2048
+    K = 8192
+    call = lambda splits: tg.tile_gemm_splitk_noalloc(M, N, K, 1.0, 0, A, K, B, K, D, M, tg.BF16, tg.F32, splits,
+                                                      None, -1)
+    assert call(3) == -10                      # 3 x 16 MiB > 32 MiB
+    assert call(-1) == -1 and call(257) == -1
+    if not torch.cuda.is_available():
+        assert call(2) == -8                   # exactly 32 MiB fits
+        assert call(0) == -8
