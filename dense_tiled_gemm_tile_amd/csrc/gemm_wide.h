@@ -52,8 +52,10 @@ namespace tg {
 // is bound by the write burst and the shuffles add VALU work), bit 6 =
 // 8-bit operands with block scales (their loads sit in the main loop, and the
 // waits the compiler puts before their use also wait for copies, so the
-// instances without scales do not carry them).
-template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
+// instances without scales do not carry them).  LC = 16: copies by LDS-DMA,
+// which needs 16-byte aligned row starts; LC = 4 or 2: rows only 4- or 2-byte
+// aligned, copied through registers (see the register-staged schedule below).
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI, int LC>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     select_batch(p);
     constexpr int BM = 256, BN = 256, WM = 2;
@@ -71,8 +73,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     static_assert(NS == 4 || NS == 5, "4 or 5 half-stage slots");
     static_assert(SCHED == 0 || NS == 5, "the spread copy schedule needs 5 slots");
     static_assert(RS >= 1 && RS <= MF, "reads spread over at most one slab");
+    static_assert(LC == 16 || (LC >= 2 && ADDR == 1 && NS == 4 && !F8 && (ES == 2 || LC == 4)),
+                  "register-staged copies: buffer addressing, 4 slots, 16-bit or fp32 operands");
 
-    __shared__ __attribute__((aligned(1024))) char smem[NS * SLOT];
+    // the whole 160 KiB of a CU (one workgroup per CU): the ring uses NS
+    // slots, the transposing epilogues may use all of it
+    constexpr int LDS_BYTES = 5 * SLOT;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -309,6 +316,153 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 pair(pp, nfull, [](int) {});
             }
         }
+    } else if constexpr (LC < 16) {
+        // Operand rows only 4- or 2-byte aligned: LDS-DMA needs 16-byte
+        // aligned sources, so each lane gathers the same 16-byte chunks the
+        // DMA copies would move (row dma128_row, logical chunk dma128_chunk
+        // of copy j) into registers with buffer loads, and scatters them with
+        // ds_write_b128 into the same swizzled slots.  A 2-byte aligned chunk
+        // is loaded as the dword-aligned 16 bytes at or below it plus the next
+        // dword and shifted into place (v_alignbyte).  Per stage the 16 chunk
+        // groups of a lane (8 of A, 8 of B) are scattered in slabs 0-2, each
+        // one stage after its gather, and the same registers then gather the
+        // chunk group of the stage after next: one stage of loads in flight,
+        // 64 KiB per workgroup in registers.  Stage s lives in slots
+        // 2(s % 2) and 2(s % 2) + 1; the scatters of stage s+1 in slabs 0-2 of
+        // stage s go to slots freed by barrier B_{s-1}, and B_s (after slab 2,
+        // with every scatter complete) publishes them.
+        // Rows past M or N get an offset beyond the buffer range and load
+        // zeros; the extra dword is only loaded for rows that need the shift,
+        // so every dword read holds at least one byte of a valid row.  The
+        // buffer base is the tile's first row rounded down to 4 bytes and
+        // every offset is a multiple of 4: dword loads at offsets that are
+        // not measured wrong on gfx950 when the base itself was not aligned.
+        u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+        constexpr int NG = 2 * NC;  // chunk groups per lane and stage: 8 of A, then 8 of B
+        constexpr unsigned kOut = 0x80000000u;  // beyond every buffer range (256 rows x stride <= 2^31)
+        const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+        const char* first[2] = {p.A + static_cast<int64_t>(m0) * p.lda_b, p.B + static_cast<int64_t>(n0) * p.ldb_b};
+        const unsigned lead[2] = {static_cast<unsigned>(reinterpret_cast<uintptr_t>(first[0]) & 3u),
+                                  static_cast<unsigned>(reinterpret_cast<uintptr_t>(first[1]) & 3u)};
+        const __amdgpu_buffer_rsrc_t br[2] = {
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(first[0] - lead[0]), static_cast<short>(0),
+                                              static_cast<int>(lead[0] + rows_a * p.lda_b), 0x00020000),
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(first[1] - lead[1]), static_cast<short>(0),
+                                              static_cast<int>(lead[1] + rows_b * p.ldb_b), 0x00020000)};
+        unsigned off_lo[NG], off_hi[NG], shift[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int o = g / NC, j = wave * NC + g % NC;
+            const int r = dma128_row(j, lane);
+            const unsigned ldb = static_cast<unsigned>(o == 0 ? p.lda_b : p.ldb_b);
+            const unsigned at = lead[o] + static_cast<unsigned>(r) * ldb + dma128_chunk(j, lane) * kChunkBytes;
+            const unsigned sub = at & 3u;  // 0 or 2 (rows are 2-byte aligned), 0 for LC 4
+            const bool valid = r < (o == 0 ? rows_a : rows_b);
+            off_lo[g] = valid ? at - sub : kOut;
+            off_hi[g] = (valid && sub) ? at - sub + kChunkBytes : kOut;
+            shift[g] = sub;
+        }
+        u32x4 glo[NG];
+        unsigned ghi[NG];
+        // gather chunk group g of stage t into registers
+        auto gather = [&](int g, int t) {
+            const int o = g / NC;
+            const int soff = __builtin_amdgcn_readfirstlane(t * kRowBytes);
+            glo[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br[o], static_cast<int>(off_lo[g]),
+                                                                                     soff, 0));
+            if constexpr (LC == 2)
+                ghi[g] = __builtin_amdgcn_raw_buffer_load_b32(br[o], static_cast<int>(off_hi[g]), soff, 0);
+        };
+        // scatter chunk group g into slot `slot`
+        auto scatter = [&](int g, int slot) {
+            u32x4 v = glo[g];
+            if constexpr (LC == 2) {
+                const unsigned sh = shift[g];
+                v.x = __builtin_amdgcn_alignbyte(glo[g].y, glo[g].x, sh);
+                v.y = __builtin_amdgcn_alignbyte(glo[g].z, glo[g].y, sh);
+                v.z = __builtin_amdgcn_alignbyte(glo[g].w, glo[g].z, sh);
+                v.w = __builtin_amdgcn_alignbyte(ghi[g], glo[g].w, sh);
+            }
+            *reinterpret_cast<u32x4*>(smem + slot * SLOT + (wave * NC + g % NC) * 1024 + lane * kChunkBytes) = v;
+        };
+        // chunk group p of a stage goes out after MFMA 3p + 1 of slabs 0-2
+        auto pairs_at = [&](int k, int m, auto&& f) {
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+                if (3 * q + 1 == 16 * k + m) f(q);
+        };
+
+        if (nfull > 0) {
+            // prologue: stage 0 through registers into slots 0/1, then stage 1 in flight
+#pragma unroll
+            for (int g = 0; g < NG; ++g) gather(g, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) scatter(g, g / NC);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) gather(g, min(1, nfull - 1));
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+            barrier();
+    #pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
+
+            int slot0 = 0;  // slot of stage s's A half: 2 * (s % 2)
+            for (int s = 0; s < nfull; ++s) {
+                const int sa = slot0, sb = slot0 + 1;
+                const int na = slot0 ^ 2, nb = na + 1;
+                // a stage index past the last full stage reloads it (values unused)
+                const int t2 = min(s + 2, nfull - 1);
+                auto step = [&](int q) {
+                    scatter(q, q < NC ? na : nb);  // stage s+1, gathered one stage ago
+                    gather(q, t2);
+                };
+                slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
+                    pairs_at(0, m, step);
+                });
+                slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); });
+                    pairs_at(1, m, step);
+                });
+                slab_with_side<DT, FM, FN, MF>(acc, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); });
+                    pairs_at(2, m, step);
+                });
+                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+                barrier();
+                // on the last stage the reads below fetch values that go unused
+                slab_with_side<DT, FM, FN, MF>(acc, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
+                });
+                slot0 = na;
+            }
+            wait_vm<0>();  // no load outlives the loop
+        }
+
+        if (K % BKE != 0) {
+            // ragged last stage through registers into slots 0 (A) and 1 (B);
+            // k >= K become exact zeros
+            __syncthreads();
+            const int c = stage_chunk(tid);
+            const int k0 = nfull * BKE + c * EPC;
+    #pragma unroll
+            for (int i = 0; i < BM / 32; ++i) {
+                const int r = stage_row(tid, i);
+                const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+                const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+            }
+            __syncthreads();
+    #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
+    #pragma unroll
+                for (int i = 0; i < FN; ++i)
+    #pragma unroll
+                    for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+            }
+        }
     } else {
         u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
@@ -520,7 +674,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         // store instruction writes two whole 512-byte row runs, instead of
         // 64-byte pieces of lines that other instructions complete later.
         constexpr int PITCH16 = 528;
-        static_assert((EPI & 4) == 0 || 256 * PITCH16 <= NS * SLOT, "16-bit tile fits the ring");
+        static_assert((EPI & 4) == 0 || 256 * PITCH16 <= LDS_BYTES, "16-bit tile fits the LDS");
         __syncthreads();  // every wave is done with the ring
         with_out_type(p.out_dtype, [&](auto out) {
             constexpr int OUT = decltype(out)::value;
@@ -567,7 +721,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         // 1056 bytes keeps the two half-waves of each LDS write on disjoint
         // banks.
         constexpr int PITCH = 1056;
-        static_assert(EPI < 2 || 128 * PITCH <= NS * SLOT, "transpose buffer fits the ring");
+        static_assert(EPI < 2 || 128 * PITCH <= LDS_BYTES, "transpose buffer fits the LDS");
         __syncthreads();  // every wave is done with the ring
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
@@ -602,9 +756,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     }
 }
 
-template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI>
+template <int DT, int GM, int NS, int RS, int ADDR, int SCHED, int EPI, int LC>
 static hipError_t launch_wide(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>),
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>),
                        dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -612,14 +766,14 @@ static hipError_t launch_wide(const GemmArgs& a, int64_t grid, int batch, hipStr
 }  // namespace tg
 
 // Instance rows of the wide kernel: (id, dtype, group_m, slots NS, read spread
-// RS, ADDR, SCHED, EPI, eff%).  eff% weighs the instance's tiles in the host
-// plan chooser.  ADDR 1 instances address a tile through 32-bit byte offsets,
-// so they take operand row strides up to 8 MiB (256 rows x stride < 2^31); the
-// ADDR 0 twins cover longer rows.
-#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF) \
-    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI>(GemmArgs);
+// RS, ADDR, SCHED, EPI, row alignment class LC, eff%).  eff% weighs the
+// instance's tiles in the host plan chooser.  ADDR 1 instances address a tile
+// through 32-bit byte offsets, so they take operand row strides up to 8 MiB
+// (256 rows x stride < 2^31); the ADDR 0 twins cover longer rows.
+#define TG_INSTANTIATE_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, LC, EFF) \
+    template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>(GemmArgs);
 
-#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, EFF)                                             \
-    {id, DT, 256, 256, 128 / TG_ELEM_BYTES(DT), 2, 2, 128, 128, 256, NS, (NS) * 256 * 128, 256, 16, GM, EFF,  \
-     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI>, (ADDR) ? (int64_t(1) << 23) : 0, ((EPI) & 8) ? 1 : 0, \
-     (EPI) & 1, ((EPI) & 64) ? 1 : 0},
+#define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, LC, EFF)                                         \
+    {id, DT, 256, 256, 128 / TG_ELEM_BYTES(DT), 2, 2, 128, 128, 256, NS, 5 * 256 * 128, 256, LC, GM, EFF,     \
+     &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>, (ADDR) ? (int64_t(1) << 23) : 0,                  \
+     ((EPI) & 8) ? 1 : 0, (EPI) & 1, ((EPI) & 64) ? 1 : 0},

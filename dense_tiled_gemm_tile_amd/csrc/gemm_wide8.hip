@@ -3,10 +3,10 @@
 #include "gemm_wide.h"
 
 #define TG_WIDE8_LIST(X)                           \
-    X(10, TG_E4M3, 4, 5, 16, 1, 1, 17, 107)        \
-    X(11, TG_E5M2, 4, 5, 16, 1, 1, 17, 107)        \
-    X(12, TG_E4M3, 4, 5, 16, 1, 1, 81, 90)         \
-    X(13, TG_E5M2, 4, 5, 16, 1, 1, 81, 90)
+    X(10, TG_E4M3, 4, 5, 16, 1, 1, 17, 16, 107)        \
+    X(11, TG_E5M2, 4, 5, 16, 1, 1, 17, 16, 107)        \
+    X(12, TG_E4M3, 4, 5, 16, 1, 1, 81, 16, 90)         \
+    X(13, TG_E5M2, 4, 5, 16, 1, 1, 81, 16, 90)
 
 TG_WIDE8_LIST(TG_INSTANTIATE_WIDE)
 
