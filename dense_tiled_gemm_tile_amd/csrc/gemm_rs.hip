@@ -327,34 +327,30 @@ static hipError_t launch_rs(const GemmArgs& a, int64_t grid, int batch, hipStrea
 // host plan chooser weighs tiles by (instances with the 2-byte shifting loader
 // measure about 0.8x their 4-byte twins).
 #define TG_RS_LIST(X)                              \
-    X(19, TG_BF16, 256, 256, 4, 1, 4, 0, 70)       \
-    X(20, TG_BF16, 256, 256, 2, 1, 4, 0, 56)       \
-    X(21, TG_F16, 256, 256, 4, 1, 4, 0, 70)        \
-    X(22, TG_F16, 256, 256, 2, 1, 4, 0, 56)        \
-    X(23, TG_BF16, 128, 128, 4, 2, 4, 1, 45)       \
-    X(24, TG_BF16, 128, 128, 2, 2, 4, 1, 36)       \
-    X(25, TG_F16, 128, 128, 4, 2, 4, 1, 45)        \
-    X(26, TG_F16, 128, 128, 2, 2, 4, 1, 36)        \
-    X(27, TG_F32, 128, 128, 4, 2, 4, 1, 45)        \
-    X(28, TG_BF16, 64, 64, 4, 2, 4, 1, 25)         \
-    X(29, TG_F16, 64, 64, 4, 2, 4, 1, 25)          \
-    X(30, TG_F32, 64, 64, 4, 2, 4, 1, 25)          \
-    X(31, TG_BF16, 64, 64, 2, 2, 4, 1, 20)         \
-    X(32, TG_F16, 64, 64, 2, 2, 4, 1, 20)          \
-    X(33, TG_BF16, 256, 256, 4, 1, 4, 1, 69)       \
-    X(34, TG_BF16, 256, 256, 2, 1, 4, 1, 55)       \
-    X(35, TG_F16, 256, 256, 4, 1, 4, 1, 69)        \
-    X(36, TG_F16, 256, 256, 2, 1, 4, 1, 55)        \
-    X(37, TG_E4M3, 256, 256, 4, 1, 4, 0, 70)       \
-    X(38, TG_E4M3, 256, 256, 1, 1, 4, 0, 56)       \
-    X(39, TG_E4M3, 128, 128, 4, 2, 4, 0, 45)       \
-    X(40, TG_E4M3, 64, 64, 4, 2, 4, 0, 25)         \
-    X(41, TG_E4M3, 64, 64, 1, 2, 4, 0, 20)         \
-    X(42, TG_E5M2, 256, 256, 4, 1, 4, 0, 70)       \
-    X(43, TG_E5M2, 256, 256, 1, 1, 4, 0, 56)       \
-    X(44, TG_E5M2, 128, 128, 4, 2, 4, 0, 45)       \
-    X(45, TG_E5M2, 64, 64, 4, 2, 4, 0, 25)         \
-    X(46, TG_E5M2, 64, 64, 1, 2, 4, 0, 20)
+    X(19, TG_BF16, 128, 128, 4, 2, 4, 1, 45)       \
+    X(20, TG_BF16, 128, 128, 2, 2, 4, 1, 36)       \
+    X(21, TG_F16, 128, 128, 4, 2, 4, 1, 45)        \
+    X(22, TG_F16, 128, 128, 2, 2, 4, 1, 36)        \
+    X(23, TG_F32, 128, 128, 4, 2, 4, 1, 45)        \
+    X(24, TG_BF16, 64, 64, 4, 2, 4, 1, 25)         \
+    X(25, TG_F16, 64, 64, 4, 2, 4, 1, 25)          \
+    X(26, TG_F32, 64, 64, 4, 2, 4, 1, 25)          \
+    X(27, TG_BF16, 64, 64, 2, 2, 4, 1, 20)         \
+    X(28, TG_F16, 64, 64, 2, 2, 4, 1, 20)          \
+    X(29, TG_BF16, 256, 256, 4, 1, 4, 1, 69)       \
+    X(30, TG_BF16, 256, 256, 2, 1, 4, 1, 55)       \
+    X(31, TG_F16, 256, 256, 4, 1, 4, 1, 69)        \
+    X(32, TG_F16, 256, 256, 2, 1, 4, 1, 55)        \
+    X(33, TG_E4M3, 256, 256, 4, 1, 4, 0, 70)       \
+    X(34, TG_E4M3, 256, 256, 1, 1, 4, 0, 56)       \
+    X(35, TG_E4M3, 128, 128, 4, 2, 4, 0, 45)       \
+    X(36, TG_E4M3, 64, 64, 4, 2, 4, 0, 25)         \
+    X(37, TG_E4M3, 64, 64, 1, 2, 4, 0, 20)         \
+    X(38, TG_E5M2, 256, 256, 4, 1, 4, 0, 70)       \
+    X(39, TG_E5M2, 256, 256, 1, 1, 4, 0, 56)       \
+    X(40, TG_E5M2, 128, 128, 4, 2, 4, 0, 45)       \
+    X(41, TG_E5M2, 64, 64, 4, 2, 4, 0, 25)         \
+    X(42, TG_E5M2, 64, 64, 1, 2, 4, 0, 20)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \

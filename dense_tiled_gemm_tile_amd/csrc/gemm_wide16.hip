@@ -6,8 +6,9 @@
 // 128-byte lines (nontemporal stores of the partial lines at the tile edges
 // measured about 20 % slower), fp32 D through the LDS transpose; 4/5: 64-bit
 // addresses for row strides beyond 8 MiB; 6/7: with the softmax epilogue;
-// 47-50: operand rows only 4- or 2-byte aligned, copied through registers
-// (47/48 with the plain-store epilogue of 2/3, 49/50 with that of 0/1).
+// 43-46: operand rows only 4- or 2-byte aligned, copied through registers
+// (43/44 with the nontemporal-store epilogue of 0/1, 45/46 with the
+// plain-store one of 2/3).
 #define TG_WIDE16_LIST(X)                          \
     X(0, TG_BF16, 4, 5, 16, 1, 1, 17, 16, 107)         \
     X(1, TG_F16, 4, 5, 16, 1, 1, 17, 16, 107)          \
@@ -17,10 +18,10 @@
     X(5, TG_F16, 4, 5, 16, 0, 0, 0, 16, 105)           \
     X(6, TG_BF16, 4, 5, 16, 1, 1, 13, 16, 106)         \
     X(7, TG_F16, 4, 5, 16, 1, 1, 13, 16, 106)          \
-    X(47, TG_BF16, 4, 4, 16, 1, 0, 18, 2, 95)          \
-    X(48, TG_F16, 4, 4, 16, 1, 0, 18, 2, 95)           \
-    X(49, TG_BF16, 4, 4, 16, 1, 0, 17, 2, 95)          \
-    X(50, TG_F16, 4, 4, 16, 1, 0, 17, 2, 95)
+    X(43, TG_BF16, 4, 4, 16, 1, 0, 17, 2, 95)          \
+    X(44, TG_F16, 4, 4, 16, 1, 0, 17, 2, 95)           \
+    X(45, TG_BF16, 4, 4, 16, 1, 0, 18, 2, 95)          \
+    X(46, TG_F16, 4, 4, 16, 1, 0, 18, 2, 95)
 
 TG_WIDE16_LIST(TG_INSTANTIATE_WIDE)
 

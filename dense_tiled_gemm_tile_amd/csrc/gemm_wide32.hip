@@ -4,12 +4,12 @@
 #include "gemm_wide.h"
 
 // 8: buffer addressing, nontemporal stores; 9: 64-bit addresses and plain
-// stores (row strides beyond 8 MiB, D columns not on 128-byte lines); 51:
+// stores (row strides beyond 8 MiB, D columns not on 128-byte lines); 47:
 // rows only 4-byte aligned, copied through registers.
 #define TG_WIDE32_LIST(X)                          \
     X(8, TG_F32, 4, 5, 16, 1, 1, 5, 16, 96)            \
     X(9, TG_F32, 4, 5, 16, 0, 0, 0, 16, 93)            \
-    X(51, TG_F32, 4, 4, 16, 1, 0, 18, 4, 88)
+    X(47, TG_F32, 4, 4, 16, 1, 0, 18, 4, 88)
 
 TG_WIDE32_LIST(TG_INSTANTIATE_WIDE)
 
