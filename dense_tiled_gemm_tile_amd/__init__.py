@@ -46,7 +46,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "kernel_id", "dtype", "block_m", "block_n", "block_k", "waves_m", "waves_n",
         "wave_tile_m", "wave_tile_n", "threads", "stages", "lds_bytes", "acc_per_lane",
-        "load_class", "group_m", "staged")] + [
+        "load_class", "group_m", "staged", "k_slices")] + [
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:

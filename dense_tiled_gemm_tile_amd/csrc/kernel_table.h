@@ -74,6 +74,7 @@ struct TgKernelDesc {
     int softmax;             // 1: the epilogue can also take a softmax over n (N <= block_n)
     int nt_store;            // 1: D is written with nontemporal stores
     int block_scales;        // 1: 8-bit instance that applies block scales (GemmArgs::scale_a/b)
+    int k_slices;            // waves that split K inside a workgroup, each over the whole tile (0: 1)
 };
 
 // Element bytes of an operand type.
@@ -90,6 +91,8 @@ extern const TgKernelDesc tg_entries_stream[];
 extern const int tg_entries_stream_count;
 extern const TgKernelDesc tg_entries_rs[];
 extern const int tg_entries_rs_count;
+extern const TgKernelDesc tg_entries_kslice[];
+extern const int tg_entries_kslice_count;
 
 // The instance table, indexed by kernel id (ids are 0 .. tg_kernel_count()-1).
 int tg_kernel_count();

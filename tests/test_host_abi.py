@@ -177,8 +177,9 @@ def test_every_instance_has_consistent_ownership_arithmetic():
     for k in range(tg.kernel_count()):
         info = tg.kernel_info(k)
         assert info.kernel_id == k
-        assert info.acc_per_lane * info.threads == info.block_m * info.block_n
-        assert info.threads == 64 * info.waves_m * info.waves_n
+        # K-sliced instances hold k_slices copies of the tile (summed at the end)
+        assert info.acc_per_lane * info.threads == info.block_m * info.block_n * info.k_slices
+        assert info.threads == 64 * info.waves_m * info.waves_n * info.k_slices
         assert info.wave_tile_m * info.waves_m == info.block_m
         assert info.wave_tile_n * info.waves_n == info.block_n
         es = {tg.F32: 4, tg.E4M3: 1, tg.E5M2: 1}.get(info.dtype, 2)
@@ -361,10 +362,11 @@ def test_staging_decision_scales_with_the_problem():
 
 def test_plan_choices_follow_the_kernel_trace_table():
     """The automatic choice for aligned bf16 operands is the instance that was
-    fastest in the kernel trace for each of these shapes (small streaming 64^2
-    for long-K few-tile products, 128^2 at 2048^2, the wide kernel beyond)."""
+    fastest in the kernel trace for each of these shapes (the K-sliced 64^2
+    when at most half the CUs get a tile, small streaming 64^2 for 1024^2
+    outputs, 128^2 at 2048^2, the wide kernel beyond)."""
     A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
-    expect = {(1024, 1024, 1024): 14, (2048, 2048, 2048): 16, (512, 512, 16384): 14, (1024, 1024, 4096): 14,
+    expect = {(1024, 1024, 1024): 14, (2048, 2048, 2048): 16, (512, 512, 16384): 48, (1024, 1024, 4096): 14,
               (2048, 2048, 8192): 16, (4096, 4096, 1024): 0, (3072, 3072, 3072): 0}
     for (M, N, K), kid in expect.items():
         assert tg.query_plan(M, N, K, tg.BF16, A2, K, B2, K, D2, M).kernel_id == kid, (M, N, K)
