@@ -47,12 +47,17 @@ def _kernels(text: str):
 
 
 def _loops(lines):
-    """(header, back-edge) line index pairs of the loops in a function body."""
+    """(header, back-edge) line index pairs of the loops in a function body
+    (the compiler marks loop headers with a comment; the label is on that
+    line or the one before)."""
     out = []
     for h, line in enumerate(lines):
-        if "Loop Header" in line:
-            label = line.split(":")[0]
-            back = [i for i, l in enumerate(lines) if re.search(r"s_c?branch\w* " + re.escape(label) + r"\s*$", l)]
+        if "Loop Header" not in line:
+            continue
+        lab = next(lines[i] for i in range(h, -1, -1) if lines[i].startswith(".LBB"))
+        label = lab.split(":")[0]
+        back = [i for i, l in enumerate(lines) if i > h and re.search(r"s_c?branch\w* " + re.escape(label) + r"\b", l)]
+        if back:
             out.append((h, max(back)))
     return out
 
@@ -66,7 +71,9 @@ def test_wide_kernels_keep_their_loops_free_of_spills(wide_asm):
         epi = args[6]
         loops = _loops(lines)
         assert loops, name
-        mfma_loop = [(a, b) for a, b in loops if any("v_mfma" in lines[i] for i in range(a, b + 1))]
+        # the K loop: the innermost loop with MFMAs (an outer loop walks the tiles)
+        mfma_loop = [(a, b) for a, b in loops if any("v_mfma" in lines[i] for i in range(a, b + 1))
+                     and not any(a < h <= b for h, _ in loops)]
         assert len(mfma_loop) == 1, (name, loops)
         a, b = mfma_loop[0]
         spills = [lines[i].strip() for i in range(a, b + 1) if re.search(r"\bscratch_(load|store)", lines[i])]
