@@ -117,14 +117,18 @@ def summarize_profile(prof: Path, key: str, flops: float, alg_bytes: float, peak
     rd, wr = fetch * 1024 * scale["FETCH_SIZE"], write * 1024 * scale["WRITE_SIZE"]
     mops = [c for c in a[0] if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
     mfma_flops = sum(mean(a, c) for c in mops) * 512
+    # GRBM_GUI_ACTIVE covers more than the dispatch itself (the counter window
+    # opens before the first wave and closes after the last), which only
+    # matters for short kernels: no clock or busy fraction below 50 us
+    short = avg_ns < 50e3
     entry = {
         "kernel": kernel, "source_hash": kernel_source_hash(kernel),
         "sources": [p.name for p in kernel_sources(kernel)],
         "trace_average_ns": round(avg_ns), "trace_calls": int(top["Calls"]),
-        "effective_sclk_ghz": round(sum(clocks) / len(clocks), 3),
-        "mfma_busy_frac": round(sum(busy) / len(busy), 4),
+        "effective_sclk_ghz": None if short else round(sum(clocks) / len(clocks), 3),
+        "mfma_busy_frac": None if short else round(sum(busy) / len(busy), 4),
         "mfma_util_pct_rocprof": round(mean(b, "MfmaUtil"), 2) if b and "MfmaUtil" in b[0] else None,
-        "frac_from_counters": round(sum(frac) / len(frac), 4),
+        "frac_from_counters": None if short else round(sum(frac) / len(frac), 4),
         "frac_from_duration": round(sum(frac_time) / len(frac_time), 4),
         "mfma_flops_counted": mfma_flops, "flops_2mnk": flops,
         "mfma_insts": mean(a, "SQ_INSTS_MFMA"), "valu_insts": mean(a, "SQ_INSTS_VALU"),
@@ -145,7 +149,9 @@ def summarize_profile(prof: Path, key: str, flops: float, alg_bytes: float, peak
         f"{avg_ns:.0f} ns, min {float(top['MinNs']):.0f} ns, max {float(top['MaxNs']):.0f} ns; "
         f"{flops / avg_ns / 1e3:.1f} TFLOP/s at the average (2MNK/t), {flops / avg_ns / 1e3 / peak:.4f} of "
         f"the {peak} TFLOP/s dense peak.", "",
-        "Counters per dispatch (the first launch of each counter run left out):", "",
+        "Counters per dispatch (the first launch of each counter run left out)" + (
+            "; the kernel is shorter than 50 us, so the clock and busy columns, which divide by the "
+            "GRBM_GUI_ACTIVE window (longer than the dispatch), are not meaningful here:" if short else ":"), "",
         "| dispatch ms | effective SCLK GHz (GRBM_GUI_ACTIVE / 8 XCDs / duration) | MFMA busy "
         "(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)) | busy x SCLK / 2.4 GHz | 2MNK / t / peak |",
         "|---|---|---|---|---|",
