@@ -17,8 +17,10 @@ Storage follows the Tylo manual, section 2: A is (M,K) stored K-contiguous with
 leading stride lda (element m*lda + k), B is (K,N) stored K-contiguous with
 leading stride ldb (element k + n*ldb).  Arrays passed here are the raw storage:
 ``uint16`` bit patterns for bf16/fp16, ``float32`` for fp32, ``uint8`` for the
-8-bit formats e4m3/e5m2, which may carry block scales (``ref_gemm.c`` states
-the formats and the scale reading).
+8-bit formats e4m3/e5m2 and for the packed bytes of the 4-bit (e2m1) and 6-bit
+(e2m3, e3m2) formats, which may all carry block scales (``ref_gemm.c`` states
+the formats, the packing and the scale reading).  Leading strides and element
+counts are in elements for every format.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, exact integer and rational arithmetic, and library decoders.
@@ -32,8 +34,11 @@ from pathlib import Path
 
 import numpy as np
 
-BF16, F16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
-_DTYPES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2}
+BF16, F16, F32, E4M3, E5M2, E2M1, E2M3, E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
+_DTYPES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2,
+           "e2m1": E2M1, "e2m3": E2M3, "e3m2": E3M2}
+# bits per element; the 4- and 6-bit formats are packed (ref_gemm.c states how)
+_BITS = {BF16: 16, F16: 16, F32: 32, E4M3: 8, E5M2: 8, E2M1: 4, E2M3: 6, E3M2: 6}
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "ref_gemm.c"
@@ -132,21 +137,34 @@ def _code(dtype) -> int:
     return _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
 
 
+def bits(dtype) -> int:
+    """Bits per stored element of a dtype."""
+    return _BITS[_code(dtype)]
+
+
 def _storage(arr: np.ndarray, dtype: int) -> np.ndarray:
-    want = np.float32 if dtype == F32 else np.uint8 if dtype in (E4M3, E5M2) else np.uint16
+    want = np.float32 if dtype == F32 else np.uint8 if _BITS[dtype] <= 8 else np.uint16
     arr = np.ascontiguousarray(arr)
     if arr.dtype != want:
         raise TypeError(f"storage for dtype {dtype} must be {np.dtype(want)}, got {arr.dtype}")
     return arr
 
 
-def decode(bits: np.ndarray, dtype, lib=None) -> np.ndarray:
+def decode(bits: np.ndarray, dtype, lib=None, count=None) -> np.ndarray:
     """Decode raw storage (uint16 for bf16/fp16, float32 for fp32, uint8 for
-    e4m3/e5m2) to fp64."""
+    e4m3/e5m2 and for packed e2m1/e2m3/e3m2) to fp64.  Packed storage decodes
+    to a flat array of ``count`` elements (default: every whole element the
+    bytes hold); other storage keeps its shape."""
     dt = _code(dtype)
     src = _storage(np.asarray(bits), dt)
-    out = np.empty(src.shape, dtype=np.float64)
-    rc = (lib or _load()).oracle_decode(src.ctypes.data, dt, src.size, out.ctypes.data)
+    if _BITS[dt] < 8:
+        n = src.size * 8 // _BITS[dt] if count is None else int(count)
+        if n < 0 or n * _BITS[dt] > src.size * 8:
+            raise ValueError("count exceeds the packed storage")
+        out = np.empty(n, dtype=np.float64)
+    else:
+        out = np.empty(src.shape, dtype=np.float64)
+    rc = (lib or _load()).oracle_decode(src.ctypes.data, dt, out.size, out.ctypes.data)
     if rc:
         raise ValueError(f"oracle_decode failed ({rc})")
     return out
@@ -183,7 +201,7 @@ def gemm(M, N, K, alpha, relu, A, lda, B, ldb, dtype, n0=0, n1=None, threads=Non
 
     A is the raw storage of A (at least (M-1)*lda + K elements, row-major
     (M, lda) is the usual shape), B likewise for B ((N, ldb)).  For the
-    8-bit formats, scale_a / scale_b are optional block-scale exponents
+    8-, 6- and 4-bit formats, scale_a / scale_b are optional block-scale exponents
     (uint8, byte m*lds_a + k//32 for A row m, n*lds_b + k//32 for B column n).
     Returns ``(ref, mag)``, both float64 arrays of shape (n1 - n0, M): row j
     holds output column n0 + j, i.e. the M-contiguous storage of the result.

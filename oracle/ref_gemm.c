@@ -35,11 +35,28 @@
  *   e5m2: 8-bit float, 1 sign, 5 exponent bits with bias 15, 2 fraction
  *         bits; subnormals fraction * 2^-16; exponent 31 is infinity
  *         (fraction 0) or NaN, as in the IEEE formats.
+ *   e2m1: 4-bit float (the MX FP4 element), 1 sign, 2 exponent bits with
+ *         bias 1, 1 fraction bit; exponent 0 holds zero and the subnormal
+ *         0.5 (fraction * 2^-1); every code is finite (largest 6);
+ *   e2m3: 6-bit float (MX FP6, E2M3), 1 sign, 2 exponent bits with bias 1,
+ *         3 fraction bits; subnormals fraction * 2^-3; all finite (largest
+ *         7.5);
+ *   e3m2: 6-bit float (MX FP6, E3M2), 1 sign, 3 exponent bits with bias 3,
+ *         2 fraction bits; subnormals fraction * 2^-4; all finite (largest
+ *         28).
+ * The pages name FP4 among the block-scaled matmul formats without defining
+ * it; the plain reading is the OCP microscaling (MX) element formats above.
  * Every decoded value is exactly representable in fp64.
  *
- * Block scales (8-bit operands only; the pages name block-scaled 8-bit
- * matmuls but do not define them, so the plain reading of the MX formats is
- * taken): an optional unsigned 8-bit exponent per 32 consecutive k of every
+ * Packing of the 4- and 6-bit formats: element i of a stored array occupies
+ * bits [w*i, w*i + w) of the array read as one little-endian bit string (bit
+ * j of byte x is bit 8x + j), w = 4 or 6: two fp4 elements per byte, low
+ * nibble first, and four fp6 elements in every three bytes.  Element indices
+ * (m*lda + k, k + n*ldb) count elements, not bytes.
+ *
+ * Block scales (8-, 6- and 4-bit operands; the pages name block-scaled 8-bit
+ * and 4-bit matmuls but do not define them, so the plain reading of the MX
+ * formats is taken): an optional unsigned 8-bit exponent per 32 consecutive k of every
  * A row and every B column, value 2^(e - 127), e = 255 meaning NaN.  With
  * scales, a[m,k] stands for decode(a[m,k]) * 2^(sa[m, k/32] - 127), and b
  * likewise with sb[n, k/32]; the scale of A row m for k-block j is byte
@@ -53,7 +70,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_F32 = 3, ORACLE_E4M3 = 4, ORACLE_E5M2 = 5 };
+enum { ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_F32 = 3, ORACLE_E4M3 = 4, ORACLE_E5M2 = 5,
+       ORACLE_E2M1 = 6, ORACLE_E2M3 = 7, ORACLE_E3M2 = 8 };
 
 double oracle_decode_bf16(uint16_t bits) {
     uint32_t word = (uint32_t)bits << 16;
@@ -110,16 +128,68 @@ double oracle_decode_e5m2(uint8_t bits) {
     return sign ? -v : v;
 }
 
+double oracle_decode_e2m1(uint8_t bits) {
+    int sign = (bits >> 3) & 1;
+    int expo = (bits >> 1) & 3;
+    int frac = bits & 1;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -1);              /* zero and the subnormal 0.5 */
+    else
+        v = ldexp((double)(2 + frac), expo - 2);  /* (1 + f/2) * 2^(e-1) */
+    return sign ? -v : v;
+}
+
+double oracle_decode_e2m3(uint8_t bits) {
+    int sign = (bits >> 5) & 1;
+    int expo = (bits >> 3) & 3;
+    int frac = bits & 7;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -3);              /* zero and subnormals */
+    else
+        v = ldexp((double)(8 + frac), expo - 4);  /* (1 + f/8) * 2^(e-1) */
+    return sign ? -v : v;
+}
+
+double oracle_decode_e3m2(uint8_t bits) {
+    int sign = (bits >> 5) & 1;
+    int expo = (bits >> 2) & 7;
+    int frac = bits & 3;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -4);              /* zero and subnormals */
+    else
+        v = ldexp((double)(4 + frac), expo - 5);  /* (1 + f/4) * 2^(e-3) */
+    return sign ? -v : v;
+}
+
+/* The w-bit code of element idx of a packed array (w = 4 or 6): bits
+ * [w*idx, w*idx + w) of the little-endian bit string.  Only the bytes that
+ * hold those bits are read. */
+static uint8_t packed_code(const uint8_t* base, int w, int64_t idx) {
+    const int64_t bit = (int64_t)w * idx;
+    const int64_t byte = bit >> 3;
+    const int sh = (int)(bit & 7);
+    unsigned v = base[byte] >> sh;
+    if (sh + w > 8) v |= (unsigned)base[byte + 1] << (8 - sh);
+    return (uint8_t)(v & ((1u << w) - 1u));
+}
+
 /* Block scale: 2^(e - 127), e = 255 is NaN. */
 double oracle_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
 
-static int elem_size(int dtype) {
+/* Bits per stored element (0: unknown dtype). */
+static int elem_bits(int dtype) {
     switch (dtype) {
-        case ORACLE_F32: return 4;
+        case ORACLE_F32: return 32;
         case ORACLE_BF16:
-        case ORACLE_F16: return 2;
+        case ORACLE_F16: return 16;
         case ORACLE_E4M3:
-        case ORACLE_E5M2: return 1;
+        case ORACLE_E5M2: return 8;
+        case ORACLE_E2M3:
+        case ORACLE_E3M2: return 6;
+        case ORACLE_E2M1: return 4;
         default: return 0;
     }
 }
@@ -130,6 +200,9 @@ static double decode_at(const void* base, int dtype, int64_t idx) {
         case ORACLE_F16: return oracle_decode_f16(((const uint16_t*)base)[idx]);
         case ORACLE_E4M3: return oracle_decode_e4m3(((const uint8_t*)base)[idx]);
         case ORACLE_E5M2: return oracle_decode_e5m2(((const uint8_t*)base)[idx]);
+        case ORACLE_E2M1: return oracle_decode_e2m1(packed_code((const uint8_t*)base, 4, idx));
+        case ORACLE_E2M3: return oracle_decode_e2m3(packed_code((const uint8_t*)base, 6, idx));
+        case ORACLE_E3M2: return oracle_decode_e3m2(packed_code((const uint8_t*)base, 6, idx));
         default: return oracle_decode_f32(((const uint32_t*)base)[idx]);
     }
 }
@@ -145,7 +218,7 @@ static double scaled_at(const void* base, int dtype, int64_t rowoff, int64_t k, 
 
 /* Decode `count` stored elements into fp64 (used by tests of the decoders). */
 int oracle_decode(const void* src, int dtype, int64_t count, double* dst) {
-    if (!elem_size(dtype)) return -5;
+    if (!elem_bits(dtype)) return -5;
     for (int64_t i = 0; i < count; ++i) dst[i] = decode_at(src, dtype, i);
     return 0;
 }
@@ -270,16 +343,20 @@ static int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t ld
                       const void* B, int64_t ldb, int dtype) {
     if (M < 0 || N < 0 || K < 0) return -1;
     if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1)) return -2;
-    if (!elem_size(dtype)) return -5;
+    const int w = elem_bits(dtype);
+    if (!w) return -5;
+    /* packed formats: every row and column starts on a byte boundary */
+    if (w < 8 && (((lda * w) & 7) || ((ldb * w) & 7))) return -2;
     if (K > 0 && ((M > 0 && !A) || (N > 0 && !B))) return -3;
     return 0;
 }
 
-/* Scales are for 8-bit operands only; each row holds ceil(K/32) of them. */
+/* Scales are for the 8-, 6- and 4-bit formats only; each row holds
+ * ceil(K/32) of them. */
 static int check_scales(int64_t K, int dtype, const uint8_t* sa, int64_t lds_a, const uint8_t* sb,
                         int64_t lds_b) {
     if (!sa && !sb) return 0;
-    if (elem_size(dtype) != 1) return -5;
+    if (elem_bits(dtype) > 8) return -5;
     const int64_t blocks = (K + 31) / 32;
     if ((sa && lds_a < blocks) || (sb && lds_b < blocks)) return -2;
     return 0;

@@ -22,6 +22,13 @@ Pins used:
     the stride padding never reaches the result, the alpha-then-clamp order of
     the scalar epilogue (Tylo.jl manual, "Walk through GEMM", section 5),
     sampled entries equal the full result, K = 0 gives zeros;
+  * the 4- and 6-bit formats (e2m1, e2m3, e3m2): every normal code against
+    torch's float8_e4m3fn decoding of the same sign, exponent and fraction
+    re-biased into e4m3 (every such value is an e4m3 value), zero and
+    subnormal codes and hand-packed byte strings against a golden table
+    written from the MX format definitions, and packed products (odd K,
+    padded strides, block scales) against numpy on values unpacked with
+    numpy's own bit unpacking;
   * the 16-bit output encoder (round to nearest, ties to even): every finite
     bf16/fp16 value encodes to itself, fp16 agrees with numpy's float64 ->
     float16 conversion and bf16 with torch's float32 -> bfloat16 conversion
@@ -369,11 +376,133 @@ def pin_fp8_gemm_brute_force(lib):
         assert np.isnan(ref2[:, 2]).all() and np.isfinite(np.delete(ref2, 2, axis=1)).all()
 
 
+# ------------------------------------------------------------- 4- and 6-bit formats
+
+# bits per element, exponent bits, fraction bits, exponent bias (MX FP4/FP6 element formats)
+_NARROW = {"e2m1": (4, 2, 1, 1), "e2m3": (6, 2, 3, 1), "e3m2": (6, 3, 2, 3)}
+
+
+def _narrow_golden():
+    codes: dict = {dt: {} for dt in _NARROW}
+    packed = []
+    for line in (GOLDEN.parent / "mx_narrow_codes.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        kind, dt, hx, rest = line.split(None, 3)
+        if kind == "code":
+            num, den = rest.split()
+            codes[dt][int(hx, 16)] = Fraction(int(num), int(den))
+        else:
+            vals = [Fraction(int(a), int(b)) for a, b in (v.split("/") for v in rest.split(","))]
+            packed.append((dt, bytes.fromhex(hx), vals))
+    return codes, packed
+
+
+def _narrow_table(dt) -> np.ndarray:
+    """The value of every code of a 4- or 6-bit format, without the oracle:
+    normal codes become the e4m3 bit pattern with the same sign, exponent
+    (re-biased from the format's bias to 7) and fraction (left-aligned in the
+    3 fraction bits) and are decoded by torch's float8_e4m3fn; zero and
+    subnormal codes come from the golden table (a negative code is the
+    negation of its positive twin)."""
+    w, eb, mb, bias = _NARROW[dt]
+    golden = _narrow_golden()[0][dt]
+    out = np.empty(1 << w)
+    for c in range(1 << w):
+        sign, e, m = c >> (w - 1), (c >> mb) & ((1 << eb) - 1), c & ((1 << mb) - 1)
+        if e == 0:
+            v = float(golden[c & ((1 << (w - 1)) - 1)])
+            out[c] = -v if sign else v
+        else:
+            bits = (sign << 7) | ((e - bias + 7) << 3) | (m << (3 - mb))
+            out[c] = torch.tensor([bits], dtype=torch.uint8).view(torch.float8_e4m3fn).double().item()
+    return out
+
+
+def _pack(codes: np.ndarray, w: int) -> np.ndarray:
+    """Pack w-bit codes (last axis) into bytes, little-endian bit order, with
+    numpy's bit packing."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    bits = np.unpackbits(codes[..., None], axis=-1, bitorder="little")[..., :w]
+    flat = bits.reshape(*codes.shape[:-1], codes.shape[-1] * w)
+    return np.packbits(flat, axis=-1, bitorder="little")
+
+
+def _unpack(storage: np.ndarray, w: int, count: int) -> np.ndarray:
+    """Codes of the first `count` w-bit elements of each row of packed bytes."""
+    bits = np.unpackbits(np.asarray(storage, dtype=np.uint8), axis=-1, bitorder="little")
+    bits = bits[..., : count * w].reshape(*storage.shape[:-1], count, w)
+    return (bits * (1 << np.arange(w))).sum(axis=-1).astype(np.int64)
+
+
+def pin_narrow_decode(lib):
+    """Every code of e2m1, e2m3 and e3m2 decodes to the value of the
+    torch-based table, and the golden rows hold exactly."""
+    golden, _ = _narrow_golden()
+    for dt, (w, _, _, _) in _NARROW.items():
+        table = _narrow_table(dt)
+        codes = np.arange(1 << w, dtype=np.uint8)
+        got = oracle.decode(_pack(codes, w), dt, lib=lib, count=1 << w)
+        assert np.array_equal(got, table), dt
+        for c, v in golden[dt].items():
+            assert Fraction(float(got[c])) == v, (dt, hex(c), got[c], v)
+        assert table.max() == {"e2m1": 6.0, "e2m3": 7.5, "e3m2": 28.0}[dt]
+
+
+def pin_narrow_packing_golden(lib):
+    """Hand-packed byte strings decode element by element to the listed
+    values (fp4 nibble order, fp6 elements straddling bytes)."""
+    _, packed = _narrow_golden()
+    for dt, raw, vals in packed:
+        got = oracle.decode(np.frombuffer(raw, dtype=np.uint8), dt, lib=lib, count=len(vals))
+        assert [Fraction(float(g)) for g in got] == vals, (dt, raw.hex(), list(got))
+
+
+def pin_narrow_gemm_brute_force(lib):
+    """Packed 4- and 6-bit products against numpy on values unpacked by
+    numpy and looked up in the torch-based table: exact without scales (every
+    value and sum is a small multiple of 2^-4, exact in fp64), within 2^-50 of
+    the summed magnitudes with block scales; padding codes past K are large
+    and would show if read."""
+    rng = np.random.default_rng(17)
+    M, N = 5, 6
+    for dt, (w, _, _, _) in _NARROW.items():
+        K = 69 if w == 4 else 70
+        lda, ldb = (72, 76) if w == 4 else (72, 80)   # whole bytes per row
+        top = (1 << (w - 1)) - 1                        # the largest positive code
+        A = np.full((M, lda), top, dtype=np.uint8)
+        B = np.full((N, ldb), top, dtype=np.uint8)
+        A[:, :K] = rng.integers(0, 1 << w, size=(M, K))
+        B[:, :K] = rng.integers(0, 1 << w, size=(N, K))
+        pa, pb = _pack(A, w), _pack(B, w)
+        table = _narrow_table(dt)
+        a = table[_unpack(pa, w, K)]
+        b = table[_unpack(pb, w, K)]
+        ref, mag = oracle.gemm(M, N, K, 0.75, False, pa.ravel(), lda, pb.ravel(), ldb, dt, lib=lib)
+        assert np.array_equal(ref, (0.75 * (a @ b.T)).T), dt
+        assert np.array_equal(mag, (0.75 * (np.abs(a) @ np.abs(b).T)).T), dt
+        lds_a, lds_b = 3, 4
+        sa = rng.integers(120, 135, size=(M, lds_a)).astype(np.uint8)
+        sb = rng.integers(120, 135, size=(N, lds_b)).astype(np.uint8)
+        blk = np.arange(K) // 32
+        a_s = a * np.exp2(sa[:, blk].astype(np.float64) - 127)
+        b_s = b * np.exp2(sb[:, blk].astype(np.float64) - 127)
+        ref, _ = oracle.gemm(M, N, K, 0.75, True, pa.ravel(), lda, pb.ravel(), ldb, dt, lib=lib, scale_a=sa,
+                             lds_a=lds_a, scale_b=sb, lds_b=lds_b)
+        want = np.maximum(0.75 * (a_s @ b_s.T), 0).T
+        assert np.all(np.abs(ref - want) <= 2.0 ** -50 * (0.75 * (np.abs(a_s) @ np.abs(b_s).T)).T), dt
+        ms, ns = np.array([0, 4, 2]), np.array([5, 0, 3])
+        e, _ = oracle.gemm_entries(M, N, K, 0.75, True, pa.ravel(), lda, pb.ravel(), ldb, dt, ms, ns, lib=lib,
+                                   scale_a=sa, lds_a=lds_a, scale_b=sb, lds_b=lds_b)
+        assert np.array_equal(e, ref[ns, ms]), dt
+
+
 PINS = [pin_decode_golden, pin_decode_all_patterns, pin_permutation, pin_identity, pin_rank1,
         pin_small_integers, pin_tiny_rational, pin_zero_padded_k, pin_nan_padding_unread,
         pin_alpha_then_relu, pin_entries_and_column_ranges, pin_degenerate,
         pin_encode_roundtrip, pin_encode_f16_vs_numpy, pin_encode_bf16_vs_torch, pin_encode_golden,
-        pin_fp8_decode_vs_torch, pin_fp8_gemm_brute_force]
+        pin_fp8_decode_vs_torch, pin_fp8_gemm_brute_force,
+        pin_narrow_decode, pin_narrow_packing_golden, pin_narrow_gemm_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -396,6 +525,12 @@ MUTATIONS = {
     "scale_block_16": ("scales[scale_off + k / 32]", "scales[scale_off + k / 16]"),
     "scale_b_dropped": ("p.sb = sb; p.lds_b = lds_b;\n    int64_t cols", "p.lds_b = lds_b;\n    int64_t cols"),
     "e8m0_bias_128": ("(int)e - 127", "(int)e - 128"),
+    "e2m1_bias_2": ("ldexp((double)(2 + frac), expo - 2)", "ldexp((double)(2 + frac), expo - 3)"),
+    "e2m3_fraction_scale": ("ldexp((double)(8 + frac), expo - 4)", "ldexp((double)(8 + frac), expo - 3)"),
+    "e3m2_subnormal_scale": ("ldexp((double)frac, -4);", "ldexp((double)frac, -3);"),
+    "e2m1_sign_bit": ("int sign = (bits >> 3) & 1;", "int sign = (bits >> 2) & 1;"),
+    "fp4_high_nibble_first": ("const int sh = (int)(bit & 7);", "const int sh = (int)((bit & 7) ^ (w == 4 ? 4 : 0));"),
+    "fp6_no_straddle": ("if (sh + w > 8) v |=", "if (0) v |="),
     "f16_subnormal_flush": ("v = ldexp((double)frac, -24);", "v = 0.0;"),
     "f16_bias_off_by_one": ("expo - 25", "expo - 24"),
     "bf16_wrong_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
