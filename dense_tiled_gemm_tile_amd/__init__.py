@@ -12,7 +12,10 @@ through ``tile_gemm_out``).  ``gemm`` takes
 torch views with exactly those logical shapes and unit strides along K (A, B)
 and along M (D), e.g. ``A = A_st[:, :K]``, ``B = B_st[:, :K].t()``,
 ``D = D_st[:, :M].t()`` for row-major storages A_st (M, lda), B_st (N, ldb),
-D_st (N, ldd).
+D_st (N, ldd).  Packed 4-bit operands come as ``torch.float4_e2m1fn_x2``
+views (two elements per storage element, low nibble first): A (M, K/2) with
+unit stride along K, B (K/2, N) likewise, so K is even there; the raw entry
+points take any K and strides in elements.
 """
 from __future__ import annotations
 
@@ -24,8 +27,8 @@ _PKG = Path(__file__).resolve().parent
 LIB_PATH = _PKG / "_lib" / "libtile_gemm.so"
 HEADER_PATH = _PKG.parent / "include" / "tile_gemm.h"
 
-BF16, F16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
-DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2}
+BF16, F16, F32, E4M3, E5M2, E2M1 = 1, 2, 3, 4, 5, 6
+DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}
 
 TG_OK = 0
 STATUS = {0: "TG_OK", -1: "TG_ERR_DIMS", -2: "TG_ERR_LD", -3: "TG_ERR_NULL", -4: "TG_ERR_ALIGN",
@@ -46,7 +49,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "kernel_id", "dtype", "block_m", "block_n", "block_k", "waves_m", "waves_n",
         "wave_tile_m", "wave_tile_n", "threads", "stages", "lds_bytes", "acc_per_lane",
-        "load_class", "group_m", "staged", "k_slices")] + [
+        "load_class", "group_m", "staged", "k_slices", "block_scales")] + [
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
@@ -246,12 +249,20 @@ def _operand_args(A, B, D):
     import torch
 
     codes = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32,
-             torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
+             torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.float4_e2m1fn_x2: E2M1}
     out_codes = (BF16, F16, F32)
     if A.dim() != 2 or B.dim() != 2 or D.dim() != 2:
         raise ValueError("A, B and D must be 2-D views")
     M, K = A.shape
     K2, N = B.shape
+    if A.dtype == torch.float4_e2m1fn_x2 and B.dtype == A.dtype:
+        # two elements per storage element: sizes and strides in elements
+        M, N, K, lda, ldb, ldd, dt, ot = _operand_args_checked(A, B, D, M, N, K, K2, codes, out_codes)
+        return M, N, 2 * K, 2 * lda, 2 * ldb, ldd, dt, ot
+    return _operand_args_checked(A, B, D, M, N, K, K2, codes, out_codes)
+
+
+def _operand_args_checked(A, B, D, M, N, K, K2, codes, out_codes):
     if K2 != K or tuple(D.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
     if A.dtype != B.dtype or A.dtype not in codes:

@@ -41,16 +41,28 @@ constexpr double kSecondsPerCostStage = 2.5e-11;
 constexpr double kCopyBytesPerSecond = 4.0e12;
 constexpr double kLaunchSeconds = 6e-6;
 
-int elem_size(int dtype) {
+// Bits per element of an operand or output type (0: unknown).
+int elem_bits(int dtype) {
     switch (dtype) {
+        case TG_E2M1: return 4;
         case TG_E4M3:
-        case TG_E5M2: return 1;
+        case TG_E5M2: return 8;
         case TG_BF16:
-        case TG_F16: return 2;
-        case TG_F32: return 4;
+        case TG_F16: return 16;
+        case TG_F32: return 32;
         default: return 0;
     }
 }
+
+// Bytes of an element type (1 for the packed 4-bit format: its pointers need
+// byte alignment only).
+int elem_size(int dtype) {
+    const int b = elem_bits(dtype);
+    return b >= 8 ? b / 8 : (b ? 1 : 0);
+}
+
+// Bytes spanned by `elems` consecutive elements (rounded up for packed types).
+int64_t bytes_of(int64_t elems, int dtype) { return (elems * elem_bits(dtype) + 7) / 8; }
 
 // Types D may have.
 bool out_type_ok(int dtype) { return dtype == TG_F32 || dtype == TG_BF16 || dtype == TG_F16; }
@@ -69,6 +81,9 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     if (bt.stride_a < 0 || bt.stride_b < 0 || bt.stride_d < 0 || bt.stride_a > kMaxBatchStride ||
         bt.stride_b > kMaxBatchStride || bt.stride_d > kMaxBatchStride)
         return TG_ERR_LD;
+    // packed types: every operand row (and matrix) starts on a byte
+    const int eb = elem_bits(dtype);
+    if (eb < 8 && (((lda * eb) | (ldb * eb) | (bt.stride_a * eb) | (bt.stride_b * eb)) & 7)) return TG_ERR_LD;
     if (M == 0 || N == 0 || bt.batch == 0) return TG_OK;
     // the output matrices of a batch must not overlap one another
     if (bt.batch > 1 && bt.stride_d < (N - 1) * ldd + M) return TG_ERR_LD;
@@ -83,22 +98,22 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
         const uintptr_t d1 = d0 + uintptr_t(last * bt.stride_d + (N - 1) * ldd + M) * uintptr_t(os);
         const uintptr_t a0 = reinterpret_cast<uintptr_t>(A);
-        const uintptr_t a1 = a0 + uintptr_t(last * bt.stride_a + (M - 1) * lda + K) * uintptr_t(es);
+        const uintptr_t a1 = a0 + uintptr_t(bytes_of(last * bt.stride_a + (M - 1) * lda + K, dtype));
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(B);
-        const uintptr_t b1 = b0 + uintptr_t(last * bt.stride_b + (N - 1) * ldb + K) * uintptr_t(es);
+        const uintptr_t b1 = b0 + uintptr_t(bytes_of(last * bt.stride_b + (N - 1) * ldb + K, dtype));
         if (overlaps(d0, d1, a0, a1) || overlaps(d0, d1, b0, b1)) return TG_ERR_ALIAS;
     }
     return TG_OK;
 }
 
 // Byte alignment class shared by every operand row start (of every matrix of
-// a batch): 16, 4, 2 or (8-bit operands) 1.
-int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, int64_t ldb, int es,
+// a batch): 16, 4, 2 or (8- and 4-bit operands) 1.
+int row_class(int64_t M, int64_t N, const void* A, int64_t lda, const void* B, int64_t ldb, int dtype,
               const Batch& bt) {
     uintptr_t bits = reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B);
-    if (M > 1) bits |= uintptr_t(lda * es);
-    if (N > 1) bits |= uintptr_t(ldb * es);
-    if (bt.batch > 1) bits |= uintptr_t(bt.stride_a * es) | uintptr_t(bt.stride_b * es);
+    if (M > 1) bits |= uintptr_t(bytes_of(lda, dtype));
+    if (N > 1) bits |= uintptr_t(bytes_of(ldb, dtype));
+    if (bt.batch > 1) bits |= uintptr_t(bytes_of(bt.stride_a, dtype)) | uintptr_t(bytes_of(bt.stride_b, dtype));
     if ((bits & 15u) == 0) return 16;
     if ((bits & 3u) == 0) return 4;
     if ((bits & 1u) == 0) return 2;
@@ -167,6 +182,7 @@ void describe(const TgKernelDesc& k, int64_t M, int64_t N, tile_gemm_plan_info* 
     out->load_class = k.load_class;
     out->group_m = k.group_m;
     out->k_slices = k.k_slices > 0 ? k.k_slices : 1;
+    out->block_scales = k.block_scales;
     if (M > 0 && N > 0) {
         out->tiles_m = cdiv(M, k.block_m);
         out->tiles_n = cdiv(N, k.block_n);
@@ -201,14 +217,14 @@ struct Staging {
 Staging decide_staging(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
                        int64_t ldb, bool d_lines, int mode) {
     Staging st;
-    if (mode == 0 || M == 0 || N == 0 || K == 0) return st;
+    if (mode == 0 || M == 0 || N == 0 || K == 0 || elem_bits(dtype) < 8) return st;
     const int es = elem_size(dtype);
     const int64_t rb = staged_row_bytes(K, es);
     if (rb / es > kMaxDim) return st;
     const int sid = choose(M, N, 1, dtype, 16, rb, d_lines);
     if (sid < 0) return st;
     if (mode != 1) {
-        const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
+        const int cls = row_class(M, N, A, lda, B, ldb, dtype, Batch());
         if (cls == 16) return st;
         const int did = choose(M, N, 1, dtype, cls, (lda > ldb ? lda : ldb) * es, d_lines);
         if (did >= 0) {
@@ -229,9 +245,8 @@ int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
          const Batch& bt = Batch(), int64_t splits = 1) {
     const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, bt);
     if (rc) return rc;
-    const int es = elem_size(dtype);
-    const int cls = row_class(M, N, A, lda, B, ldb, es, bt);
-    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    const int cls = row_class(M, N, A, lda, B, ldb, dtype, bt);
+    const int64_t row_stride = bytes_of(lda > ldb ? lda : ldb, dtype);
     const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), bt);
     int id = kernel_id;
     if (id < 0) {
@@ -290,6 +305,10 @@ Staging staged_decision(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
                         const void* D, int64_t ldd, int dtype, int out_dtype, const void* workspace,
                         int64_t workspace_bytes, int mode, int* rc) {
     *rc = TG_OK;
+    if (mode == 1 && elem_bits(dtype) < 8 && M > 0 && N > 0 && K > 0) {
+        *rc = TG_ERR_DTYPE;  // packed operands are never staged
+        return Staging();
+    }
     Staging st = decide_staging(M, N, K, dtype, A, lda, B, ldb, d_lines_aligned(D, ldd, elem_size(out_dtype), Batch()),
                                 mode);
     if (!st.on) return st;
@@ -347,9 +366,8 @@ int softmax_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
     if (rc) return rc;
     if (M == 0 || N == 0) return TG_OK;
-    const int es = elem_size(dtype);
-    const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
-    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    const int cls = row_class(M, N, A, lda, B, ldb, dtype, Batch());
+    const int64_t row_stride = bytes_of(lda > ldb ? lda : ldb, dtype);
     // fused: an instance whose tile spans all of N
     if (kernel_id >= 0) {
         if (kernel_id >= tg_kernel_count()) return TG_ERR_PLAN;
@@ -379,11 +397,16 @@ int scaled_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     const int rc = validate(M, N, K, A, lda, B, ldb, D, ldd, dtype, out_dtype, Batch());
     if (rc) return rc;
     if (!scale_a && !scale_b) return TG_OK;
-    if (elem_size(dtype) != 1) return TG_ERR_DTYPE;
-    // whole dwords per 128-k stage: 4*ceil(K/128) bytes per row, 4-byte aligned
-    const int64_t need = 4 * cdiv(K, 128);
-    if ((scale_a && (lds_a < need || (lds_a & 3))) || (scale_b && (lds_b < need || (lds_b & 3)))) return TG_ERR_LD;
-    if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & 3u) return TG_ERR_ALIGN;
+    if (elem_bits(dtype) > 8) return TG_ERR_DTYPE;
+    // 8-bit: whole dwords per 128-k stage, 4*ceil(K/128) bytes per row,
+    // 4-byte aligned; 4-bit: whole 16-byte pieces per two 256-k stages,
+    // 16*ceil(K/512) bytes per row, 16-byte aligned
+    const int64_t unit = elem_bits(dtype) == 8 ? 4 : 16;
+    const int64_t need = unit * cdiv(K, elem_bits(dtype) == 8 ? 128 : 512);
+    if ((scale_a && (lds_a < need || (lds_a % unit))) || (scale_b && (lds_b < need || (lds_b % unit))))
+        return TG_ERR_LD;
+    if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & uintptr_t(unit - 1))
+        return TG_ERR_ALIGN;
     if (M > 0 && N > 0 && K > 0) {
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
         const uintptr_t d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(elem_size(out_dtype));
@@ -408,9 +431,8 @@ int scaled_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
         if (*kernel_id >= tg_kernel_count() || !tg_kernel(*kernel_id).block_scales) return TG_ERR_PLAN;
         return scale_rows_fit(tg_kernel(*kernel_id)) ? TG_OK : TG_ERR_PLAN;
     }
-    const int es = elem_size(dtype);
-    const int cls = row_class(M, N, A, lda, B, ldb, es, Batch());
-    const int64_t row_stride = (lda > ldb ? lda : ldb) * es;
+    const int cls = row_class(M, N, A, lda, B, ldb, dtype, Batch());
+    const int64_t row_stride = bytes_of(lda > ldb ? lda : ldb, dtype);
     const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), Batch());
     double best = 0;
     for (int i = 0; i < tg_kernel_count(); ++i) {
@@ -482,13 +504,12 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
     if (M == 0 || N == 0 || batch == 0) return TG_OK;
     rc = device_ok();
     if (rc) return rc;
-    const int es = elem_size(dtype);
     GemmArgs a{};  // every field starts at zero (split_k = 0: no split)
     a.A = static_cast<const char*>(A);
     a.B = static_cast<const char*>(B);
     a.D = D;
-    a.lda_b = lda * es;
-    a.ldb_b = ldb * es;
+    a.lda_b = bytes_of(lda, dtype);
+    a.ldb_b = bytes_of(ldb, dtype);
     a.ldd = ldd;
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
@@ -499,8 +520,8 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
     a.tiles_n = static_cast<int>(pl.tiles_n);
     a.group_m = pl.group_m;
     a.out_dtype = out_dtype;
-    a.batch_a_b = stride_a * es;
-    a.batch_b_b = stride_b * es;
+    a.batch_a_b = bytes_of(stride_a, dtype);
+    a.batch_b_b = bytes_of(stride_b, dtype);
     a.batch_d_b = stride_d * elem_size(out_dtype);
     a.scale_a = sc.a;
     a.scale_b = sc.b;
@@ -572,10 +593,10 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
         if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u))
             return TG_ERR_WORKSPACE;
         const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + uintptr_t(need);
-        const int es = elem_size(dtype), os = elem_size(out_dtype);
+        const int os = elem_size(out_dtype);
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(D), d1 = d0 + uintptr_t((N - 1) * ldd + M) * uintptr_t(os);
-        const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), a1 = a0 + uintptr_t((M - 1) * lda + K) * uintptr_t(es);
-        const uintptr_t b0 = reinterpret_cast<uintptr_t>(B), b1 = b0 + uintptr_t((N - 1) * ldb + K) * uintptr_t(es);
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(A), a1 = a0 + uintptr_t(bytes_of((M - 1) * lda + K, dtype));
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(B), b1 = b0 + uintptr_t(bytes_of((N - 1) * ldb + K, dtype));
         if (overlaps(w0, w1, d0, d1) || (K > 0 && (overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1))))
             return TG_ERR_ALIAS;
     }
@@ -585,13 +606,12 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
         (void)hipGetLastError();
         return TG_ERR_LAUNCH;
     }
-    const int es = elem_size(dtype);
     GemmArgs a{};  // every field starts at zero (split_k = 0: no split)
     a.A = static_cast<const char*>(A);
     a.B = static_cast<const char*>(B);
     a.D = workspace;
-    a.lda_b = lda * es;
-    a.ldb_b = ldb * es;
+    a.lda_b = bytes_of(lda, dtype);
+    a.ldb_b = bytes_of(ldb, dtype);
     a.ldd = M;
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
@@ -602,8 +622,8 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
     a.tiles_n = static_cast<int>(pl.tiles_n);
     a.group_m = pl.group_m;
     a.out_dtype = TG_F32;
-    a.batch_a_b = chunk * es;
-    a.batch_b_b = chunk * es;
+    a.batch_a_b = bytes_of(chunk, dtype);  // whole stages: whole bytes
+    a.batch_b_b = bytes_of(chunk, dtype);
     a.batch_d_b = M * N * 4;
     a.split_k = static_cast<int>(chunk);
     hipError_t err = hipSuccess;
@@ -651,14 +671,13 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha, const void* 
     }
     rc = device_ok();
     if (rc) return rc;
-    const int es = elem_size(dtype);
     const TgKernelDesc& k = tg_kernel(id);
     GemmArgs a{};
     a.A = static_cast<const char*>(A);
     a.B = static_cast<const char*>(B);
     a.D = D;
-    a.lda_b = lda * es;
-    a.ldb_b = ldb * es;
+    a.lda_b = bytes_of(lda, dtype);
+    a.ldb_b = bytes_of(ldb, dtype);
     a.ldd = ldd;
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
@@ -747,7 +766,7 @@ int tile_gemm_query_plan_staged(int64_t M, int64_t N, int64_t K, int dtype, cons
 }
 
 int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype) {
-    const int es = elem_size(dtype);
+    const int es = elem_bits(dtype) >= 8 ? elem_size(dtype) : 0;  // packed operands are never staged
     if (!es || M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
     if (M == 0 || N == 0 || K == 0) return 0;
     return staged_bytes(M, N, K, es);

@@ -103,7 +103,49 @@ __device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int
     return v;
 }
 
+// A chunk of 4-bit (e2m1) elements, two per byte with the low nibble first,
+// that starts at element k0 (a multiple of 32) of a row and may run past K:
+// elements with k >= K become exact zeros, and no byte that holds only such
+// elements is read.
+__device__ __forceinline__ u32x4 load_chunk_bounded_e2m1(const char* row, int k0, int K) {
+    const unsigned char* r = reinterpret_cast<const unsigned char*>(row) + k0 / 2;
+    unsigned w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        unsigned v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + 8 * d + 2 * e;  // the byte's low element
+            if (k + 1 < K)
+                v |= static_cast<unsigned>(r[4 * d + e]) << (8 * e);
+            else if (k < K)
+                v |= (static_cast<unsigned>(r[4 * d + e]) & 0xFu) << (8 * e);
+        }
+        w[d] = v;
+    }
+    u32x4 v;
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+    return v;
+}
+
 // ---------------------------------------------------------------- MFMA step
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 4-bit (e2m1) operands: one 32x32x64 MFMA per 16-byte fragment.  Lane l
+// supplies row l & 31; half-wave h = l >> 5 supplies k [32h, 32h + 32) of the
+// 64, element i of the fragment in bits [4i, 4i + 4), for both operands alike
+// (so a fragment is one 16-byte chunk of the row), and the block-scale
+// exponent of its row's k-block h: byte SEL of sn for the n side and of sm
+// for the m side (127 means a scale of 1).
+template <int SEL = 0>
+__device__ __forceinline__ f32x16 mfma_f4(u32x4 n, u32x4 m, f32x16 acc, int sn, int sm) {
+    const i32x8 a = {static_cast<int>(n.x), static_cast<int>(n.y), static_cast<int>(n.z), static_cast<int>(n.w),
+                     0, 0, 0, 0};
+    const i32x8 b = {static_cast<int>(m.x), static_cast<int>(m.y), static_cast<int>(m.z), static_cast<int>(m.w),
+                     0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, SEL, sn, SEL, sm);
+}
 
 // One 128-byte K slab of the (n-block i, m-block j) accumulator: the lane's
 // 16-byte fragments of two consecutive chunks (lanes 0-31 chunk 2q, lanes
@@ -117,6 +159,8 @@ __device__ __forceinline__ f32x16 mfma_slab(u32x4 nfrag, u32x4 mfrag, f32x16 acc
     } else if constexpr (DT == TG_F16) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(
             __builtin_bit_cast(f16x8, nfrag), __builtin_bit_cast(f16x8, mfrag), acc, 0, 0, 0);
+    } else if constexpr (DT == TG_E2M1) {
+        return mfma_f4(nfrag, mfrag, acc, 127, 127);
     } else {
         // fp32: four K=2 MFMAs, element e of each lane's 4-float fragment.
         // (Cast the whole vector: a bit-cast of a single vector element
@@ -137,7 +181,6 @@ __device__ __forceinline__ f32x16 mfma_slab(u32x4 nfrag, u32x4 mfrag, f32x16 acc
 // alike.  Half-wave h also supplies the block-scale exponent of k-block h of
 // its row (low byte of sn for the n side, sm for the m side); 127 means a
 // scale of 1.
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 template <int DT>
 __device__ __forceinline__ f32x16 mfma_f8(const u32x4 (&n)[2], const u32x4 (&m)[2], f32x16 acc, int sn, int sm) {
     constexpr int FMT = (DT == TG_E4M3) ? 0 : 1;  // operand format codes: 0 e4m3, 1 e5m2

@@ -60,9 +60,10 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     select_batch(p);
     constexpr int BM = 256, BN = 256, WM = 2;
     constexpr bool F8 = (DT == TG_E4M3 || DT == TG_E5M2);
-    constexpr int ES = (DT == TG_F32) ? 4 : F8 ? 1 : 2;
-    constexpr int EPC = 16 / ES;
-    constexpr int BKE = kRowBytes / ES;          // K elements per stage
+    constexpr bool F4 = (DT == TG_E2M1);          // packed two per byte
+    constexpr int ES = (DT == TG_F32) ? 4 : (F8 || F4) ? 1 : 2;  // bytes per element (4-bit: per pair)
+    constexpr int EPC = F4 ? 32 : 16 / ES;       // K elements per 16-byte chunk
+    constexpr int BKE = F4 ? 2 * kRowBytes : kRowBytes / ES;  // K elements per stage
     constexpr int WTM = 128, WTN = 128;          // output owned by one wave
     constexpr int FM = WTM / 32, FN = WTN / 32;  // 32 x 32 MFMA blocks per wave
     constexpr int NC = BM / (8 * 4);             // 1 KiB copies per wave per half-stage
@@ -73,8 +74,18 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     static_assert(NS == 4 || NS == 5, "4 or 5 half-stage slots");
     static_assert(SCHED == 0 || NS == 5, "the spread copy schedule needs 5 slots");
     static_assert(RS >= 1 && RS <= MF, "reads spread over at most one slab");
-    static_assert(LC == 16 || (LC >= 2 && ADDR == 1 && NS == 4 && !F8 && (ES == 2 || LC == 4)),
-                  "register-staged copies: buffer addressing, 4 slots, 16-bit or fp32 operands");
+    static_assert(LC == 16 || (ADDR == 1 && NS == 4 && !F8 && (ES == 2 ? LC >= 2 : ES == 4 ? LC == 4 : LC >= 1)),
+                  "register-staged copies: buffer addressing, 4 slots, 16-bit, fp32 or 4-bit operands");
+    static_assert(!F4 || (EPI & 8) == 0, "no softmax epilogue on 4-bit instances");
+    static_assert(!F4 || (EPI & 64) == 0 || (LC == 16 && NS == 4 && SCHED == 0 && ADDR == 1),
+                  "4-bit block scales ride the four-slot schedule, the fifth slot holds them");
+    // a chunk of the ragged last stage, exact zeros for k >= K
+    auto tail_chunk = [](const char* row, int k0, int K) {
+        if constexpr (F4)
+            return load_chunk_bounded_e2m1(row, k0, K);
+        else
+            return load_chunk_bounded<ES>(row, k0, K);
+    };
 
     // the whole 160 KiB of a CU (one workgroup per CU): the ring uses NS
     // slots, the transposing epilogues may use all of it
@@ -300,9 +311,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 const int r = stage_row(tid, i);
                 const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
                 const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
-                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = tail_chunk(arow, k0, K);
                 *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) =
-                    load_chunk_bounded<ES>(brow, k0, K);
+                    tail_chunk(brow, k0, K);
             }
             if (nfull == 0) load_scales(0);  // otherwise loaded at the end of the last full stage
             __syncthreads();
@@ -316,14 +327,184 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 pair(pp, nfull, [](int) {});
             }
         }
+    } else if constexpr (F4 && (EPI & 64) != 0) {
+        // 4-bit operands with block scales.  A stage is 256 k, i.e. eight
+        // 32-k scale blocks per row, and slab q of a stage is one 32x32x64
+        // MFMA per block whose half-wave h takes k-block 2q + h (mfma_f4).
+        // The scales reach the lanes through LDS: a 16-byte piece of each
+        // operand row holds the blocks of two stages (a "pair"), and LDS-DMA
+        // copies the pieces of pair p -- two copies per wave, 64 rows each --
+        // into the fifth slot (which the four-slot ring leaves free) during
+        // slab 0 of stage 2p - 2.  Every barrier of this schedule waits for all
+        // of the wave's copies, so pair p is complete at the barrier of stage
+        // 2p - 2; its buffer (p & 1) was last read in slab 3 of stage 2p - 4.
+        // After each barrier (slab 3 of stage t - 1) a lane reads the 8
+        // bytes of stage t for each of its rows and permutes them into one
+        // dword whose byte q is block 2q + h, which the MFMA of slab q selects.
+        // The scale loads thus go through the same explicit waits as the
+        // operand copies instead of the compiler's own (which cannot see the
+        // copies and would wait for all of them).
+        u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+        constexpr int SC_BUF = 2 * BM * 16;  // one pair of stages: A rows, then B rows, 16 bytes each
+        static_assert(4 * SLOT + 2 * SC_BUF <= LDS_BYTES, "scale buffers fit the fifth slot");
+        const bool has_a = p.scale_a != nullptr, has_b = p.scale_b != nullptr;  // uniform
+        const i32x4 srs[2] = {
+            buffer_rsrc(has_a ? p.scale_a + static_cast<int64_t>(m0) * p.lds_a : nullptr,
+                        has_a ? static_cast<unsigned>(min(BM, M - m0) * p.lds_a) : 0u),
+            buffer_rsrc(has_b ? p.scale_b + static_cast<int64_t>(n0) * p.lds_b : nullptr,
+                        has_b ? static_cast<unsigned>(min(BN, N - n0) * p.lds_b) : 0u)};
+        const unsigned svoff[2] = {static_cast<unsigned>((64 * wave + lane) * p.lds_a),
+                                   static_cast<unsigned>((64 * wave + lane) * p.lds_b)};
+        // scale pieces of pair pr (stages 2pr, 2pr + 1) into buffer pr & 1;
+        // rows past M or N fall outside the range and read zeros (they only
+        // scale accumulators that are never stored)
+        auto scale_copy = [&](int pr) {
+#pragma unroll
+            for (int o = 0; o < 2; ++o) {
+                const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + 4 * SLOT + (pr & 1) * SC_BUF +
+                                                                     o * (BM * 16) + wave * 64 * 16);
+                dma16_buf(srs[o], svoff[o], __builtin_amdgcn_readfirstlane(16 * pr), dst);
+            }
+        };
+        const unsigned sel = (lane >> 5) ? 0x07050301u : 0x06040200u;  // bytes h, 2 + h, 4 + h, 6 + h
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        unsigned scm[FM], scn[FN], nscm[FM], nscn[FN];
+        // the lane's scales of stage t from its pair buffer
+        auto read_scales = [&](int t, unsigned (&sm)[FM], unsigned (&sn)[FN]) {
+            const char* buf = smem + 4 * SLOT + ((t >> 1) & 1) * SC_BUF + (t & 1) * 8;
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(buf + (wave_m * WTM + 32 * j + frag_row(lane)) * 16);
+                sm[j] = has_a ? __builtin_amdgcn_perm(v.y, v.x, sel) : 0x7F7F7F7Fu;
+            }
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const u32x2 v =
+                    *reinterpret_cast<const u32x2*>(buf + BM * 16 + (wave_n * WTN + 32 * i + frag_row(lane)) * 16);
+                sn[i] = has_b ? __builtin_amdgcn_perm(v.y, v.x, sel) : 0x7F7F7F7Fu;
+            }
+        };
+        // slab Q of the stage: 16 MFMAs, side(m) after MFMA m
+        auto slab_sc = [&](auto qc, const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], auto&& side) {
+            constexpr int Q = decltype(qc)::value;
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                const int i = m / FM, j = m % FM;
+                acc[i][j] = mfma_f4<Q>(fb[i], fa[j], acc[i][j], static_cast<int>(scn[i]), static_cast<int>(scm[j]));
+                side(m);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        using Q0 = std::integral_constant<int, 0>;
+        using Q1 = std::integral_constant<int, 1>;
+        using Q2 = std::integral_constant<int, 2>;
+        using Q3 = std::integral_constant<int, 3>;
+
+        if (nfull > 0) {
+            // prologue: the scales of pair 0 first, then half-stages 0 .. 2;
+            // the wait leaves only half-stage 2 in flight
+            scale_copy(0);
+            constexpr int PRO = 3 * NC;
+#pragma unroll
+            for (int c = 0; c < PRO; ++c) {
+                const int h = c / NC;
+                copy(h & 1, c % NC, min(h >> 1, nfull - 1), h);
+            }
+            wait_vm<PRO - 2 * NC>();
+            barrier();
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
+            read_scales(0, scm, scn);
+
+            int slot0 = 0;  // slot of stage s's A half, (2s) % 4
+            for (int s = 0; s < nfull; ++s) {
+                const int sa = slot0, sb = slot0 + 1;
+                const int na = (slot0 + 2) & 3, nb = (slot0 + 3) & 3;
+                const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
+                const bool pair_copy = (s & 1) == 0 && s + 2 < nfull;
+                // slab 0: the copies of B(s+1) (into nb), and on even stages
+                // the scales of the pair of stages s+2 and s+3
+                slab_sc(Q0{}, fa0, fb0, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 1, sa, sb, fa1, fb1); });
+                    if (m & 1) copy(1, m >> 1, t1, nb);
+                    if (m == 2 && pair_copy) scale_copy((s >> 1) + 1);
+                });
+                slab_sc(Q1{}, fa1, fb1, [&](int m) { reads_at(m, [&](int k) { read(k, 2, sa, sb, fa0, fb0); }); });
+                slab_sc(Q2{}, fa0, fb0, [&](int m) { reads_at(m, [&](int k) { read(k, 3, sa, sb, fa1, fb1); }); });
+                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+                wait_vm<0>();
+                barrier();
+                // slab 3: read slab 0 and the scales of stage s+1; copy A(s+2)
+                // into the slot A(s) just left (on the last stage the reads
+                // fetch values that go unused)
+                slab_sc(Q3{}, fa1, fb1, [&](int m) {
+                    reads_at(m, [&](int k) { read(k, 0, na, nb, fa0, fb0); });
+                    if (m & 1) copy(0, m >> 1, t2, sa);
+                    if (m == 4) read_scales(s + 1, nscm, nscn);
+                });
+#pragma unroll
+                for (int j = 0; j < FM; ++j) scm[j] = nscm[j];
+#pragma unroll
+                for (int i = 0; i < FN; ++i) scn[i] = nscn[i];
+                slot0 = na;
+            }
+            wait_vm<0>();  // no copy outlives the loop
+        }
+
+        if (K % BKE != 0) {
+            // ragged last stage through registers into slots 0 (A) and 1 (B);
+            // k >= K become exact zeros, and its scales come straight from
+            // memory: blocks past the last one of K count as 1 (their elements
+            // are zeros, and a NaN scale byte there must not reach the sums),
+            // rows past M or N are not read
+            __syncthreads();
+            const int c = stage_chunk(tid);
+            const int k0 = nfull * BKE + c * EPC;
+#pragma unroll
+            for (int i = 0; i < BM / 32; ++i) {
+                const int r = stage_row(tid, i);
+                const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
+                const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = tail_chunk(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = tail_chunk(brow, k0, K);
+            }
+            const int nblk = (K + 31) / 32;
+            const int h = lane >> 5;
+            unsigned live = 0;  // byte q: 0xFF when block 8 * nfull + 2q + h holds elements below K
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (8 * nfull + 2 * q + h < nblk) live |= 0xFFu << (8 * q);
+            auto tail_scale = [&](const unsigned char* sc, int64_t lds, int row, int rows) {
+                if (!sc || row >= rows) return 0x7F7F7F7Fu;
+                const u32x2 v = *reinterpret_cast<const u32x2*>(sc + static_cast<int64_t>(row) * lds + 8 * nfull);
+                return (__builtin_amdgcn_perm(v.y, v.x, sel) & live) | (0x7F7F7F7Fu & ~live);
+            };
+#pragma unroll
+            for (int j = 0; j < FM; ++j) scm[j] = tail_scale(p.scale_a, p.lds_a, m0 + wave_m * WTM + 32 * j + frag_row(lane), M);
+#pragma unroll
+            for (int i = 0; i < FN; ++i) scn[i] = tail_scale(p.scale_b, p.lds_b, n0 + wave_n * WTN + 32 * i + frag_row(lane), N);
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
+            slab_sc(Q0{}, fa0, fb0, [](int) {});
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 1, 0, 1, fa0, fb0);
+            slab_sc(Q1{}, fa0, fb0, [](int) {});
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 2, 0, 1, fa0, fb0);
+            slab_sc(Q2{}, fa0, fb0, [](int) {});
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read(r, 3, 0, 1, fa0, fb0);
+            slab_sc(Q3{}, fa0, fb0, [](int) {});
+        }
     } else if constexpr (LC < 16) {
         // Operand rows only 4- or 2-byte aligned: LDS-DMA needs 16-byte
         // aligned sources, so each lane gathers the same 16-byte chunks the
         // DMA copies would move (row dma128_row, logical chunk dma128_chunk
         // of copy j) into registers with buffer loads, and scatters them with
-        // ds_write_b128 into the same swizzled slots.  A 2-byte aligned chunk
-        // is loaded as the dword-aligned 16 bytes at or below it plus the next
-        // dword and shifted into place (v_alignbyte).  Per stage the 16 chunk
+        // ds_write_b128 into the same swizzled slots.  A chunk that starts
+        // mid-dword is loaded as the dword-aligned 16 bytes at or below it plus
+        // the next dword and shifted into place (v_alignbyte).  Per stage the 16 chunk
         // groups of a lane (8 of A, 8 of B) are scattered in slabs 0-2, each
         // one stage after its gather, and the same registers then gather the
         // chunk group of the stage after next: one stage of loads in flight,
@@ -356,7 +537,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             const int r = dma128_row(j, lane);
             const unsigned ldb = static_cast<unsigned>(o == 0 ? p.lda_b : p.ldb_b);
             const unsigned at = lead[o] + static_cast<unsigned>(r) * ldb + dma128_chunk(j, lane) * kChunkBytes;
-            const unsigned sub = at & 3u;  // 0 or 2 (rows are 2-byte aligned), 0 for LC 4
+            const unsigned sub = at & 3u;  // 0 for LC 4; 0 or 2 for LC 2; any for LC 1
             const bool valid = r < (o == 0 ? rows_a : rows_b);
             off_lo[g] = valid ? at - sub : kOut;
             off_hi[g] = (valid && sub) ? at - sub + kChunkBytes : kOut;
@@ -370,13 +551,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             const int soff = __builtin_amdgcn_readfirstlane(t * kRowBytes);
             glo[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br[o], static_cast<int>(off_lo[g]),
                                                                                      soff, 0));
-            if constexpr (LC == 2)
+            if constexpr (LC < 4)
                 ghi[g] = __builtin_amdgcn_raw_buffer_load_b32(br[o], static_cast<int>(off_hi[g]), soff, 0);
         };
         // scatter chunk group g into slot `slot`
         auto scatter = [&](int g, int slot) {
             u32x4 v = glo[g];
-            if constexpr (LC == 2) {
+            if constexpr (LC < 4) {
                 const unsigned sh = shift[g];
                 v.x = __builtin_amdgcn_alignbyte(glo[g].y, glo[g].x, sh);
                 v.y = __builtin_amdgcn_alignbyte(glo[g].z, glo[g].y, sh);
@@ -449,8 +630,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 const int r = stage_row(tid, i);
                 const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
                 const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
-                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
-                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = tail_chunk(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = tail_chunk(brow, k0, K);
             }
             __syncthreads();
     #pragma unroll
@@ -540,8 +721,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 const int r = stage_row(tid, i);
                 const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
                 const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
-                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(arow, k0, K);
-                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = load_chunk_bounded<ES>(brow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = tail_chunk(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) = tail_chunk(brow, k0, K);
             }
             __syncthreads();
     #pragma unroll
@@ -774,6 +955,6 @@ static hipError_t launch_wide(const GemmArgs& a, int64_t grid, int batch, hipStr
     template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>(GemmArgs);
 
 #define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, LC, EFF)                                         \
-    {id, DT, 256, 256, 128 / TG_ELEM_BYTES(DT), 2, 2, 128, 128, 256, NS, 5 * 256 * 128, 256, LC, GM, EFF,     \
+    {id, DT, 256, 256, 1024 / TG_ELEM_BITS(DT), 2, 2, 128, 128, 256, NS, 5 * 256 * 128, 256, LC, GM, EFF,     \
      &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>, (ADDR) ? (int64_t(1) << 23) : 0,                  \
      ((EPI) & 8) ? 1 : 0, (EPI) & 1, ((EPI) & 64) ? 1 : 0},

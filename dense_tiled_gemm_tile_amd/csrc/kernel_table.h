@@ -9,7 +9,7 @@
 #include "tile_gemm.h"
 
 struct GemmArgs {
-    const char* A;   // a[m,k] at A + m*lda_b + k*s
+    const char* A;   // a[m,k] at A + m*lda_b + k*s (4-bit: nibble k of the row, low first)
     const char* B;   // b[k,n] at B + n*ldb_b + k*s
     void* D;         // d[m,n] at element m + n*ldd of D, in type out_dtype
     int64_t lda_b;   // A leading stride in bytes
@@ -23,7 +23,7 @@ struct GemmArgs {
     int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
     int split_k;     // split-K partial products: K elements per split (grid y = split), 0 = off
     int epi;         // epilogue: 0 = alpha then optional ReLU per element, 1 = softmax over n
-    // 8-bit operands: block-scale exponents (2^(e-127) per 32 consecutive k),
+    // 8- and 4-bit operands: block-scale exponents (2^(e-127) per 32 consecutive k),
     // byte m*lds_a + k/32 for A row m and n*lds_b + k/32 for B column n;
     // nullptr = no scales
     const unsigned char* scale_a;
@@ -73,12 +73,15 @@ struct TgKernelDesc {
     int64_t max_row_stride;  // largest lda/ldb in bytes the instance can address (0: any)
     int softmax;             // 1: the epilogue can also take a softmax over n (N <= block_n)
     int nt_store;            // 1: D is written with nontemporal stores
-    int block_scales;        // 1: 8-bit instance that applies block scales (GemmArgs::scale_a/b)
+    int block_scales;        // 1: 8- or 4-bit instance that applies block scales (GemmArgs::scale_a/b)
     int k_slices;            // waves that split K inside a workgroup, each over the whole tile (0: 1)
 };
 
-// Element bytes of an operand type.
-#define TG_ELEM_BYTES(DT) ((DT) == TG_F32 ? 4 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 1 : 2)
+// Element bits of an operand type (the 4-bit format is packed).
+#define TG_ELEM_BITS(DT) \
+    ((DT) == TG_F32 ? 32 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 8 : (DT) == TG_E2M1 ? 4 : 16)
+// Element bytes of an operand type of at least 8 bits.
+#define TG_ELEM_BYTES(DT) (TG_ELEM_BITS(DT) / 8)
 
 // The instances each kernel translation unit contributes (host pass only).
 extern const TgKernelDesc tg_entries_wide16[];
@@ -93,6 +96,8 @@ extern const TgKernelDesc tg_entries_rs[];
 extern const int tg_entries_rs_count;
 extern const TgKernelDesc tg_entries_kslice[];
 extern const int tg_entries_kslice_count;
+extern const TgKernelDesc tg_entries_wide4[];
+extern const int tg_entries_wide4_count;
 
 // The instance table, indexed by kernel id (ids are 0 .. tg_kernel_count()-1).
 int tg_kernel_count();

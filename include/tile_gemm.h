@@ -15,6 +15,13 @@
  *   B is logically (K,N), stored K-contiguous:  b[k,n] at byte B + (k + n*ldb)*s
  *   D is logically (M,N), fp32, M-contiguous:   d[m,n] at byte D + (m + n*ldd)*4
  *
+ * The 4-bit format (TG_E2M1) is packed: element i of an operand array holds
+ * bits [4i, 4i + 4) of the array read as a little-endian bit string, i.e.
+ * a[m,k] is the low nibble of byte A + (m*lda + k)/2 when m*lda + k is even
+ * and the high nibble otherwise (b[k,n] likewise at index k + n*ldb).  Every
+ * row must start on a byte, so lda and ldb are even for it (TG_ERR_LD), and
+ * its pointers need only byte alignment.  Strides and sizes count elements.
+ *
  * For 0 <= m < M and 0 <= n < N the call writes
  *
  *     d[m,n] = relu ? max(alpha * S, 0) : alpha * S,   S = sum_{k<K} a[m,k]*b[k,n]
@@ -70,13 +77,17 @@ enum tile_gemm_dtype {
     TG_F16 = 2,  /* IEEE binary16 operands, fp16 MFMA */
     TG_F32 = 3,  /* IEEE binary32 operands, fp32 MFMA (full fp32 products) */
     TG_E4M3 = 4, /* 8-bit float operands (1-4-3, bias 7, no infinity), 8-bit MFMA */
-    TG_E5M2 = 5  /* 8-bit float operands (1-5-2, bias 15, IEEE-style), 8-bit MFMA */
+    TG_E5M2 = 5, /* 8-bit float operands (1-5-2, bias 15, IEEE-style), 8-bit MFMA */
+    TG_E2M1 = 6  /* 4-bit float operands (the MX FP4 element: 1-2-1, bias 1, values
+                    0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, no infinity or
+                    NaN), packed two per byte, 4-bit MFMA */
 };
 
 enum tile_gemm_status {
     TG_OK = 0,
     TG_ERR_DIMS = -1,   /* M, N or K negative or above 2^30, or more than 2^24 tiles */
-    TG_ERR_LD = -2,     /* lda < max(1,K), ldb < max(1,K) or ldd < max(1,M) */
+    TG_ERR_LD = -2,     /* lda < max(1,K), ldb < max(1,K) or ldd < max(1,M), or a
+                           packed operand row that does not start on a byte */
     TG_ERR_NULL = -3,   /* NULL pointer for an operand that is read or written */
     TG_ERR_ALIGN = -4,  /* pointer not aligned to its element size */
     TG_ERR_DTYPE = -5,  /* dtype or out_dtype not one of tile_gemm_dtype */
@@ -106,6 +117,7 @@ typedef struct tile_gemm_plan_info {
     int32_t group_m;       /* tile-rows per group in the grouped tile order */
     int32_t staged;        /* always 0 for a query (tile_gemm_staged decides per call) */
     int32_t k_slices;      /* waves of a workgroup that each take 1/k_slices of K over the whole tile */
+    int32_t block_scales;  /* 1: the instance applies block scales (tile_gemm_scaled) */
     int64_t tiles_m;       /* ceil(M / block_m) */
     int64_t tiles_n;       /* ceil(N / block_n) */
     int64_t grid;          /* workgroups launched = tiles_m * tiles_n */
@@ -236,22 +248,25 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
                       void* stream, int kernel_id);
 
 /*
- * 8-bit operands (TG_E4M3, TG_E5M2) with optional block scales: every 32
- * consecutive k of an A row (and of a B column) share one unsigned 8-bit
- * exponent e, and the elements of that block stand for their decoded value
- * times 2^(e - 127) (e = 255: NaN).  The pages name block-scaled 8-bit
- * matmuls (cuTile.jl tutorial "Matrix Multiplication", "Where to go from
- * here") without defining them; this is the plain reading of the MX
- * formats, and the product then is
+ * 8-bit (TG_E4M3, TG_E5M2) and 4-bit (TG_E2M1) operands with optional block
+ * scales: every 32 consecutive k of an A row (and of a B column) share one
+ * unsigned 8-bit exponent e, and the elements of that block stand for their
+ * decoded value times 2^(e - 127) (e = 255: NaN).  The pages name
+ * block-scaled 8-bit and 4-bit matmuls (cuTile.jl tutorial "Matrix
+ * Multiplication", "Where to go from here") without defining them; this is
+ * the plain reading of the MX formats, and the product then is
  *
  *     d[m,n] = epilogue(alpha * sum_k a[m,k]*sa[m,k/32] * b[k,n]*sb[n,k/32])
  *
  * accumulated in fp32 on the 8-bit MFMA (which applies the scales itself).
  * Scale of A row m, block j: byte scale_a[m*lds_a + j]; of B column n:
- * scale_b[n*lds_b + j].  lds_a, lds_b >= 4*ceil(K/128) and multiples of 4,
- * scale pointers 4-byte aligned (TG_ERR_LD / TG_ERR_ALIGN): the kernel reads
- * the four scales of each 128-k stage as one dword; scales of blocks past
- * ceil(K/32) are read but ignored.  Either pointer may be NULL (no scale on
+ * scale_b[n*lds_b + j].  8-bit operands: lds_a, lds_b >= 4*ceil(K/128) and
+ * multiples of 4, scale pointers 4-byte aligned (the kernels read the four
+ * scales of each 128-k stage as one dword); 4-bit operands: lds_a, lds_b >=
+ * 16*ceil(K/512) and multiples of 16, scale pointers 16-byte aligned (the
+ * kernels copy the sixteen scales of two 256-k stages as one 16-byte piece);
+ * otherwise TG_ERR_LD / TG_ERR_ALIGN.  Scales of blocks past ceil(K/32) are
+ * read but ignored.  Either pointer may be NULL (no scale on
  * that side); scales with 16-bit or fp32 operands give TG_ERR_DTYPE; the
  * scales must not overlap D (TG_ERR_ALIAS).  kernel_id as tile_gemm_ex
  * (only instances that apply block scales accept scales; others give
@@ -283,8 +298,9 @@ int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
  * workspace does not suffice; mode 0: never (as tile_gemm_out).  workspace:
  * device memory owned by the caller, not overlapping A, B or D
  * (TG_ERR_ALIAS), reusable once the stream has passed the call.  M, N or K
- * = 0 never stages.  Other rules and errors as tile_gemm_out with kernel_id
- * -1.
+ * = 0 never stages.  Packed 4-bit operands are never staged (mode 1 gives
+ * TG_ERR_DTYPE; mode -1 runs the direct plan, which takes rows of any byte
+ * alignment).  Other rules and errors as tile_gemm_out with kernel_id -1.
  */
 int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -292,7 +308,7 @@ int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      void* workspace, int64_t workspace_bytes, void* stream, int mode);
 
 /* Workspace bytes tile_gemm_staged needs for these sizes (0 when M, N or K
- * is 0; -1 for an unknown dtype or sizes out of range). */
+ * is 0; -1 for an unknown or packed dtype or sizes out of range). */
 int64_t tile_gemm_staged_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype);
 
 /* Workspace a split-K call needs: splits * M * N * 4 bytes (0 for splits = 1
@@ -364,7 +380,7 @@ const char* tile_gemm_strerror(int code);
 /* ABI version of this header (bumped on any incompatible change). */
 int tile_gemm_abi_version(void);
 
-#define TILE_GEMM_ABI_VERSION 8
+#define TILE_GEMM_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,9 @@ import torch
 
 TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
                 "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+# packed operand types: bits per element (element i of a stored array holds
+# bits [w*i, w*i + w) of the bytes read as a little-endian bit string)
+PACKED_BITS = {"e2m1": 4}
 D_SENTINEL = -7777.0  # value planted in D storage that the product must never write
 
 
@@ -39,8 +42,8 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str            # operand type of A and B: "bf16", "f16" or "f32"
-    dist: str             # "uniform_pm1", "uniform_01" or "normal_invsqrtk"
+    dtype: str            # operand type of A and B: "bf16", "f16", "f32", "e4m3" or "e2m1"
+    dist: str             # "uniform_pm1", "uniform_01", "normal_invsqrtk" or (packed types) "codes"
     alpha: float
     relu: bool
     lda: int
@@ -96,6 +99,11 @@ WORKLOADS = {
     "batched_16x1024_bf16": _w("batched_16x1024_bf16", 1024, 1024, 1024, "bf16", "uniform_pm1",
                                1.0, True, 6000, batch=16,
                                notes="16 products; A (16*M, lda), B (16*N, ldb), D (16*N, ldd) storages"),
+    # 4-bit operands (the block-scaled FP4 matmul of the cuTile tutorial's
+    # closing section, here without scales): every e2m1 code equally likely,
+    # alpha 2^-10 keeps D near unit scale
+    "square_8192_e2m1_relu": _w("square_8192_e2m1_relu", 8192, 8192, 8192, "e2m1", "codes", 2.0 ** -10, True,
+                                9500, notes="packed two per byte; A (M, lda/2), B (N, ldb/2) byte storages"),
 }
 
 
@@ -129,7 +137,11 @@ def operands(M, N, K, dtype, dist, seed_a, seed_b, lda=None, ldb=None, pad=float
 
 def workload_operands(w: Workload, pad=float("nan")):
     """A and B storages; a batched workload stacks its matrices: A is
-    (batch*M, lda), matrix b in rows b*M .. b*M+M-1 (B likewise with N)."""
+    (batch*M, lda), matrix b in rows b*M .. b*M+M-1 (B likewise with N).
+    Packed types give uint8 byte storages (see ``packed_operands``)."""
+    if w.dtype in PACKED_BITS:
+        a, b = packed_operands(w.batch * w.M, w.batch * w.N, w.K, w.dtype, w.seed_a, w.seed_b, w.lda, w.ldb)
+        return torch.from_numpy(a), torch.from_numpy(b)
     if w.batch == 1:
         return operands(w.M, w.N, w.K, w.dtype, w.dist, w.seed_a, w.seed_b, w.lda, w.ldb, pad)
     ga = torch.Generator().manual_seed(int(w.seed_a))
@@ -150,14 +162,54 @@ def int_operands(M, N, K, dtype, seed, lda=None, ldb=None, lo=-3, hi=3, pad=floa
     return _stored(M, K, lda, a, dtype, pad), _stored(N, K, ldb, b, dtype, pad)
 
 
-def block_scales(rows: int, K: int, seed: int, lo: int = 124, hi: int = 130, pad: int = 0) -> np.ndarray:
-    """Seeded block-scale exponents for 8-bit operands: (rows, lds) uint8 with
-    lds = 4*ceil(K/128) + pad (whole dwords per 128-k stage), exponents in
-    [lo, hi] for the ceil(K/32) live blocks and 127 elsewhere."""
-    nblk = -(-K // 32)
-    lds = 4 * -(-K // 128) + pad
+def pack_codes(codes: np.ndarray, w: int) -> np.ndarray:
+    """Pack w-bit codes along the last axis into bytes: element i at bits
+    [w*i, w*i + w) of the little-endian bit string (the last axis times w
+    must be a multiple of 8)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    if (codes.shape[-1] * w) % 8:
+        raise ValueError("rows must fill whole bytes")
+    bitarr = np.unpackbits(codes[..., None], axis=-1, bitorder="little")[..., :w]
+    flat = bitarr.reshape(*codes.shape[:-1], codes.shape[-1] * w)
+    return np.packbits(flat, axis=-1, bitorder="little")
+
+
+def packed_storage(rows: int, K: int, ld: int, dtype: str, seed: int, pool=None, pad_code=None) -> np.ndarray:
+    """Seeded packed storage of a (rows, ld)-element operand: codes drawn
+    uniformly from `pool` (default every code) for k < K and `pad_code`
+    (default the largest positive code, so a read of the padding shows)
+    beyond; (rows, ld*w/8) uint8."""
+    w = PACKED_BITS[dtype]
     g = np.random.default_rng(int(seed))
-    s = np.full((rows, max(lds, 4)), 127, dtype=np.uint8)
+    top = (1 << (w - 1)) - 1
+    codes = np.full((rows, ld), top if pad_code is None else pad_code, dtype=np.uint8)
+    if pool is None:
+        codes[:, :K] = g.integers(0, 1 << w, size=(rows, K), dtype=np.uint8)
+    else:
+        codes[:, :K] = g.choice(np.asarray(pool, dtype=np.uint8), size=(rows, K))
+    return pack_codes(codes, w)
+
+
+def packed_operands(M, N, K, dtype, seed_a, seed_b, lda=None, ldb=None, pool=None, pad_code=None):
+    """Seeded packed storages for A ((M, lda*w/8) bytes) and B ((N, ldb*w/8)
+    bytes), numpy uint8."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    return (packed_storage(M, K, lda, dtype, seed_a, pool, pad_code),
+            packed_storage(N, K, ldb, dtype, seed_b, pool, pad_code))
+
+
+def block_scales(rows: int, K: int, seed: int, lo: int = 124, hi: int = 130, pad: int = 0,
+                 dtype: str = "e4m3", fill: int = 127) -> np.ndarray:
+    """Seeded block-scale exponents: (rows, lds) uint8 with lds =
+    4*ceil(K/128) + pad for 8-bit operands (whole dwords per 128-k stage) or
+    16*ceil(K/512) + pad for 4-bit ones (16-byte pieces per two 256-k
+    stages), exponents in [lo, hi] for the ceil(K/32) live blocks and `fill`
+    elsewhere."""
+    nblk = -(-K // 32)
+    lds = (16 * -(-K // 512) if dtype in PACKED_BITS else 4 * -(-K // 128)) + pad
+    g = np.random.default_rng(int(seed))
+    s = np.full((rows, max(lds, 4)), fill, dtype=np.uint8)
     s[:, :nblk] = g.integers(lo, hi + 1, size=(rows, nblk), dtype=np.uint8)
     return s
 

@@ -12,6 +12,12 @@ def dtype_name(info) -> str:
     return DT_NAMES[info.dtype]
 
 
+def unpacked_instances() -> list:
+    """Ids of the instances whose operands are whole bytes or more; the
+    packed 4-bit instances have tests of their own (test_gpu_fp4.py)."""
+    return [k for k in range(tg.kernel_count()) if tg.kernel_info(k).dtype in DT_NAMES]
+
+
 def strides_for_class(cls: int, K: int, es: int):
     """(lda, ldb) >= K, in elements, whose row byte offsets (from a 256-byte
     aligned base) are aligned to exactly `cls` bytes for odd rows."""

@@ -14,7 +14,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
-from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class, unpacked_instances
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +95,7 @@ def _strides(info_class, M, N, K, es):
     return lda, ldb
 
 
-@pytest.mark.parametrize("kid", list(range(tg.kernel_count())))
+@pytest.mark.parametrize("kid", unpacked_instances())
 def test_every_instance_batched(kid):
     """Three products with gaps between them, every instance forced: exact on
     integer data with alpha < 0 and ReLU."""

@@ -16,7 +16,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
-from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class, unpacked_instances
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,7 @@ def check_tol(D_st, A_st, B_st, M, N, K, alpha, relu, dt, out):
 
 
 @pytest.mark.parametrize("out", ["bf16", "f16"])
-@pytest.mark.parametrize("kid", list(range(tg.kernel_count())))
+@pytest.mark.parametrize("kid", unpacked_instances())
 def test_every_instance_low_precision_output(kid, out):
     """Every instance, forced, writes bf16/fp16 D: exact on integer data (large
     enough sums that the output format has to round), within the bound on

@@ -16,7 +16,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
-from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class, unpacked_instances
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def test_workload_integer_exact(name):
 
 
 def _instances():
-    return list(range(tg.kernel_count()))
+    return unpacked_instances()
 
 
 @pytest.mark.parametrize("kid", _instances())
@@ -144,7 +144,7 @@ EDGE_DIMS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 
 
 
 def _stream_instances():
-    return [k for k in range(tg.kernel_count()) if tg.kernel_info(k).load_class == 16]
+    return [k for k in unpacked_instances() if tg.kernel_info(k).load_class == 16]
 
 
 @pytest.mark.parametrize("kid", _stream_instances())

@@ -15,7 +15,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
-from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class, unpacked_instances
 
 pytestmark = pytest.mark.gpu
 
@@ -91,7 +91,7 @@ def test_fused_softmax_low_precision_output(out):
 
 def _softmax_instances():
     ids = []
-    for k in range(tg.kernel_count()):
+    for k in unpacked_instances():
         info = tg.kernel_info(k)
         dt = dtype_name(info)
         M, N, K = 2 * info.block_m + 7, info.block_n - 3, 2 * info.block_k + 5

@@ -15,7 +15,7 @@ import torch
 import dense_tiled_gemm_tile_amd as tg
 import oracle
 import seeded_inputs as si
-from instance_cases import ELEM_SIZE, dtype_name, strides_for_class
+from instance_cases import ELEM_SIZE, dtype_name, strides_for_class, unpacked_instances
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,7 @@ def check(D_st, A_st, B_st, M, N, K, alpha, relu, dt, exact, out="f32"):
     return ratio
 
 
-@pytest.mark.parametrize("kid", list(range(tg.kernel_count())))
+@pytest.mark.parametrize("kid", unpacked_instances())
 def test_every_instance_splitk(kid):
     """Every instance as the partial-product kernel, 3 splits of a ragged K, exact."""
     info = tg.kernel_info(kid)

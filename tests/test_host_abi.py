@@ -21,7 +21,7 @@ def test_library_exports_every_declared_function():
             "tile_gemm_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
-    assert tg.abi_version() == 8
+    assert tg.abi_version() == 9
 
 
 def test_library_neither_allocates_nor_synchronises():
@@ -182,8 +182,8 @@ def test_every_instance_has_consistent_ownership_arithmetic():
         assert info.threads == 64 * info.waves_m * info.waves_n * info.k_slices
         assert info.wave_tile_m * info.waves_m == info.block_m
         assert info.wave_tile_n * info.waves_n == info.block_n
-        es = {tg.F32: 4, tg.E4M3: 1, tg.E5M2: 1}.get(info.dtype, 2)
-        row_bytes = info.block_k * es
+        bits = {tg.F32: 32, tg.E4M3: 8, tg.E5M2: 8, tg.E2M1: 4}.get(info.dtype, 16)
+        row_bytes = info.block_k * bits // 8
         assert row_bytes in (64, 128)
         # every instance keeps at least its A stages in LDS, within the 160 KiB of a CU
         assert info.stages * info.block_m * row_bytes <= info.lds_bytes <= 160 * 1024
@@ -407,6 +407,52 @@ def test_scaled_entry_point_validation():
     assert tg.query_plan(8192, 8192, 8192, tg.E4M3, A, 8192, B, 8192, D, 8192).block_k == 128
 
 
+def test_4bit_validation_and_plans():
+    """Packed 4-bit operands: rows must start on a byte (even strides), block
+    scales come in 16-byte pieces per two 256-k stages (16-byte aligned),
+    staging is refused, and the plans take the 4-bit instances: the
+    streaming one for aligned rows (256 k per stage), the register-staged one
+    for rows on odd bytes, the scaled ones only with 16-byte aligned rows."""
+    import torch
+
+    A2, B2, D2, S2, W2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000, 0x7E0000000000
+    M, N, K = 300, 200, 701
+    gpu = torch.cuda.is_available()
+    ok = 0 if gpu else -8
+    ex = lambda lda, ldb, a=A2, b=B2: tg.tile_gemm_ex(M, N, K, 1.0, 0, a, lda, b, ldb, D2, M, tg.E2M1, None, -1)
+    if not gpu:
+        assert ex(702, 704) == -8                 # valid: reaches the device check
+        assert ex(702, 704, a=A2 + 1) == -8       # byte alignment is enough
+    assert ex(703, 704) == -2 and ex(702, 705) == -2   # a row would start mid-byte
+    assert ex(700, 704) == -2                          # lda < K
+    # batch strides must keep whole bytes too
+    assert tg.tile_gemm_batched(M, N, K, 1.0, 0, A2, 702, 702 * M + 1, B2, 702, 702 * N, D2, M, M * N, 2, tg.E2M1,
+                                tg.F32, None, -1) == -2
+    # staging: packed operands are never staged
+    assert tg.staged_workspace_bytes(M, N, K, tg.E2M1) == -1
+    assert tg.tile_gemm_staged(M, N, K, 1.0, 0, A2, 702, B2, 702, D2, M, tg.E2M1, tg.F32, W2, 1 << 30, None,
+                               1) == -5
+    # scales: 16*ceil(K/512) bytes per row, multiples of 16, 16-byte aligned
+    need = 16 * -(-K // 512)
+    sc = lambda sa, la, sb=0, lb=0, lda=704: tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, lda, sa, la, B2, lda, sb, lb, D2,
+                                                               M, tg.E2M1, tg.F32, None, -1)
+    assert sc(S2, need - 16) == -2 and sc(S2, need + 4) == -2
+    assert sc(S2 + 4, need) == -4
+    assert sc(S2, need, lda=706) == -9        # rows on odd bytes: no scaled instance
+    if not gpu:
+        assert sc(S2, need, S2 + (1 << 20), need) == -8
+    # plans
+    p = tg.query_plan(8192, 8192, 8192, tg.E2M1, A2, 8192, B2, 8192, D2, 8192)
+    assert p.kernel_id == 51 and p.block_k == 256 and p.load_class == 16
+    assert tg.query_plan(8192, 8192, 8192, tg.E2M1, A2, 8192, B2, 8192, D2, 8193).kernel_id == 52
+    p = tg.query_plan(M, N, K, tg.E2M1, A2, 706, B2, 706, D2, M)
+    assert p.kernel_id == 53 and p.load_class == 1
+    p = tg.query_plan_scaled(8192, 8192, 8192, tg.E2M1, A2, 8192, S2, 256, B2, 8192, S2 + (1 << 24), 256, D2, 8192)
+    assert p.kernel_id == 54 and p.block_scales == 1
+    assert tg.kernel_info(51).block_scales == 0 and tg.kernel_info(55).block_scales == 1
+    assert ok in (0, -8)
+
+
 def test_8bit_staging_and_streaming_plans():
     """8-bit operands: aligned rows run the streaming 8-bit instance; a large
     product with 1-byte aligned rows runs the 1-byte loader directly, or is
@@ -445,37 +491,43 @@ def _chosen_instances():
     """Every instance some automatic plan picks, over a grid of shapes, dtypes,
     row alignments, D line alignments and entry points."""
     A2, B2, D2, S2, W2 = 0x100000000000, 0x200000000000, 0x300000000000, 0x400000000000, 0x500000000000
-    es_of = {tg.BF16: 2, tg.F16: 2, tg.F32: 4, tg.E4M3: 1, tg.E5M2: 1}
+    bits_of = {tg.BF16: 16, tg.F16: 16, tg.F32: 32, tg.E4M3: 8, tg.E5M2: 8, tg.E2M1: 4}
     dims = [17, 65, 200, 512, 1024, 2048, 4096, 8192, 12289]
     Ks = [9, 73, 1024, 4099, 8192, 16384]
     chosen = set()
 
-    def stride(K, es, cls):
-        for ld in range(K, K + 64):
-            b = ld * es
+    def stride(K, bits, cls):
+        for ld in range(K, K + 256):
+            if (ld * bits) % 8:
+                continue
+            b = ld * bits // 8
             c = 16 if b % 16 == 0 else 4 if b % 4 == 0 else 2 if b % 2 == 0 else 1
             if c == cls:
                 return ld
         return None
 
-    for dt, es in es_of.items():
-        classes = [c for c in (16, 4, 2, 1) if c >= es]
+    for dt, bits in bits_of.items():
+        classes = [c for c in (16, 4, 2, 1) if 8 * c >= bits]
         for M in dims:
             for N in dims[::2]:
                 for K in Ks:
                     for cls in classes:
-                        ld = stride(K, es, cls)
+                        ld = stride(K, bits, cls)
                         for ldd in (-(-M // 32) * 32, M + 1):
                             chosen.add(tg.query_plan(M, N, K, dt, A2, ld, B2, ld, D2, ldd, -1, tg.F32).kernel_id)
-                            if es == 1:
-                                sc = 4 * -(-K // 128)
-                                chosen.add(tg.query_plan_scaled(M, N, K, dt, A2, ld, S2, sc, B2, ld, 0, 0, D2,
-                                                                ldd).kernel_id)
+                            if bits <= 8:
+                                sc = 4 * -(-K // 128) if bits == 8 else 16 * -(-K // 512)
+                                try:
+                                    chosen.add(tg.query_plan_scaled(M, N, K, dt, A2, ld, S2, sc, B2, ld, 0, 0, D2,
+                                                                    ldd).kernel_id)
+                                except tg.TileGemmError as e:
+                                    # 4-bit block scales need 16-byte aligned operand rows
+                                    assert bits == 4 and cls < 16 and e.code == -9, (dt, cls, e.code)
                             elif N <= 256:
                                 p = tg.query_plan_softmax(M, N, K, dt, A2, ld, B2, ld, D2, ldd)
                                 chosen.add(p.kernel_id)
         # operand rows longer than 8 MiB
-        K = (1 << 23) // es + 64
+        K = (1 << 23) * 8 // bits + 64
         chosen.add(tg.query_plan(8192, 8192, K, dt, A2, K, B2, K, D2, 8192, -1, tg.F32).kernel_id)
     chosen.discard(-1)
     return chosen
