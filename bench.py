@@ -25,7 +25,9 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "TFLOP/s (2MNK/t) bf16 GEMM+ReLU at 8192³; % of dense MFMA peak"
 # MI355X dense peaks (no sparsity): 256 CUs at 2.4 GHz
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "e4m3": 5033.2, "e5m2": 5033.2}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "e4m3": 5033.2, "e5m2": 5033.2, "e2m1": 10066.3,
+               "e2m3": 10066.3, "e3m2": 10066.3}
+ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5, "e2m3": 0.75, "e3m2": 0.75}
 COUNTERS_FILE = ROOT / "profiles" / "counters.json"
 PROFILES = ROOT / "profiles"
 KERNEL_SOURCES = ROOT / "dense_tiled_gemm_tile_amd" / "csrc"
@@ -35,8 +37,10 @@ XCDS, SIMDS, SPEC_GHZ = 8, 1024, 2.4  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs, 2.4 G
 def kernel_sources(kernel_name: str) -> list[Path]:
     """The device sources one compiled kernel is built from (its instance unit
     and the headers every kernel unit includes)."""
-    family = {"gemm_wide_kernel": ["gemm_wide.h", "gemm_wide16.hip", "gemm_wide32.hip", "gemm_wide8.hip"],
+    family = {"gemm_wide_kernel": ["gemm_wide.h", "gemm_wide16.hip", "gemm_wide32.hip", "gemm_wide8.hip",
+                                   "gemm_wide4.hip", "gemm_wide6.hip"],
               "gemm_stream_kernel": ["gemm_stream.hip"], "gemm_kernel": ["gemm_rs.hip"],
+              "gemm_kslice_kernel": ["gemm_kslice.hip"],
               "splitk_reduce_kernel": ["gemm_aux.hip"], "stage_rows_kernel": ["gemm_aux.hip"]}
     base = ["gemm_common.h", "tile_math.h", "kernel_table.h"]
     for key, files in family.items():
@@ -221,8 +225,8 @@ def main() -> int:
     ap.add_argument("--out-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="element type of D (bf16/f16: fp32 epilogue rounded on the way out)")
     ap.add_argument("--block-scales", action="store_true",
-                    help="8-bit workloads: seeded block scales (one exponent per 32 k of every A row and B "
-                         "column) through tile_gemm_scaled")
+                    help="8- and 4-bit workloads: seeded block scales (one exponent per 32 k of every A row and "
+                         "B column) through tile_gemm_scaled")
     ap.add_argument("--cpu-cols", type=int, default=4096,
                     help="output columns the CPU-baseline oracle computes (all rows, full K)")
     ap.add_argument("--staged", action="store_true",
@@ -251,7 +255,7 @@ def main() -> int:
 
         w = si.WORKLOADS[args.workload]
         os_ = {"f32": 4, "bf16": 2, "f16": 2}[args.out_dtype]
-        es = {"bf16": 2, "f16": 2, "f32": 4, "e4m3": 1, "e5m2": 1}[w.dtype]
+        es = ELEM_BYTES[w.dtype]
         alg = float(w.batch * ((w.M * w.K + w.K * w.N) * es + w.M * w.N * os_))
         key = w.name if args.out_dtype == "f32" else f"{w.name}:out_{args.out_dtype}"
         cmd = f"--workload {w.name}" + (f" --out-dtype {args.out_dtype}" if args.out_dtype != "f32" else "")
@@ -274,21 +278,55 @@ def main() -> int:
     torch.cuda.set_device(dev)
     A_st, B_st = si.workload_operands(w)
     A, B = A_st.to(dev), B_st.to(dev)
+    kv = w.K  # storage columns holding K
+    if w.dtype == "e2m1":  # packed pairs: torch's two-element storage type
+        A, B, kv = A.view(torch.float4_e2m1fn_x2), B.view(torch.float4_e2m1fn_x2), w.K // 2
+    raw = w.dtype in ("e2m3", "e3m2")  # 6-bit: no torch type, raw pointers and element strides
     out_torch = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.out_dtype]
     D = si.out_storage(w.M, w.batch * w.N, w.ldd).to(out_torch).to(dev)
-    if w.batch == 1:
-        Av, Bv, Dv = A[:, :w.K], B[:, :w.K].t(), D[:, :w.M].t()
+    if raw:
+        if w.batch != 1 or args.staged or args.splits != 1 or args.epilogue != "pointwise":
+            print("6-bit workloads: plain and block-scaled single products only", file=sys.stderr)
+            return 2
+        code, ocode = tg.DTYPE_CODES[w.dtype], tg.DTYPE_CODES[args.out_dtype]
+        Av = Bv = Dv = None
+        lib = tg.load_library()
+        s_ptr = torch.cuda.current_stream(dev).cuda_stream
+        if args.block_scales:
+            sc_a_np = si.block_scales(w.M, w.K, w.seed_a + 50, dtype=w.dtype)
+            sc_b_np = si.block_scales(w.N, w.K, w.seed_b + 50, dtype=w.dtype)
+            sc_a, sc_b = torch.from_numpy(sc_a_np).to(dev), torch.from_numpy(sc_b_np).to(dev)
+            fn, fargs = lib.tile_gemm_scaled, (w.M, w.N, w.K, float(w.alpha), int(w.relu), A.data_ptr(), w.lda,
+                                               sc_a.data_ptr(), sc_a_np.shape[1], B.data_ptr(), w.ldb,
+                                               sc_b.data_ptr(), sc_b_np.shape[1], D.data_ptr(), w.ldd, code, ocode,
+                                               s_ptr, args.kernel_id)
+            plan = tg.query_plan_scaled(w.M, w.N, w.K, code, A.data_ptr(), w.lda, sc_a.data_ptr(), sc_a_np.shape[1],
+                                        B.data_ptr(), w.ldb, sc_b.data_ptr(), sc_b_np.shape[1], D.data_ptr(), w.ldd,
+                                        ocode, args.kernel_id)
+        else:
+            fn, fargs = lib.tile_gemm_out, (w.M, w.N, w.K, float(w.alpha), int(w.relu), A.data_ptr(), w.lda,
+                                            B.data_ptr(), w.ldb, D.data_ptr(), w.ldd, code, ocode, s_ptr,
+                                            args.kernel_id)
+            plan = tg.query_plan(w.M, w.N, w.K, code, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, D.data_ptr(), w.ldd,
+                                 args.kernel_id, ocode)
+
+        def launch(*_args, **_kw):
+            rc = fn(*fargs)
+            if rc != 0:
+                raise tg.TileGemmError(rc, tg.strerror(rc))
+    elif w.batch == 1:
+        Av, Bv, Dv = A[:, :kv], B[:, :kv].t(), D[:, :w.M].t()
         plan = tg.plan_for(Av, Bv, Dv, args.kernel_id)
         launch = tg.gemm
         if args.epilogue == "softmax":
             def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):
                 return tg.gemm_softmax(A_, B_, D_, alpha, stream=stream, kernel_id=kernel_id)
         if args.block_scales:
-            if w.dtype not in ("e4m3", "e5m2"):
-                print("--block-scales needs an 8-bit workload", file=sys.stderr)
+            if w.dtype not in ("e4m3", "e5m2", "e2m1"):
+                print("--block-scales needs an 8- or 4-bit workload", file=sys.stderr)
                 return 2
-            sc_a_np = si.block_scales(w.M, w.K, w.seed_a + 50)
-            sc_b_np = si.block_scales(w.N, w.K, w.seed_b + 50)
+            sc_a_np = si.block_scales(w.M, w.K, w.seed_a + 50, dtype=w.dtype)
+            sc_b_np = si.block_scales(w.N, w.K, w.seed_b + 50, dtype=w.dtype)
             sc_a, sc_b = torch.from_numpy(sc_a_np).to(dev), torch.from_numpy(sc_b_np).to(dev)
 
             def launch(A_, B_, D_, alpha, relu, stream=None, kernel_id=-1):

@@ -15,7 +15,8 @@ and along M (D), e.g. ``A = A_st[:, :K]``, ``B = B_st[:, :K].t()``,
 D_st (N, ldd).  Packed 4-bit operands come as ``torch.float4_e2m1fn_x2``
 views (two elements per storage element, low nibble first): A (M, K/2) with
 unit stride along K, B (K/2, N) likewise, so K is even there; the raw entry
-points take any K and strides in elements.
+points take any K and strides in elements (6-bit operands have no torch
+type and go through them).
 """
 from __future__ import annotations
 
@@ -27,8 +28,9 @@ _PKG = Path(__file__).resolve().parent
 LIB_PATH = _PKG / "_lib" / "libtile_gemm.so"
 HEADER_PATH = _PKG.parent / "include" / "tile_gemm.h"
 
-BF16, F16, F32, E4M3, E5M2, E2M1 = 1, 2, 3, 4, 5, 6
-DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}
+BF16, F16, F32, E4M3, E5M2, E2M1, E2M3, E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
+DTYPE_CODES = {"bf16": BF16, "f16": F16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1, "e2m3": E2M3,
+               "e3m2": E3M2}
 
 TG_OK = 0
 STATUS = {0: "TG_OK", -1: "TG_ERR_DIMS", -2: "TG_ERR_LD", -3: "TG_ERR_NULL", -4: "TG_ERR_ALIGN",

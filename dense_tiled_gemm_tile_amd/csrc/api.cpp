@@ -45,6 +45,8 @@ constexpr double kLaunchSeconds = 6e-6;
 int elem_bits(int dtype) {
     switch (dtype) {
         case TG_E2M1: return 4;
+        case TG_E2M3:
+        case TG_E3M2: return 6;
         case TG_E4M3:
         case TG_E5M2: return 8;
         case TG_BF16:
@@ -398,11 +400,12 @@ int scaled_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
     if (rc) return rc;
     if (!scale_a && !scale_b) return TG_OK;
     if (elem_bits(dtype) > 8) return TG_ERR_DTYPE;
-    // 8-bit: whole dwords per 128-k stage, 4*ceil(K/128) bytes per row,
-    // 4-byte aligned; 4-bit: whole 16-byte pieces per two 256-k stages,
+    // 8- and 6-bit: whole dwords per 128-k stage, 4*ceil(K/128) bytes per
+    // row, 4-byte aligned; 4-bit: whole 16-byte pieces per two 256-k stages,
     // 16*ceil(K/512) bytes per row, 16-byte aligned
-    const int64_t unit = elem_bits(dtype) == 8 ? 4 : 16;
-    const int64_t need = unit * cdiv(K, elem_bits(dtype) == 8 ? 128 : 512);
+    const bool f4 = elem_bits(dtype) == 4;
+    const int64_t unit = f4 ? 16 : 4;
+    const int64_t need = unit * cdiv(K, f4 ? 512 : 128);
     if ((scale_a && (lds_a < need || (lds_a % unit))) || (scale_b && (lds_b < need || (lds_b % unit))))
         return TG_ERR_LD;
     if ((reinterpret_cast<uintptr_t>(scale_a) | reinterpret_cast<uintptr_t>(scale_b)) & uintptr_t(unit - 1))

@@ -128,9 +128,51 @@ __device__ __forceinline__ u32x4 load_chunk_bounded_e2m1(const char* row, int k0
     return v;
 }
 
+// Sixteen bytes of a packed row from byte b0 on, of which only the first
+// `nbits` bits of the row hold elements below K: every later bit becomes
+// zero (a 6-bit element past K then decodes to +0) and no byte wholly past
+// them is read.
+__device__ __forceinline__ u32x4 load_chunk_bounded_bits(const char* row, int64_t b0, int64_t nbits) {
+    const unsigned char* r = reinterpret_cast<const unsigned char*>(row);
+    unsigned w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        unsigned v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t b = b0 + 4 * d + e;
+            const int64_t left = nbits - 8 * b;  // bits of this byte below K
+            if (left >= 8)
+                v |= static_cast<unsigned>(r[b]) << (8 * e);
+            else if (left > 0)
+                v |= (static_cast<unsigned>(r[b]) & ((1u << left) - 1u)) << (8 * e);
+        }
+        w[d] = v;
+    }
+    u32x4 v;
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+    return v;
+}
+
 // ---------------------------------------------------------------- MFMA step
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 6-bit (e2m3, FMT 2; e3m2, FMT 3) operands: one 32x32x64 MFMA per 24-byte
+// fragment, given as three 8-byte pieces in order.  Lane l supplies row
+// l & 31; half-wave h = l >> 5 supplies k [32h, 32h + 32) of the 64, element i
+// in bits [6i, 6i + 6) of the 24 bytes, for both operands alike, and the
+// block-scale exponent of its row's k-block h (low byte of sn / sm).
+template <int FMT>
+__device__ __forceinline__ f32x16 mfma_f6(const u32x2 (&n)[3], const u32x2 (&m)[3], f32x16 acc, int sn, int sm) {
+    const i32x8 a = {static_cast<int>(n[0].x), static_cast<int>(n[0].y), static_cast<int>(n[1].x),
+                     static_cast<int>(n[1].y), static_cast<int>(n[2].x), static_cast<int>(n[2].y), 0, 0};
+    const i32x8 b = {static_cast<int>(m[0].x), static_cast<int>(m[0].y), static_cast<int>(m[1].x),
+                     static_cast<int>(m[1].y), static_cast<int>(m[2].x), static_cast<int>(m[2].y), 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, FMT, FMT, 0, sn, 0, sm);
+}
 
 // 4-bit (e2m1) operands: one 32x32x64 MFMA per 16-byte fragment.  Lane l
 // supplies row l & 31; half-wave h = l >> 5 supplies k [32h, 32h + 32) of the

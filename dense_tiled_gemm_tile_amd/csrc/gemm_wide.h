@@ -61,9 +61,11 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256, WM = 2;
     constexpr bool F8 = (DT == TG_E4M3 || DT == TG_E5M2);
     constexpr bool F4 = (DT == TG_E2M1);          // packed two per byte
-    constexpr int ES = (DT == TG_F32) ? 4 : (F8 || F4) ? 1 : 2;  // bytes per element (4-bit: per pair)
-    constexpr int EPC = F4 ? 32 : 16 / ES;       // K elements per 16-byte chunk
-    constexpr int BKE = F4 ? 2 * kRowBytes : kRowBytes / ES;  // K elements per stage
+    constexpr bool F6 = (DT == TG_E2M3 || DT == TG_E3M2);  // packed four per three bytes
+    constexpr int ES = (DT == TG_F32) ? 4 : (F8 || F4 || F6) ? 1 : 2;  // bytes per element (packed: per byte)
+    constexpr int EPC = F4 ? 32 : 16 / ES;       // K elements per 16-byte chunk (not for 6-bit)
+    constexpr int BKE = F4 ? 2 * kRowBytes : F6 ? 128 : kRowBytes / ES;  // K elements per stage
+    constexpr int STB = F6 ? 96 : kRowBytes;     // bytes of each row one stage covers
     constexpr int WTM = 128, WTN = 128;          // output owned by one wave
     constexpr int FM = WTM / 32, FN = WTN / 32;  // 32 x 32 MFMA blocks per wave
     constexpr int NC = BM / (8 * 4);             // 1 KiB copies per wave per half-stage
@@ -77,6 +79,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
     static_assert(LC == 16 || (ADDR == 1 && NS == 4 && !F8 && (ES == 2 ? LC >= 2 : ES == 4 ? LC == 4 : LC >= 1)),
                   "register-staged copies: buffer addressing, 4 slots, 16-bit, fp32 or 4-bit operands");
     static_assert(!F4 || (EPI & 8) == 0, "no softmax epilogue on 4-bit instances");
+    static_assert(!F6 || (ADDR == 1 && LC == 16 && NS == 5 && SCHED == 1 && (EPI & 8) == 0),
+                  "6-bit operands: buffer addressing (the copies of the two unused chunks of a row fall "
+                  "outside the range), 16-byte aligned rows, the spread five-slot schedule");
     static_assert(!F4 || (EPI & 64) == 0 || (LC == 16 && NS == 4 && SCHED == 0 && ADDR == 1),
                   "4-bit block scales ride the four-slot schedule, the fifth slot holds them");
     // a chunk of the ragged last stage, exact zeros for k >= K
@@ -131,15 +136,17 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             const int j = wave * NC + i;
             voff[0][i] = static_cast<unsigned>(dma128_row(j, lane) * p.lda_b) + dma128_chunk(j, lane) * kChunkBytes;
             voff[1][i] = static_cast<unsigned>(dma128_row(j, lane) * p.ldb_b) + dma128_chunk(j, lane) * kChunkBytes;
+            if (F6 && dma128_chunk(j, lane) >= STB / kChunkBytes)  // past the 96 bytes of a 6-bit stage
+                voff[0][i] = voff[1][i] = 0x80000000u;             // beyond every range: nothing is read
         }
     }
     // copy i of operand o (0: A, 1: B) of stage t into slot `slot`
     auto copy = [&](int o, int i, int t, int slot) {
         const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + i) * 1024);
         if constexpr (ADDR == 0)
-            dma16(src[o][i] + static_cast<int64_t>(t) * kRowBytes, dst);
+            dma16(src[o][i] + static_cast<int64_t>(t) * STB, dst);
         else
-            dma16_buf(rsrc[o], voff[o][i], __builtin_amdgcn_readfirstlane(t * kRowBytes), dst);
+            dma16_buf(rsrc[o], voff[o][i], __builtin_amdgcn_readfirstlane(t * STB), dst);
     };
     auto wrap = [](int x) { return x >= NS ? x - NS : x; };
 
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nfull = K / BKE;
-    if constexpr (F8) {
+    if constexpr (F8 || F6) {
         // 8-bit operands: a stage (128 k) is two 32x32x64 MFMAs per block.
         // The fragments of slabs 2p and 2p + 1 (chunks 4p + h and 4p + 2 + h
         // of half-wave h) together feed MFMA pair p; pair 0 runs while slabs
@@ -186,10 +193,39 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
         // order and the wait counts are those of the 16-bit schedule.  Block
         // scales (when given) come from the lane's rows, as in the
         // register-staged kernel.
+        // 6-bit operands run the same schedule: a stage is 128 k as well (96
+        // bytes, chunks 0-5 of each LDS row), and pair p takes the 24 bytes
+        // [48p + 24h, 48p + 24h + 24) of half-wave h's row as three 8-byte
+        // reads, each inside one chunk (24 reads a pair instead of 16).
         static_assert(SCHED == 1 && NS == 5, "the 8-bit schedule follows the spread copy schedule");
         constexpr bool SC = (EPI & 64) != 0;  // the instance applies block scales
         const int nk = nfull + ((K % BKE) != 0 ? 1 : 0);  // stages including a ragged one
         u32x4 g[4][FM], h[4][FN];
+        u32x2 g6[2][FM][3], h6[2][FN][3];  // 6-bit fragments of pairs 0 and 1
+        // 6-bit read offsets within a slot: piece i of pair pp
+        int m6[2][3], n6[2][3];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int b = 48 * pp + 24 * (lane >> 5) + 8 * i;
+                m6[pp][i] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), b >> 4) + (b & 15);
+                n6[pp][i] = wave_n * WTN * kRowBytes + lds_chunk_offset(frag_row(lane), b >> 4) + (b & 15);
+            }
+        // 6-bit read k (0..23) of pair pp: fragment r = k / 3 (even: m-side
+        // block r / 2, odd: n-side), piece k % 3
+        auto read6 = [&](int k, int pp, int sa, int sb, u32x2 (&fa)[FM][3], u32x2 (&fb)[FN][3]) {
+            const int r = k / 3, i = k % 3, blk = r >> 1;
+            if ((r & 1) == 0)
+                fa[blk][i] = *reinterpret_cast<const u32x2*>(smem + sa * SLOT + m6[pp][i] + blk * 32 * kRowBytes);
+            else
+                fb[blk][i] = *reinterpret_cast<const u32x2*>(smem + sb * SLOT + n6[pp][i] + blk * 32 * kRowBytes);
+        };
+        // the reads of pair pp (from slots sa/sb) that go out after MFMA m of 16
+        auto reads6_at = [&](int m, int pp, int sa, int sb, u32x2 (&fa)[FM][3], u32x2 (&fb)[FN][3]) {
+#pragma unroll
+            for (int k = (3 * m + 1) / 2; k < (3 * (m + 1) + 1) / 2; ++k) read6(k, pp, sa, sb, fa, fb);
+        };
         // block scales of the lane's rows for the stage being consumed: one
         // dword per row (the stage's four 32-k blocks), loaded at the end of
         // the previous stage, after its copies, so that the waits the
@@ -245,14 +281,17 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
 #pragma unroll
             for (int m = 0; m < MF; ++m) {
                 const int i = m / FM, j = m % FM;
-                const u32x4 nn[2] = {h[2 * pp][i], h[2 * pp + 1][i]};
-                const u32x4 mm[2] = {g[2 * pp][j], g[2 * pp + 1][j]};
+                int sn = 127, sm = 127;
                 if constexpr (SC) {
-                    const int sn = live ? static_cast<int>((scn[i] >> (8 * sub)) & 0xFFu) : 127;
-                    const int sm = live ? static_cast<int>((scm[j] >> (8 * sub)) & 0xFFu) : 127;
-                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], sn, sm);
+                    sn = live ? static_cast<int>((scn[i] >> (8 * sub)) & 0xFFu) : 127;
+                    sm = live ? static_cast<int>((scm[j] >> (8 * sub)) & 0xFFu) : 127;
+                }
+                if constexpr (F6) {
+                    acc[i][j] = mfma_f6<DT == TG_E2M3 ? 2 : 3>(h6[pp][i], g6[pp][j], acc[i][j], sn, sm);
                 } else {
-                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], 127, 127);
+                    const u32x4 nn[2] = {h[2 * pp][i], h[2 * pp + 1][i]};
+                    const u32x4 mm[2] = {g[2 * pp][j], g[2 * pp + 1][j]};
+                    acc[i][j] = mfma_f8<DT>(nn, mm, acc[i][j], sn, sm);
                 }
                 side(m);
                 __builtin_amdgcn_sched_barrier(0);
@@ -267,10 +306,15 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             }
             wait_vm<PRO - 2 * NC>();
             barrier();
+            if constexpr (F6) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                read(r, 0, 0, 1, g[0], h[0]);
-                read(r, 1, 0, 1, g[1], h[1]);
+                for (int k = 0; k < 3 * NR; ++k) read6(k, 0, 0, 1, g6[0], h6[0]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    read(r, 0, 0, 1, g[0], h[0]);
+                    read(r, 1, 0, 1, g[1], h[1]);
+                }
             }
             load_scales(0);
             int slot0 = 0;
@@ -280,7 +324,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 const int slot_h0 = wrap(slot0 + NS - 1);
                 const int t1 = min(s + 1, nfull - 1), t2 = min(s + 2, nfull - 1);
                 pair(0, s, [&](int m) {
-                    if (m < NR) read(m, 2, sa, sb, g[2], h[2]); else read(m - NR, 3, sa, sb, g[3], h[3]);
+                    if constexpr (F6)
+                        reads6_at(m, 1, sa, sb, g6[1], h6[1]);
+                    else if (m < NR)
+                        read(m, 2, sa, sb, g[2], h[2]);
+                    else
+                        read(m - NR, 3, sa, sb, g[3], h[3]);
                     if ((m & 3) != 3) {
                         const int c = m - (m >> 2);  // 0 .. 11
                         if (c < 4) copy(1, NC / 2 + c, t1, nb);
@@ -293,7 +342,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
                 barrier();
                 // on the last stage the reads below fetch values that go unused
                 pair(1, s, [&](int m) {
-                    if (m < NR) read(m, 0, na, nb, g[0], h[0]); else read(m - NR, 1, na, nb, g[1], h[1]);
+                    if constexpr (F6)
+                        reads6_at(m, 0, na, nb, g6[0], h6[0]);
+                    else if (m < NR)
+                        read(m, 0, na, nb, g[0], h[0]);
+                    else
+                        read(m - NR, 1, na, nb, g[1], h[1]);
                     if ((m & 3) == 1) copy(1, m >> 2, t2, sa);
                 });
                 if (s + 1 < nk) load_scales(s + 1);
@@ -306,23 +360,32 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             __syncthreads();
             const int c = stage_chunk(tid);
             const int k0 = nfull * BKE + c * EPC;
+            // 6-bit rows: the stage starts at byte 96 * nfull, and every bit
+            // from bit 6K of the row on is zero
+            const int64_t b0 = static_cast<int64_t>(nfull) * STB + c * kChunkBytes, kbits = 6 * static_cast<int64_t>(K);
 #pragma unroll
             for (int i = 0; i < BM / 32; ++i) {
                 const int r = stage_row(tid, i);
                 const char* arow = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
                 const char* brow = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
-                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) = tail_chunk(arow, k0, K);
+                *reinterpret_cast<u32x4*>(smem + lds_chunk_offset(r, c)) =
+                    F6 ? load_chunk_bounded_bits(arow, b0, kbits) : tail_chunk(arow, k0, K);
                 *reinterpret_cast<u32x4*>(smem + SLOT + lds_chunk_offset(r, c)) =
-                    tail_chunk(brow, k0, K);
+                    F6 ? load_chunk_bounded_bits(brow, b0, kbits) : tail_chunk(brow, k0, K);
             }
             if (nfull == 0) load_scales(0);  // otherwise loaded at the end of the last full stage
             __syncthreads();
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
+                if constexpr (F6) {
 #pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    read(r, 2 * pp, 0, 1, g[2 * pp], h[2 * pp]);
-                    read(r, 2 * pp + 1, 0, 1, g[2 * pp + 1], h[2 * pp + 1]);
+                    for (int k = 0; k < 3 * NR; ++k) read6(k, pp, 0, 1, g6[pp], h6[pp]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        read(r, 2 * pp, 0, 1, g[2 * pp], h[2 * pp]);
+                        read(r, 2 * pp + 1, 0, 1, g[2 * pp + 1], h[2 * pp + 1]);
+                    }
                 }
                 pair(pp, nfull, [](int) {});
             }
@@ -955,6 +1018,6 @@ static hipError_t launch_wide(const GemmArgs& a, int64_t grid, int batch, hipStr
     template __global__ void tg::gemm_wide_kernel<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>(GemmArgs);
 
 #define TG_ENTRY_WIDE(id, DT, GM, NS, RS, ADDR, SCHED, EPI, LC, EFF)                                         \
-    {id, DT, 256, 256, 1024 / TG_ELEM_BITS(DT), 2, 2, 128, 128, 256, NS, 5 * 256 * 128, 256, LC, GM, EFF,     \
+    {id, DT, 256, 256, TG_WIDE_STAGE_K(DT), 2, 2, 128, 128, 256, NS, 5 * 256 * 128, 256, LC, GM, EFF,         \
      &tg::launch_wide<DT, GM, NS, RS, ADDR, SCHED, EPI, LC>, (ADDR) ? (int64_t(1) << 23) : 0,                  \
      ((EPI) & 8) ? 1 : 0, (EPI) & 1, ((EPI) & 64) ? 1 : 0},

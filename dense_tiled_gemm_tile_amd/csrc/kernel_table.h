@@ -77,9 +77,13 @@ struct TgKernelDesc {
     int k_slices;            // waves that split K inside a workgroup, each over the whole tile (0: 1)
 };
 
-// Element bits of an operand type (the 4-bit format is packed).
-#define TG_ELEM_BITS(DT) \
-    ((DT) == TG_F32 ? 32 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 8 : (DT) == TG_E2M1 ? 4 : 16)
+// Element bits of an operand type (the 4- and 6-bit formats are packed).
+#define TG_ELEM_BITS(DT)                                                                        \
+    ((DT) == TG_F32 ? 32 : ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 8 : (DT) == TG_E2M1 ? 4      \
+     : ((DT) == TG_E2M3 || (DT) == TG_E3M2) ? 6 : 16)
+// K elements in one 128-byte row segment of a wide-kernel stage (6-bit: a
+// stage is 128 elements, 96 bytes).
+#define TG_WIDE_STAGE_K(DT) (TG_ELEM_BITS(DT) == 6 ? 128 : 1024 / TG_ELEM_BITS(DT))
 // Element bytes of an operand type of at least 8 bits.
 #define TG_ELEM_BYTES(DT) (TG_ELEM_BITS(DT) / 8)
 
@@ -98,6 +102,8 @@ extern const TgKernelDesc tg_entries_kslice[];
 extern const int tg_entries_kslice_count;
 extern const TgKernelDesc tg_entries_wide4[];
 extern const int tg_entries_wide4_count;
+extern const TgKernelDesc tg_entries_wide6[];
+extern const int tg_entries_wide6_count;
 
 // The instance table, indexed by kernel id (ids are 0 .. tg_kernel_count()-1).
 int tg_kernel_count();

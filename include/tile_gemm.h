@@ -78,9 +78,13 @@ enum tile_gemm_dtype {
     TG_F32 = 3,  /* IEEE binary32 operands, fp32 MFMA (full fp32 products) */
     TG_E4M3 = 4, /* 8-bit float operands (1-4-3, bias 7, no infinity), 8-bit MFMA */
     TG_E5M2 = 5, /* 8-bit float operands (1-5-2, bias 15, IEEE-style), 8-bit MFMA */
-    TG_E2M1 = 6  /* 4-bit float operands (the MX FP4 element: 1-2-1, bias 1, values
+    TG_E2M1 = 6, /* 4-bit float operands (the MX FP4 element: 1-2-1, bias 1, values
                     0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, no infinity or
                     NaN), packed two per byte, 4-bit MFMA */
+    TG_E2M3 = 7, /* 6-bit float operands (MX FP6 E2M3: 1-2-3, bias 1, largest 7.5,
+                    no infinity or NaN), packed four per three bytes, 6-bit MFMA */
+    TG_E3M2 = 8  /* 6-bit float operands (MX FP6 E3M2: 1-3-2, bias 3, largest 28,
+                    no infinity or NaN), packed as TG_E2M3 */
 };
 
 enum tile_gemm_status {

@@ -31,7 +31,7 @@ TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float
                 "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 # packed operand types: bits per element (element i of a stored array holds
 # bits [w*i, w*i + w) of the bytes read as a little-endian bit string)
-PACKED_BITS = {"e2m1": 4}
+PACKED_BITS = {"e2m1": 4, "e2m3": 6, "e3m2": 6}
 D_SENTINEL = -7777.0  # value planted in D storage that the product must never write
 
 
@@ -104,6 +104,9 @@ WORKLOADS = {
     # alpha 2^-10 keeps D near unit scale
     "square_8192_e2m1_relu": _w("square_8192_e2m1_relu", 8192, 8192, 8192, "e2m1", "codes", 2.0 ** -10, True,
                                 9500, notes="packed two per byte; A (M, lda/2), B (N, ldb/2) byte storages"),
+    # 6-bit operands (MX FP6, E2M3), every code equally likely
+    "square_8192_e2m3_relu": _w("square_8192_e2m3_relu", 8192, 8192, 8192, "e2m3", "codes", 2.0 ** -10, True,
+                                9600, notes="packed four per three bytes; A (M, 3*lda/4), B (N, 3*ldb/4) bytes"),
 }
 
 
@@ -202,12 +205,12 @@ def packed_operands(M, N, K, dtype, seed_a, seed_b, lda=None, ldb=None, pool=Non
 def block_scales(rows: int, K: int, seed: int, lo: int = 124, hi: int = 130, pad: int = 0,
                  dtype: str = "e4m3", fill: int = 127) -> np.ndarray:
     """Seeded block-scale exponents: (rows, lds) uint8 with lds =
-    4*ceil(K/128) + pad for 8-bit operands (whole dwords per 128-k stage) or
-    16*ceil(K/512) + pad for 4-bit ones (16-byte pieces per two 256-k
-    stages), exponents in [lo, hi] for the ceil(K/32) live blocks and `fill`
-    elsewhere."""
+    4*ceil(K/128) + pad for 8- and 6-bit operands (whole dwords per 128-k
+    stage) or 16*ceil(K/512) + pad for 4-bit ones (16-byte pieces per two
+    256-k stages), exponents in [lo, hi] for the ceil(K/32) live blocks and
+    `fill` elsewhere."""
     nblk = -(-K // 32)
-    lds = (16 * -(-K // 512) if dtype in PACKED_BITS else 4 * -(-K // 128)) + pad
+    lds = (16 * -(-K // 512) if dtype == "e2m1" else 4 * -(-K // 128)) + pad
     g = np.random.default_rng(int(seed))
     s = np.full((rows, max(lds, 4)), fill, dtype=np.uint8)
     s[:, :nblk] = g.integers(lo, hi + 1, size=(rows, nblk), dtype=np.uint8)
@@ -222,8 +225,10 @@ def out_storage(M, N, ldd=None, sentinel=D_SENTINEL) -> torch.Tensor:
 
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw storage of a CPU tensor as numpy: uint16 for bf16/fp16, float32 for
-    fp32, uint8 for the 8-bit formats."""
+    fp32, uint8 for the 8-bit formats and for packed byte storages."""
     t = t.contiguous()
+    if t.dtype == torch.uint8:
+        return t.numpy()
     if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8).numpy()
     if t.dtype in (torch.bfloat16, torch.float16):

@@ -62,7 +62,7 @@ A, B, D = 0x7F0000000000, 0x7F0010000000, 0x7F0020000000
     (dict(lda=63), -2), (dict(ldb=10), -2), (dict(ldd=63), -2),
     (dict(A=0), -3), (dict(B=0), -3), (dict(D=0), -3),
     (dict(A=A + 1), -4), (dict(D=D + 2), -4), (dict(dtype=3, B=B + 2), -4),
-    (dict(dtype=0), -5), (dict(dtype=7), -5),
+    (dict(dtype=0), -5), (dict(dtype=9), -5),
     (dict(D=A + 64), -6), (dict(D=B - 16), -6),
 ])
 def test_validation_codes(args, code):
@@ -182,9 +182,11 @@ def test_every_instance_has_consistent_ownership_arithmetic():
         assert info.threads == 64 * info.waves_m * info.waves_n * info.k_slices
         assert info.wave_tile_m * info.waves_m == info.block_m
         assert info.wave_tile_n * info.waves_n == info.block_n
-        bits = {tg.F32: 32, tg.E4M3: 8, tg.E5M2: 8, tg.E2M1: 4}.get(info.dtype, 16)
+        bits = {tg.F32: 32, tg.E4M3: 8, tg.E5M2: 8, tg.E2M1: 4, tg.E2M3: 6, tg.E3M2: 6}.get(info.dtype, 16)
         row_bytes = info.block_k * bits // 8
-        assert row_bytes in (64, 128)
+        # a stage covers 64 or 128 bytes of each row (6-bit: 96 of a 128-byte LDS row)
+        assert row_bytes in (64, 128) or (bits == 6 and row_bytes == 96)
+        row_bytes = 128 if bits == 6 else row_bytes
         # every instance keeps at least its A stages in LDS, within the 160 KiB of a CU
         assert info.stages * info.block_m * row_bytes <= info.lds_bytes <= 160 * 1024
 
@@ -453,6 +455,34 @@ def test_4bit_validation_and_plans():
     assert ok in (0, -8)
 
 
+def test_6bit_validation_and_plans():
+    """Packed 6-bit operands: rows must start on a byte (strides multiples of
+    4 elements), the streaming instances need 16-byte aligned rows (strides
+    multiples of 64 elements), block scales follow the 8-bit rule (a dword
+    per 128-k stage), a stage is 128 elements (96 bytes), and staging is
+    refused."""
+    import torch
+
+    A2, B2, D2, S2, W2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000, 0x7E0000000000
+    M, N, K = 300, 200, 701
+    for dt in (tg.E2M3, tg.E3M2):
+        ex = lambda lda, ldb: tg.tile_gemm_ex(M, N, K, 1.0, 0, A2, lda, B2, ldb, D2, M, dt, None, -1)
+        assert ex(702, 704) == -2 and ex(704, 706) == -2         # a row would start mid-byte
+        assert ex(704, 708) == -9                                  # whole bytes, not 16-byte aligned rows
+        if not torch.cuda.is_available():
+            assert ex(704, 768) == -8
+        assert tg.staged_workspace_bytes(M, N, K, dt) == -1
+        p = tg.query_plan(8192, 8192, 8192, dt, A2, 8192, B2, 8192, D2, 8192)
+        assert p.block_k == 128 and p.load_class == 16 and p.block_scales == 0
+        q = tg.query_plan_scaled(8192, 8192, 8192, dt, A2, 8192, S2, 256, B2, 8192, 0, 0, D2, 8192)
+        assert q.block_scales == 1 and q.kernel_id != p.kernel_id
+        sc = lambda la: tg.tile_gemm_scaled(M, N, K, 1.0, 0, A2, 704, S2, la, B2, 768, 0, 0, D2, M, dt, tg.F32, None,
+                                            -1)
+        assert sc(4 * 5) == -2 and sc(4 * 6 + 2) == -2
+        if not torch.cuda.is_available():
+            assert sc(4 * 6) == -8
+
+
 def test_8bit_staging_and_streaming_plans():
     """8-bit operands: aligned rows run the streaming 8-bit instance; a large
     product with 1-byte aligned rows runs the 1-byte loader directly, or is
@@ -491,7 +521,7 @@ def _chosen_instances():
     """Every instance some automatic plan picks, over a grid of shapes, dtypes,
     row alignments, D line alignments and entry points."""
     A2, B2, D2, S2, W2 = 0x100000000000, 0x200000000000, 0x300000000000, 0x400000000000, 0x500000000000
-    bits_of = {tg.BF16: 16, tg.F16: 16, tg.F32: 32, tg.E4M3: 8, tg.E5M2: 8, tg.E2M1: 4}
+    bits_of = {tg.BF16: 16, tg.F16: 16, tg.F32: 32, tg.E4M3: 8, tg.E5M2: 8, tg.E2M1: 4, tg.E2M3: 6, tg.E3M2: 6}
     dims = [17, 65, 200, 512, 1024, 2048, 4096, 8192, 12289]
     Ks = [9, 73, 1024, 4099, 8192, 16384]
     chosen = set()
@@ -514,9 +544,14 @@ def _chosen_instances():
                     for cls in classes:
                         ld = stride(K, bits, cls)
                         for ldd in (-(-M // 32) * 32, M + 1):
+                            if bits == 6 and cls < 16:
+                                # 6-bit operands need 16-byte aligned rows
+                                with pytest.raises(tg.TileGemmError):
+                                    tg.query_plan(M, N, K, dt, A2, ld, B2, ld, D2, ldd, -1, tg.F32)
+                                continue
                             chosen.add(tg.query_plan(M, N, K, dt, A2, ld, B2, ld, D2, ldd, -1, tg.F32).kernel_id)
                             if bits <= 8:
-                                sc = 4 * -(-K // 128) if bits == 8 else 16 * -(-K // 512)
+                                sc = 16 * -(-K // 512) if bits == 4 else 4 * -(-K // 128)
                                 try:
                                     chosen.add(tg.query_plan_scaled(M, N, K, dt, A2, ld, S2, sc, B2, ld, 0, 0, D2,
                                                                     ldd).kernel_id)
@@ -526,9 +561,11 @@ def _chosen_instances():
                             elif N <= 256:
                                 p = tg.query_plan_softmax(M, N, K, dt, A2, ld, B2, ld, D2, ldd)
                                 chosen.add(p.kernel_id)
-        # operand rows longer than 8 MiB
-        K = (1 << 23) * 8 // bits + 64
-        chosen.add(tg.query_plan(8192, 8192, K, dt, A2, K, B2, K, D2, 8192, -1, tg.F32).kernel_id)
+        # operand rows longer than 8 MiB (6-bit instances address rows through
+        # 32-bit offsets only)
+        K = -(-((1 << 23) * 8 // bits + 64) // 64) * 64
+        if bits != 6:
+            chosen.add(tg.query_plan(8192, 8192, K, dt, A2, K, B2, K, D2, 8192, -1, tg.F32).kernel_id)
     chosen.discard(-1)
     return chosen
 

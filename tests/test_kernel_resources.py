@@ -20,7 +20,7 @@ import pytest
 
 from dense_tiled_gemm_tile_amd import build as tgbuild
 
-UNITS = ["gemm_wide16.hip", "gemm_wide8.hip", "gemm_wide32.hip", "gemm_wide4.hip"]
+UNITS = ["gemm_wide16.hip", "gemm_wide8.hip", "gemm_wide32.hip", "gemm_wide4.hip", "gemm_wide6.hip"]
 
 
 @pytest.fixture(scope="module")
@@ -84,4 +84,4 @@ def test_wide_kernels_keep_their_loops_free_of_spills(wide_asm):
         # epilogue (EPI bit 3) takes more
         limit = 128 if epi & 8 else 24
         assert meta["private_segment_fixed_size"] <= limit, (name, meta)
-    assert seen >= 24  # every wide instance of the four units
+    assert seen >= 28  # every wide instance of the five units
