@@ -65,7 +65,9 @@ __device__ __forceinline__ u32x4 load_chunk(const char* p) {
 }
 
 // A chunk that starts at element k0 of a row and may run past K: each element
-// with k >= K becomes an exact zero and is not read.
+// with k >= K becomes an exact zero and is not read.  Every load reads an
+// element below K (the index is clamped to K - 1, the value then replaced by
+// zero), so the loads carry no branches and go out back to back.  K >= 1.
 template <int ES>
 __device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int K) {
     unsigned w[4];
@@ -77,7 +79,8 @@ __device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int k = k0 + 4 * d + e;
-                if (k < K) v |= static_cast<unsigned>(r[k]) << (8 * e);
+                const unsigned x = r[min(k, K - 1)];
+                v |= (k < K ? x : 0u) << (8 * e);
             }
             w[d] = v;
         }
@@ -86,16 +89,16 @@ __device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int k = k0 + 2 * d;
-            const unsigned lo = (k < K) ? r[k] : 0u;
-            const unsigned hi = (k + 1 < K) ? r[k + 1] : 0u;
-            w[d] = lo | (hi << 16);
+            const unsigned lo = r[min(k, K - 1)], hi = r[min(k + 1, K - 1)];
+            w[d] = (k < K ? lo : 0u) | ((k + 1 < K ? hi : 0u) << 16);
         }
     } else {
         const unsigned* r = reinterpret_cast<const unsigned*>(row);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int k = k0 + d;
-            w[d] = (k < K) ? r[k] : 0u;
+            const unsigned x = r[min(k, K - 1)];
+            w[d] = k < K ? x : 0u;
         }
     }
     u32x4 v;
@@ -105,10 +108,11 @@ __device__ __forceinline__ u32x4 load_chunk_bounded(const char* row, int k0, int
 
 // A chunk of 4-bit (e2m1) elements, two per byte with the low nibble first,
 // that starts at element k0 (a multiple of 32) of a row and may run past K:
-// elements with k >= K become exact zeros, and no byte that holds only such
-// elements is read.
+// elements with k >= K become exact zeros.  Every load reads a byte that
+// holds an element below K (clamped, as above).  K >= 1.
 __device__ __forceinline__ u32x4 load_chunk_bounded_e2m1(const char* row, int k0, int K) {
-    const unsigned char* r = reinterpret_cast<const unsigned char*>(row) + k0 / 2;
+    const unsigned char* r = reinterpret_cast<const unsigned char*>(row);
+    const int last = (K - 1) / 2;  // the last byte holding an element below K
     unsigned w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -116,10 +120,8 @@ __device__ __forceinline__ u32x4 load_chunk_bounded_e2m1(const char* row, int k0
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int k = k0 + 8 * d + 2 * e;  // the byte's low element
-            if (k + 1 < K)
-                v |= static_cast<unsigned>(r[4 * d + e]) << (8 * e);
-            else if (k < K)
-                v |= (static_cast<unsigned>(r[4 * d + e]) & 0xFu) << (8 * e);
+            const unsigned x = r[min(k / 2, last)];
+            v |= (k + 1 < K ? x : k < K ? (x & 0xFu) : 0u) << (8 * e);
         }
         w[d] = v;
     }
@@ -130,10 +132,11 @@ __device__ __forceinline__ u32x4 load_chunk_bounded_e2m1(const char* row, int k0
 
 // Sixteen bytes of a packed row from byte b0 on, of which only the first
 // `nbits` bits of the row hold elements below K: every later bit becomes
-// zero (a 6-bit element past K then decodes to +0) and no byte wholly past
-// them is read.
+// zero (a 6-bit element past K then decodes to +0).  Every load reads a byte
+// that holds bits below nbits (clamped, as above).  nbits >= 1.
 __device__ __forceinline__ u32x4 load_chunk_bounded_bits(const char* row, int64_t b0, int64_t nbits) {
     const unsigned char* r = reinterpret_cast<const unsigned char*>(row);
+    const int64_t last = (nbits - 1) / 8;
     unsigned w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -142,10 +145,8 @@ __device__ __forceinline__ u32x4 load_chunk_bounded_bits(const char* row, int64_
         for (int e = 0; e < 4; ++e) {
             const int64_t b = b0 + 4 * d + e;
             const int64_t left = nbits - 8 * b;  // bits of this byte below K
-            if (left >= 8)
-                v |= static_cast<unsigned>(r[b]) << (8 * e);
-            else if (left > 0)
-                v |= (static_cast<unsigned>(r[b]) & ((1u << left) - 1u)) << (8 * e);
+            const unsigned x = r[b < last ? b : last];
+            v |= (left >= 8 ? x : left > 0 ? (x & ((1u << left) - 1u)) : 0u) << (8 * e);
         }
         w[d] = v;
     }

@@ -377,6 +377,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             __syncthreads();
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
+                if (nfull * BKE + pp * (BKE / 2) >= K) break;  // the rest of the stage is zeros
                 if constexpr (F6) {
 #pragma unroll
                     for (int k = 0; k < 3 * NR; ++k) read6(k, pp, 0, 1, g6[pp], h6[pp]);
@@ -547,18 +548,26 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < FN; ++i) scn[i] = tail_scale(p.scale_b, p.lds_b, n0 + wave_n * WTN + 32 * i + frag_row(lane), N);
             __syncthreads();
+            // slabs wholly past K hold zeros and are skipped
+            const int live_slabs = (K - nfull * BKE + BKE / 4 - 1) / (BKE / 4);
 #pragma unroll
             for (int r = 0; r < NR; ++r) read(r, 0, 0, 1, fa0, fb0);
             slab_sc(Q0{}, fa0, fb0, [](int) {});
+            if (live_slabs > 1) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read(r, 1, 0, 1, fa0, fb0);
-            slab_sc(Q1{}, fa0, fb0, [](int) {});
+                for (int r = 0; r < NR; ++r) read(r, 1, 0, 1, fa0, fb0);
+                slab_sc(Q1{}, fa0, fb0, [](int) {});
+            }
+            if (live_slabs > 2) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read(r, 2, 0, 1, fa0, fb0);
-            slab_sc(Q2{}, fa0, fb0, [](int) {});
+                for (int r = 0; r < NR; ++r) read(r, 2, 0, 1, fa0, fb0);
+                slab_sc(Q2{}, fa0, fb0, [](int) {});
+            }
+            if (live_slabs > 3) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read(r, 3, 0, 1, fa0, fb0);
-            slab_sc(Q3{}, fa0, fb0, [](int) {});
+                for (int r = 0; r < NR; ++r) read(r, 3, 0, 1, fa0, fb0);
+                slab_sc(Q3{}, fa0, fb0, [](int) {});
+            }
         }
     } else if constexpr (LC < 16) {
         // Operand rows only 4- or 2-byte aligned: LDS-DMA needs 16-byte
@@ -699,6 +708,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             __syncthreads();
     #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (nfull * BKE + q * (BKE / 4) >= K) break;  // the rest of the stage is zeros
     #pragma unroll
                 for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
     #pragma unroll
@@ -790,6 +800,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmArgs p) {
             __syncthreads();
     #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (nfull * BKE + q * (BKE / 4) >= K) break;  // the rest of the stage is zeros
     #pragma unroll
                 for (int r = 0; r < NR; ++r) read(r, q, 0, 1, fa0, fb0);
     #pragma unroll
