@@ -15,12 +15,16 @@
  *   B is logically (K,N), stored K-contiguous:  b[k,n] at byte B + (k + n*ldb)*s
  *   D is logically (M,N), fp32, M-contiguous:   d[m,n] at byte D + (m + n*ldd)*4
  *
- * The 4-bit format (TG_E2M1) is packed: element i of an operand array holds
- * bits [4i, 4i + 4) of the array read as a little-endian bit string, i.e.
- * a[m,k] is the low nibble of byte A + (m*lda + k)/2 when m*lda + k is even
- * and the high nibble otherwise (b[k,n] likewise at index k + n*ldb).  Every
- * row must start on a byte, so lda and ldb are even for it (TG_ERR_LD), and
- * its pointers need only byte alignment.  Strides and sizes count elements.
+ * The 4-bit (TG_E2M1) and 6-bit (TG_E2M3, TG_E3M2) formats are packed:
+ * element i of an operand array holds bits [w*i, w*i + w) of the array read
+ * as a little-endian bit string (w = 4 or 6), i.e. a 4-bit a[m,k] is the low
+ * nibble of byte A + (m*lda + k)/2 when m*lda + k is even and the high nibble
+ * otherwise, and four 6-bit elements fill three bytes (b[k,n] likewise at
+ * index k + n*ldb).  Every row must start on a byte, so lda and ldb are even
+ * (4-bit) or multiples of 4 (6-bit) (TG_ERR_LD), and the pointers need only
+ * byte alignment.  Strides and sizes count elements.  The 6-bit kernels
+ * also need every row to start on a 16-byte boundary (pointers 16-byte
+ * aligned, strides multiples of 64); other 6-bit rows give TG_ERR_PLAN.
  *
  * For 0 <= m < M and 0 <= n < N the call writes
  *
@@ -252,8 +256,8 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
                       void* stream, int kernel_id);
 
 /*
- * 8-bit (TG_E4M3, TG_E5M2) and 4-bit (TG_E2M1) operands with optional block
- * scales: every 32 consecutive k of an A row (and of a B column) share one
+ * 8-bit (TG_E4M3, TG_E5M2), 6-bit (TG_E2M3, TG_E3M2) and 4-bit (TG_E2M1)
+ * operands with optional block scales: every 32 consecutive k of an A row (and of a B column) share one
  * unsigned 8-bit exponent e, and the elements of that block stand for their
  * decoded value times 2^(e - 127) (e = 255: NaN).  The pages name
  * block-scaled 8-bit and 4-bit matmuls (cuTile.jl tutorial "Matrix
@@ -262,9 +266,9 @@ int tile_gemm_softmax(int64_t M, int64_t N, int64_t K, float alpha,
  *
  *     d[m,n] = epilogue(alpha * sum_k a[m,k]*sa[m,k/32] * b[k,n]*sb[n,k/32])
  *
- * accumulated in fp32 on the 8-bit MFMA (which applies the scales itself).
+ * accumulated in fp32 on the scaled MFMA (which applies the scales itself).
  * Scale of A row m, block j: byte scale_a[m*lds_a + j]; of B column n:
- * scale_b[n*lds_b + j].  8-bit operands: lds_a, lds_b >= 4*ceil(K/128) and
+ * scale_b[n*lds_b + j].  8- and 6-bit operands: lds_a, lds_b >= 4*ceil(K/128) and
  * multiples of 4, scale pointers 4-byte aligned (the kernels read the four
  * scales of each 128-k stage as one dword); 4-bit operands: lds_a, lds_b >=
  * 16*ceil(K/512) and multiples of 16, scale pointers 16-byte aligned (the
@@ -302,9 +306,9 @@ int tile_gemm_scaled(int64_t M, int64_t N, int64_t K, float alpha, int relu,
  * workspace does not suffice; mode 0: never (as tile_gemm_out).  workspace:
  * device memory owned by the caller, not overlapping A, B or D
  * (TG_ERR_ALIAS), reusable once the stream has passed the call.  M, N or K
- * = 0 never stages.  Packed 4-bit operands are never staged (mode 1 gives
- * TG_ERR_DTYPE; mode -1 runs the direct plan, which takes rows of any byte
- * alignment).  Other rules and errors as tile_gemm_out with kernel_id -1.
+ * = 0 never stages.  Packed 4- and 6-bit operands are never staged (mode 1
+ * gives TG_ERR_DTYPE; mode -1 runs the direct plan).  Other rules and errors
+ * as tile_gemm_out with kernel_id -1.
  */
 int tile_gemm_staged(int64_t M, int64_t N, int64_t K, float alpha, int relu,
                      const void* A, int64_t lda, const void* B, int64_t ldb,
