@@ -1,6 +1,6 @@
 // Register-staged tiled GEMM kernel for gfx950 (CDNA4): the instances for
-// operand rows that are only 4-, 2- or (8-bit operands) 1-byte aligned, for
-// small problems and for the fused row-softmax epilogue.
+// operand rows that are only 4-, 2- or (8-, 6- and 4-bit operands) 1-byte
+// aligned, for small problems and for the fused row-softmax epilogue.
 //
 // One workgroup owns one BM x BN output tile (cuTile.jl tutorial "Matrix
 // Multiplication", Step 2: each output tile depends on no other, so each gets
@@ -33,9 +33,14 @@ template <int DT, int BM, int BN, int LOADCLASS, int MINWAVES, int SM>
 __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     select_batch(p);
     constexpr bool F8 = (DT == TG_E4M3 || DT == TG_E5M2);
-    constexpr int ES = (DT == TG_F32) ? 4 : F8 ? 1 : 2;  // element bytes
-    constexpr int EPC = 16 / ES;                    // elements per 16-byte chunk
-    constexpr int BKE = kRowBytes / ES;             // K elements per stage
+    constexpr bool F4 = (DT == TG_E2M1);                   // packed two per byte
+    constexpr bool F6 = (DT == TG_E2M3 || DT == TG_E3M2);  // packed four per three bytes
+    constexpr bool SCL = F8 || F4 || F6;                   // block scales apply
+    constexpr int ES = (DT == TG_F32) ? 4 : (F8 || F4 || F6) ? 1 : 2;  // element bytes (packed: per byte)
+    constexpr int EPC = F4 ? 32 : 16 / ES;          // elements per 16-byte chunk (not for 6-bit)
+    constexpr int BKE = F4 ? 256 : F6 ? 128 : kRowBytes / ES;  // K elements per stage
+    constexpr int STB = F6 ? 96 : kRowBytes;        // bytes of a row per stage (6-bit: chunks 0-5)
+    constexpr int SCW = F4 ? 2 : 1;                 // scale dwords per row and stage
     constexpr int WTM = BM / 2, WTN = BN / 2;       // 2 x 2 waves
     constexpr int FM = WTM / 32, FN = WTN / 32;     // 32 x 32 MFMA blocks per wave
     constexpr int RA = BM / 32, RB = BN / 32;       // staged rows per thread
@@ -91,42 +96,75 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
             mread8[q][e] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), ch);
             nread8[q][e] = (BM + wave_n * WTN) * kRowBytes + lds_chunk_offset(frag_row(lane), ch);
         }
-    // block scales of the lane's rows: one dword per row and stage (the four
-    // 32-k blocks of the stage's 128 k), for the stage being consumed (cur)
-    // and the one being loaded (nxt)
-    unsigned scm_cur[FM], scn_cur[FN], scm_nxt[FM], scn_nxt[FN];
+    // 6-bit operands: pair p of a stage is the 48 bytes [48p, 48p + 48) of a
+    // row; half-wave h takes bytes [48p + 24h, 48p + 24h + 24) as three 8-byte
+    // reads, each inside one 16-byte chunk (mfma_f6)
+    int mread6[2][3], nread6[2][3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+            const int b = 48 * q + 24 * (lane >> 5) + 8 * e;
+            mread6[q][e] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag_row(lane), b >> 4) + (b & 15);
+            nread6[q][e] = (BM + wave_n * WTN) * kRowBytes + lds_chunk_offset(frag_row(lane), b >> 4) + (b & 15);
+        }
+    // block scales of the lane's rows: SCW dwords per row and stage (the
+    // stage's 32-k blocks, four per dword), for the stage being consumed
+    // (cur) and the one being loaded (nxt)
+    unsigned scm_cur[FM][SCW], scn_cur[FN][SCW], scm_nxt[FM][SCW], scn_nxt[FN][SCW];
     const int nblk = (K + 31) / 32;
     auto load_scales = [&](int s) {
-        if constexpr (F8) {
+        if constexpr (SCL) {
             if (p.scale_a) {
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
                     const int m = min(m0 + wave_m * WTM + 32 * j + frag_row(lane), M - 1);
-                    scm_nxt[j] = *reinterpret_cast<const unsigned*>(p.scale_a + m * p.lds_a + 4 * static_cast<int64_t>(s));
+#pragma unroll
+                    for (int w = 0; w < SCW; ++w)
+                        scm_nxt[j][w] = *reinterpret_cast<const unsigned*>(
+                            p.scale_a + m * p.lds_a + 4 * (SCW * static_cast<int64_t>(s) + w));
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < FM; ++j) scm_nxt[j] = 0x7F7F7F7Fu;
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int w = 0; w < SCW; ++w) scm_nxt[j][w] = 0x7F7F7F7Fu;
             }
             if (p.scale_b) {
 #pragma unroll
                 for (int i = 0; i < FN; ++i) {
                     const int n = min(n0 + wave_n * WTN + 32 * i + frag_row(lane), N - 1);
-                    scn_nxt[i] = *reinterpret_cast<const unsigned*>(p.scale_b + n * p.lds_b + 4 * static_cast<int64_t>(s));
+#pragma unroll
+                    for (int w = 0; w < SCW; ++w)
+                        scn_nxt[i][w] = *reinterpret_cast<const unsigned*>(
+                            p.scale_b + n * p.lds_b + 4 * (SCW * static_cast<int64_t>(s) + w));
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < FN; ++i) scn_nxt[i] = 0x7F7F7F7Fu;
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int w = 0; w < SCW; ++w) scn_nxt[i][w] = 0x7F7F7F7Fu;
             }
         }
     };
     auto next_scales = [&]() {
-        if constexpr (F8) {
+        if constexpr (SCL) {
 #pragma unroll
-            for (int j = 0; j < FM; ++j) scm_cur[j] = scm_nxt[j];
+            for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int i = 0; i < FN; ++i) scn_cur[i] = scn_nxt[i];
+                for (int w = 0; w < SCW; ++w) scm_cur[j][w] = scm_nxt[j][w];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int w = 0; w < SCW; ++w) scn_cur[i][w] = scn_nxt[i][w];
         }
+    };
+    // exponent of 32-k block b (0 .. 4*SCW-1) of stage s from a row's dwords;
+    // blocks past the last one of K (their data is zero) count as 1
+    // (a select, not an index, picks the dword: b varies by lane)
+    auto scale_byte = [&](const unsigned (&w)[SCW], int b, int s) {
+        const unsigned d = (SCW == 2 && b >= 4) ? w[SCW - 1] : w[0];
+        return 4 * SCW * s + b < nblk ? static_cast<int>((d >> (8 * (b & 3))) & 0xFFu) : 127;
     };
 
     f32x16 acc[FN][FM];
@@ -143,9 +181,13 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     const int nk = nfull + ((K % BKE) != 0 ? 1 : 0);
 
     u32x4 sa[RA], sb[RB];
+    // 6-bit stages cover chunks 0-5 of each LDS row; chunks 6 and 7 are never
+    // read, and their threads load nothing
+    const bool chunk_used = !F6 || c < STB / 16;
     auto load_full = [&](int s) {
         load_scales(s);
-        const int64_t kb = static_cast<int64_t>(s) * kRowBytes + c * 16;
+        const int64_t kb = static_cast<int64_t>(s) * STB + c * 16;
+        if (!chunk_used) return;
 #pragma unroll
         for (int i = 0; i < RA; ++i) sa[i] = load_chunk<LOADCLASS>(arow[i] + kb);
 #pragma unroll
@@ -153,11 +195,27 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     };
     auto load_ragged = [&](int s) {
         load_scales(s);
+        if (!chunk_used) return;
         const int k0 = s * BKE + c * EPC;
+        const int64_t b0 = static_cast<int64_t>(s) * STB + c * 16, kbits = 6 * static_cast<int64_t>(K);
 #pragma unroll
-        for (int i = 0; i < RA; ++i) sa[i] = load_chunk_bounded<ES>(arow[i], k0, K);
+        for (int i = 0; i < RA; ++i) {
+            if constexpr (F6)
+                sa[i] = load_chunk_bounded_bits(arow[i], b0, kbits);
+            else if constexpr (F4)
+                sa[i] = load_chunk_bounded_e2m1(arow[i], k0, K);
+            else
+                sa[i] = load_chunk_bounded<ES>(arow[i], k0, K);
+        }
 #pragma unroll
-        for (int i = 0; i < RB; ++i) sb[i] = load_chunk_bounded<ES>(brow[i], k0, K);
+        for (int i = 0; i < RB; ++i) {
+            if constexpr (F6)
+                sb[i] = load_chunk_bounded_bits(brow[i], b0, kbits);
+            else if constexpr (F4)
+                sb[i] = load_chunk_bounded_e2m1(brow[i], k0, K);
+            else
+                sb[i] = load_chunk_bounded<ES>(brow[i], k0, K);
+        }
     };
     auto store_stage = [&](int buf) {
         char* base = smem + buf * STAGE;
@@ -198,22 +256,54 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
         for (int q = 0; q < 2; ++q) {
             if (q == 0) read_pair(1, mf[1], nf[1]);
             const int sub = 2 * q + (lane >> 5);      // block within the stage
-            const bool live = 4 * s + sub < nblk;
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
-                    const int sn = live ? static_cast<int>(scn_cur[i] >> (8 * sub)) : 127;
-                    const int sm = live ? static_cast<int>(scm_cur[j] >> (8 * sub)) : 127;
-                    acc[i][j] = mfma_f8<DT>(nf[q][i], mf[q][j], acc[i][j], sn & 0xFF, sm & 0xFF);
+                    const int sn = scale_byte(scn_cur[i], sub, s), sm = scale_byte(scm_cur[j], sub, s);
+                    acc[i][j] = mfma_f8<DT>(nf[q][i], mf[q][j], acc[i][j], sn, sm);
                 }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // 6-bit operands, stage s in buffer buf: two MFMAs of 64 k per block
+    auto compute6 = [&](int buf, int s) {
+        const char* base = smem + buf * STAGE;
+        u32x2 mf[2][FM][3], nf[2][FN][3];
+        auto read_pair = [&](int q, u32x2 (&m6)[FM][3], u32x2 (&n6)[FN][3]) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    m6[j][e] = *reinterpret_cast<const u32x2*>(base + mread6[q][e] + j * 32 * kRowBytes);
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+                    n6[i][e] = *reinterpret_cast<const u32x2*>(base + nread6[q][e] + i * 32 * kRowBytes);
+            }
+        };
+        read_pair(0, mf[0], nf[0]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (q == 0) read_pair(1, mf[1], nf[1]);
+            const int sub = 2 * q + (lane >> 5);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[i][j] = mfma_f6<DT == TG_E2M3 ? 2 : 3>(nf[q][i], mf[q][j], acc[i][j],
+                                                                scale_byte(scn_cur[i], sub, s),
+                                                                scale_byte(scm_cur[j], sub, s));
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto compute = [&](int buf, int s) {
         if constexpr (F8) {
             compute8(buf, s);
+            return;
+        } else if constexpr (F6) {
+            compute6(buf, s);
             return;
         }
         const char* base = smem + buf * STAGE;
@@ -229,7 +319,16 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(nf[q & 1][i], mf[q & 1][j], acc[i][j]);
+                for (int j = 0; j < FM; ++j) {
+                    if constexpr (F4) {
+                        // slab q: half-wave h takes 32-k block 2q + h of the stage
+                        const int sub = 2 * q + (lane >> 5);
+                        acc[i][j] = mfma_f4(nf[q & 1][i], mf[q & 1][j], acc[i][j], scale_byte(scn_cur[i], sub, s),
+                                            scale_byte(scm_cur[j], sub, s));
+                    } else {
+                        acc[i][j] = mfma_slab<DT>(nf[q & 1][i], mf[q & 1][j], acc[i][j]);
+                    }
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -350,7 +449,13 @@ static hipError_t launch_rs(const GemmArgs& a, int64_t grid, int batch, hipStrea
     X(39, TG_E5M2, 256, 256, 1, 1, 4, 0, 56)       \
     X(40, TG_E5M2, 128, 128, 4, 2, 4, 0, 45)       \
     X(41, TG_E5M2, 64, 64, 4, 2, 4, 0, 25)         \
-    X(42, TG_E5M2, 64, 64, 1, 2, 4, 0, 20)
+    X(42, TG_E5M2, 64, 64, 1, 2, 4, 0, 20)        \
+    X(61, TG_E2M1, 256, 256, 1, 1, 4, 0, 56)       \
+    X(62, TG_E2M1, 64, 64, 1, 2, 4, 0, 20)         \
+    X(63, TG_E2M3, 256, 256, 1, 1, 4, 0, 56)       \
+    X(64, TG_E2M3, 64, 64, 1, 2, 4, 0, 20)         \
+    X(65, TG_E3M2, 256, 256, 1, 1, 4, 0, 56)       \
+    X(66, TG_E3M2, 64, 64, 1, 2, 4, 0, 20)
 
 // Explicit instantiation, seen by both the device and the host pass.
 #define TG_INSTANTIATE_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF) \
@@ -360,9 +465,9 @@ TG_RS_LIST(TG_INSTANTIATE_RS)
 // The descriptors hold host launch functions, so they exist only in the host pass.
 #ifndef __HIP_DEVICE_COMPILE__
 #define TG_ENTRY_RS(id, DT, BM, BN, LC, MW, GM, SM, EFF)                                                  \
-    {id, DT, BM, BN, 128 / TG_ELEM_BYTES(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,  \
+    {id, DT, BM, BN, TG_WIDE_STAGE_K(DT), 2, 2, (BM) / 2, (BN) / 2, 256, 2, 2 * ((BM) + (BN)) * 128,      \
      ((BM) / 2) * ((BN) / 2) / 64, LC, GM, EFF, &tg::launch_rs<DT, BM, BN, LC, MW, SM>, 0, SM, 0,          \
-     ((DT) == TG_E4M3 || (DT) == TG_E5M2) ? 1 : 0},
+     TG_ELEM_BITS(DT) <= 8 ? 1 : 0},
 extern const TgKernelDesc tg_entries_rs[] = {TG_RS_LIST(TG_ENTRY_RS)};
 extern const int tg_entries_rs_count = sizeof(tg_entries_rs) / sizeof(tg_entries_rs[0]);
 #endif  // __HIP_DEVICE_COMPILE__

@@ -22,9 +22,7 @@
  * otherwise, and four 6-bit elements fill three bytes (b[k,n] likewise at
  * index k + n*ldb).  Every row must start on a byte, so lda and ldb are even
  * (4-bit) or multiples of 4 (6-bit) (TG_ERR_LD), and the pointers need only
- * byte alignment.  Strides and sizes count elements.  The 6-bit kernels
- * also need every row to start on a 16-byte boundary (pointers 16-byte
- * aligned, strides multiples of 64); other 6-bit rows give TG_ERR_PLAN.
+ * byte alignment.  Strides and sizes count elements.
  *
  * For 0 <= m < M and 0 <= n < N the call writes
  *

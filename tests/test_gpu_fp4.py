@@ -151,6 +151,19 @@ def test_block_scaled_exact(shape):
     _log(f"[fp4 scaled] {M}x{N}x{K}: exact on {ran - 1} instances and the plan")
 
 
+def test_block_scaled_rows_on_odd_bytes():
+    """Rows starting on odd bytes with block scales: the register-staged
+    instances (large and small products), bit-exact."""
+    for M, N, K in ((600, 700, 1001), (70, 90, 260)):
+        lda, ldb = strides(K, False)
+        A, B = si.packed_operands(M, N, K, DT, 3 + K, 4 + K, lda, ldb)
+        sa, _ = scales(M, K, 5 + K)
+        sb, _ = scales(N, K, 6 + K)
+        ref, _ = oracle.gemm(M, N, K, 2.0, True, A, lda, B, ldb, DT, scale_a=sa, lds_a=sa.shape[1], scale_b=sb,
+                             lds_b=sb.shape[1])
+        _exact(run(A, B, M, N, K, lda, ldb, 2.0, True, sa, sb), ref, M, f"{M}x{N}x{K} odd rows scaled")
+
+
 @pytest.mark.parametrize("side", ["a", "b"])
 def test_one_sided_scales(side):
     M, N, K = 300, 270, 1100

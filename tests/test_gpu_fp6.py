@@ -35,11 +35,15 @@ def _instances(dt):
     return [k for k in range(tg.kernel_count()) if tg.kernel_info(k).dtype == tg.DTYPE_CODES[dt]]
 
 
-def strides(K):
+def strides(K, aligned=True):
     """Element strides whose rows start 16-byte aligned (multiples of 64
-    elements, 48 bytes), padding included."""
-    lda = -(-K // 64) * 64 + 64
-    return lda, lda + 128
+    elements, 48 bytes), or (aligned False) only on whole bytes (multiples of
+    4 elements, 3 bytes, that are not multiples of 64), padding included."""
+    if aligned:
+        lda = -(-K // 64) * 64 + 64
+        return lda, lda + 128
+    lda = -(-K // 64) * 64 + 4
+    return lda, lda + 8
 
 
 def pool(dt):
@@ -94,12 +98,13 @@ def test_exact_every_instance(dt, shape):
     """Every 6-bit instance of the type (and the automatic plan), ragged M, N
     and K: bit-exact, padding untouched."""
     M, N, K = shape
-    lda, ldb = strides(K)
     for kid in [-1] + _instances(dt):
-        A, B = si.packed_operands(M, N, K, dt, M + K + kid, N + K + kid, lda, ldb, pool=pool(dt))
-        ref, _ = oracle.gemm(M, N, K, -0.75, True, A, lda, B, ldb, dt)
-        _exact(run(dt, A, B, M, N, K, lda, ldb, -0.75, True, ldd=M + 3, kernel_id=kid), ref, M,
-               f"{dt} instance {kid}")
+        for aligned in ([True, False] if kid < 0 else [tg.kernel_info(kid).load_class == 16]):
+            lda, ldb = strides(K, aligned)
+            A, B = si.packed_operands(M, N, K, dt, M + K + kid, N + K + kid, lda, ldb, pool=pool(dt))
+            ref, _ = oracle.gemm(M, N, K, -0.75, True, A, lda, B, ldb, dt)
+            _exact(run(dt, A, B, M, N, K, lda, ldb, -0.75, True, ldd=M + 3, kernel_id=kid), ref, M,
+                   f"{dt} instance {kid} aligned={aligned}")
     _log(f"[fp6] {dt} {M}x{N}x{K}: exact on every instance")
 
 
@@ -112,7 +117,7 @@ def test_instance_k_sweep(dt):
         info = tg.kernel_info(kid)
         M, N = info.block_m + 45, 2 * info.block_n - 3
         for K in (1, 3, 127, 128, 129, 256, 383, 384, 385, 640, 1031):
-            lda, ldb = strides(K)
+            lda, ldb = strides(K, info.load_class == 16)
             A, B = si.packed_operands(M, N, K, dt, 50 + K, 60 + K, lda, ldb, pool=pool(dt))
             ref, _ = oracle.gemm(M, N, K, 1.25, False, A, lda, B, ldb, dt)
             _exact(run(dt, A, B, M, N, K, lda, ldb, 1.25, False, kernel_id=kid), ref, M, f"instance {kid} K={K}")
@@ -146,7 +151,7 @@ def test_block_scaled_exact_and_refusals(dt):
             continue
         _exact(D_st, ref, M, f"{dt} instance {kid}")
         ran += 1
-    assert ran == 2
+    assert ran == 1 + sum(tg.kernel_info(k).block_scales for k in _instances(dt))
     # one-sided scales and a NaN scale poisoning exactly its row
     ref, _ = oracle.gemm(M, N, K, 0.5, False, A, lda, B, ldb, dt, scale_b=sb, lds_b=sb.shape[1])
     _exact(run(dt, A, B, M, N, K, lda, ldb, 0.5, False, None, sb), ref, M, f"{dt} scales on B only")
@@ -177,6 +182,20 @@ def test_full_range_within_bound(dt):
     ok, r3 = oracle.check(run(dt, A, B, M, N, K, lda, ldb, 0.5, True)[:, :M].double().numpy(), ref, mag, K)
     assert ok, f"unscaled: worst ratio {r3}"
     _log(f"[fp6 full range] {dt}: worst ratio {r:.3g} (scaled), {r2:.3g} (bf16 D), {r3:.3g} (unscaled)")
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_block_scaled_rows_on_any_byte(dt):
+    """Rows on 3-byte boundaries with block scales: the register-staged
+    instances, large and small products, bit-exact."""
+    for M, N, K in ((600, 700, 1001), (70, 90, 260)):
+        lda, ldb = strides(K, False)
+        A, B = si.packed_operands(M, N, K, dt, 3 + K, 4 + K, lda, ldb, pool=pool(dt))
+        sa, _ = scales(M, K, 5 + K)
+        sb, _ = scales(N, K, 6 + K)
+        ref, _ = oracle.gemm(M, N, K, 2.0, True, A, lda, B, ldb, dt, scale_a=sa, lds_a=sa.shape[1], scale_b=sb,
+                             lds_b=sb.shape[1])
+        _exact(run(dt, A, B, M, N, K, lda, ldb, 2.0, True, sa, sb), ref, M, f"{dt} {M}x{N}x{K} misaligned scaled")
 
 
 def test_fp6_workload_sampled():

@@ -414,7 +414,8 @@ def test_4bit_validation_and_plans():
     scales come in 16-byte pieces per two 256-k stages (16-byte aligned),
     staging is refused, and the plans take the 4-bit instances: the
     streaming one for aligned rows (256 k per stage), the register-staged one
-    for rows on odd bytes, the scaled ones only with 16-byte aligned rows."""
+    for rows on odd bytes (the register-staged ones for small or scaled
+    products)."""
     import torch
 
     A2, B2, D2, S2, W2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000, 0x7E0000000000
@@ -440,15 +441,18 @@ def test_4bit_validation_and_plans():
                                                                M, tg.E2M1, tg.F32, None, -1)
     assert sc(S2, need - 16) == -2 and sc(S2, need + 4) == -2
     assert sc(S2 + 4, need) == -4
-    assert sc(S2, need, lda=706) == -9        # rows on odd bytes: no scaled instance
+    p = tg.query_plan_scaled(M, N, K, tg.E2M1, A2, 706, S2, need, B2, 706, 0, 0, D2, M)
+    assert p.load_class == 1 and p.block_scales == 1   # rows on odd bytes: the register-staged instance
     if not gpu:
         assert sc(S2, need, S2 + (1 << 20), need) == -8
     # plans
     p = tg.query_plan(8192, 8192, 8192, tg.E2M1, A2, 8192, B2, 8192, D2, 8192)
     assert p.kernel_id == 51 and p.block_k == 256 and p.load_class == 16
     assert tg.query_plan(8192, 8192, 8192, tg.E2M1, A2, 8192, B2, 8192, D2, 8193).kernel_id == 52
-    p = tg.query_plan(M, N, K, tg.E2M1, A2, 706, B2, 706, D2, M)
+    p = tg.query_plan(4096, 4096, K, tg.E2M1, A2, 706, B2, 706, D2, 4096)
     assert p.kernel_id == 53 and p.load_class == 1
+    p = tg.query_plan(M, N, K, tg.E2M1, A2, 706, B2, 706, D2, M)   # small: the 64 x 64 register-staged one
+    assert p.kernel_id == 62 and p.load_class == 1
     p = tg.query_plan_scaled(8192, 8192, 8192, tg.E2M1, A2, 8192, S2, 256, B2, 8192, S2 + (1 << 24), 256, D2, 8192)
     assert p.kernel_id == 54 and p.block_scales == 1
     assert tg.kernel_info(51).block_scales == 0 and tg.kernel_info(55).block_scales == 1
@@ -457,10 +461,10 @@ def test_4bit_validation_and_plans():
 
 def test_6bit_validation_and_plans():
     """Packed 6-bit operands: rows must start on a byte (strides multiples of
-    4 elements), the streaming instances need 16-byte aligned rows (strides
-    multiples of 64 elements), block scales follow the 8-bit rule (a dword
-    per 128-k stage), a stage is 128 elements (96 bytes), and staging is
-    refused."""
+    4 elements), the streaming instances take 16-byte aligned rows (strides
+    multiples of 64 elements) and the register-staged ones any other, block
+    scales follow the 8-bit rule (a dword per 128-k stage), a stage is 128
+    elements (96 bytes), and staging is refused."""
     import torch
 
     A2, B2, D2, S2, W2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000, 0x7FC000000000, 0x7E0000000000
@@ -468,9 +472,10 @@ def test_6bit_validation_and_plans():
     for dt in (tg.E2M3, tg.E3M2):
         ex = lambda lda, ldb: tg.tile_gemm_ex(M, N, K, 1.0, 0, A2, lda, B2, ldb, D2, M, dt, None, -1)
         assert ex(702, 704) == -2 and ex(704, 706) == -2         # a row would start mid-byte
-        assert ex(704, 708) == -9                                  # whole bytes, not 16-byte aligned rows
+        p = tg.query_plan(M, N, K, dt, A2, 704, B2, 708, D2, M)    # rows on 3-byte boundaries
+        assert p.load_class == 1 and p.block_m in (64, 256) and p.block_k == 128
         if not torch.cuda.is_available():
-            assert ex(704, 768) == -8
+            assert ex(704, 768) == -8 and ex(704, 708) == -8
         assert tg.staged_workspace_bytes(M, N, K, dt) == -1
         p = tg.query_plan(8192, 8192, 8192, dt, A2, 8192, B2, 8192, D2, 8192)
         assert p.block_k == 128 and p.load_class == 16 and p.block_scales == 0
@@ -544,20 +549,11 @@ def _chosen_instances():
                     for cls in classes:
                         ld = stride(K, bits, cls)
                         for ldd in (-(-M // 32) * 32, M + 1):
-                            if bits == 6 and cls < 16:
-                                # 6-bit operands need 16-byte aligned rows
-                                with pytest.raises(tg.TileGemmError):
-                                    tg.query_plan(M, N, K, dt, A2, ld, B2, ld, D2, ldd, -1, tg.F32)
-                                continue
                             chosen.add(tg.query_plan(M, N, K, dt, A2, ld, B2, ld, D2, ldd, -1, tg.F32).kernel_id)
                             if bits <= 8:
                                 sc = 16 * -(-K // 512) if bits == 4 else 4 * -(-K // 128)
-                                try:
-                                    chosen.add(tg.query_plan_scaled(M, N, K, dt, A2, ld, S2, sc, B2, ld, 0, 0, D2,
-                                                                    ldd).kernel_id)
-                                except tg.TileGemmError as e:
-                                    # 4-bit block scales need 16-byte aligned operand rows
-                                    assert bits == 4 and cls < 16 and e.code == -9, (dt, cls, e.code)
+                                chosen.add(tg.query_plan_scaled(M, N, K, dt, A2, ld, S2, sc, B2, ld, 0, 0, D2,
+                                                                ldd).kernel_id)
                             elif N <= 256:
                                 p = tg.query_plan_softmax(M, N, K, dt, A2, ld, B2, ld, D2, ldd)
                                 chosen.add(p.kernel_id)
