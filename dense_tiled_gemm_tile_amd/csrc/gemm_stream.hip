@@ -2,37 +2,43 @@
 // tiles for problems with few output tiles and a long K, on operand rows that
 // start 16-byte aligned.
 //
-// Stages of 64 bytes of K per row go global -> LDS directly (gfx950 LDS-DMA,
-// one 16-byte vector per lane per instruction, no register staging; Tylo.jl
-// manual, "Walk through GEMM", section 3 "Copy one K stage"), S stages deep,
-// so each copy is issued about S-2 stages before its data is consumed.  Per
-// stage, each wave runs two slabs of MFMAs; the LDS reads of the next slab and
-// the copies of a future stage are issued one per MFMA so that the MFMA pipe
-// never waits for them.  One barrier per stage, between the two slabs, both
-// publishes stage s+1 (every wave waited for its own copies first) and frees
-// the buffer of stage s-1 for the copies issued right after it (section 4
-// "Consume, then release, the shared stage").
+// Stages of SW = 64 or 128 bytes of K per row go global -> LDS directly
+// (gfx950 LDS-DMA, one 16-byte vector per lane per instruction, no register
+// staging; Tylo.jl manual, "Walk through GEMM", section 3 "Copy one K stage"),
+// S stages deep, so each copy is issued about S-2 stages before its data is
+// consumed.  Per stage, each wave runs SW/32 slabs of MFMAs; the LDS reads of
+// the next slab and the copies of a future stage are issued one per MFMA so
+// that the MFMA pipe never waits for them.  One barrier per stage, before its
+// last slab, both publishes stage s+1 (every wave waited for its own copies
+// first) and frees the buffer of stage s-1 for the copies issued right after
+// it (section 4 "Consume, then release, the shared stage").  128-byte stages
+// fetch whole 128-byte lines per row and need half the barriers per MFMA.
 #include "gemm_common.h"
 
 namespace tg {
 
-template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
+template <int DT, int BM, int BN, int WM, int WN, int S, int GM, int SW>
 __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kernel(GemmArgs p) {
     select_batch(p);
     constexpr int NW = WM * WN;                 // waves per workgroup
     constexpr int NT = 64 * NW;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
     constexpr int EPC = 16 / ES;
-    constexpr int BKE = kRow64Bytes / ES;       // K elements per stage
+    static_assert(SW == 64 || SW == 128, "stages of 64 or 128 bytes per row");
+    constexpr int Q = SW / 32;                  // slabs (32 bytes of K per row) per stage
+    constexpr int CPR = SW / kChunkBytes;       // 16-byte chunks per row
+    constexpr int RPC = 1024 / SW;              // rows per 1 KiB copy
+    constexpr int BKE = SW / ES;                // K elements per stage
     constexpr int WTM = BM / WM, WTN = BN / WN; // output owned by one wave
     constexpr int FM = WTM / 32, FN = WTN / 32; // 32 x 32 MFMA blocks per wave
-    constexpr int NA = BM / (16 * NW);          // 1 KiB copies of A per wave per stage
-    constexpr int NB = BN / (16 * NW);
+    constexpr int NA = BM / (RPC * NW);         // 1 KiB copies of A per wave per stage
+    constexpr int NB = BN / (RPC * NW);
     constexpr int PER = NA + NB;
     constexpr int NR = FM + FN;                 // fragment reads per slab
-    constexpr int STAGE = (BM + BN) * kRow64Bytes;
-    static_assert(NA * 16 * NW == BM && NB * 16 * NW == BN, "copies must tile the stage");
+    constexpr int STAGE = (BM + BN) * SW;
+    static_assert(NA * RPC * NW == BM && NB * RPC * NW == BN, "copies must tile the stage");
     static_assert(S >= 3, "at least one stage in flight beyond the next");
+    static_assert(Q % 2 == 0, "the last slab of a stage uses the second fragment set");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -56,31 +62,36 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int j = wave * NA + i;
-        asrc[i] = p.A + static_cast<int64_t>(min(m0 + dma_row(j, lane), M - 1)) * p.lda_b +
-                  dma_chunk(j, lane) * kChunkBytes;
+        const int row = SW == 64 ? dma_row(j, lane) : dma128_row(j, lane);
+        const int chunk = SW == 64 ? dma_chunk(j, lane) : dma128_chunk(j, lane);
+        asrc[i] = p.A + static_cast<int64_t>(min(m0 + row, M - 1)) * p.lda_b + chunk * kChunkBytes;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int j = wave * NB + i;
-        bsrc[i] = p.B + static_cast<int64_t>(min(n0 + dma_row(j, lane), N - 1)) * p.ldb_b +
-                  dma_chunk(j, lane) * kChunkBytes;
+        const int row = SW == 64 ? dma_row(j, lane) : dma128_row(j, lane);
+        const int chunk = SW == 64 ? dma_chunk(j, lane) : dma128_chunk(j, lane);
+        bsrc[i] = p.B + static_cast<int64_t>(min(n0 + row, N - 1)) * p.ldb_b + chunk * kChunkBytes;
     }
     // copy d of stage t into buffer b
     auto copy = [&](int d, int t, int b) {
         const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + b * STAGE);
-        const int64_t kb = static_cast<int64_t>(t) * kRow64Bytes;
+        const int64_t kb = static_cast<int64_t>(t) * SW;
         if (d < NA)
             dma16(asrc[d] + kb, dst + (wave * NA + d) * 1024);
         else
-            dma16(bsrc[d - NA] + kb, dst + BM * kRow64Bytes + (wave * NB + d - NA) * 1024);
+            dma16(bsrc[d - NA] + kb, dst + BM * SW + (wave * NB + d - NA) * 1024);
     };
 
     // ---- fragment read offsets within a stage; block steps are 32 rows
-    int mread[2], nread[2];
+    auto chunk_offset = [](int row, int chunk) {
+        return SW == 64 ? lds64_chunk_offset(row, chunk) : lds_chunk_offset(row, chunk);
+    };
+    int mread[Q], nread[Q];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        mread[q] = wave_m * WTM * kRow64Bytes + lds64_chunk_offset(frag_row(lane), frag_chunk(lane, q));
-        nread[q] = (BM + wave_n * WTN) * kRow64Bytes + lds64_chunk_offset(frag_row(lane), frag_chunk(lane, q));
+    for (int q = 0; q < Q; ++q) {
+        mread[q] = wave_m * WTM * SW + chunk_offset(frag_row(lane), frag_chunk(lane, q));
+        nread[q] = (BM + wave_n * WTN) * SW + chunk_offset(frag_row(lane), frag_chunk(lane, q));
     }
     // read r of slab q from buffer b: m-side and n-side fragments alternate
     // while both last, so the first MFMAs of the slab get their operands first
@@ -97,9 +108,9 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
             blk = r - P;
         }
         if (is_m)
-            fa[blk] = *reinterpret_cast<const u32x4*>(base + mread[q] + blk * 32 * kRow64Bytes);
+            fa[blk] = *reinterpret_cast<const u32x4*>(base + mread[q] + blk * 32 * SW);
         else
-            fb[blk] = *reinterpret_cast<const u32x4*>(base + nread[q] + blk * 32 * kRow64Bytes);
+            fb[blk] = *reinterpret_cast<const u32x4*>(base + nread[q] + blk * 32 * SW);
     };
 
     f32x16 acc[FN][FM];
@@ -111,7 +122,7 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nfull = K / BKE;
-    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    u32x4 fa[2][FM], fb[2][FN];  // fragments of two consecutive slabs
 
     if (nfull > 0) {
         // prologue: stages 0 .. S-2 (indices past the last full stage reload
@@ -123,22 +134,26 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
         wait_vm<(S - 2) * PER>();
         barrier();
 #pragma unroll
-        for (int r = 0; r < NR; ++r) read(r, 0, 0, fa0, fb0);
+        for (int r = 0; r < NR; ++r) read(r, 0, 0, fa[0], fb[0]);
 
         int buf = 0;           // buffer of stage s
         int fill = S - 1;      // buffer that receives stage s + S - 1
         for (int s = 0; s < nfull; ++s) {
-            // slab 0 of stage s; meanwhile read slab 1 of stage s
-            slab_with_side<DT, FM, FN, NR>(acc, fa0, fb0, [&](int k) { read(k, 1, buf, fa1, fb1); });
+            // slabs 0 .. Q-2 of stage s, each while reading the next slab of stage s
+#pragma unroll
+            for (int q = 0; q + 1 < Q; ++q)
+                slab_with_side<DT, FM, FN, NR>(acc, fa[q & 1], fb[q & 1],
+                                               [&](int k) { read(k, q + 1, buf, fa[(q + 1) & 1], fb[(q + 1) & 1]); });
             wait_vm<(S - 3) * PER>();  // this wave's copies of stage s+1 have landed
             barrier();                 // ... and everyone's; stage s-1's buffer is free
             const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
             const int tload = min(s + S - 1, nfull - 1);
-            // slab 1 of stage s; meanwhile read slab 0 of stage s+1 (on the last
-            // stage this reads a buffer whose values go unused), then copy stage s+S-1
-            slab_with_side<DT, FM, FN, NR + PER>(acc, fa1, fb1, [&](int k) {
+            // the last slab of stage s; meanwhile read slab 0 of stage s+1 (on the
+            // last stage this reads a buffer whose values go unused), then copy
+            // stage s+S-1
+            slab_with_side<DT, FM, FN, NR + PER>(acc, fa[1], fb[1], [&](int k) {
                 if (k < NR)
-                    read(k, 0, nbuf, fa0, fb0);
+                    read(k, 0, nbuf, fa[0], fb[0]);
                 else
                     copy(k - NR, tload, fill);
             });
@@ -152,31 +167,32 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
         // ragged last stage: loaded through registers, elements with k >= K
         // become exact zeros; buffer 0 is free once every wave is past the loop
         __syncthreads();
-        const int c = tid & 3;
+        const int c = tid % CPR;
         const int k0 = nfull * BKE + c * EPC;
         char* base = smem;
 #pragma unroll
-        for (int i = 0; i < BM * 4 / NT; ++i) {
-            const int r = (tid >> 2) + (NT / 4) * i;
+        for (int i = 0; i < BM * CPR / NT; ++i) {
+            const int r = tid / CPR + (NT / CPR) * i;
             const char* row = p.A + static_cast<int64_t>(min(m0 + r, M - 1)) * p.lda_b;
-            *reinterpret_cast<u32x4*>(base + lds64_chunk_offset(r, c)) = load_chunk_bounded<ES>(row, k0, K);
+            *reinterpret_cast<u32x4*>(base + chunk_offset(r, c)) = load_chunk_bounded<ES>(row, k0, K);
         }
 #pragma unroll
-        for (int i = 0; i < BN * 4 / NT; ++i) {
-            const int r = (tid >> 2) + (NT / 4) * i;
+        for (int i = 0; i < BN * CPR / NT; ++i) {
+            const int r = tid / CPR + (NT / CPR) * i;
             const char* row = p.B + static_cast<int64_t>(min(n0 + r, N - 1)) * p.ldb_b;
-            *reinterpret_cast<u32x4*>(base + BM * kRow64Bytes + lds64_chunk_offset(r, c)) =
-                load_chunk_bounded<ES>(row, k0, K);
+            *reinterpret_cast<u32x4*>(base + BM * SW + chunk_offset(r, c)) = load_chunk_bounded<ES>(row, k0, K);
         }
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < Q; ++q) {
+            // slabs wholly past K hold zeros only
+            if (nfull * BKE + q * (BKE / Q) >= K) break;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read(r, q, 0, fa0, fb0);
+            for (int r = 0; r < NR; ++r) read(r, q, 0, fa[0], fb[0]);
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb0[i], fa0[j], acc[i][j]);
+                for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb[0][i], fa[0][j], acc[i][j]);
         }
     }
 
@@ -204,9 +220,9 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
     });
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int S, int GM>
+template <int DT, int BM, int BN, int WM, int WN, int S, int GM, int SW>
 static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>),
+    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM, SW>),
                        dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
                        dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
@@ -215,27 +231,32 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 }  // namespace tg
 
 // Instances: (id, dtype, BM, BN, waves along m, waves along n, LDS stages,
-// group_m, eff%).  They keep 7 stages of copies in flight and win where few
-// tiles each run a long K (kernel trace, bf16: 512x512x16384 64 us against
-// 109 us for the register-staged 64 x 64; 2048^3 26.5 us against 30.0 us for
-// the register-staged 128 x 128); the fp32 128 x 128 instance takes 2048^3 in
-// 143.5 us against 162 us for the register-staged 128 x 128.
+// group_m, stage bytes per row, eff%).  Each copy is issued S-2 stages
+// ahead of its use; they win where few tiles each run a long K (kernel trace, bf16:
+// 512x512x16384 64 us against 109 us for the register-staged 64 x 64; 2048^3
+// 26.5 us against 30.0 us for the register-staged 128 x 128); the fp32
+// 128 x 128 instance takes 2048^3 in 143.5 us against 162 us for the
+// register-staged 128 x 128.  128-byte stages against 64-byte ones (bf16,
+// same box): 64 x 64 at 1024 x 1024 x 4096 17.6 against 19.2 us, a tie at
+// 1024^3; 128 x 128 at 2048^3 22.7 against 24.7 us and at 2048 x 2048 x 4096
+// 36.9 against 40.5 us; fp32 (16 k per 64 bytes) gained nothing and keeps
+// 64-byte stages.
 #define TG_STREAM_LIST(X)                          \
-    X(14, TG_BF16, 64, 64, 2, 2, 8, 4, 25)         \
-    X(15, TG_F16, 64, 64, 2, 2, 8, 4, 25)          \
-    X(16, TG_BF16, 128, 128, 2, 2, 8, 4, 46)       \
-    X(17, TG_F16, 128, 128, 2, 2, 8, 4, 46)        \
-    X(18, TG_F32, 128, 128, 2, 2, 8, 4, 50)
+    X(14, TG_BF16, 64, 64, 2, 2, 8, 4, 128, 25)    \
+    X(15, TG_F16, 64, 64, 2, 2, 8, 4, 128, 25)     \
+    X(16, TG_BF16, 128, 128, 2, 2, 5, 4, 128, 46)  \
+    X(17, TG_F16, 128, 128, 2, 2, 5, 4, 128, 46)   \
+    X(18, TG_F32, 128, 128, 2, 2, 8, 4, 64, 50)
 
-#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF) \
-    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM>(GemmArgs);
+#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, WM, WN, S, GM, SW, EFF) \
+    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM, SW>(GemmArgs);
 TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 
 #ifndef __HIP_DEVICE_COMPILE__
-#define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, EFF)                                         \
-    {id, DT, BM, BN, 64 / TG_ELEM_BYTES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,  \
-     (S) * ((BM) + (BN)) * 64, ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                     \
-     &tg::launch_stream<DT, BM, BN, WM, WN, S, GM>},
+#define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, SW, EFF)                                     \
+    {id, DT, BM, BN, (SW) / TG_ELEM_BYTES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,  \
+     (S) * ((BM) + (BN)) * (SW), ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                     \
+     &tg::launch_stream<DT, BM, BN, WM, WN, S, GM, SW>},
 extern const TgKernelDesc tg_entries_stream[] = {TG_STREAM_LIST(TG_ENTRY_STREAM)};
 extern const int tg_entries_stream_count = sizeof(tg_entries_stream) / sizeof(tg_entries_stream[0]);
 #endif  // __HIP_DEVICE_COMPILE__
