@@ -366,18 +366,27 @@ def main() -> int:
     for _ in range(args.warmup):
         launch(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
     torch.cuda.synchronize()
-    # one event before every launch and one after the last, all on the stream
-    # the kernel runs on: the whole-region average is the launch duration used
-    # for the throughput and the roofline, the per-launch median is reported too
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # the timed region: one event before the first launch and one after the
+    # last, both on the stream the kernel runs on, and the launches back to
+    # back between them; the region average is the launch duration used for
+    # the throughput and the roofline.  A second, untimed-for-throughput pass
+    # with an event between every two launches gives the per-launch median
+    # (those events add a gap per launch, which matters for short kernels).
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        launch(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for i in range(args.steps):
         ev[i].record(stream)
         launch(Av, Bv, Dv, w.alpha, w.relu, stream=stream, kernel_id=args.kernel_id)
     ev[args.steps].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[args.steps]) / args.steps
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     median_ms = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
     tflops = w.flops / (ms * 1e-3) / 1e12

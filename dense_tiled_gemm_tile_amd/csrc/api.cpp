@@ -148,16 +148,19 @@ bool d_lines_aligned(const void* D, int64_t ldd, int os, const Batch& bt) {
 // column pieces end in partial lines that a neighbouring tile completes
 // later, and nontemporal stores of them measure about 20 % slower on the whole
 // product than ordinary ones; such instances are then weighed down.
-// Instances that split K across the waves of a workgroup only pay when most
-// CUs would otherwise idle (at most half as many tiles as CUs; measured:
-// 512x512x16384 41 us against 64 us, 1024x1024x4096 a tie, 1024^3 slower).
+// Instances whose every wave holds the whole tile and a share of K (the
+// K-sliced kernel) only pay when most CUs would otherwise idle (at most half
+// as many tiles as CUs; measured: 512x512x16384 41 us against 64 us,
+// 1024x1024x4096 a tie, 1024^3 slower).
 int choose(int64_t M, int64_t N, int64_t batch, int dtype, int cls, int64_t row_stride, bool d_lines = true) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tg_kernel_count(); ++i) {
         const TgKernelDesc& k = tg_kernel(i);
         if (!usable(k, dtype, cls, row_stride)) continue;
-        if (k.k_slices > 1 && cdiv(M, k.block_m) * cdiv(N, k.block_n) * batch > kCusPerGpu / 2) continue;
+        if (k.k_slices > 1 && k.waves_m * k.waves_n == 1 &&
+            cdiv(M, k.block_m) * cdiv(N, k.block_n) * batch > kCusPerGpu / 2)
+            continue;
         // among equal costs prefer the instance that needs the strongest alignment
         double c = plan_cost(k, M, N, batch) * (1.0 + 0.001 / k.load_class);
         if (k.nt_store && !d_lines) c *= 1.25;

@@ -6,7 +6,11 @@
 // (gfx950 LDS-DMA, one 16-byte vector per lane per instruction, no register
 // staging; Tylo.jl manual, "Walk through GEMM", section 3 "Copy one K stage"),
 // S stages deep, so each copy is issued about S-2 stages before its data is
-// consumed.  Per stage, each wave runs SW/32 slabs of MFMAs; the LDS reads of
+// consumed.  The WM x WN waves that own the tile may be doubled into KG = 2
+// groups, group 1 taking the second half of every stage's slabs: two waves
+// per SIMD, so each SIMD keeps twice the LDS reads in flight, and the second
+// group's partial tile is added into the first's through LDS at the end.
+// Per stage, each wave runs SW/32/KG slabs of MFMAs; the LDS reads of
 // the next slab and the copies of a future stage are issued one per MFMA so
 // that the MFMA pipe never waits for them.  One barrier per stage, before its
 // last slab, both publishes stage s+1 (every wave waited for its own copies
@@ -17,15 +21,16 @@
 
 namespace tg {
 
-template <int DT, int BM, int BN, int WM, int WN, int S, int GM, int SW>
-__global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kernel(GemmArgs p) {
+template <int DT, int BM, int BN, int WM, int WN, int S, int GM, int SW, int KG>
+__global__ __launch_bounds__(64 * WM * WN * KG, (WM * WN * KG) / 4) void gemm_stream_kernel(GemmArgs p) {
     select_batch(p);
-    constexpr int NW = WM * WN;                 // waves per workgroup
+    constexpr int NW = WM * WN * KG;            // waves per workgroup
     constexpr int NT = 64 * NW;
     constexpr int ES = (DT == TG_F32) ? 4 : 2;
     constexpr int EPC = 16 / ES;
     static_assert(SW == 64 || SW == 128, "stages of 64 or 128 bytes per row");
     constexpr int Q = SW / 32;                  // slabs (32 bytes of K per row) per stage
+    constexpr int QL = Q / KG;                  // slabs per stage of one wave
     constexpr int CPR = SW / kChunkBytes;       // 16-byte chunks per row
     constexpr int RPC = 1024 / SW;              // rows per 1 KiB copy
     constexpr int BKE = SW / ES;                // K elements per stage
@@ -38,14 +43,17 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
     constexpr int STAGE = (BM + BN) * SW;
     static_assert(NA * RPC * NW == BM && NB * RPC * NW == BN, "copies must tile the stage");
     static_assert(S >= 3, "at least one stage in flight beyond the next");
-    static_assert(Q % 2 == 0, "the last slab of a stage uses the second fragment set");
+    static_assert(KG == 1 || KG == 2, "one or two groups of waves over K");
+    static_assert(QL % 2 == 0, "the last slab of a stage uses the second fragment set");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    const int wave_m = wave % WM, wave_n = wave / WM;
+    const int wave_mn = wave % (WM * WN);
+    const int kg = wave / (WM * WN);                              // K group: slabs kg*QL .. kg*QL+QL-1 of each stage
+    const int wave_m = wave_mn % WM, wave_n = wave_mn / WM;
 
     const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
@@ -87,11 +95,11 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
     auto chunk_offset = [](int row, int chunk) {
         return SW == 64 ? lds64_chunk_offset(row, chunk) : lds_chunk_offset(row, chunk);
     };
-    int mread[Q], nread[Q];
+    int mread[QL], nread[QL];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        mread[q] = wave_m * WTM * SW + chunk_offset(frag_row(lane), frag_chunk(lane, q));
-        nread[q] = (BM + wave_n * WTN) * SW + chunk_offset(frag_row(lane), frag_chunk(lane, q));
+    for (int q = 0; q < QL; ++q) {
+        mread[q] = wave_m * WTM * SW + chunk_offset(frag_row(lane), frag_chunk(lane, kg * QL + q));
+        nread[q] = (BM + wave_n * WTN) * SW + chunk_offset(frag_row(lane), frag_chunk(lane, kg * QL + q));
     }
     // read r of slab q from buffer b: m-side and n-side fragments alternate
     // while both last, so the first MFMAs of the slab get their operands first
@@ -139,18 +147,18 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
         int buf = 0;           // buffer of stage s
         int fill = S - 1;      // buffer that receives stage s + S - 1
         for (int s = 0; s < nfull; ++s) {
-            // slabs 0 .. Q-2 of stage s, each while reading the next slab of stage s
+            // this wave's slabs 0 .. QL-2 of stage s, each while reading the next
 #pragma unroll
-            for (int q = 0; q + 1 < Q; ++q)
+            for (int q = 0; q + 1 < QL; ++q)
                 slab_with_side<DT, FM, FN, NR>(acc, fa[q & 1], fb[q & 1],
                                                [&](int k) { read(k, q + 1, buf, fa[(q + 1) & 1], fb[(q + 1) & 1]); });
             wait_vm<(S - 3) * PER>();  // this wave's copies of stage s+1 have landed
             barrier();                 // ... and everyone's; stage s-1's buffer is free
             const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
             const int tload = min(s + S - 1, nfull - 1);
-            // the last slab of stage s; meanwhile read slab 0 of stage s+1 (on the
-            // last stage this reads a buffer whose values go unused), then copy
-            // stage s+S-1
+            // its last slab of stage s; meanwhile read its slab 0 of stage s+1 (on
+            // the last stage this reads a buffer whose values go unused), then
+            // copy stage s+S-1
             slab_with_side<DT, FM, FN, NR + PER>(acc, fa[1], fb[1], [&](int k) {
                 if (k < NR)
                     read(k, 0, nbuf, fa[0], fb[0]);
@@ -184,9 +192,9 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
         }
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
+        for (int q = 0; q < QL; ++q) {
             // slabs wholly past K hold zeros only
-            if (nfull * BKE + q * (BKE / Q) >= K) break;
+            if (nfull * BKE + (kg * QL + q) * (BKE / Q) >= K) break;
 #pragma unroll
             for (int r = 0; r < NR; ++r) read(r, q, 0, fa[0], fb[0]);
 #pragma unroll
@@ -194,6 +202,29 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
 #pragma unroll
                 for (int j = 0; j < FM; ++j) acc[i][j] = mfma_slab<DT>(fb[0][i], fa[0][j], acc[i][j]);
         }
+    }
+
+    if constexpr (KG == 2) {
+        // the second group's partial tile through LDS into the first group's
+        // accumulators (one fixed order: the same bits on every launch)
+        __syncthreads();  // every wave is done with the ring
+        float* part = reinterpret_cast<float*>(smem) + wave_mn * (FN * FM * 16 * 64) + lane;
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) part[((i * FM + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] += part[((i * FM + j) * 16 + r) * 64];
     }
 
     // ---- epilogue: alpha, optional ReLU, store by ownership (as above)
@@ -220,18 +251,18 @@ __global__ __launch_bounds__(64 * WM * WN, (WM * WN) / 4) void gemm_stream_kerne
     });
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int S, int GM, int SW>
+template <int DT, int BM, int BN, int WM, int WN, int S, int GM, int SW, int KG>
 static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM, SW>),
+    hipLaunchKernelGGL((gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM, SW, KG>),
                        dim3(static_cast<unsigned>(grid), static_cast<unsigned>(batch)),
-                       dim3(64 * WM * WN), 0, stream, a);
+                       dim3(64 * WM * WN * KG), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace tg
 
 // Instances: (id, dtype, BM, BN, waves along m, waves along n, LDS stages,
-// group_m, stage bytes per row, eff%).  Each copy is issued S-2 stages
+// group_m, stage bytes per row, K groups, eff%).  Each copy is issued S-2 stages
 // ahead of its use; they win where few tiles each run a long K (kernel trace, bf16:
 // 512x512x16384 64 us against 109 us for the register-staged 64 x 64; 2048^3
 // 26.5 us against 30.0 us for the register-staged 128 x 128); the fp32
@@ -240,23 +271,26 @@ static hipError_t launch_stream(const GemmArgs& a, int64_t grid, int batch, hipS
 // same box): 64 x 64 at 1024 x 1024 x 4096 17.6 against 19.2 us, a tie at
 // 1024^3; 128 x 128 at 2048^3 22.7 against 24.7 us and at 2048 x 2048 x 4096
 // 36.9 against 40.5 us; fp32 (16 k per 64 bytes) gained nothing and keeps
-// 64-byte stages.
+// 64-byte stages.  KG = 2 groups of waves (two waves per SIMD) on the 64 x 64
+// tile: 1024^3 7.0 against 7.8 us, 1024 x 1024 x 4096 16.4 against 18.8 us,
+// 512 x 512 x 16384 42.7 against 54.8 us; on 128 x 128, whose waves already
+// run four MFMAs per fragment pair, no gain.
 #define TG_STREAM_LIST(X)                          \
-    X(14, TG_BF16, 64, 64, 2, 2, 8, 4, 128, 25)    \
-    X(15, TG_F16, 64, 64, 2, 2, 8, 4, 128, 25)     \
-    X(16, TG_BF16, 128, 128, 2, 2, 5, 4, 128, 46)  \
-    X(17, TG_F16, 128, 128, 2, 2, 5, 4, 128, 46)   \
-    X(18, TG_F32, 128, 128, 2, 2, 8, 4, 64, 50)
+    X(14, TG_BF16, 64, 64, 2, 2, 8, 4, 128, 2, 25)    \
+    X(15, TG_F16, 64, 64, 2, 2, 8, 4, 128, 2, 25)     \
+    X(16, TG_BF16, 128, 128, 2, 2, 5, 4, 128, 1, 46)  \
+    X(17, TG_F16, 128, 128, 2, 2, 5, 4, 128, 1, 46)   \
+    X(18, TG_F32, 128, 128, 2, 2, 8, 4, 64, 1, 50)
 
-#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, WM, WN, S, GM, SW, EFF) \
-    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM, SW>(GemmArgs);
+#define TG_INSTANTIATE_STREAM(id, DT, BM, BN, WM, WN, S, GM, SW, KG, EFF) \
+    template __global__ void tg::gemm_stream_kernel<DT, BM, BN, WM, WN, S, GM, SW, KG>(GemmArgs);
 TG_STREAM_LIST(TG_INSTANTIATE_STREAM)
 
 #ifndef __HIP_DEVICE_COMPILE__
-#define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, SW, EFF)                                     \
-    {id, DT, BM, BN, (SW) / TG_ELEM_BYTES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN), S,  \
-     (S) * ((BM) + (BN)) * (SW), ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                     \
-     &tg::launch_stream<DT, BM, BN, WM, WN, S, GM, SW>},
+#define TG_ENTRY_STREAM(id, DT, BM, BN, WM, WN, S, GM, SW, KG, EFF)                                       \
+    {id, DT, BM, BN, (SW) / TG_ELEM_BYTES(DT), WM, WN, (BM) / (WM), (BN) / (WN), 64 * (WM) * (WN) * (KG), S,  \
+     (S) * ((BM) + (BN)) * (SW), ((BM) / (WM)) * ((BN) / (WN)) / 64, 16, GM, EFF,                            \
+     &tg::launch_stream<DT, BM, BN, WM, WN, S, GM, SW, KG>, 0, 0, 0, 0, KG},
 extern const TgKernelDesc tg_entries_stream[] = {TG_STREAM_LIST(TG_ENTRY_STREAM)};
 extern const int tg_entries_stream_count = sizeof(tg_entries_stream) / sizeof(tg_entries_stream[0]);
 #endif  // __HIP_DEVICE_COMPILE__

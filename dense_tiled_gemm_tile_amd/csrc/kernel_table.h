@@ -74,7 +74,7 @@ struct TgKernelDesc {
     int softmax;             // 1: the epilogue can also take a softmax over n (N <= block_n)
     int nt_store;            // 1: D is written with nontemporal stores
     int block_scales;        // 1: 8- or 4-bit instance that applies block scales (GemmArgs::scale_a/b)
-    int k_slices;            // waves that split K inside a workgroup, each over the whole tile (0: 1)
+    int k_slices;            // groups of waves that split K inside a workgroup, each over the whole tile (0: 1)
 };
 
 // Element bits of an operand type (the 4- and 6-bit formats are packed).

@@ -122,7 +122,7 @@ typedef struct tile_gemm_plan_info {
     int32_t load_class;    /* 16, 4 or 2: byte alignment of every operand row start */
     int32_t group_m;       /* tile-rows per group in the grouped tile order */
     int32_t staged;        /* always 0 for a query (tile_gemm_staged decides per call) */
-    int32_t k_slices;      /* waves of a workgroup that each take 1/k_slices of K over the whole tile */
+    int32_t k_slices;      /* groups of waves of a workgroup that each take 1/k_slices of K over the whole tile */
     int32_t block_scales;  /* 1: the instance applies block scales (tile_gemm_scaled) */
     int64_t tiles_m;       /* ceil(M / block_m) */
     int64_t tiles_n;       /* ceil(N / block_n) */
