@@ -9,6 +9,11 @@ the output against the oracle on the CPU-baseline sample, and the oracle's own
 throughput on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--kernel-id ID]
+
+The defaults (W = 50, K = 100) time the settled clock; with a short warmup
+(W = 5, K = 20) the timed region still covers most of the power controller's
+settling after an idle GPU, and the average runs about 5-8 % slower than the
+per-launch median the line also reports.
 """
 from __future__ import annotations
 
@@ -213,8 +218,11 @@ def copy_calibration(nbytes: int) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults long enough for the power controller to settle: after an idle
+    # GPU the 8192^3 launches run 0.83 ms, then 1.0-1.07 ms, and only after
+    # about 30 launches (25 ms of load) their steady 0.80 ms
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="square_8192_bf16_relu")
     ap.add_argument("--kernel-id", type=int, default=-1)
     ap.add_argument("--splits", type=int, default=1,
