@@ -92,3 +92,48 @@ def test_noalloc_rejects_partials_beyond_the_scratch():
     assert rc == 0
     torch.cuda.synchronize()
     assert bool((D == 0).all())
+
+
+def test_noalloc_replays_from_a_graph():
+    """The no-allocation split-K captured into a graph (the callers it is for):
+    every replay equals the eager call bit for bit, also when other eager
+    calls have rewritten the static scratch between replays."""
+    dev = torch.device("cuda:0")
+    M, N, K, splits = 512, 384, 8192 + 40, 4
+    lda, ldb, ldd = K + 8, K + 8, M + 4
+    A_st, B_st = si.operands(M, N, K, "bf16", "normal_invsqrtk", 81, 82, lda=lda, ldb=ldb)
+    A, B = A_st.to(dev), B_st.to(dev)
+    eager = si.out_storage(M, N, ldd).to(dev)
+    _log(f"[no-alloc graph] eager {M}x{N}x{K} splits={splits}")
+    _call("noalloc", A, B, eager, M, N, K, lda, ldb, ldd, 0.5, True, splits, tg.BF16, tg.F32)
+    torch.cuda.synchronize()
+    want = eager.cpu()
+    ref, mag = oracle.gemm(M, N, K, 0.5, True, si.bits(A_st), lda, si.bits(B_st), ldb, "bf16")
+    ok, r = oracle.check(want[:, :M].double().numpy(), ref, mag, K)
+    assert ok, f"eager: worst ratio {r}"
+    # another problem whose partials overwrite the scratch between replays
+    M2, N2, K2 = 256, 256, 4096
+    A2 = torch.ones(M2, K2, dtype=torch.bfloat16, device=dev)
+    B2 = torch.ones(N2, K2, dtype=torch.bfloat16, device=dev)
+    D2 = torch.zeros(N2, M2, device=dev)
+
+    D = si.out_storage(M, N, ldd).to(dev)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    _log("[no-alloc graph] capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            _call("noalloc", A, B, D, M, N, K, lda, ldb, ldd, 0.5, True, splits, tg.BF16, tg.F32)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        D.fill_(si.D_SENTINEL)
+        _call("noalloc", A2, B2, D2, M2, N2, K2, K2, K2, M2, 1.0, False, 2, tg.BF16, tg.F32)
+        torch.cuda.synchronize()
+        assert bool((D2 == float(K2)).all()), f"replay {rep}: the eager call in between"
+        _log(f"[no-alloc graph] replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(D.cpu(), want), f"replay {rep} differs from the eager call"
+    del g
