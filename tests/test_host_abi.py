@@ -340,10 +340,11 @@ def test_staged_workspace_size_and_validation():
 
 def test_staging_decision_scales_with_the_problem():
     """tile_gemm_staged (mode -1) copies misaligned rows only when the copy
-    pays and the caller's workspace holds the copies: 16384^3 yes, 4096^3 and
-    1024^3 no (the direct 2-byte-row path of the wide kernel is only a few
-    percent slower than the aligned one); aligned rows never; mode 1 always
-    (with a workspace), mode 0 never."""
+    pays and the caller's workspace holds the copies: 16384^3 and the ragged
+    workload yes (the direct 2-byte-row path of the wide kernel runs about
+    0.8 of the aligned rate), 4096^3 and 1024^3 no (the copy costs more than
+    it saves); aligned rows never; mode 1 always (with a workspace), mode 0
+    never."""
     A2, B2, D2, W2 = 0x100000000000, 0x200000000000, 0x300000000000, 0x400000000000
     for n, staged in ((16384, 1), (4096, 0), (1024, 0)):
         need = tg.staged_workspace_bytes(n, n, n, tg.BF16)
@@ -360,6 +361,11 @@ def test_staging_decision_scales_with_the_problem():
         with pytest.raises(tg.TileGemmError) as e:
             q(B2, mode=1, ws=0, nbytes=0)
         assert e.value.code == -10
+    # the ragged workload: rows of K + 8 elements (2-byte aligned), D columns of M + 16
+    M, N, K = 12289, 5003, 4099
+    need = tg.staged_workspace_bytes(M, N, K, tg.BF16)
+    p = tg.query_plan_staged(M, N, K, tg.BF16, A2, K + 8, B2, K + 8, D2, M + 16, tg.F32, W2, need, -1)
+    assert p.staged == 1 and tg.kernel_info(p.kernel_id).load_class == 16
 
 
 def test_plan_choices_follow_the_kernel_trace_table():
