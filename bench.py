@@ -44,7 +44,7 @@ def kernel_sources(kernel_name: str) -> list[Path]:
     and the headers every kernel unit includes)."""
     family = {"gemm_wide_kernel": ["gemm_wide.h", "gemm_wide16.hip", "gemm_wide32.hip", "gemm_wide8.hip",
                                    "gemm_wide4.hip", "gemm_wide6.hip"],
-              "gemm_stream_kernel": ["gemm_stream.hip"], "gemm_kernel": ["gemm_rs.hip"],
+              "gemm_wide_m16_kernel": ["gemm_wide_m16.hip"], "gemm_stream_kernel": ["gemm_stream.hip"], "gemm_kernel": ["gemm_rs.hip"],
               "gemm_kslice_kernel": ["gemm_kslice.hip"],
               "splitk_reduce_kernel": ["gemm_aux.hip"], "stage_rows_kernel": ["gemm_aux.hip"]}
     base = ["gemm_common.h", "tile_math.h", "kernel_table.h"]

@@ -22,7 +22,7 @@ LIB = PKG / "_lib" / "libtile_gemm.so"
 # host-side units first, then the kernel units (largest first, so the
 # parallel build ends sooner)
 SOURCES = [CSRC / "gemm_wide16.hip", CSRC / "gemm_rs.hip", CSRC / "gemm_wide8.hip", CSRC / "gemm_wide32.hip",
-           CSRC / "gemm_wide4.hip", CSRC / "gemm_wide6.hip", CSRC / "gemm_stream.hip", CSRC / "gemm_kslice.hip",
+           CSRC / "gemm_wide4.hip", CSRC / "gemm_wide6.hip", CSRC / "gemm_wide_m16.hip", CSRC / "gemm_stream.hip", CSRC / "gemm_kslice.hip",
            CSRC / "gemm_aux.hip",
            CSRC / "api.cpp", CSRC / "kernel_table.cpp"]
 ARCH = "gfx950"

@@ -153,12 +153,24 @@ bool d_lines_aligned(const void* D, int64_t ldd, int os, const Batch& bt) {
 // K-sliced kernel) only pay when most CUs would otherwise idle (at most half
 // as many tiles as CUs; measured: 512x512x16384 41 us against 64 us,
 // 1024x1024x4096 a tie, 1024^3 slower).
-int choose(int64_t M, int64_t N, int64_t batch, int dtype, int cls, int64_t row_stride, bool d_lines = true) {
+// Instances marked power_bound (the 16x16x32 wide kernel) are only
+// considered when the product keeps every CU busy for a long K loop: their
+// MFMAs cost less energy, which pays when the power limit sets the clock
+// (8192^3 bf16: 1535 against 1445 TFLOP/s, 4096^3: 1414 against 1330), but
+// their loop keeps the MFMA pipe less busy at a given clock, which costs when
+// it does not (3072^3 on 144 CUs: 955 against 1036; 8192x8192x1024, 16
+// stages: 930 against 960).
+constexpr int kPowerBoundStages = 32;
+int choose(int64_t M, int64_t N, int64_t batch, int64_t K, int dtype, int cls, int64_t row_stride,
+           bool d_lines = true) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tg_kernel_count(); ++i) {
         const TgKernelDesc& k = tg_kernel(i);
         if (!usable(k, dtype, cls, row_stride)) continue;
+        if (k.power_bound && (cdiv(M, k.block_m) * cdiv(N, k.block_n) * batch < kCusPerGpu ||
+                              cdiv(K, k.block_k) < kPowerBoundStages))
+            continue;
         if (k.k_slices > 1 && k.waves_m * k.waves_n == 1 &&
             cdiv(M, k.block_m) * cdiv(N, k.block_n) * batch > kCusPerGpu / 2)
             continue;
@@ -227,12 +239,12 @@ Staging decide_staging(int64_t M, int64_t N, int64_t K, int dtype, const void* A
     const int es = elem_size(dtype);
     const int64_t rb = staged_row_bytes(K, es);
     if (rb / es > kMaxDim) return st;
-    const int sid = choose(M, N, 1, dtype, 16, rb, d_lines);
+    const int sid = choose(M, N, 1, rb / es, dtype, 16, rb, d_lines);
     if (sid < 0) return st;
     if (mode != 1) {
         const int cls = row_class(M, N, A, lda, B, ldb, dtype, Batch());
         if (cls == 16) return st;
-        const int did = choose(M, N, 1, dtype, cls, (lda > ldb ? lda : ldb) * es, d_lines);
+        const int did = choose(M, N, 1, K, dtype, cls, (lda > ldb ? lda : ldb) * es, d_lines);
         if (did >= 0) {
             const double copy = double((M + N) * (K * es + rb)) / kCopyBytesPerSecond + kLaunchSeconds;
             const double staged = plan_seconds(tg_kernel(sid), M, N, rb / es) + copy;
@@ -256,7 +268,7 @@ int plan(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
     const bool d_lines = d_lines_aligned(D, ldd, elem_size(out_dtype), bt);
     int id = kernel_id;
     if (id < 0) {
-        id = choose(M, N, bt.batch * splits, dtype, cls, row_stride, d_lines);
+        id = choose(M, N, bt.batch * splits, cdiv(K, splits), dtype, cls, row_stride, d_lines);
         if (id < 0) return TG_ERR_PLAN;
     } else if (id >= tg_kernel_count() || !usable(tg_kernel(id), dtype, cls, row_stride)) {
         return TG_ERR_PLAN;

@@ -17,7 +17,8 @@ struct Table {
         } parts[] = {{tg_entries_wide16, tg_entries_wide16_count}, {tg_entries_wide32, tg_entries_wide32_count},
                      {tg_entries_wide8, tg_entries_wide8_count},   {tg_entries_stream, tg_entries_stream_count},
                      {tg_entries_rs, tg_entries_rs_count},         {tg_entries_kslice, tg_entries_kslice_count},
-                     {tg_entries_wide4, tg_entries_wide4_count},   {tg_entries_wide6, tg_entries_wide6_count}};
+                     {tg_entries_wide4, tg_entries_wide4_count},   {tg_entries_wide6, tg_entries_wide6_count},
+                     {tg_entries_wide_m16, tg_entries_wide_m16_count}};
         bool seen[kMax] = {};
         for (const auto& part : parts)
             for (int i = 0; i < part.count; ++i) {

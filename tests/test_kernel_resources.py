@@ -20,7 +20,8 @@ import pytest
 
 from dense_tiled_gemm_tile_amd import build as tgbuild
 
-UNITS = ["gemm_wide16.hip", "gemm_wide8.hip", "gemm_wide32.hip", "gemm_wide4.hip", "gemm_wide6.hip"]
+UNITS = ["gemm_wide16.hip", "gemm_wide8.hip", "gemm_wide32.hip", "gemm_wide4.hip", "gemm_wide6.hip",
+         "gemm_wide_m16.hip"]
 
 
 @pytest.fixture(scope="module")
