@@ -31,20 +31,29 @@ namespace tg {
 // fragment ma, accumulating in place in four AGPRs.  Written as tied inline
 // assembly: with 64 accumulators per lane the builtin's untied form makes the
 // register allocator copy accumulators between MFMAs (over 300 moves per
-// stage).  Nothing but these MFMAs touches the accumulators between the
-// zeroing before the K loop and the epilogue, which starts after
-// mfma16_drain().
+// stage).  Volatile, so the MFMAs keep their order against the other
+// volatile statements below.
 template <int DT>
 __device__ __forceinline__ void mfma16(f32x4& c, const u32x4& nb, const u32x4& ma) {
     if constexpr (DT == TG_BF16)
-        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(nb), "v"(ma));
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(nb), "v"(ma));
     else
-        asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(nb), "v"(ma));
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(nb), "v"(ma));
 }
 // The compiler does not see the assembly above as MFMAs, so it cannot count
-// the wait states an MFMA result needs before other instructions read it
-// (passes + 2, at most 18 for these): wait them out explicitly.
+// the wait states between them and other instructions that write or read the
+// accumulators (the zeroing before the K loop, the epilogue after it; at most
+// passes + 2 = 18 for these): the kernel waits them out with these nops, and
+// pins the accumulators on the right side of them with an empty statement
+// that claims to rewrite each one.
 __device__ __forceinline__ void mfma16_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+template <int FN, int FM>
+__device__ __forceinline__ void acc_fence(f32x4 (&acc)[FN][FM]) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
 
 // EPI: bit 0 = nontemporal D stores, bit 1 = fp32 D of interior tiles through
 // an LDS transpose (whole 1 KiB row runs per store instruction).
@@ -126,6 +135,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    acc_fence(acc);  // the zeros are written here, and waited out before the first MFMA
+    mfma16_drain();
 
     // fragments: m-side double buffered (set 0 for slab 0, set 1 for slab 1);
     // n-side rows 0-5 in fb[0..5], rows 6-7 in fb[6..7] on slab 0 and in
@@ -224,6 +235,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
         }
     }
     mfma16_drain();
+    acc_fence(acc);  // the epilogue reads the accumulators only after the wait
 
     // epilogue: alpha, then ReLU, in registers; register r of block (i, j)
     // is (n, m) = (16 i + acc16_row(lane, r), 16 j + acc16_col(lane)) of the
