@@ -102,10 +102,11 @@ TG_HD int dma_chunk(int j, int lane) { return (lane & 3) ^ lds64_swizzle(dma_row
 TG_HD int frag_row(int lane) { return lane & 31; }
 TG_HD int frag_chunk(int lane, int q) { return 2 * q + (lane >> 5); }
 
-// 16x16x32 MFMA blocks (used where one operand is loaded straight into
-// registers): lane l supplies row frag16_row(l) and the 16-byte chunk
-// frag16_chunk(l) of the stage's 64-byte K slice; register r of lane l holds
-// output element (acc16_row(l, r), acc16_col(l)) of the 16x16 block.
+// 16x16x32 MFMA block: lane l supplies row frag16_row(l) of the block and
+// the 8 consecutive k of its k-group frag16_chunk(l) (0..3, one 16-byte chunk
+// of a 64-byte K slice; which chunk is the caller's choice, the same on both
+// sides); register r of lane l holds output element (acc16_row(l, r),
+// acc16_col(l)) of the 16x16 block (rows n, columns m).
 TG_HD int frag16_row(int lane) { return lane & 15; }
 TG_HD int frag16_chunk(int lane) { return lane >> 4; }
 TG_HD int acc16_row(int lane, int r) { return 4 * (lane >> 4) + r; }
