@@ -40,6 +40,11 @@ __device__ __forceinline__ void mfma16(f32x4& c, const u32x4& nb, const u32x4& m
     else
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(nb), "v"(ma));
 }
+// Per-lane copy offset of a row past the operand's end: beyond every buffer
+// range the plan allows (256 rows of at most 8 MiB), also less the largest
+// immediate offset, and far enough below 2^32 that no offset sum wraps.
+constexpr unsigned kFarOffset = 0xF0000000u;
+
 // The compiler does not see the assembly above as MFMAs, so it cannot count
 // the wait states between them and other instructions that write or read the
 // accumulators (the zeroing before the K loop, the epilogue after it; at most
@@ -70,6 +75,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
     constexpr int NC = BM / (8 * 4);             // 1 KiB copies per wave per half-stage
     constexpr int SLOT = BM * kRowBytes;         // 32 KiB
     constexpr int LDS_BYTES = 5 * SLOT;
+    static_assert(NS == 5, "the K loop is unrolled over the five slots");
     static_assert(FM == 8 && FN == 8 && NC == 8, "schedule assumes 8 x 8 blocks and 8 copies per half-stage");
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -92,19 +98,58 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
     const i32x4 rsrc[2] = {
         buffer_rsrc(p.A + static_cast<int64_t>(m0) * p.lda_b, static_cast<unsigned>(min(BM, M - m0) * p.lda_b)),
         buffer_rsrc(p.B + static_cast<int64_t>(n0) * p.ldb_b, static_cast<unsigned>(min(BN, N - n0) * p.ldb_b))};
+    // Copies 4g .. 4g + 3 of a wave share one LDS base in M0 and take the
+    // immediate offsets 0, 1024, 2048 and 3072, which move the global address
+    // by the same amount, so their per-lane offsets are lowered by it (copy j
+    // starts 8 j rows, at least 1024 j bytes, into the operand, so they stay
+    // non-negative).  Rows past the operand's end get an offset far beyond any
+    // range: with or without the immediate they load zeros.
     unsigned voff[2][NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int j = wave * NC + i;
-        voff[0][i] = static_cast<unsigned>(dma128_row(j, lane) * p.lda_b) + dma128_chunk(j, lane) * kChunkBytes;
-        voff[1][i] = static_cast<unsigned>(dma128_row(j, lane) * p.ldb_b) + dma128_chunk(j, lane) * kChunkBytes;
+        const int r = dma128_row(j, lane);
+        const unsigned low = 1024u * (i & 3), chunk = dma128_chunk(j, lane) * kChunkBytes;
+        voff[0][i] = r < min(BM, M - m0) ? static_cast<unsigned>(r * p.lda_b) + chunk - low : kFarOffset;
+        voff[1][i] = r < min(BN, N - n0) ? static_cast<unsigned>(r * p.ldb_b) + chunk - low : kFarOffset;
     }
-    // copy i of operand o (0: A, 1: B) of stage t into slot `slot`
-    auto copy = [&](int o, int i, int t, int slot) {
-        const unsigned dst = __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + i) * 1024);
-        dma16_buf(rsrc[o], voff[o][i], __builtin_amdgcn_readfirstlane(t * kRowBytes), dst);
+    // LDS base of copies 4g .. 4g + 3 of this wave into slot `slot`
+    auto copy_base = [&](int g, int slot) {
+        return __builtin_amdgcn_readfirstlane(lds_base + slot * SLOT + (wave * NC + 4 * g) * 1024);
     };
-    auto wrap = [](int x) { return x >= NS ? x - NS : x; };
+    // M0 for the group of copies 4g .. 4g + 3 into `slot`, then the wait
+    // state an LDS-DMA load needs after an M0 write.  The copies read M0
+    // without naming it, so that the compiler neither reloads it in front of
+    // each one nor drops the wait; the kernel has no other M0 user (its
+    // assembly is checked on the host: every M0 write is this one, and every
+    // copy follows one).  Both are volatile, so they stay in program order.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved: nothing is kept in it across this
+    auto set_m0 = [&](int g, int slot) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(copy_base(g, slot)) : "m0");
+    };
+#pragma clang diagnostic pop
+    // copy i of operand o (0: A, 1: B) of stage t (byte offset so = t * 128)
+    // into the slot whose group base set_m0 put in M0
+    auto copy = [&](int o, int i, unsigned so) {
+        switch (i & 3) {
+            case 0:
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff[o][i]), "s"(rsrc[o]), "s"(so) : "memory");
+                break;
+            case 1:
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:1024 lds"
+                             : : "v"(voff[o][i]), "s"(rsrc[o]), "s"(so) : "memory");
+                break;
+            case 2:
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:2048 lds"
+                             : : "v"(voff[o][i]), "s"(rsrc[o]), "s"(so) : "memory");
+                break;
+            default:
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:3072 lds"
+                             : : "v"(voff[o][i]), "s"(rsrc[o]), "s"(so) : "memory");
+                break;
+        }
+    };
 
     // fragment read offsets within a slot: lane l reads row l % 16 of a
     // 16-row block and, for its k-group g = l / 16, chunk 4q + (0, 2, 1, 3)[g]
@@ -123,11 +168,23 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
         mread[q] = wave_m * WTM * kRowBytes + lds_chunk_offset(frag16_row(lane), 4 * q + gchunk);
         nread[q] = wave_n * WTN * kRowBytes + lds_chunk_offset(frag16_row(lane), 4 * q + gchunk);
     }
+    // A read's immediate offset reaches 64 KiB, two slots: each read position
+    // keeps one base per slot pair (slots 0-1, 2-3, 4), set up here once, so
+    // that with the slot known at compile time no read needs an address add.
+    int mbase[2][3], nbase[2][3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            mbase[q][k] = mread[q] + 2 * k * SLOT;
+            nbase[q][k] = nread[q] + 2 * k * SLOT;
+            asm volatile("" : "+v"(mbase[q][k]), "+v"(nbase[q][k]));  // kept as registers
+        }
     auto rd_m = [&](int j, int q, int slot) {
-        return *reinterpret_cast<const u32x4*>(smem + slot * SLOT + mread[q] + j * 16 * kRowBytes);
+        return *reinterpret_cast<const u32x4*>(smem + mbase[q][slot >> 1] + (slot & 1) * SLOT + j * 16 * kRowBytes);
     };
     auto rd_n = [&](int i, int q, int slot) {
-        return *reinterpret_cast<const u32x4*>(smem + slot * SLOT + nread[q] + i * 16 * kRowBytes);
+        return *reinterpret_cast<const u32x4*>(smem + nbase[q][slot >> 1] + (slot & 1) * SLOT + i * 16 * kRowBytes);
     };
 
     f32x4 acc[FN][FM];
@@ -164,7 +221,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
 #pragma unroll
         for (int c = 0; c < PRO; ++c) {
             const int h = c / NC;
-            copy(h & 1, c % NC, min(h >> 1, nfull - 1), h);
+            if (c % 4 == 0) set_m0((c % NC) >> 2, h);
+            copy(h & 1, c % NC, __builtin_amdgcn_readfirstlane(min(h >> 1, nfull - 1) * kRowBytes));
         }
         wait_vm<PRO - 2 * NC>();
         barrier();
@@ -173,35 +231,67 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < FN; ++i) fb[i] = rd_n(i, 0, 1);
 
-        int slot0 = 0;  // slot of stage s's A half, (2s) % 5
-        for (int s = 0; s < nfull; ++s) {
-            const int sa = slot0, sb = wrap(slot0 + 1);
-            const int na = wrap(slot0 + 2), nb = wrap(slot0 + 3);
-            // a stage index past the last full stage reloads it (values unused)
-            const int t2 = min(s + 2, nfull - 1), t3 = min(s + 3, nfull - 1);
+        // The ring turns by two slots a stage and repeats after five, so the
+        // loop body is five stages with their slots known at compile time:
+        // stage 5k + U keeps A in slot 2U mod 5 and B in the next one.
+        const int last_so = (nfull - 1) * kRowBytes;
+        auto stage = [&](auto u, int s) {
+            constexpr int U = decltype(u)::value;
+            constexpr int SA = (2 * U) % NS, SB = (2 * U + 1) % NS, NA = (2 * U + 2) % NS, NB = (2 * U + 3) % NS;
+            // byte offsets of stages s+2 (B) and s+3 (A) along K; past the last
+            // full stage they reload it (values unused)
+            unsigned so2 = 0, so3 = 0;
             // slab 0: read slab 1 (m-side set 1 first, rows 6/7 into the spares,
-            // rows 0-5 after their last MFMA); no copies
+            // rows 0-5 after their last MFMA); the scalar work of slab 1's
+            // copies goes into its quiet second half
             slab(std::integral_constant<int, 0>(), [&](int m) {
-                if (m < FM) fa[1][m] = rd_m(m, 1, sa);
-                if (m == 8 || m == 9) fs[m - 8] = rd_n(m - 2, 1, sb);
-                if ((m & 7) == 7 && m < 48) fb[m >> 3] = rd_n(m >> 3, 1, sb);
+                if (m < FM) fa[1][m] = rd_m(m, 1, SA);
+                if (m == 8 || m == 9) fs[m - 8] = rd_n(m - 2, 1, SB);
+                if ((m & 7) == 7 && m < 48) fb[m >> 3] = rd_n(m >> 3, 1, SB);
+                if (m == 50) {
+                    so2 = __builtin_amdgcn_readfirstlane(min((s + 2) * kRowBytes, last_so));
+                    asm volatile("" : "+s"(so2));  // computed here
+                }
+                if (m == 52) {
+                    so3 = __builtin_amdgcn_readfirstlane(min((s + 3) * kRowBytes, last_so));
+                    asm volatile("" : "+s"(so3));
+                }
+                if (m == 56) set_m0(0, SA);
             });
-            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-            wait_vm<NC>();  // this wave's copies of stage s+1 have landed (A(s+2) may be in flight)
-            barrier();      // ... and everyone's; both slots of stage s are free
+            // this wave's fragment reads are done and its copies of stage s+1
+            // have landed (A(s+2) may be in flight): vmcnt(8) lgkmcnt(0), in
+            // the builtin that the compiler's wait-count pass sees
+            static_assert(NC == 8, "vmcnt field below");
+            __builtin_amdgcn_s_waitcnt(0x0078);
+            barrier();  // ... and everyone's; both slots of stage s are free
             // slab 1: read slab 0 of stage s+1 (on the last stage the values go
-            // unused); copies: B(s+2) into slot sa, then A(s+3) into slot sb
+            // unused); copies: B(s+2) into slot SA, then A(s+3) into slot SB,
+            // one every four MFMAs, M0 set one MFMA ahead of each group of four
             slab(std::integral_constant<int, 1>(), [&](int m) {
-                if (m < FM) fa[0][m] = rd_m(m, 0, na);
-                if (m == 8 || m == 9) fb[m - 2] = rd_n(m - 2, 0, nb);
-                if ((m & 7) == 7 && m < 48) fb[m >> 3] = rd_n(m >> 3, 0, nb);
+                if (m < FM) fa[0][m] = rd_m(m, 0, NA);
+                if (m == 8 || m == 9) fb[m - 2] = rd_n(m - 2, 0, NB);
+                if ((m & 7) == 7 && m < 48) fb[m >> 3] = rd_n(m >> 3, 0, NB);
                 if ((m & 3) == 1) {
                     const int c = m >> 2;  // 0 .. 15
-                    if (c < NC) copy(1, c, t2, sa);
-                    else copy(0, c - NC, t3, sb);
+                    if (c < NC) copy(1, c, so2);
+                    else copy(0, c - NC, so3);
                 }
+                if (m == 14) set_m0(1, SA);
+                if (m == 30) set_m0(0, SB);
+                if (m == 46) set_m0(1, SB);
             });
-            slot0 = na;
+        };
+        for (int s = 0;;) {
+            stage(std::integral_constant<int, 0>(), s);
+            if (++s == nfull) break;
+            stage(std::integral_constant<int, 1>(), s);
+            if (++s == nfull) break;
+            stage(std::integral_constant<int, 2>(), s);
+            if (++s == nfull) break;
+            stage(std::integral_constant<int, 3>(), s);
+            if (++s == nfull) break;
+            stage(std::integral_constant<int, 4>(), s);
+            if (++s == nfull) break;
         }
         wait_vm<0>();  // no copy outlives the loop
     }
@@ -330,8 +420,6 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
         with_out_type(p.out_dtype, [&](auto out) {
             constexpr int OUT = decltype(out)::value;
             const int64_t ldd = p.ldd;
-            const int64_t lane_off = static_cast<int64_t>(n0 + wave_n * WTN + acc16_row(lane, 0)) * ldd +
-                                     (m0 + wave_m * WTM + acc16_col(lane));
             if (interior) {
                 const int64_t pair_off = static_cast<int64_t>(n0 + wave_n * WTN + 8 * (lane >> 5)) * ldd +
                                          (m0 + wave_m * WTM + (lane & 31));

@@ -88,3 +88,25 @@ def test_wide_kernels_keep_their_loops_free_of_spills(wide_asm):
         limit = 128 if epi & 8 else 24
         assert meta["private_segment_fixed_size"] <= limit, (name, meta)
     assert seen >= 32  # every wide instance of the six units
+
+
+def test_m16_copies_follow_their_own_m0_writes(wide_asm):
+    """The 16x16x32 kernel loads M0 once per group of four LDS-DMA copies with
+    its own `s_mov_b32 m0` + `s_nop 0`, and the copies read M0 without naming
+    it: so no other instruction may write or read M0 in those kernels, every
+    M0 write must carry its wait state, and no copy may come before the first
+    write."""
+    seen = 0
+    for name, body in re.findall(r"^(_ZN2tg20gemm_wide_m16_kernel\w+):[^\n]*\n(.*?)^\.Lfunc_end", wide_asm, re.S | re.M):
+        seen += 1
+        lines = [l.split(";")[0].strip() for l in body.split("\n")]
+        lines = [l for l in lines if l and not (l.startswith(".") and not l.startswith(".LBB"))]
+        writes = [i for i, l in enumerate(lines) if re.match(r"s_\w+\s+m0\s*,", l)]
+        assert writes, name
+        for i in writes:
+            assert lines[i].startswith("s_mov_b32 m0,") and lines[i + 1] == "s_nop 0", (name, lines[i:i + 2])
+        loads = [i for i, l in enumerate(lines) if l.startswith("buffer_load") and l.endswith(" lds")]
+        assert loads and loads[0] > writes[0], name
+        others = [l for l in lines if re.search(r"\bm0\b", l) and not l.startswith("s_mov_b32 m0,")]
+        assert not others, (name, others[:3])
+    assert seen == 4
