@@ -16,6 +16,7 @@
 #include <atomic>
 
 #include "kernel_table.h"
+#include "tile_math.h"
 #include "tile_gemm.h"
 
 namespace {
@@ -33,6 +34,7 @@ struct Batch {
     int64_t batch = 1, stride_a = 0, stride_b = 0, stride_d = 0;
 };
 constexpr int kCusPerGpu = 256;
+constexpr int64_t kMaxGridY = 65535;  // largest grid y dimension
 
 // Time model of the staging decision: seconds per unit of plan_cost per K
 // stage (fitted to the 256x256 streaming kernel on an 8192^3 bf16 product),
@@ -589,6 +591,8 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
             // never more than the workspace holds
             const int64_t fit = (M > 0 && N > 0 && (workspace || use_static)) ? workspace_bytes / (M * N * 4) : 0;
             if (s > fit) s = fit;
+            // a multiple of the XCD count, so that every split runs whole on one XCD
+            if (s >= tg::kXcdCount) s -= s % tg::kXcdCount;
         }
         splits = static_cast<int>(s < 1 ? 1 : s);
     }
@@ -645,8 +649,14 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
     a.batch_b_b = bytes_of(chunk, dtype);
     a.batch_d_b = M * N * 4;
     a.split_k = static_cast<int>(chunk);
+    // with a multiple of eight splits the grid is splits (x) by tiles (y),
+    // so that each XCD runs whole splits and reads only its own K ranges of
+    // A and B (no operand byte is fetched into more than one XCD's L2)
+    a.xcd_splits = (used % tg::kXcdCount == 0 && pl.grid <= kMaxGridY) ? 1 : 0;
     hipError_t err = hipSuccess;
-    if (K > 0)
+    if (K > 0 && a.xcd_splits)
+        err = tg_kernel(pl.kernel_id).launch(a, used, static_cast<int>(pl.grid), static_cast<hipStream_t>(stream));
+    else if (K > 0)
         err = tg_kernel(pl.kernel_id).launch(a, pl.grid, static_cast<int>(used), static_cast<hipStream_t>(stream));
     if (err == hipSuccess)
         err = tg_splitk_reduce(static_cast<const float*>(workspace), K > 0 ? static_cast<int>(used) : 0,

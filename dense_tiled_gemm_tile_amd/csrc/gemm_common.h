@@ -274,7 +274,19 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
 // along K: split s covers k in [s*split_k, min((s+1)*split_k, K)) and writes
 // its fp32 partial product to its own workspace matrix.
 __device__ __forceinline__ void select_batch(GemmArgs& p) {
-    const int64_t b = blockIdx.y;
+    // Split-K over a multiple of kXcdCount splits runs on a grid of splits
+    // (x) by tiles (y): workgroups go to the XCDs round-robin in x-major
+    // order, so split s runs whole on XCD s mod 8 and each XCD streams only
+    // its own K ranges of A and B through its L2; the tiles of a split follow
+    // the grouped walk.
+    int64_t b;
+    if (p.xcd_splits) {
+        b = blockIdx.x;
+        p.tile = blockIdx.y;
+    } else {
+        b = blockIdx.y;
+        p.tile = xcd_order(blockIdx.x, gridDim.x);
+    }
     p.A += b * p.batch_a_b;
     p.B += b * p.batch_b_b;
     p.D = static_cast<char*>(p.D) + b * p.batch_d_b;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kslice_kernel(GemmArgs p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
+    const TileCoord tile = grouped_tile(p.tile, p.tiles_m, p.tiles_n, GM);
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads, MINWAVES) void gemm_kernel(GemmArgs p) {
     const int wave = tid >> 6;
     const int wave_m = wave & 1, wave_n = wave >> 1;
 
-    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+    const TileCoord tile = grouped_tile(p.tile, p.tiles_m, p.tiles_n, p.group_m);
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 

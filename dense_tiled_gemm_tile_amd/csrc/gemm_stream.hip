@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, (WM * WN * KG) / 4) void gemm_st
     const int kg = wave / (WM * WN);                              // K group: slabs kg*QL .. kg*QL+QL-1 of each stage
     const int wave_m = wave_mn % WM, wave_n = wave_mn / WM;
 
-    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
+    const TileCoord tile = grouped_tile(p.tile, p.tiles_m, p.tiles_n, GM);
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 

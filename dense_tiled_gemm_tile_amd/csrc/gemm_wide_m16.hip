@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_m = wave % WM, wave_n = wave / WM;
 
-    const TileCoord tile = tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, GM);
+    const TileCoord tile = grouped_tile(p.tile, p.tiles_m, p.tiles_n, GM);
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 

@@ -28,10 +28,16 @@ struct TileCoord {
     int tm, tn;
 };
 
-TG_HD TileCoord tile_of(int wg, int nwg, int tiles_m, int tiles_n, int group_m) {
+// Position of workgroup wg of nwg (dispatched round-robin over the XCDs) in
+// an order where the workgroups of one XCD are consecutive.
+TG_HD int xcd_order(int wg, int nwg) {
     const int xcd = wg % kXcdCount, slot = wg / kXcdCount;
     const int base = nwg / kXcdCount, rem = nwg % kXcdCount;
-    const int t = (xcd < rem) ? xcd * (base + 1) + slot : rem * (base + 1) + (xcd - rem) * base + slot;
+    return (xcd < rem) ? xcd * (base + 1) + slot : rem * (base + 1) + (xcd - rem) * base + slot;
+}
+
+// Tile t of the grouped walk: group_m tile-rows at a time, column by column.
+TG_HD TileCoord grouped_tile(int t, int tiles_m, int tiles_n, int group_m) {
     const int per_group = group_m * tiles_n;
     const int g = t / per_group;
     const int first_m = g * group_m;
@@ -41,6 +47,10 @@ TG_HD TileCoord tile_of(int wg, int nwg, int tiles_m, int tiles_n, int group_m) 
     c.tm = first_m + within % gm;
     c.tn = within / gm;
     return c;
+}
+
+TG_HD TileCoord tile_of(int wg, int nwg, int tiles_m, int tiles_n, int group_m) {
+    return grouped_tile(xcd_order(wg, nwg), tiles_m, tiles_n, group_m);
 }
 
 // ---------------------------------------------------------------- LDS layout
