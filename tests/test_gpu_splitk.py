@@ -75,6 +75,22 @@ def test_every_instance_splitk(kid):
     check(D_st, A_st, B_st, M, N, K, -1.5, True, dt, exact=True)
 
 
+@pytest.mark.parametrize("kid", unpacked_instances())
+def test_every_instance_splitk_whole_splits_per_xcd(kid):
+    """Every instance on the split-K grid of splits by tiles (eight splits
+    used, each run whole on one XCD), the last split ragged, exact."""
+    info = tg.kernel_info(kid)
+    dt = dtype_name(info)
+    es = ELEM_SIZE[dt]
+    # 15 stages and a ragged tail: 8 splits of 2 stages, all used, the last short
+    M, N, K = info.block_m + 19, info.block_n + 3, 15 * info.block_k + 7
+    lda, ldb = strides_for_class(info.load_class, K, es)
+    _log(f"[split-K on XCDs] instance {kid} ({dt}): {M}x{N}x{K}, 8 splits")
+    A_st, B_st = si.int_operands(M, N, K, dt, seed=950 + kid, lda=lda, ldb=ldb)
+    D_st = run_splitk(A_st, B_st, M, N, K, 0.5, False, 8, ldd=M + 4, kernel_id=kid)
+    check(D_st, A_st, B_st, M, N, K, 0.5, False, dt, exact=True)
+
+
 @pytest.mark.parametrize("splits", [2, 4, 7, 16, 64])
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_splitk_random_within_bound(dt, splits):
