@@ -27,23 +27,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const float* src = ws + static_cast<int64_t>(n) * M + m;
     const int cnt = min(4, M - m);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if ((M & 3) == 0) {
-        // whole 16-byte groups (the workspace base is 16-byte aligned)
-        for (int s = 0; s < splits; ++s) {
-            const f32x4 q = *reinterpret_cast<const f32x4*>(src + s * plane);
-            acc[0] += q.x;
-            acc[1] += q.y;
-            acc[2] += q.z;
-            acc[3] += q.w;
-        }
-    } else {
-        for (int s = 0; s < splits; ++s) {
-            const float* q = src + s * plane;
+    // partials of split s at src + s * plane, added in split order; the loads
+    // of eight splits go out together (one round trip each batch, not one per
+    // split), the additions keep their order, so the sum has the same bits
+    constexpr int BATCH = 8;
+    auto load4 = [&](int s) {
+        f32x4 q = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float* x = src + s * plane;
+        if ((M & 3) == 0) {
+            q = *reinterpret_cast<const f32x4*>(x);  // whole 16-byte groups (16-byte aligned base)
+        } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (e < cnt) acc[e] += q[e];
+                if (e < cnt) q[e] = x[e];
         }
+        return q;
+    };
+    auto add4 = [&](const f32x4& q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += q[e];
+    };
+    int s = 0;
+    for (; s + BATCH <= splits; s += BATCH) {
+        f32x4 q[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) q[u] = load4(s + u);
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) add4(q[u]);
     }
+    for (; s < splits; ++s) add4(load4(s));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (e < cnt) {
