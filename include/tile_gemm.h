@@ -195,9 +195,10 @@ int tile_gemm_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu,
  * splits: 1 .. 256 requested (fewer are used when K has fewer stages; 1 is the
  * plain product), or 0 for an automatic choice (no split unless the output
  * has fewer tiles than the GPU has CUs and K has at least 64 stages; then
- * about two workgroups per CU, at least 16 stages per split, at most 64
- * splits, never more than `workspace_bytes` holds, and from 8 on a multiple
- * of 8, so that every split runs whole on one XCD); workspace: device
+ * about 32 stages per split but at least one workgroup per CU, at least 16
+ * stages per split, at most 64 splits, never more than `workspace_bytes`
+ * holds, and from 8 on a multiple of 8, so that every split runs whole on one
+ * XCD); workspace: device
  * memory of at least
  * tile_gemm_splitk_workspace_bytes(M, N, splits) bytes, 16-byte aligned, not
  * overlapping A, B or D, owned by the caller and reusable once the stream has
