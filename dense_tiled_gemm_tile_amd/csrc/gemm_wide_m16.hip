@@ -101,9 +101,10 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_m16_kernel(GemmArgs p) {
     // Copies 4g .. 4g + 3 of a wave share one LDS base in M0 and take the
     // immediate offsets 0, 1024, 2048 and 3072, which move the global address
     // by the same amount, so their per-lane offsets are lowered by it (copy j
-    // starts 8 j rows, at least 1024 j bytes, into the operand, so they stay
-    // non-negative).  Rows past the operand's end get an offset far beyond any
-    // range: with or without the immediate they load zeros.
+    // starts 8 j rows into the operand, and rows hold at least the 128 bytes
+    // of a full stage whenever copies run, so the offsets stay non-negative).
+    // Rows past the operand's end get an offset far beyond any range: with or
+    // without the immediate they load zeros.
     unsigned voff[2][NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {

@@ -21,7 +21,8 @@ struct GemmArgs {
     int tiles_m, tiles_n, group_m;
     int out_dtype;   // element type of D: TG_F32, TG_BF16 or TG_F16
     int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
-    int split_k;     // split-K partial products: K elements per split (grid y = split), 0 = off
+    int split_k;     // split-K partial products: K elements per split (grid y = split, or grid x
+                     // with xcd_splits), 0 = off
     int xcd_splits;  // split-K, 1 = grid x is the split and grid y the tile (see select_batch)
     int tile;        // set on the device by select_batch: the workgroup's tile in the grouped walk
     int epi;         // epilogue: 0 = alpha then optional ReLU per element, 1 = softmax over n
