@@ -140,6 +140,25 @@ def test_every_kernel_instance(kid):
     check_full(D_st, A_st, B_st, M, N, K, 0.75, False, dt)
 
 
+@pytest.mark.parametrize("kid", [67, 68, 69, 70])
+def test_wide_m16_ragged_long_k(kid):
+    """The 16x16x32 wide instances on a product with ragged M, N and K and 64
+    full stages: every unrolled stage of the K loop and each of its exits,
+    edge rows past M and N (copied as zeros), the register-staged K tail;
+    integer data exactly, random data within the bound (sampled)."""
+    info = tg.kernel_info(kid)
+    dt = dtype_name(info)
+    M, N, K = 4100, 2900, 4159
+    lda, ldb = K + 1, K + 9  # 16-byte aligned rows (4160 and 4168 elements)
+    _log(f"[m16 long K] instance {kid} ({dt}): {M}x{N}x{K}")
+    A_st, B_st = si.int_operands(M, N, K, dt, seed=1300 + kid, lda=lda, ldb=ldb)
+    D_st = run(A_st, B_st, M, N, K, -0.5, True, M + 4, kernel_id=kid)
+    check_sampled(D_st, A_st, B_st, M, N, K, -0.5, True, dt, 20000, seed=kid, exact=True)
+    A_st, B_st = si.operands(M, N, K, dt, "normal_invsqrtk", 1400 + kid, 1500 + kid, lda=lda, ldb=ldb)
+    D_st = run(A_st, B_st, M, N, K, 1.25, False, M, kernel_id=kid)
+    check_sampled(D_st, A_st, B_st, M, N, K, 1.25, False, dt, 20000, seed=100 + kid)
+
+
 EDGE_DIMS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
 
 
