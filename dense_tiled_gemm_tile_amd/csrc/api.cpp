@@ -155,14 +155,15 @@ bool d_lines_aligned(const void* D, int64_t ldd, int os, const Batch& bt) {
 // K-sliced kernel) only pay when most CUs would otherwise idle (at most half
 // as many tiles as CUs; measured: 512x512x16384 41 us against 64 us,
 // 1024x1024x4096 a tie, 1024^3 slower).
-// Instances marked power_bound (the 16x16x32 wide kernel) are only
-// considered when the product keeps every CU busy for a long K loop: their
-// MFMAs cost less energy, which pays when the power limit sets the clock
-// (8192^3 bf16: 1535 against 1445 TFLOP/s, 4096^3: 1414 against 1330), but
-// their loop keeps the MFMA pipe less busy at a given clock, which costs when
-// it does not (3072^3 on 144 CUs: 955 against 1036; 8192x8192x1024, 16
-// stages: 930 against 960).
-constexpr int kPowerBoundStages = 32;
+// Instances marked power_bound (the 16x16x32 wide kernel) need K loops of at
+// least 16 stages: their MFMAs cost less energy, which pays when the power
+// limit sets the clock, and since their loop issues its copies in groups
+// and knows its ring slots at compile time it also matches the 32x32x16
+// kernel at a given clock (one box: 8192x8192x1024 904 against 899
+// TFLOP/s, 4096x4096x1024 958-965 against 886-898, 3072^3 on 144 CUs
+// 986-1014 against 946-990, 6144x6144x1536 973 against 932); below 16
+// stages it is untested and the 32x32x16 kernel stays.
+constexpr int kPowerBoundStages = 16;
 int choose(int64_t M, int64_t N, int64_t batch, int64_t K, int dtype, int cls, int64_t row_stride,
            bool d_lines = true) {
     int best = -1;
@@ -170,9 +171,7 @@ int choose(int64_t M, int64_t N, int64_t batch, int64_t K, int dtype, int cls, i
     for (int i = 0; i < tg_kernel_count(); ++i) {
         const TgKernelDesc& k = tg_kernel(i);
         if (!usable(k, dtype, cls, row_stride)) continue;
-        if (k.power_bound && (cdiv(M, k.block_m) * cdiv(N, k.block_n) * batch < kCusPerGpu ||
-                              cdiv(K, k.block_k) < kPowerBoundStages))
-            continue;
+        if (k.power_bound && cdiv(K, k.block_k) < kPowerBoundStages) continue;
         if (k.k_slices > 1 && k.waves_m * k.waves_n == 1 &&
             cdiv(M, k.block_m) * cdiv(N, k.block_n) * batch > kCusPerGpu / 2)
             continue;

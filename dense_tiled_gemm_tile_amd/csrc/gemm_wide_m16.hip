@@ -504,8 +504,8 @@ static hipError_t launch_wide_m16(const GemmArgs& a, int64_t grid, int batch, hi
 // Instances: (id, dtype, group_m, EPI, eff%): 67/68 nontemporal D stores,
 // 69/70 plain stores and the fp32 LDS transpose (for D columns not on
 // 128-byte lines), as the 32x32x16 instances 0-3 of the wide kernel; they
-// weigh a little more than those, and the plan chooser only considers them
-// for products that keep the GPU at its power limit (see `choose`).
+// weigh a little more than those, and the plan chooser considers them for K
+// loops of at least 16 stages (see `choose`).
 #define TG_WIDE_M16_LIST(X)                \
     X(67, TG_BF16, 4, 1, 109)              \
     X(68, TG_F16, 4, 1, 109)               \

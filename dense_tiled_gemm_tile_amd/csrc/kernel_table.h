@@ -78,8 +78,8 @@ struct TgKernelDesc {
     int nt_store;            // 1: D is written with nontemporal stores
     int block_scales;        // 1: 8- or 4-bit instance that applies block scales (GemmArgs::scale_a/b)
     int k_slices;            // groups of waves that split K inside a workgroup, each over the whole tile (0: 1)
-    int power_bound;         // 1: only faster while the GPU runs at its power limit, i.e. with at least one
-                             // tile per CU and at least kPowerBoundStages K stages per tile
+    int power_bound;         // 1: considered only for K loops of at least kPowerBoundStages stages (the
+                             // 16x16x32 wide kernel; shorter loops are untested there)
 };
 
 // Element bits of an operand type (the 4- and 6-bit formats are packed).

@@ -374,11 +374,11 @@ def test_plan_choices_follow_the_kernel_trace_table():
     fastest in the kernel trace for each of these shapes (the K-sliced 64^2
     when at most half the CUs get a tile, small streaming 64^2 for 1024^2
     outputs, 128^2 at 2048^2, the wide kernel beyond: on 16x16x32 MFMAs when
-    every CU gets a tile and K has at least 32 stages, else on 32x32x16)."""
+    K has at least 16 stages, else on 32x32x16)."""
     A2, B2, D2 = 0x7F0000000000, 0x7F4000000000, 0x7F8000000000
     expect = {(1024, 1024, 1024): 14, (2048, 2048, 2048): 16, (512, 512, 16384): 48, (1024, 1024, 4096): 14,
-              (2048, 2048, 8192): 16, (4096, 4096, 1024): 0, (3072, 3072, 3072): 0, (4096, 4096, 4096): 67,
-              (8192, 8192, 1024): 0, (8192, 8192, 2048): 67}
+              (2048, 2048, 8192): 16, (4096, 4096, 1024): 67, (3072, 3072, 3072): 67, (4096, 4096, 4096): 67,
+              (8192, 8192, 1024): 67, (8192, 8192, 2048): 67, (4096, 4096, 512): 0, (8192, 8192, 768): 0}
     for (M, N, K), kid in expect.items():
         assert tg.query_plan(M, N, K, tg.BF16, A2, K, B2, K, D2, M).kernel_id == kid, (M, N, K)
 
