@@ -162,7 +162,8 @@ bool d_lines_aligned(const void* D, int64_t ldd, int os, const Batch& bt) {
 // kernel at a given clock (one box: 8192x8192x1024 904 against 899
 // TFLOP/s, 4096x4096x1024 958-965 against 886-898, 3072^3 on 144 CUs
 // 986-1014 against 946-990, 6144x6144x1536 973 against 932); below 16
-// stages it is untested and the 32x32x16 kernel stays.
+// stages the two trade places (8192x8192x512 604-606 against 630,
+// 4096x4096x512 651-653 against 629-647) and the 32x32x16 kernel stays.
 constexpr int kPowerBoundStages = 16;
 int choose(int64_t M, int64_t N, int64_t batch, int64_t K, int dtype, int cls, int64_t row_stride,
            bool d_lines = true) {

@@ -79,7 +79,7 @@ struct TgKernelDesc {
     int block_scales;        // 1: 8- or 4-bit instance that applies block scales (GemmArgs::scale_a/b)
     int k_slices;            // groups of waves that split K inside a workgroup, each over the whole tile (0: 1)
     int power_bound;         // 1: considered only for K loops of at least kPowerBoundStages stages (the
-                             // 16x16x32 wide kernel; shorter loops are untested there)
+                             // 16x16x32 wide kernel; below that it and the 32x32x16 one trade places)
 };
 
 // Element bits of an operand type (the 4- and 6-bit formats are packed).
