@@ -149,6 +149,22 @@ def test_short_workspace_is_refused():
     assert rc == -10
 
 
+@pytest.mark.parametrize("M,N,K,integer", [(384, 384, 32768, True), (1024, 512, 16384, False)])
+def test_automatic_splits_on_long_k(M, N, K, integer):
+    """splits = 0 on long-K shapes whose automatic count is a multiple of eight
+    (16 and 8 splits of about 32 stages, each split whole on one XCD): exact
+    on small-integer data, within the bound on random data."""
+    lda = ldb = K + 8
+    if integer:
+        A_st, B_st = si.int_operands(M, N, K, "bf16", seed=M + K, lda=lda, ldb=ldb)
+    else:
+        A_st, B_st = si.operands(M, N, K, "bf16", "normal_invsqrtk", M + 1, K + 1, lda=lda, ldb=ldb)
+    _log(f"[split-K auto long K] {M}x{N}x{K} integer={integer}")
+    D_st = run_splitk(A_st, B_st, M, N, K, 0.75, True, 0, ldd=M + 3)
+    ratio = check(D_st, A_st, B_st, M, N, K, 0.75, True, "bf16", exact=integer)
+    _log(f"[split-K auto long K] worst ratio {ratio:.3g}")
+
+
 def test_automatic_splits():
     """splits = 0: the tall-K workload is split (and stays within the bound), the
     1024^3 workload (already one tile per CU) is not (same bits as the plain
