@@ -36,6 +36,14 @@ struct Batch {
 constexpr int kCusPerGpu = 256;
 constexpr int64_t kMaxGridY = 65535;  // largest grid y dimension
 
+// Whether `count` matrices (a batch, or the splits of a split-K) of `tiles`
+// tiles each run on a grid of matrices by tiles, every matrix whole on one
+// XCD (select_batch): for a multiple of eight matrices, when the tiles fit
+// the grid's y dimension.
+int whole_matrices_per_xcd(int64_t count, int64_t tiles) {
+    return (count > 1 && count % tg::kXcdCount == 0 && tiles <= kMaxGridY) ? 1 : 0;
+}
+
 // Time model of the staging decision: seconds per unit of plan_cost per K
 // stage (fitted to the 256x256 streaming kernel on an 8192^3 bf16 product),
 // the HBM rate of the staging copy (measured: 286 MB read and written for
@@ -548,8 +556,14 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
     a.scale_b = sc.b;
     a.lds_a = sc.lds_a;
     a.lds_b = sc.lds_b;
-    const hipError_t err = tg_kernel(pl.kernel_id).launch(a, pl.grid, static_cast<int>(batch),
-                                                                static_cast<hipStream_t>(stream));
+    // a multiple of eight products runs on a grid of products (x) by tiles
+    // (y), each product whole on one XCD (one box: 32 x 256x256x4096 40.6
+    // against 76.9 us, 24 x 1024x1024x2048 98-99 against 112-113, 16 x 1024^3
+    // 39-40 against 44-45; the same bits)
+    a.xcd_batches = whole_matrices_per_xcd(batch, pl.grid);
+    const hipError_t err =
+        a.xcd_batches ? tg_kernel(pl.kernel_id).launch(a, batch, static_cast<int>(pl.grid), static_cast<hipStream_t>(stream))
+                      : tg_kernel(pl.kernel_id).launch(a, pl.grid, static_cast<int>(batch), static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
@@ -656,9 +670,9 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
     // with a multiple of eight splits the grid is splits (x) by tiles (y),
     // so that each XCD runs whole splits and reads only its own K ranges of
     // A and B (no operand byte is fetched into more than one XCD's L2)
-    a.xcd_splits = (used % tg::kXcdCount == 0 && pl.grid <= kMaxGridY) ? 1 : 0;
+    a.xcd_batches = whole_matrices_per_xcd(used, pl.grid);
     hipError_t err = hipSuccess;
-    if (K > 0 && a.xcd_splits)
+    if (K > 0 && a.xcd_batches)
         err = tg_kernel(pl.kernel_id).launch(a, used, static_cast<int>(pl.grid), static_cast<hipStream_t>(stream));
     else if (K > 0)
         err = tg_kernel(pl.kernel_id).launch(a, pl.grid, static_cast<int>(used), static_cast<hipStream_t>(stream));

@@ -22,8 +22,8 @@ struct GemmArgs {
     int out_dtype;   // element type of D: TG_F32, TG_BF16 or TG_F16
     int64_t batch_a_b, batch_b_b, batch_d_b;  // byte distance between consecutive matrices (grid y)
     int split_k;     // split-K partial products: K elements per split (grid y = split, or grid x
-                     // with xcd_splits), 0 = off
-    int xcd_splits;  // split-K, 1 = grid x is the split and grid y the tile (see select_batch)
+                     // with xcd_batches), 0 = off
+    int xcd_batches; // 1: grid x is the matrix (or split) and grid y the tile (see select_batch)
     int tile;        // set on the device by select_batch: the workgroup's tile in the grouped walk
     int epi;         // epilogue: 0 = alpha then optional ReLU per element, 1 = softmax over n
     // 8- and 4-bit operands: block-scale exponents (2^(e-127) per 32 consecutive k),

@@ -95,16 +95,18 @@ def _strides(info_class, M, N, K, es):
     return lda, ldb
 
 
+@pytest.mark.parametrize("batch", [3, 8])
 @pytest.mark.parametrize("kid", unpacked_instances())
-def test_every_instance_batched(kid):
-    """Three products with gaps between them, every instance forced: exact on
-    integer data with alpha < 0 and ReLU."""
+def test_every_instance_batched(kid, batch):
+    """Products with gaps between them, every instance forced: exact on
+    integer data with alpha < 0 and ReLU.  Eight products run on the grid of
+    products by tiles (each product whole on one XCD), three on the other."""
     info = tg.kernel_info(kid)
     dt = dtype_name(info)
     es = ELEM_SIZE[dt]
     M, N, K = info.block_m + 21, info.block_n + 45, 2 * info.block_k + 5
     lda, ldb = strides_for_class(info.load_class, K, es)
-    batch, ldd = 3, M + 3
+    ldd = M + 3
     parts_a, parts_b = [], []
     for b in range(batch):
         a, bb = si.int_operands(M, N, K, dt, seed=700 + 10 * kid + b, lda=lda, ldb=ldb)
@@ -113,7 +115,7 @@ def test_every_instance_batched(kid):
     A_all = stacked(parts_a, 1, lda, dt)
     B_all = stacked(parts_b, 2, ldb, dt)
     sa, sb, sd = (M + 1) * lda, (N + 2) * ldb, N * ldd + 40
-    _log(f"[batched] instance {kid} ({dt}): 3 x {M}x{N}x{K}")
+    _log(f"[batched] instance {kid} ({dt}): {batch} x {M}x{N}x{K}")
     D_all = run_batched(A_all, B_all, M, N, K, lda, ldb, ldd, sa, sb, sd, batch, -1.5, True, kernel_id=kid)
     check_batch(D_all, A_all, B_all, M, N, K, lda, ldb, ldd, sa, sb, sd, batch, -1.5, True, dt, exact=True)
 
