@@ -37,11 +37,15 @@ constexpr int kCusPerGpu = 256;
 constexpr int64_t kMaxGridY = 65535;  // largest grid y dimension
 
 // Whether `count` matrices (a batch, or the splits of a split-K) of `tiles`
-// tiles each run on a grid of matrices by tiles, every matrix whole on one
-// XCD (select_batch): for a multiple of eight matrices, when the tiles fit
-// the grid's y dimension.
+// tiles each run on a grid of matrices by tiles (select_batch): matrix b's
+// tiles then go to 8 / gcd(count, 8) of the XCDs (one for a multiple of
+// eight), so fewer L2s fetch its operands.  For an even count from six on,
+// when the tiles fit the grid's y dimension (one box, same bits: 12 x
+// 512x512x2048 22.4 against 28.1 us, 20 x 256x256x4096 32.7 against 53.9,
+// 12 x 1024^3 32.5 against 35.5, 6 x 1024^3 25.9 against 26.9; 2 and 4
+// products of 1024^3 or 2048^3 neither gained nor lost).
 int whole_matrices_per_xcd(int64_t count, int64_t tiles) {
-    return (count > 1 && count % tg::kXcdCount == 0 && tiles <= kMaxGridY) ? 1 : 0;
+    return (count >= 6 && count % 2 == 0 && tiles <= kMaxGridY) ? 1 : 0;
 }
 
 // Time model of the staging decision: seconds per unit of plan_cost per K
@@ -556,10 +560,10 @@ int launch_batched(int64_t M, int64_t N, int64_t K, float alpha, int relu, const
     a.scale_b = sc.b;
     a.lds_a = sc.lds_a;
     a.lds_b = sc.lds_b;
-    // a multiple of eight products runs on a grid of products (x) by tiles
-    // (y), each product whole on one XCD (one box: 32 x 256x256x4096 40.6
-    // against 76.9 us, 24 x 1024x1024x2048 98-99 against 112-113, 16 x 1024^3
-    // 39-40 against 44-45; the same bits)
+    // an even number of products from six on runs on a grid of products (x)
+    // by tiles (y); with a multiple of eight each product is whole on one XCD
+    // (one box: 32 x 256x256x4096 40.6 against 76.9 us, 24 x 1024x1024x2048
+    // 98-99 against 112-113, 16 x 1024^3 39-40 against 44-45; the same bits)
     a.xcd_batches = whole_matrices_per_xcd(batch, pl.grid);
     const hipError_t err =
         a.xcd_batches ? tg_kernel(pl.kernel_id).launch(a, batch, static_cast<int>(pl.grid), static_cast<hipStream_t>(stream))
@@ -667,9 +671,9 @@ int splitk_impl(int64_t M, int64_t N, int64_t K, float alpha, int relu, const vo
     a.batch_b_b = bytes_of(chunk, dtype);
     a.batch_d_b = M * N * 4;
     a.split_k = static_cast<int>(chunk);
-    // with a multiple of eight splits the grid is splits (x) by tiles (y),
-    // so that each XCD runs whole splits and reads only its own K ranges of
-    // A and B (no operand byte is fetched into more than one XCD's L2)
+    // with an even number of splits from six on the grid is splits (x) by
+    // tiles (y); with a multiple of eight each XCD runs whole splits and reads
+    // only its own K ranges of A and B
     a.xcd_batches = whole_matrices_per_xcd(used, pl.grid);
     hipError_t err = hipSuccess;
     if (K > 0 && a.xcd_batches)

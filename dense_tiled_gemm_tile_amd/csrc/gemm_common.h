@@ -274,11 +274,12 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
 // along K: split s covers k in [s*split_k, min((s+1)*split_k, K)) and writes
 // its fp32 partial product to its own workspace matrix.
 __device__ __forceinline__ void select_batch(GemmArgs& p) {
-    // A batch (or split-K) of a multiple of kXcdCount matrices runs on a grid
-    // of matrices (x) by tiles (y): workgroups go to the XCDs round-robin in
-    // x-major order, so matrix b runs whole on XCD b mod 8 and no operand byte
-    // is fetched into more than one XCD's L2; the tiles of a matrix follow the
-    // grouped walk.
+    // A batch (or split-K) of an even number of matrices from six on may run
+    // on a grid of matrices (x) by tiles (y): workgroups go to the XCDs
+    // round-robin in x-major order, so matrix b's tiles land on 8 / gcd(count,
+    // 8) XCDs (for a multiple of kXcdCount, matrix b runs whole on XCD b mod 8
+    // and no operand byte is fetched into more than one XCD's L2); the tiles
+    // of a matrix follow the grouped walk.
     int64_t b;
     if (p.xcd_batches) {
         b = blockIdx.x;

@@ -95,12 +95,13 @@ def _strides(info_class, M, N, K, es):
     return lda, ldb
 
 
-@pytest.mark.parametrize("batch", [3, 8])
+@pytest.mark.parametrize("batch", [3, 6, 8])
 @pytest.mark.parametrize("kid", unpacked_instances())
 def test_every_instance_batched(kid, batch):
     """Products with gaps between them, every instance forced: exact on
-    integer data with alpha < 0 and ReLU.  Eight products run on the grid of
-    products by tiles (each product whole on one XCD), three on the other."""
+    integer data with alpha < 0 and ReLU.  Six and eight products run on the
+    grid of products by tiles (eight: each product whole on one XCD), three
+    on the other."""
     info = tg.kernel_info(kid)
     dt = dtype_name(info)
     es = ELEM_SIZE[dt]

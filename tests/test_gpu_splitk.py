@@ -91,7 +91,7 @@ def test_every_instance_splitk_whole_splits_per_xcd(kid):
     check(D_st, A_st, B_st, M, N, K, 0.5, False, dt, exact=True)
 
 
-@pytest.mark.parametrize("splits", [2, 4, 7, 16, 64])
+@pytest.mark.parametrize("splits", [2, 4, 6, 7, 16, 64])
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_splitk_random_within_bound(dt, splits):
     M, N, K = 300, 200, 2011
